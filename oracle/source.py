@@ -1,0 +1,38 @@
+"""Host-side fp64 view of seeded decode inputs, for the oracle.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring). Converts the input tensors
+to fp64 numpy arrays (an exact widening of bf16 / fp16 / fp32) and fetches raw
+K/V rows on demand, so full-size caches never have to be widened whole.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def _f64(t):
+    return None if t is None else t.detach().to("cpu").double().numpy()
+
+
+class HostSource:
+    """Inputs of one decode step as the oracle reads them.
+
+    ``inputs`` maps names (q, K, V, Kg, Vg, Kmg, P, Kp) to tensors on any
+    device. Small arrays are widened once; K and V rows are gathered per call.
+    """
+
+    def __init__(self, inputs: dict):
+        self._K = inputs["K"]
+        self._V = inputs["V"]
+        self.q = _f64(inputs["q"])
+        self.Kg = _f64(inputs.get("Kg"))
+        self.Vg = _f64(inputs.get("Vg"))
+        self.Kmg = _f64(inputs.get("Kmg"))
+        self.P = _f64(inputs.get("P"))
+        self.Kp = _f64(inputs.get("Kp"))
+
+    def kv_rows(self, bk: int, g: int, rows: np.ndarray):
+        idx = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=self._K.device)
+        Kr = self._K[bk, g].index_select(0, idx)
+        Vr = self._V[bk, g].index_select(0, idx)
+        return _f64(Kr), _f64(Vr)

@@ -1,0 +1,264 @@
+"""Plain fp64 CPU oracle of query-adaptive sparse decode attention.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline leg may import this module; the decode library never does.
+
+Sources (cited by page title and section):
+
+* [SSA] AI Trends summary of "SSA / H-SSA" (aitrends.kr/articles/69798), sections
+  "방법론" (method) and "기술 상세" (technical detail): relevance of chunk m to
+  query q_t is ``s_{t,m} = q_t^T k_{g_m}``; the top-k chunks form I_t; K/V_hybrid
+  is the union of the gist KV and raw KV of the chunks in I_t; standard attention
+  runs over it. Section "핵심 기여" (contributions): H-SSA scores meta-gists
+  first, keeps candidate segments, re-scores the gists inside them; decode
+  builds a compact list of selected key indices, runs split-K partial attention
+  and combines. Glossary "Grouped-Query Attention": per-head top-k, then the
+  union over the group so every KV block is loaded once.
+* [RTP] Review of "Full Attention Strikes Back" (blog.secrett2633.cloud),
+  section "1. Key Terms & Definitions": retrieval heads keep the full KV cache; a
+  16-dim low-dimensional projection scores token importance; dynamic top-p picks
+  a per-query variable budget that secures attention mass instead of a fixed k.
+* [HiLS] Review of "Hierarchical Sparse Attention Done Right", section 1: a
+  landmark token's key summarises its chunk; GQA extended to group-wise chunk
+  selection.
+
+Readings where the pages are silent (each is a fixed choice of this oracle):
+
+* Order: scores sorted descending, equal scores by lower index first, so every
+  selection is unique.
+* Top-p: the minimal prefix of that order whose softmax mass (logits
+  ``select_scale * s`` over ALL entries) reaches ``p * Z``; p >= 1 selects all.
+* Forced chunks (sink / most recent) and the local-head window are added to the
+  group union; they are not part of a head's own top-p set.
+* Two-level: the top ``k_seg`` segments by meta score give candidate chunks in
+  ascending order; the top ``k`` candidates by chunk score are kept in total.
+* Hybrid context: the raw tokens of the selected chunks plus, when enabled, the
+  summary K/V of those same chunks. Every head of a GQA group attends to the
+  group union.
+* Proxy scoring: the same d x r projection maps the query and the keys;
+  ``q_p = q P`` in fp64, score ``q_p . k_p``.
+
+Arithmetic: inputs arrive as fp64 (their bf16 / fp16 / fp32 values are exact in
+fp64). Scores are summed in index order, one rounding per multiply and per
+add. Attention uses fp64 matmuls and max-subtracted exponentials.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TOPK, TOPP, HIER, PROXY_TOPP = "topk", "topp", "hier", "proxy"
+
+
+# --------------------------------------------------------------------------- scores
+def chunk_scores(q: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """[SSA] method: ``s_m = q^T k_{g_m}`` for every summary key row of ``keys``.
+
+    ``q`` is [d], ``keys`` is [M, d]; the sum runs over i = 0..d-1 in order.
+    """
+    acc = np.zeros(keys.shape[0], dtype=np.float64)
+    for i in range(q.shape[0]):
+        acc = acc + q[i] * keys[:, i]
+    return acc
+
+
+def proxy_query(q: np.ndarray, P: np.ndarray) -> np.ndarray:
+    """[RTP] key terms: the query's low-dimensional projection ``q_p = q P`` ([d] x [d, r])."""
+    acc = np.zeros(P.shape[1], dtype=np.float64)
+    for i in range(q.shape[0]):
+        acc = acc + q[i] * P[i, :]
+    return acc
+
+
+def proxy_scores(qp: np.ndarray, Kp: np.ndarray) -> np.ndarray:
+    """[RTP] key terms: token importance ``s_t = q_p . k_p[t]`` over the r proxy dims, in order."""
+    acc = np.zeros(Kp.shape[0], dtype=np.float64)
+    for j in range(qp.shape[0]):
+        acc = acc + qp[j] * Kp[:, j]
+    return acc
+
+
+# ------------------------------------------------------------------------ selection
+def order_desc(s: np.ndarray) -> np.ndarray:
+    """Positions sorted by score descending; equal scores by lower position first."""
+    return np.lexsort((np.arange(s.shape[0]), -s))
+
+
+def select_top_k(s: np.ndarray, k: int) -> np.ndarray:
+    """[SSA] method: the k highest-scoring entries (all of them when k >= len), ascending."""
+    if k <= 0:
+        raise ValueError("top-k needs k >= 1")
+    return np.sort(order_desc(s)[: min(k, s.shape[0])])
+
+
+def select_top_p(s: np.ndarray, p: float, scale: float):
+    """[RTP] dynamic top-p: minimal descending prefix whose softmax mass reaches ``p``.
+
+    Returns (ascending selection, margin). ``margin`` is the distance of the
+    decision from the threshold, ``min(|c_n - pZ|, |c_{n-1} - pZ|) / Z``, where
+    ``c_j`` is the mass of the first j entries of the order.
+    """
+    n = s.shape[0]
+    if not p > 0:
+        raise ValueError("top-p needs p > 0")
+    if p >= 1.0:
+        return np.arange(n), math.inf
+    ell = scale * s
+    mass = np.exp(ell - ell.max())
+    Z = math.fsum(mass.tolist())
+    target = p * Z
+    o = order_desc(s)
+    c = np.cumsum(mass[o])
+    hit = np.nonzero(c >= target)[0]
+    n_sel = int(hit[0]) + 1 if hit.size else n
+    above = abs(c[n_sel - 1] - target)
+    below = abs(c[n_sel - 2] - target) if n_sel >= 2 else abs(target)
+    return np.sort(o[:n_sel]), min(above, below) / Z
+
+
+def candidates(segments: np.ndarray, seg_size: int) -> np.ndarray:
+    """[SSA] H-SSA: the chunks under the kept segments, ascending."""
+    return (np.sort(segments)[:, None] * seg_size + np.arange(seg_size)[None, :]).ravel()
+
+
+def select_two_level(s_seg: np.ndarray, score_chunks, k_seg: int, k: int, seg_size: int):
+    """[SSA] H-SSA coarse-to-fine: top-k_seg segments, then top-k of their chunks.
+
+    ``score_chunks(chunk_ids)`` returns the chunk scores of the candidates.
+    Returns (selected chunk ids ascending, kept segments, candidates, candidate scores).
+    """
+    segs = select_top_k(s_seg, k_seg)
+    cand = candidates(segs, seg_size)
+    s2 = score_chunks(cand)
+    pick = select_top_k(s2, k)
+    return cand[pick], segs, cand, s2
+
+
+def edge_entries(n: int, first: int, last: int) -> np.ndarray:
+    """Entries [0, first) and [n - last, n): forced sink / recent chunks, or a local
+    head's sink tokens plus sliding window."""
+    a = np.arange(min(first, n))
+    b = np.arange(max(0, n - last), n)
+    return np.union1d(a, b)
+
+
+def group_union(sets) -> np.ndarray:
+    """[SSA] glossary GQA / [HiLS] section 1: union of the group's per-head selections."""
+    u = np.zeros(0, dtype=np.int64)
+    for s in sets:
+        u = np.union1d(u, s)
+    return u.astype(np.int64)
+
+
+# ------------------------------------------------------------------------ attention
+def attend(qh: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, scale: float):
+    """Exact softmax attention of queries ``qh`` [G, d] over rows ``Kc, Vc`` [T, d].
+
+    Returns (o [G, d], lse [G]) with ``lse = log sum_j exp(scale * q . k_j)``.
+    """
+    logits = scale * (Kc @ qh.T)                  # [T, G]
+    mx = logits.max(axis=0)
+    e = np.exp(logits - mx[None, :])
+    L = e.sum(axis=0)
+    o = (e.T @ Vc) / L[:, None]
+    return o, mx + np.log(L)
+
+
+def lse_combine(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """[SSA] decode kernel, combine stage: merge split partials (o_s, lse_s).
+
+    ``LSE = log sum_s exp(lse_s)``, ``o = sum_s exp(lse_s - LSE) o_s``.
+    """
+    mx = lse_parts.max(axis=0)
+    w = np.exp(lse_parts - mx[None, ...])
+    L = w.sum(axis=0)
+    o = (w[..., None] * o_parts).sum(axis=0) / L[..., None]
+    return o, mx + np.log(L)
+
+
+def hybrid_rows(U: np.ndarray, chunk_size: int) -> np.ndarray:
+    """[SSA] technical detail: raw token positions of the selected chunks, ascending."""
+    U = np.asarray(U, dtype=np.int64)
+    return (U[:, None] * chunk_size + np.arange(chunk_size)[None, :]).ravel()
+
+
+# ------------------------------------------------------------------------ the step
+def select_group(w, src, b: int, g: int) -> dict:
+    """Per-head selections and the group union for sequence b, KV group g."""
+    G = w.n_q_heads // w.n_kv_heads
+    bk = b if w.kv_batch > 1 else 0
+    n_ent = w.n_ctx // w.chunk_size
+    res = {"heads": {}, "scores": {}, "margin": math.inf, "segments": {}, "cand": {}}
+    if g in tuple(w.local_kv_heads):
+        res["union"] = edge_entries(n_ent, w.sink, w.window)
+        return res
+    per_head = []
+    for j in range(G):
+        h = g * G + j
+        q = src.q[b, h]
+        if w.mode == TOPK:
+            s = chunk_scores(q, src.Kg[bk, g])
+            sel = select_top_k(s, w.top_k)
+        elif w.mode == TOPP:
+            s = chunk_scores(q, src.Kg[bk, g])
+            sel, mg = select_top_p(s, w.top_p, w.select_scale)
+            res["margin"] = min(res["margin"], mg)
+        elif w.mode == HIER:
+            s = chunk_scores(q, src.Kmg[bk, g])
+            sel, segs, cand, s2 = select_two_level(
+                s, lambda c: chunk_scores(q, src.Kg[bk, g][c]), w.top_k_seg, w.top_k, w.seg_size)
+            res["segments"][h] = segs
+            res["cand"][h] = (cand, s2)
+        elif w.mode == PROXY_TOPP:
+            qp = proxy_query(q, src.P[g])
+            s = proxy_scores(qp, src.Kp[bk, g])
+            sel, mg = select_top_p(s, w.top_p, w.select_scale)
+            res["margin"] = min(res["margin"], mg)
+        else:
+            raise ValueError(w.mode)
+        res["heads"][h] = sel
+        res["scores"][h] = s
+        per_head.append(sel)
+    U = group_union(per_head)
+    if w.keep_first or w.keep_last:
+        U = group_union([U, edge_entries(n_ent, w.keep_first, w.keep_last)])
+    res["union"] = U
+    return res
+
+
+def attend_group(w, src, b: int, g: int, U: np.ndarray):
+    """Every query head of group g attends to the hybrid context of union U."""
+    G = w.n_q_heads // w.n_kv_heads
+    bk = b if w.kv_batch > 1 else 0
+    rows = hybrid_rows(U, w.chunk_size)
+    Kc, Vc = src.kv_rows(bk, g, rows)
+    if w.attend_summary and w.mode != PROXY_TOPP:
+        Kc = np.concatenate([Kc, src.Kg[bk, g][U]], axis=0)
+        Vc = np.concatenate([Vc, src.Vg[bk, g][U]], axis=0)
+    qh = src.q[b, g * G:(g + 1) * G]
+    return attend(qh, Kc, Vc, w.softmax_scale)
+
+
+def decode_step(w, src, groups=None, attend_groups=None) -> dict:
+    """One decode step: selections for ``groups`` (default all (b, g)), attention
+    for ``attend_groups`` (default the same). Returns per-(b, g) results and
+    output / lse arrays (NaN where not computed)."""
+    B, Hq, Hk, d = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    G = Hq // Hk
+    if groups is None:
+        groups = [(b, g) for b in range(B) for g in range(Hk)]
+    if attend_groups is None:
+        attend_groups = groups
+    out = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    sel = {}
+    for b, g in groups:
+        sel[(b, g)] = select_group(w, src, b, g)
+    for b, g in attend_groups:
+        if (b, g) not in sel:
+            sel[(b, g)] = select_group(w, src, b, g)
+        o, l = attend_group(w, src, b, g, sel[(b, g)]["union"])
+        out[b, g * G:(g + 1) * G] = o
+        lse[b, g * G:(g + 1) * G] = l
+    return {"sel": sel, "out": out, "lse": lse}

@@ -1,0 +1,128 @@
+"""Named decode workloads: shapes and selection parameters.
+
+Five full-size workloads follow the shapes of the models the pages evaluate on
+(Qwen2-7B-style SSA decode, a Llama-3.1-8B-style 128K top-p decode, H-SSA
+two-level routing at 512K, and RTPurbo-style mixed heads at 1M tokens), plus a
+tiny fp32 case. Each has a reduced twin with the same structure that the fp64
+oracle finishes in seconds; the twins span several attention tiles and end on
+ragged tails.
+
+This module holds parameters only -- no arithmetic of the method.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+TOPK = "topk"          # per-head top-k over chunk summary scores
+TOPP = "topp"          # per-head dynamic top-p over the softmax of chunk scores
+HIER = "hier"          # two-level: top-k segments (meta summaries) -> top-k chunks
+PROXY_TOPP = "proxy"   # per-token top-p on rank-r proxy-key scores; local heads
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int                 # decode queries (one per sequence)
+    kv_batch: int              # distinct KV caches; 1 = every query reads one cache
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    n_ctx: int                 # tokens in the cache
+    chunk_size: int            # tokens per chunk; 1 = token-level selection
+    dtype: str                 # "f32" | "bf16" (q, K, V, summary K/V)
+    mode: str
+    top_k: int = 0
+    top_k_seg: int = 0
+    seg_size: int = 0          # summaries per meta-summary (HIER)
+    top_p: float = 1.0
+    select_scale: float = 1.0  # logit scale of the top-p softmax
+    softmax_scale: float = 1.0
+    keep_first: int = 0        # forced leading chunks (attention sink)
+    keep_last: int = 0         # forced trailing chunks (most recent)
+    route_dim: int = 0         # proxy-key rank (PROXY_TOPP)
+    local_kv_heads: tuple = () # KV heads that run sink + sliding window
+    sink: int = 0
+    window: int = 0
+    attend_summary: bool = True
+    plant: str = ""            # synthetic structure recipe, see synth.gen
+    plants_per_head: int = 0
+    zipf_s: float = 0.0
+    split_entries: int = 0     # list entries per split-K work item (0 = library default)
+    seed: int = 0
+
+    # derived -------------------------------------------------------------
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def n_chunks(self) -> int:
+        return self.n_ctx // self.chunk_size
+
+    @property
+    def n_segments(self) -> int:
+        return self.n_chunks // self.seg_size if self.seg_size else 0
+
+    @property
+    def n_entries(self) -> int:
+        """Length of the per-group selection domain: chunks, or tokens at chunk_size 1."""
+        return self.n_chunks
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+def _inv_sqrt(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+C1 = Workload(
+    name="c1_tiny_f32", batch=16, kv_batch=1, n_q_heads=4, n_kv_heads=1, head_dim=64,
+    n_ctx=2048, chunk_size=64, dtype="f32", mode=TOPK, top_k=4,
+    softmax_scale=_inv_sqrt(64), select_scale=_inv_sqrt(64), seed=1)
+
+C2 = Workload(
+    name="c2_ssa_qwen2_7b_32k", batch=8, kv_batch=8, n_q_heads=28, n_kv_heads=4, head_dim=128,
+    n_ctx=32768, chunk_size=16, dtype="bf16", mode=TOPK, top_k=128,
+    softmax_scale=_inv_sqrt(128), select_scale=_inv_sqrt(128),
+    plant="gist_align", plants_per_head=8, seed=2)
+
+C3 = Workload(
+    name="c3_topp_llama31_8b_128k", batch=4, kv_batch=4, n_q_heads=32, n_kv_heads=8,
+    head_dim=128, n_ctx=131072, chunk_size=64, dtype="bf16", mode=TOPP, top_p=0.95,
+    softmax_scale=_inv_sqrt(128), select_scale=_inv_sqrt(128), keep_first=1, keep_last=1,
+    plant="zipf", zipf_s=1.1, seed=3)
+
+C4 = Workload(
+    name="c4_hssa_512k", batch=1, kv_batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+    n_ctx=524288, chunk_size=32, dtype="bf16", mode=HIER, top_k_seg=16, top_k=64, seg_size=32,
+    softmax_scale=_inv_sqrt(128), select_scale=_inv_sqrt(128),
+    plant="needles", plants_per_head=4, seed=4)
+
+C5 = Workload(
+    name="c5_rtpurbo_1m", batch=1, kv_batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+    n_ctx=1048576, chunk_size=1, dtype="bf16", mode=PROXY_TOPP, top_p=0.9, route_dim=16,
+    softmax_scale=_inv_sqrt(128), select_scale=1.0 / (16 * math.sqrt(128)),
+    local_kv_heads=(4, 5, 6, 7), sink=64, window=4096, attend_summary=False, seed=5)
+
+FULL = {w.name: w for w in (C1, C2, C3, C4, C5)}
+
+# Reduced twins: same structure, sizes the oracle finishes in seconds.
+C2S = replace(C2, name="c2s", batch=2, kv_batch=2, n_ctx=4096, top_k=32, seed=12)
+C3S = replace(C3, name="c3s", batch=2, kv_batch=2, n_ctx=16384, seed=13)
+C4S = replace(C4, name="c4s", n_ctx=32768, top_k_seg=4, top_k=16, seed=14)
+C5S = replace(C5, name="c5s", n_ctx=65536, window=1000, seed=15)
+C1S = replace(C1, name="c1s", seed=11)
+
+SMALL = {w.name: w for w in (C1S, C2S, C3S, C4S, C5S)}
+
+ALL = {**FULL, **SMALL}
+
+# The workload the throughput metric is quoted on: 128K context, top-p decode.
+BENCH = C3
+
+
+def get(name: str) -> Workload:
+    return ALL[name]
