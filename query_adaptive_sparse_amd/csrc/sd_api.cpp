@@ -1,0 +1,277 @@
+// Host side of the C ABI: argument checks, workspace planning, dispatch.
+// Every check runs before anything is enqueued; nothing here touches the GPU
+// except through the launchers in sd_kernels.hip.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "sd_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sd_status fail(sd_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sd_status ok() {
+  g_err[0] = 0;
+  return SD_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+sd_status check_cfg(const sd_config& c) {
+  if (c.batch < 1) return fail(SD_EINVAL, "batch must be >= 1 (got %d)", c.batch);
+  if (c.kv_batch != 1 && c.kv_batch != c.batch)
+    return fail(SD_EINVAL, "kv_batch must be 1 or batch (got %d, batch %d)", c.kv_batch, c.batch);
+  if (c.n_q_heads < 1 || c.n_kv_heads < 1 || c.n_q_heads % c.n_kv_heads)
+    return fail(SD_EINVAL, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", c.n_q_heads,
+                c.n_kv_heads);
+  if (c.n_kv_heads > sd::kMaxKvHeads)
+    return fail(SD_EUNSUPPORTED, "n_kv_heads > %d", sd::kMaxKvHeads);
+  if (c.n_q_heads / c.n_kv_heads > sd::kMaxGroup)
+    return fail(SD_EUNSUPPORTED, "group size %d > %d", c.n_q_heads / c.n_kv_heads, sd::kMaxGroup);
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(SD_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c.head_dim);
+  if (c.kv_dtype != SD_F32 && c.kv_dtype != SD_BF16) return fail(SD_EINVAL, "kv_dtype %d unknown", c.kv_dtype);
+  if (c.n_ctx < 1 || c.n_ctx >= (int64_t(1) << 31)) return fail(SD_EINVAL, "n_ctx out of range (%lld)", (long long)c.n_ctx);
+  if (c.chunk_size < 1 || c.n_ctx % c.chunk_size)
+    return fail(SD_EINVAL, "chunk_size %d must be >= 1 and divide n_ctx %lld", c.chunk_size, (long long)c.n_ctx);
+  if (c.route != SD_ROUTE_SUMMARY && c.route != SD_ROUTE_PROXY) return fail(SD_EINVAL, "route %d unknown", c.route);
+  if (c.mode != SD_TOPK && c.mode != SD_TOPP && c.mode != SD_HIER_TOPK) return fail(SD_EINVAL, "mode %d unknown", c.mode);
+  if (c.route == SD_ROUTE_PROXY) {
+    if (c.chunk_size != 1) return fail(SD_EINVAL, "proxy routing scores tokens: chunk_size must be 1");
+    if (c.route_dim != 16) return fail(SD_EUNSUPPORTED, "route_dim must be 16 (got %d)", c.route_dim);
+    if (c.mode == SD_HIER_TOPK) return fail(SD_EUNSUPPORTED, "two-level selection routes on summary keys");
+    if (c.attend_summary) return fail(SD_EINVAL, "token-level routing has no summary K/V to attend");
+  }
+  if (c.mode == SD_TOPK || c.mode == SD_HIER_TOPK) {
+    if (c.top_k < 1) return fail(SD_EINVAL, "top_k must be >= 1 (got %d)", c.top_k);
+  }
+  if (c.mode == SD_TOPP) {
+    if (!(c.top_p > 0.0) || !(c.top_p <= 1.0)) return fail(SD_EINVAL, "top_p must be in (0, 1] (got %g)", c.top_p);
+    if (!(c.select_scale > 0.0) || !std::isfinite(c.select_scale))
+      return fail(SD_EINVAL, "select_scale must be finite and > 0 (got %g)", c.select_scale);
+  }
+  if (c.mode == SD_HIER_TOPK) {
+    const int64_t M = c.n_ctx / c.chunk_size;
+    if (c.seg_size < 1 || M % c.seg_size) return fail(SD_EINVAL, "seg_size %d must divide the %lld chunks", c.seg_size, (long long)M);
+    if (c.top_k_seg < 1) return fail(SD_EINVAL, "top_k_seg must be >= 1");
+    if (M / c.seg_size > sd::kSmallRowMax) return fail(SD_EUNSUPPORTED, "more than %d segments", sd::kSmallRowMax);
+    if (M > int64_t(32) * 4096) return fail(SD_EUNSUPPORTED, "two-level selection over more than %d chunks", 32 * 4096);
+    if (int64_t(std::min<int64_t>(c.top_k_seg, M / c.seg_size)) * c.seg_size > sd::kSmallRowMax)
+      return fail(SD_EUNSUPPORTED, "top_k_seg * seg_size > %d candidates", sd::kSmallRowMax);
+  }
+  if (!(c.softmax_scale > 0.0f) || !std::isfinite(c.softmax_scale)) return fail(SD_EINVAL, "softmax_scale must be finite and > 0");
+  if (c.keep_first < 0 || c.keep_last < 0) return fail(SD_EINVAL, "keep_first / keep_last must be >= 0");
+  if (c.sink < 0 || c.window < 0) return fail(SD_EINVAL, "sink / window must be >= 0");
+  if (c.split_entries < 0 || c.split_entries > 2048) return fail(SD_EINVAL, "split_entries must be in [0, 2048]");
+  if (c.chunk_size & (c.chunk_size - 1)) return fail(SD_EUNSUPPORTED, "chunk_size must be a power of two (got %d)", c.chunk_size);
+  bool any_local = false;
+  if (c.head_mode) {
+    for (int g = 0; g < c.n_kv_heads; ++g) {
+      if (c.head_mode[g] != 0 && c.head_mode[g] != 1) return fail(SD_EINVAL, "head_mode[%d] = %d (must be 0 or 1)", g, c.head_mode[g]);
+      any_local |= c.head_mode[g] == 1;
+    }
+  }
+  if (any_local) {
+    if (c.chunk_size != 1) return fail(SD_EINVAL, "local heads select tokens: chunk_size must be 1");
+    if (c.sink + int64_t(c.window) < 1) return fail(SD_EINVAL, "local heads need sink + window >= 1");
+  }
+  return SD_OK;
+}
+
+void plan_workspace(sd::Plan& p) {
+  const sd_config& c = p.cfg;
+  const int64_t B = c.batch, Hq = c.n_q_heads, Hk = c.n_kv_heads, d = c.head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + std::max<size_t>(bytes, 1));
+    return o;
+  };
+  p.o_status = take(64);
+  p.o_qp = take(c.route == SD_ROUTE_PROXY ? size_t(B * Hq * 16) * 8 : 0);
+  p.o_s0 = take(size_t(B * Hq * p.len0) * 8);
+  p.o_s1 = take(size_t(B * Hq * p.len1) * 8);
+  p.o_cand = take(size_t(B * Hq * p.len1) * 4);
+  p.o_bits = take(size_t(B * Hq * p.words) * 4);
+  p.o_ubits = take(size_t(B * Hk * p.words) * 4);
+  p.o_rcnt = take(size_t(B * Hk * p.ranges) * 4);
+  p.o_list = take(size_t(B * Hk * p.M) * 4);
+  p.o_cnt = take(size_t(B * Hk) * 4);
+  p.o_po = take(size_t(B * Hq * p.max_splits * d) * 4);
+  p.o_pl = take(size_t(B * Hq * p.max_splits) * 4);
+  const size_t rows = p.long0 ? size_t(B * Hq) : 0;
+  // per-block score max / min: written by the proxy score pass, read by the long-row path
+  const size_t mm_rows = (p.long0 || c.route == SD_ROUTE_PROXY) ? size_t(B * Hq) : 0;
+  p.o_pmax = take(mm_rows * p.score_blocks0 * 8);
+  p.o_pmin = take(mm_rows * p.score_blocks0 * 8);
+  p.o_info = take(rows * sizeof(sd::RowInfo));
+  p.o_h1m = take(rows * sd::kBins1 * 8);
+  p.o_h1c = take(rows * sd::kBins1 * 4);
+  p.o_h2m = take(rows * sd::kBins2 * 8);
+  p.o_h2c = take(rows * sd::kBins2 * 4);
+  p.o_ckey = take(rows * sd::kResolveCap * 8);
+  p.o_cidx = take(rows * sd::kResolveCap * 4);
+  p.o_ccnt = take(rows * 4);
+  p.ws_bytes = off;
+}
+
+sd_status check_ws(const sd::Plan&, const void* ws) {
+  if (!ws) return fail(SD_EWORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(SD_EWORKSPACE, "workspace not 256-byte aligned");
+  return SD_OK;
+}
+
+sd_status check_tensors(const sd::Plan& p, const sd_tensors* t, bool for_score, int level) {
+  const sd_config& c = p.cfg;
+  if (!t) return fail(SD_EINVAL, "tensors is NULL");
+  if (!t->q || !aligned16(t->q)) return fail(SD_EINVAL, "q must be a non-NULL 16-byte aligned pointer");
+  const int es = c.kv_dtype == SD_F32 ? 4 : 2;
+  auto row_ok = [&](int64_t st) { return st >= c.head_dim && (st * es) % 16 == 0; };
+  if ((t->q_sh * es) % 16 || (t->q_sb * es) % 16 || t->q_sh < c.head_dim) return fail(SD_EINVAL, "q strides must keep 16-byte aligned rows");
+  if (for_score) {
+    if (c.route == SD_ROUTE_PROXY) {
+      if (!t->kp || !aligned16(t->kp)) return fail(SD_EINVAL, "proxy routing needs kp (16-byte aligned)");
+      if (!t->proj || !aligned16(t->proj)) return fail(SD_EINVAL, "proxy routing needs proj (16-byte aligned)");
+      if (t->kp_st < 16 || (t->kp_st * 2) % 16) return fail(SD_EINVAL, "kp token stride must keep 16-byte aligned rows");
+    } else if (c.mode == SD_HIER_TOPK && level == 0) {
+      if (!t->kmg || !aligned16(t->kmg) || !row_ok(t->mg_st)) return fail(SD_EINVAL, "two-level routing needs kmg with 16-byte aligned rows");
+    } else {
+      if (!t->kg || !aligned16(t->kg) || !row_ok(t->g_st)) return fail(SD_EINVAL, "summary routing needs kg with 16-byte aligned rows");
+    }
+  } else {
+    if (!t->k || !t->v || !aligned16(t->k) || !aligned16(t->v) || !row_ok(t->kv_st))
+      return fail(SD_EINVAL, "attend needs k and v with 16-byte aligned rows");
+    if (c.attend_summary && (!t->kg || !t->vg || !aligned16(t->kg) || !aligned16(t->vg) || !row_ok(t->g_st)))
+      return fail(SD_EINVAL, "attend_summary needs kg and vg with 16-byte aligned rows");
+  }
+  return SD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sd_status sparse_decode_init(const sd_config* cfg, sd_handle** out, size_t* workspace_bytes) {
+  if (!cfg || !out || !workspace_bytes) return fail(SD_EINVAL, "init: NULL argument");
+  *out = nullptr;
+  sd_status st = check_cfg(*cfg);
+  if (st != SD_OK) return st;
+  sd_handle* h = new (std::nothrow) sd_handle();
+  if (!h) return fail(SD_EINVAL, "init: out of host memory");
+  sd::Plan& p = h->plan;
+  p.cfg = *cfg;
+  p.cfg.head_mode = nullptr;
+  p.local_mask = 0;
+  for (int g = 0; g < cfg->n_kv_heads; ++g) {
+    p.head_mode[g] = cfg->head_mode ? cfg->head_mode[g] : 0;
+    if (p.head_mode[g]) p.local_mask |= uint64_t(1) << g;
+  }
+  const sd_config& c = p.cfg;
+  p.G = c.n_q_heads / c.n_kv_heads;
+  p.M = c.n_ctx / c.chunk_size;
+  p.S = c.mode == SD_HIER_TOPK ? int32_t(p.M / c.seg_size) : 0;
+  p.levels = c.mode == SD_HIER_TOPK ? 2 : 1;
+  p.len0 = c.mode == SD_HIER_TOPK ? p.S : p.M;
+  p.len1 = c.mode == SD_HIER_TOPK ? int64_t(std::min(c.top_k_seg, p.S)) * c.seg_size : 0;
+  p.long0 = p.len0 > sd::kSmallRowMax;
+  p.words = (p.M + 31) / 32;
+  p.ranges = int32_t((p.words + 1023) / 1024);
+  int32_t se = c.split_entries;
+  if (se == 0) se = std::max<int32_t>(1, 1024 / c.chunk_size);
+  p.split_entries = se;
+  p.max_splits = int32_t((p.M + se - 1) / se);
+  p.score_blocks0 = int32_t((p.len0 + 255) / 256);
+  p.long_blocks = int32_t((p.len0 + sd::kLongBlock - 1) / sd::kLongBlock);
+  plan_workspace(p);
+  *out = h;
+  *workspace_bytes = p.ws_bytes;
+  return ok();
+}
+
+int32_t sparse_decode_num_levels(const sd_handle* h) { return h ? h->plan.levels : 0; }
+
+sd_status sparse_decode_score_chunks(const sd_handle* h, const sd_tensors* t, int level, void* ws, void* stream) {
+  if (!h) return fail(SD_EINVAL, "score: NULL handle");
+  const sd::Plan& p = h->plan;
+  if (level < 0 || level >= p.levels) return fail(SD_EINVAL, "score: level %d out of range [0, %d)", level, p.levels);
+  sd_status st = check_ws(p, ws);
+  if (st != SD_OK) return st;
+  st = check_tensors(p, t, true, level);
+  if (st != SD_OK) return st;
+  int e = sd::launch_score(p, *t, level, static_cast<char*>(ws), stream);
+  if (e) return fail(SD_EHIP, "score: HIP error %d (%s)", e, sd::hip_error_string(e));
+  return ok();
+}
+
+sd_status sparse_decode_select(const sd_handle* h, int level, void* ws, void* stream) {
+  if (!h) return fail(SD_EINVAL, "select: NULL handle");
+  const sd::Plan& p = h->plan;
+  if (level < 0 || level >= p.levels) return fail(SD_EINVAL, "select: level %d out of range [0, %d)", level, p.levels);
+  sd_status st = check_ws(p, ws);
+  if (st != SD_OK) return st;
+  int e = sd::launch_select(p, level, static_cast<char*>(ws), stream);
+  if (e) return fail(SD_EHIP, "select: HIP error %d (%s)", e, sd::hip_error_string(e));
+  return ok();
+}
+
+sd_status sparse_decode_attend(const sd_handle* h, const sd_tensors* t, void* ws, void* stream) {
+  if (!h) return fail(SD_EINVAL, "attend: NULL handle");
+  const sd::Plan& p = h->plan;
+  sd_status st = check_ws(p, ws);
+  if (st != SD_OK) return st;
+  st = check_tensors(p, t, false, 0);
+  if (st != SD_OK) return st;
+  int e = sd::launch_attend(p, *t, static_cast<char*>(ws), stream);
+  if (e) return fail(SD_EHIP, "attend: HIP error %d (%s)", e, sd::hip_error_string(e));
+  return ok();
+}
+
+sd_status sparse_decode_combine(const sd_handle* h, void* ws, float* out, float* lse_out, void* stream) {
+  if (!h) return fail(SD_EINVAL, "combine: NULL handle");
+  const sd::Plan& p = h->plan;
+  sd_status st = check_ws(p, ws);
+  if (st != SD_OK) return st;
+  if (!out || !lse_out || !aligned16(out)) return fail(SD_EINVAL, "combine: out (16-byte aligned) and lse_out must be non-NULL");
+  int e = sd::launch_combine(p, static_cast<char*>(ws), out, lse_out, stream);
+  if (e) return fail(SD_EHIP, "combine: HIP error %d (%s)", e, sd::hip_error_string(e));
+  return ok();
+}
+
+sd_status sparse_decode_selection_view(const sd_handle* h, void* ws, sd_selection_view* v) {
+  if (!h || !v) return fail(SD_EINVAL, "selection_view: NULL argument");
+  const sd::Plan& p = h->plan;
+  sd_status st = check_ws(p, ws);
+  if (st != SD_OK) return st;
+  char* w = static_cast<char*>(ws);
+  v->scores0 = reinterpret_cast<const double*>(w + p.o_s0);
+  v->len0 = p.len0;
+  v->scores1 = reinterpret_cast<const double*>(w + p.o_s1);
+  v->len1 = p.len1;
+  v->cand1 = reinterpret_cast<const int32_t*>(w + p.o_cand);
+  v->head_bits = reinterpret_cast<const uint32_t*>(w + p.o_bits);
+  v->words = p.words;
+  v->list = reinterpret_cast<const int32_t*>(w + p.o_list);
+  v->n_entries = p.M;
+  v->count = reinterpret_cast<const int32_t*>(w + p.o_cnt);
+  v->status = reinterpret_cast<const uint32_t*>(w + p.o_status);
+  return ok();
+}
+
+const char* sparse_decode_last_error(void) { return g_err; }
+
+void sparse_decode_destroy(sd_handle* h) { delete h; }
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Internal plan shared by the host API (sd_api.cpp) and the kernels (sd_kernels.hip).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sparse_decode.h"
+
+namespace sd {
+
+// Rows up to this length are selected by one workgroup sorting them in LDS;
+// longer rows (token-level selection) take the histogram path.
+constexpr int kSmallRowMax = 4096;
+// Histogram resolution of the long-row path: coarse bins over the row's score
+// range, then fine bins inside the crossing coarse bin.
+constexpr int kBins1 = 4096;
+constexpr int kBins2 = 4096;
+// Entries of the final fine bin resolved exactly per row (sorted in LDS).
+constexpr int kResolveCap = 4096;
+// Tokens per workgroup in the long-row passes.
+constexpr int kLongBlock = 8192;
+// Attention: tokens per MFMA tile and waves per workgroup.
+constexpr int kTile = 32;
+constexpr int kWaves = 4;
+constexpr int kMaxGroup = 8;
+constexpr int kMaxKvHeads = 64;
+
+struct Plan {
+  sd_config cfg;
+  int8_t head_mode[kMaxKvHeads];
+  uint64_t local_mask;      // bit g set: KV head g is a local (sink + window) head
+  int32_t G;                // query heads per KV head
+  int64_t M;                // chunks = n_ctx / chunk_size (selection entries)
+  int32_t S;                // segments (two-level)
+  int32_t levels;
+  int64_t len0, len1;       // row lengths of level-0 / level-1 scores
+  bool long0;               // level-0 rows take the long-row (histogram) path
+  int64_t words;            // bitmap words per row = ceil(M / 32)
+  int32_t ranges;           // union compaction ranges per group
+  int32_t split_entries;    // list entries per split
+  int32_t max_splits;
+  int32_t score_blocks0;    // blocks per row of the long-row score pass (partial max/min)
+  int32_t long_blocks;      // blocks per row of the long-row histogram passes
+  // workspace byte offsets
+  size_t o_status, o_qp, o_s0, o_s1, o_cand, o_bits, o_ubits, o_rcnt, o_list, o_cnt;
+  size_t o_po, o_pl, o_pmax, o_pmin, o_info, o_h1m, o_h1c, o_h2m, o_h2c, o_ckey, o_cidx, o_ccnt;
+  size_t ws_bytes;
+};
+
+// Per-row state of the long-row selection, in the workspace.
+struct RowInfo {
+  double smax, smin, binscale;  // score range and coarse-bin scale
+  double target;                // p * Z (top-p) or k (top-k)
+  double before1, before2;      // weight of everything ahead of the crossing bins
+  int32_t bin1, bin2;           // crossing coarse / fine bin
+  int32_t all;                  // 1: the whole row is selected
+  int32_t pad;
+};
+
+// Kernel launchers (sd_kernels.hip). Each returns hipSuccess or the launch error.
+int launch_score(const Plan& p, const sd_tensors& t, int level, char* ws, void* stream);
+int launch_select(const Plan& p, int level, char* ws, void* stream);
+int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream);
+int launch_combine(const Plan& p, char* ws, float* out, float* lse, void* stream);
+const char* hip_error_string(int code);
+
+}  // namespace sd
+
+struct sd_handle {
+  sd::Plan plan;
+};

@@ -126,3 +126,17 @@ BENCH = C3
 
 def get(name: str) -> Workload:
     return ALL[name]
+
+
+def library_params(w: Workload) -> dict:
+    """Keyword arguments of query_adaptive_sparse_amd.SparseDecoder for workload ``w``."""
+    mode = {TOPK: "topk", TOPP: "topp", HIER: "hier", PROXY_TOPP: "topp"}[w.mode]
+    return dict(
+        batch=w.batch, kv_batch=w.kv_batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+        head_dim=w.head_dim, n_ctx=w.n_ctx, chunk_size=w.chunk_size, dtype=w.dtype, mode=mode,
+        route="proxy" if w.mode == PROXY_TOPP else "summary", route_dim=w.route_dim,
+        top_k=w.top_k, top_k_seg=w.top_k_seg, seg_size=w.seg_size, top_p=w.top_p,
+        select_scale=w.select_scale, softmax_scale=w.softmax_scale,
+        keep_first=w.keep_first, keep_last=w.keep_last, sink=w.sink, window=w.window,
+        attend_summary=w.attend_summary and w.mode != PROXY_TOPP, split_entries=w.split_entries,
+        head_mode=[1 if g in w.local_kv_heads else 0 for g in range(w.n_kv_heads)])

@@ -1,0 +1,130 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects bad arguments on the host before anything is enqueued (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from query_adaptive_sparse_amd import native as N
+from query_adaptive_sparse_amd.decoder import make_config
+from synth import configs
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sparse_decode.h")
+
+
+def test_header_symbols_exported():
+    src = open(HEADER).read()
+    declared = sorted(set(re.findall(r"\b(sparse_decode_\w+)\s*\(", src)))
+    assert declared, "no declarations found"
+    lib = ctypes.CDLL(N.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in the header but not exported"
+    assert sorted(N.EXPORTS) == declared
+
+
+def _params(name="c3s", **kw):
+    p = configs.library_params(configs.get(name))
+    p.update(kw)
+    return p
+
+
+def _init(**kw):
+    cfg, hm = make_config(**kw)
+    return N.sparse_decode_init(cfg)
+
+
+@pytest.mark.parametrize("name", sorted(configs.ALL))
+def test_init_every_workload(name):
+    h, n = _init(**_params(name))
+    assert n > 0 and n % 256 == 0
+    lv = N.sparse_decode_num_levels(h)
+    assert lv == (2 if configs.get(name).mode == "hier" else 1)
+    N.sparse_decode_destroy(h)
+
+
+BAD = [
+    (dict(batch=0), N.SD_EINVAL, "batch"),
+    (dict(kv_batch=3), N.SD_EINVAL, "kv_batch"),
+    (dict(n_kv_heads=5), N.SD_EINVAL, "multiple"),
+    (dict(n_q_heads=80, n_kv_heads=8), N.SD_EUNSUPPORTED, "group size"),
+    (dict(head_dim=96), N.SD_EUNSUPPORTED, "head_dim"),
+    (dict(n_ctx=16384 + 7), N.SD_EINVAL, "divide"),
+    (dict(chunk_size=48, n_ctx=48 * 100), N.SD_EUNSUPPORTED, "power of two"),
+    (dict(top_p=0.0), N.SD_EINVAL, "top_p"),
+    (dict(top_p=1.5), N.SD_EINVAL, "top_p"),
+    (dict(select_scale=0.0), N.SD_EINVAL, "select_scale"),
+    (dict(softmax_scale=-1.0), N.SD_EINVAL, "softmax_scale"),
+    (dict(mode="topk", top_k=0), N.SD_EINVAL, "top_k"),
+    (dict(split_entries=4096), N.SD_EINVAL, "split_entries"),
+    (dict(keep_first=-1), N.SD_EINVAL, "keep_first"),
+    (dict(head_mode=[0, 1, 0, 0, 0, 0, 0, 2]), N.SD_EINVAL, "head_mode"),
+    (dict(head_mode=[0, 1, 0, 0, 0, 0, 0, 0]), N.SD_EINVAL, "chunk_size must be 1"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", BAD, ids=[b[2] + str(i) for i, b in enumerate(BAD)])
+def test_init_rejects(kw, status, msg):
+    with pytest.raises(N.SparseDecodeError) as e:
+        _init(**_params(**kw))
+    assert e.value.status == status
+    assert msg in str(e.value)
+
+
+def test_init_rejects_proxy_and_hier_shapes():
+    with pytest.raises(N.SparseDecodeError) as e:
+        _init(**_params("c5s", route_dim=8))
+    assert e.value.status == N.SD_EUNSUPPORTED
+    with pytest.raises(N.SparseDecodeError) as e:
+        _init(**_params("c4s", seg_size=48))
+    assert e.value.status == N.SD_EINVAL
+    with pytest.raises(N.SparseDecodeError) as e:
+        _init(**_params("c5s", attend_summary=True))
+    assert e.value.status == N.SD_EINVAL
+
+
+def test_init_null_arguments():
+    L = N.lib()
+    h = ctypes.c_void_p()
+    n = ctypes.c_size_t()
+    assert L.sparse_decode_init(None, ctypes.byref(h), ctypes.byref(n)) == N.SD_EINVAL
+    assert b"NULL" in L.sparse_decode_last_error()
+
+
+def test_calls_reject_before_enqueue():
+    """Every compute call validates on the host; these all fail without touching a GPU."""
+    h, nbytes = _init(**_params())
+    L = N.lib()
+    t = N.sd_tensors()
+    # NULL handle
+    assert L.sparse_decode_select(None, 0, 256, None) == N.SD_EINVAL
+    # bad level
+    assert L.sparse_decode_select(h, 1, 256, None) == N.SD_EINVAL
+    assert L.sparse_decode_score_chunks(h, ctypes.byref(t), -1, 256, None) == N.SD_EINVAL
+    # workspace NULL / misaligned
+    assert L.sparse_decode_select(h, 0, None, None) == N.SD_EWORKSPACE
+    assert L.sparse_decode_attend(h, ctypes.byref(t), 0x1008, None) == N.SD_EWORKSPACE
+    assert L.sparse_decode_combine(h, 0x1001, 0x2000, 0x3000, None) == N.SD_EWORKSPACE
+    # tensors missing
+    assert L.sparse_decode_score_chunks(h, None, 0, 256, None) == N.SD_EINVAL
+    assert L.sparse_decode_score_chunks(h, ctypes.byref(t), 0, 256, None) == N.SD_EINVAL
+    assert b"q must be" in L.sparse_decode_last_error()
+    t.q, t.q_sb, t.q_sh = 0x10000, 32 * 128, 128
+    assert L.sparse_decode_score_chunks(h, ctypes.byref(t), 0, 256, None) == N.SD_EINVAL
+    assert b"kg" in L.sparse_decode_last_error()
+    assert L.sparse_decode_attend(h, ctypes.byref(t), 256, None) == N.SD_EINVAL
+    t.q_sh = 100  # rows not 16-byte aligned
+    assert L.sparse_decode_attend(h, ctypes.byref(t), 256, None) == N.SD_EINVAL
+    # outputs
+    assert L.sparse_decode_combine(h, 256, None, 0x3000, None) == N.SD_EINVAL
+    assert L.sparse_decode_combine(h, 256, 0x2004, 0x3000, None) == N.SD_EINVAL
+    v = N.sd_selection_view()
+    assert L.sparse_decode_selection_view(h, 256, ctypes.byref(v)) == N.SD_OK
+    assert v.list - 256 > 0 and v.len0 == configs.get("c3s").n_chunks
+    N.sparse_decode_destroy(h)
+
+
+def test_workspace_grows_with_batch():
+    _, a = _init(**_params("c3s", batch=1, kv_batch=1))
+    _, b = _init(**_params("c3s", batch=2, kv_batch=2))
+    assert b > a
