@@ -38,8 +38,22 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-groups", type=int, default=0, help="0 = size the sample to ~10-30 s")
-    ap.add_argument("--split-entries", type=int, default=None)
+    ap.add_argument("--attend-blocks", type=int, default=None)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch device-to-device copies of MIB MiB (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int, reps: int = 5):
+    """Plain device copies of a known size: the reference reading for HBM byte counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "reps": reps}), flush=True)
 
 
 def algorithmic_bytes(w, counts: np.ndarray) -> dict:
@@ -113,6 +127,9 @@ def _cpu_model():
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the decode path "
               "shards by sequence and KV group across GPUs, which this build does not run)", file=sys.stderr)
@@ -122,8 +139,8 @@ def main():
 
     w = configs.get(args.workload) if args.workload else configs.BENCH
     params = configs.library_params(w)
-    if args.split_entries is not None:
-        params["split_entries"] = args.split_entries
+    if args.attend_blocks is not None:
+        params["attend_blocks"] = args.attend_blocks
     torch.cuda.init()
     dev = torch.device("cuda:0")
     print(f"[bench] workload {w.name}: generating inputs on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
@@ -189,7 +206,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "context": w.n_ctx, "chunk": w.chunk_size, "mode": w.mode,
                    "top_p": w.top_p if w.mode in ("topp", "proxy") else None,
-                   "top_k": w.top_k or None, "split_entries": dec.params.get("split_entries") or "default"},
+                   "top_k": w.top_k or None, "attend_blocks": dec.params.get("attend_blocks") or 512},
         "hbm_gbps": round(step_gbps, 1),
         "hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
         "step_bytes": nb["step"],

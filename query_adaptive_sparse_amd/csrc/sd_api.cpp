@@ -75,7 +75,14 @@ sd_status check_cfg(const sd_config& c) {
   if (!(c.softmax_scale > 0.0f) || !std::isfinite(c.softmax_scale)) return fail(SD_EINVAL, "softmax_scale must be finite and > 0");
   if (c.keep_first < 0 || c.keep_last < 0) return fail(SD_EINVAL, "keep_first / keep_last must be >= 0");
   if (c.sink < 0 || c.window < 0) return fail(SD_EINVAL, "sink / window must be >= 0");
-  if (c.split_entries < 0 || c.split_entries > 2048) return fail(SD_EINVAL, "split_entries must be in [0, 2048]");
+  if (c.attend_blocks < 0 || c.attend_blocks > 65536) return fail(SD_EINVAL, "attend_blocks must be in [0, 65536]");
+  if (int64_t(c.batch) * c.n_kv_heads > sd::kMaxGroups)
+    return fail(SD_EUNSUPPORTED, "batch * n_kv_heads > %d", sd::kMaxGroups);
+  {
+    const int64_t M = c.n_ctx / c.chunk_size;
+    const int64_t tiles = int64_t(c.batch) * c.n_kv_heads * (c.n_ctx / 32 + M / 32 + 2);
+    if (tiles >= (int64_t(1) << 31)) return fail(SD_EUNSUPPORTED, "too many attention tiles per call");
+  }
   if (c.chunk_size & (c.chunk_size - 1)) return fail(SD_EUNSUPPORTED, "chunk_size must be a power of two (got %d)", c.chunk_size);
   bool any_local = false;
   if (c.head_mode) {
@@ -110,8 +117,10 @@ void plan_workspace(sd::Plan& p) {
   p.o_rcnt = take(size_t(B * Hk * p.ranges) * 4);
   p.o_list = take(size_t(B * Hk * p.M) * 4);
   p.o_cnt = take(size_t(B * Hk) * 4);
-  p.o_po = take(size_t(B * Hq * p.max_splits * d) * 4);
-  p.o_pl = take(size_t(B * Hq * p.max_splits) * 4);
+  const size_t slots = size_t(p.attend_blocks) + size_t(B * Hk);
+  p.o_gpre = take(size_t(B * Hk + 1) * 4);
+  p.o_po = take(slots * p.G * d * 4);
+  p.o_pl = take(slots * p.G * 4);
   const size_t rows = p.long0 ? size_t(B * Hq) : 0;
   // per-block score max / min: written by the proxy score pass, read by the long-row path
   const size_t mm_rows = (p.long0 || c.route == SD_ROUTE_PROXY) ? size_t(B * Hq) : 0;
@@ -189,10 +198,7 @@ sd_status sparse_decode_init(const sd_config* cfg, sd_handle** out, size_t* work
   p.long0 = p.len0 > sd::kSmallRowMax;
   p.words = (p.M + 31) / 32;
   p.ranges = int32_t((p.words + 1023) / 1024);
-  int32_t se = c.split_entries;
-  if (se == 0) se = std::max<int32_t>(1, 1024 / c.chunk_size);
-  p.split_entries = se;
-  p.max_splits = int32_t((p.M + se - 1) / se);
+  p.attend_blocks = c.attend_blocks ? c.attend_blocks : sd::kAttendBlocks;
   p.score_blocks0 = int32_t((p.len0 + 255) / 256);
   p.long_blocks = int32_t((p.len0 + sd::kLongBlock - 1) / sd::kLongBlock);
   plan_workspace(p);

@@ -1,0 +1,531 @@
+// Gathered split-K attention and the log-sum-exp combine.
+//
+// Work decomposition. Every (sequence, KV group) -- a "group" -- owns an ascending list of
+// selected entries (chunks, or tokens). Its hybrid context is cut into 16-token tiles: raw tiles
+// (the listed chunks' tokens, in list order) then summary tiles (the listed chunks' summary rows).
+// The tiles of all groups, concatenated in group order, are split into contiguous,
+// equal slices -- one per persistent workgroup (attend_blocks of them) -- so every workgroup streams the same number of
+// bytes whatever the per-group list lengths are. Inside a workgroup the 4 waves take alternate
+// tiles, each with its own online softmax, and merge in LDS whenever the slice leaves a group:
+// one partial (o, lse) per (workgroup, group), written to pool slot (workgroup + group).
+//
+// Per tile and wave: q.K^T on MFMA with tokens as M and the group's heads as N (K fragments load
+// straight from HBM in the A-operand layout), online softmax in base 2, then P.V on MFMA with head
+// slots as M. P arrives from the logit layout with no data movement; for bf16 it is split into
+// hi = bf16(p) (slots [0, G)) and lo = bf16(p - hi) (slots [G, 2G)) rows, which keeps fp32
+// accuracy. V goes through LDS (row-major, padded rows) to reach the B-operand layout. The next
+// tiles' K and V loads are issued before the current tile is computed (a ring of register stages).
+#include "sd_device.h"
+
+namespace sd {
+namespace {
+
+struct AttendArgs {
+  const void* q;
+  int64_t q_sb, q_sh;
+  const void* k;
+  const void* v;
+  int64_t kv_sb, kv_sh, kv_st;
+  const void* kg;
+  const void* vg;
+  int64_t g_sb, g_sh, g_st;
+  const int32_t* list;
+  const int32_t* cnt;
+  int32_t* gpre_out;  // [n_groups + 1] tile prefix over groups, for the combine
+  float* po;          // [attend_blocks + n_groups][G][D] partial outputs
+  float* pl;          // [attend_blocks + n_groups][G] partial lse (natural log)
+  int64_t n_list;     // list row stride (entries)
+  int n_groups, Hk, Hq, G, chunk_shift, attend_summary;
+  float scale_log2;
+};
+
+template <typename T, int D>
+struct Cfg {
+  static constexpr bool BF = sizeof(T) == 2;
+  static constexpr int EPV = 16 / int(sizeof(T));   // elements per 16-byte piece
+  static constexpr int PPR = D / EPV;               // 16-byte pieces per row
+  static constexpr int VPL = kTile * PPR / 64;      // V pieces per lane per tile
+  static constexpr int KQ = BF ? D / 32 : D / 16;   // K pieces per lane per tile
+  static constexpr int QF = BF ? D / 32 : D / 4;    // query fragment registers
+  static constexpr int kRowWords = D * int(sizeof(T)) / 4 + 4;  // padded LDS V row (32-bit words)
+  static constexpr int kVtWords = kTile * kRowWords;
+  static constexpr int kMergeWords = 16 * D + 32;
+  static constexpr int kWaveWords = kVtWords > kMergeWords ? kVtWords : kMergeWords;
+  // register stages of the load pipeline: ~128 VGPRs of tiles in flight per wave
+  static constexpr int kRegsPerStage = 4 * (KQ + VPL);
+  static constexpr int NS = 128 / kRegsPerStage >= 4 ? 4 : (128 / kRegsPerStage >= 2 ? 128 / kRegsPerStage : 2);
+};
+
+template <typename T, int D>
+struct TileRegs {
+  uint4 k[Cfg<T, D>::KQ];
+  uint4 v[Cfg<T, D>::VPL];
+};
+
+// Per-wave running state of one group.
+template <int D>
+struct SoftmaxState {
+  float m, l;
+  f32x4 acc[D / 16];
+};
+
+constexpr int kListLds = 4096;
+
+template <typename T, int D>
+struct Attender {
+  using CF = Cfg<T, D>;
+  const AttendArgs& a;
+  const int lane, wave, n, c;
+  const int32_t* lst;   // LDS list slice
+  uint32_t* vt;         // this wave's LDS region
+  // current group
+  int gid, G, hs;
+  bool lo_row;
+  const T* kb;
+  const T* vb;
+  int64_t st;
+  // query fragments
+  uint4 qf[CF::BF ? CF::QF : 1];
+  float qf32[CF::BF ? 1 : CF::QF];
+
+  __device__ Attender(const AttendArgs& args, const int32_t* l, uint32_t* v)
+      : a(args), lane(threadIdx.x & 63), wave(threadIdx.x >> 6), n(lane & 15), c(lane >> 4), lst(l), vt(v) {}
+
+  __device__ void load_query(int group) {
+    gid = group;
+    G = a.G;
+    hs = n < G ? n : (n < 2 * G ? n - G : -1);
+    lo_row = CF::BF && n >= G && n < 2 * G;
+    const int b = group / a.Hk, g = group - b * a.Hk;
+    const T* qrow = reinterpret_cast<const T*>(a.q) + b * a.q_sb + int64_t(g * G + (hs < 0 ? 0 : hs)) * a.q_sh;
+    if constexpr (CF::BF) {
+#pragma unroll
+      for (int j = 0; j < CF::QF; ++j) qf[j] = hs >= 0 ? ld16(qrow + 32 * j + 8 * c) : make_uint4(0, 0, 0, 0);
+    } else {
+      // fp32: MFMA j, lane group c covers dim (D/4) c + j
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) {
+        const uint4 v = hs >= 0 ? ld16(qrow + (D / 4) * c + 4 * j) : make_uint4(0, 0, 0, 0);
+        const float* f = reinterpret_cast<const float*>(&v);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) qf32[4 * j + u] = f[u];
+      }
+    }
+  }
+
+  // Base pointers of the raw (summary = false) or summary (true) rows of the current group.
+  __device__ void set_kind(bool summary) {
+    const int b = gid / a.Hk, g = gid - b * a.Hk;
+    if (summary) {
+      kb = reinterpret_cast<const T*>(a.kg) + b * a.g_sb + int64_t(g) * a.g_sh;
+      vb = reinterpret_cast<const T*>(a.vg) + b * a.g_sb + int64_t(g) * a.g_sh;
+      st = a.g_st;
+    } else {
+      kb = reinterpret_cast<const T*>(a.k) + b * a.kv_sb + int64_t(g) * a.kv_sh;
+      vb = reinterpret_cast<const T*>(a.v) + b * a.kv_sb + int64_t(g) * a.kv_sh;
+      st = a.kv_st;
+    }
+  }
+
+  // Cache row of token x of a tile. Raw tiles: token v = first + x of the list's token sequence;
+  // summary tiles: list entry first + x. `e0` is the first list entry held in the LDS slice.
+  __device__ __forceinline__ int64_t row_of(bool summary, int first, int x, int nv, int e0) const {
+    x = x < nv ? x : 0;  // padded positions read a valid row; their logits are masked
+    if (summary) return lst[first + x - e0];
+    const int cs = a.chunk_shift;
+    const int v = first + x;
+    return (int64_t(lst[(v >> cs) - e0]) << cs) | (v & ((1 << cs) - 1));
+  }
+
+  __device__ __forceinline__ void issue(TileRegs<T, D>& r, bool summary, int first, int nv, int e0) const {
+    const T* kr = kb + row_of(summary, first, n, nv, e0) * st;
+#pragma unroll
+    for (int q = 0; q < CF::KQ; ++q) r.k[q] = ld16(kr + (CF::BF ? 32 * q + 8 * c : (D / 4) * c + 4 * q));
+#pragma unroll
+    for (int kq = 0; kq < CF::VPL; ++kq) {
+      const int pidx = kq * 64 + lane;
+      const int x = pidx / CF::PPR, cp = pidx - x * CF::PPR;
+      r.v[kq] = ld16(vb + row_of(summary, first, x, nv, e0) * st + cp * CF::EPV);
+    }
+  }
+
+  __device__ __forceinline__ void compute(const TileRegs<T, D>& r, int nv, SoftmaxState<D>& s) {
+    // ---- logits: S^T[token][slot]; lane (n, c) gets tokens 4c + i of head slot n
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (CF::BF) {
+#pragma unroll
+      for (int j = 0; j < CF::QF; ++j)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[j]),
+                                                        __builtin_bit_cast(bf16x8, qf[j]), sacc, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int q = 0; q < CF::KQ; ++q) {
+        const float* f = reinterpret_cast<const float*>(&r.k[q]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(f[u], qf32[4 * q + u], sacc, 0, 0, 0);
+      }
+    }
+    // ---- V tile -> LDS, row-major with a 4-word pad per row
+#pragma unroll
+    for (int kq = 0; kq < CF::VPL; ++kq) {
+      const int pidx = kq * 64 + lane;
+      const int x = pidx / CF::PPR, cp = pidx - x * CF::PPR;
+      *reinterpret_cast<uint4*>(vt + x * CF::kRowWords + cp * 4) = r.v[kq];
+    }
+    // ---- online softmax (base 2)
+    float lg[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lg[i] = 4 * c + i < nv ? sacc[i] * a.scale_log2 : kNegInf;
+    float mt = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(s.m, mt);
+    const bool none = mn == kNegInf;
+    // rescale only when some head's running max grew (rare after the first tiles)
+    if (__ballot(mn > s.m)) {
+      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(s.m - mn);
+      s.l *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * c + i);
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) s.acc[nb][i] *= ai;
+      }
+      s.m = mn;
+    }
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = none ? 0.f : __builtin_amdgcn_exp2f(lg[i] - mn);
+      s.l += pr[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- P V: P is the A operand (row = head slot, k = tokens 4c .. 4c+3), V the B operand
+    if constexpr (CF::BF) {
+      const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
+      u16x4 pa;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t hi = f2bf(pr[i]);
+        pa[i] = hs < 0 ? uint16_t(0) : (lo_row ? f2bf(pr[i] - bf2f(hi)) : hi);
+      }
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) {
+        u16x4 vbf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vbf[i] = vt16[(4 * c + i) * (2 * CF::kRowWords) + 16 * nb + n];
+        s.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, pa),
+                                                               __builtin_bit_cast(bf16x4, vbf), s.acc[nb], 0, 0, 0);
+      }
+    } else {
+      const float* vtf = reinterpret_cast<const float*>(vt);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = hs >= 0 ? pr[i] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb)
+          s.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vtf[(4 * c + i) * CF::kRowWords + 16 * nb + n], s.acc[nb], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // This wave's tiles of [u0, u1) (alternating with the other waves) through an NS-stage register
+  // ring: the loads of the next NS - 1 tiles are in flight while a tile is computed. Raw tiles:
+  // tile u starts at token kTile*u of the group's token sequence; summary tiles: at list entry
+  // kTile*u. `limit` = tokens (raw) or entries (summary) in the group.
+  __device__ void run(bool summary, int u0, int u1, int limit, int e0, SoftmaxState<D>& s) {
+    constexpr int NS = CF::NS;
+    const int first = u0 + wave;
+    if (first >= u1) return;
+    const int nt = (u1 - first + kWaves - 1) / kWaves;  // this wave's tiles
+    TileRegs<T, D> R[NS];
+    auto tile = [&](int k) { return first + k * kWaves; };
+    auto nv_of = [&](int t) { return min(kTile, limit - t * kTile); };
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k)
+      if (k < nt) issue(R[k], summary, tile(k) * kTile, nv_of(tile(k)), e0);
+    for (int k0 = 0; k0 < nt; k0 += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int k = k0 + j;
+        if (k < nt) {
+          const int kn = k + NS - 1;
+          if (kn < nt) issue(R[(j + NS - 1) % NS], summary, tile(kn) * kTile, nv_of(tile(kn)), e0);
+          compute(R[j], nv_of(tile(k)), s);
+        }
+      }
+    }
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
+  using CF = Cfg<T, D>;
+  __shared__ int32_t gpre[kMaxGroups + 1];
+  __shared__ int32_t lst[kListLds];
+  __shared__ uint32_t wlds[kWaves * CF::kWaveWords];
+  __shared__ int32_t sbuf[256];
+  const int tid = threadIdx.x;
+  const int NG = a.n_groups;
+  const int cs = a.chunk_shift;
+
+  // ---- tiles per group, exclusive prefix in gpre[0..NG]
+  {
+    const int per = (NG + 255) / 256;
+    const int g0 = tid * per;
+    int sum = 0;
+    for (int gg = g0; gg < min(NG, g0 + per); ++gg) {
+      const int cnt = a.cnt[gg];
+      sum += ((cnt << cs) + kTile - 1) / kTile + (a.attend_summary ? (cnt + kTile - 1) / kTile : 0);
+    }
+    sbuf[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int add = tid >= off ? sbuf[tid - off] : 0;
+      __syncthreads();
+      sbuf[tid] += add;
+      __syncthreads();
+    }
+    int run = sbuf[tid] - sum;
+    for (int gg = g0; gg < min(NG, g0 + per); ++gg) {
+      gpre[gg] = run;
+      const int cnt = a.cnt[gg];
+      run += ((cnt << cs) + kTile - 1) / kTile + (a.attend_summary ? (cnt + kTile - 1) / kTile : 0);
+    }
+    if (tid == 255) gpre[NG] = sbuf[255];
+    __syncthreads();
+  }
+  const int total = gpre[NG];
+  if (blockIdx.x == 0)
+    for (int i = tid; i <= NG; i += 256) a.gpre_out[i] = gpre[i];
+  const int NB = gridDim.x;
+  const int b0 = int((int64_t(blockIdx.x) * total) / NB);
+  const int b1 = int((int64_t(blockIdx.x + 1) * total) / NB);
+  if (b0 >= b1) return;
+
+  // first group containing tile b0: last gi with gpre[gi] <= b0
+  int lo = 0, hi = NG;  // invariant: gpre[lo] <= b0 < gpre[hi] (gpre[NG] = total > b0)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (gpre[mid] <= b0) lo = mid; else hi = mid;
+  }
+
+  const int wave = tid >> 6;
+  uint32_t* vt = wlds + wave * CF::kWaveWords;
+  Attender<T, D> at(a, lst, vt);
+  const int lane = tid & 63, n = lane & 15, c = lane >> 4;
+
+  for (int gi = lo; gi < NG && gpre[gi] < b1; ++gi) {
+    const int s0 = max(b0, gpre[gi]) - gpre[gi];
+    const int s1 = min(b1, gpre[gi + 1]) - gpre[gi];
+    if (s0 >= s1) continue;
+    const int cnt = a.cnt[gi];
+    const int ntok = cnt << cs;
+    const int traw = (ntok + kTile - 1) / kTile;
+    at.load_query(gi);
+    SoftmaxState<D> st;
+    st.m = kNegInf;
+    st.l = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) st.acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int32_t* glist = a.list + int64_t(gi) * a.n_list;
+
+    // raw tiles [max(s0, 0), min(s1, traw)), in slices whose list entries fit the LDS buffer
+    {
+      // a slice of u tiles spans at most (u * kTile) / C + 2 list entries
+      const int64_t tps = (int64_t(kListLds - 2) << cs) / kTile;
+      const int tiles_per_slice = int(tps < 1 ? 1 : (tps > (1 << 30) ? (1 << 30) : tps));
+      at.set_kind(false);
+      for (int u0 = s0; u0 < min(s1, traw); u0 += tiles_per_slice) {
+        const int u1 = min(min(s1, traw), u0 + tiles_per_slice);
+        const int e0 = (u0 * kTile) >> cs;
+        const int e1 = min(cnt, ((u1 * kTile - 1) >> cs) + 1);
+        __syncthreads();
+        for (int i = tid; i < e1 - e0; i += 256) lst[i] = glist[e0 + i];
+        __syncthreads();
+        at.run(false, u0, u1, ntok, e0, st);
+      }
+    }
+    // summary tiles
+    if (a.attend_summary) {
+      at.set_kind(true);
+      const int tiles_per_slice = kListLds / kTile;
+      for (int u0 = max(s0, traw); u0 < s1; u0 += tiles_per_slice) {
+        const int u1 = min(s1, u0 + tiles_per_slice);
+        const int e0 = (u0 - traw) * kTile;
+        const int e1 = min(cnt, (u1 - traw) * kTile);
+        __syncthreads();
+        for (int i = tid; i < e1 - e0; i += 256) lst[i] = glist[e0 + i];
+        __syncthreads();
+        at.run(true, u0 - traw, u1 - traw, cnt, e0, st);
+      }
+    }
+
+    // ---- merge the 4 waves into partial slot (workgroup + group)
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+    __syncthreads();  // every wave is done with its V tile; reuse the LDS regions
+    float* mw = reinterpret_cast<float*>(vt);  // [16][D] acc rows, then m[16], l[16]
+    const int G = a.G;
+    const int nslots = CF::BF ? 2 * G : G;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = 4 * c + i;
+        if (slot < nslots) mw[slot * D + 16 * nb + n] = st.acc[nb][i];
+      }
+    if (c == 0 && n < G) {
+      mw[16 * D + n] = st.m;
+      mw[16 * D + 16 + n] = st.l;
+    }
+    __syncthreads();
+    const int64_t slot = int64_t(blockIdx.x) + gi;
+    for (int it = tid; it < G * D; it += 256) {
+      const int hh = it / D, dd = it - hh * D;
+      float M = kNegInf;
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, reinterpret_cast<const float*>(wlds + w * CF::kWaveWords)[16 * D + hh]);
+      float Ls = 0.f, O = 0.f;
+      for (int w = 0; w < kWaves; ++w) {
+        const float* ww = reinterpret_cast<const float*>(wlds + w * CF::kWaveWords);
+        const float mw_ = ww[16 * D + hh];
+        if (mw_ == kNegInf) continue;
+        const float f = __builtin_amdgcn_exp2f(mw_ - M);
+        Ls += ww[16 * D + 16 + hh] * f;
+        float o = ww[hh * D + dd];
+        if (CF::BF) o += ww[(hh + G) * D + dd];
+        O += o * f;
+      }
+      a.po[(slot * G + hh) * D + dd] = O / Ls;
+      if (dd == 0) a.pl[slot * G + hh] = (M + __log2f(Ls)) * 0.6931471805599453f;
+    }
+    __syncthreads();
+  }
+}
+
+// LSE combine. One workgroup per (sequence, query head): the partials of the head's group are
+// the pool slots (b + group) of the persistent workgroups b whose tile slice meets the group.
+template <int D>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ po, const float* __restrict__ pl,
+                                                 const int32_t* __restrict__ gpre, int n_groups, int nb_attend,
+                                                 int G, int Hq, int Hk, float* __restrict__ out,
+                                                 float* __restrict__ lse) {
+  constexpr int DPL = D / 64;  // dims per lane
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int gid = b * Hk + h / G, hh = h % G;
+  const int64_t hrow = int64_t(b) * Hq + h;
+  const int64_t T = gpre[n_groups];
+  const int64_t t0 = gpre[gid], t1 = gpre[gid + 1];
+  __shared__ float red[4];
+  __shared__ float ored[4][D];
+  __shared__ float lred[4];
+  if (t0 == t1) {
+    for (int d = tid; d < D; d += 256) out[hrow * D + d] = 0.f;
+    if (tid == 0) lse[hrow] = kNegInf;
+    return;
+  }
+  const int64_t NB = nb_attend;
+  const int bfirst = int(((t0 + 1) * NB - 1) / T);
+  const int blast = int((t1 * NB - 1) / T);
+  auto nonempty = [&](int k) { return (int64_t(k) * T) / NB < (int64_t(k + 1) * T) / NB; };
+  float M = kNegInf;
+  for (int k = bfirst + tid; k <= blast; k += 256)
+    if (nonempty(k)) M = fmaxf(M, pl[(int64_t(k) + gid) * G + hh]);
+  for (int o = 32; o; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float acc[DPL], wsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+#pragma unroll 4
+  for (int k = bfirst + wave; k <= blast; k += 4) {
+    if (!nonempty(k)) continue;
+    const int64_t slot = int64_t(k) + gid;
+    const float w = __expf(pl[slot * G + hh] - M);
+    wsum += w;
+    const float* src = po + (slot * G + hh) * D + lane * DPL;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] += w * src[i];
+  }
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) ored[wave][lane * DPL + i] = acc[i];
+  if (lane == 0) lred[wave] = wsum;
+  __syncthreads();
+  const float L = lred[0] + lred[1] + lred[2] + lred[3];
+  for (int d = tid; d < D; d += 256) out[hrow * D + d] = (ored[0][d] + ored[1][d] + ored[2][d] + ored[3][d]) / L;
+  if (tid == 0) lse[hrow] = M + __logf(L);
+}
+
+}  // namespace
+
+int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const sd_config& c = p.cfg;
+  AttendArgs a;
+  a.q = t.q;
+  a.q_sb = t.q_sb;
+  a.q_sh = t.q_sh;
+  a.k = t.k;
+  a.v = t.v;
+  a.kv_sb = t.kv_sb;
+  a.kv_sh = t.kv_sh;
+  a.kv_st = t.kv_st;
+  a.kg = c.attend_summary ? t.kg : t.k;
+  a.vg = c.attend_summary ? t.vg : t.v;
+  a.g_sb = t.g_sb;
+  a.g_sh = t.g_sh;
+  a.g_st = c.attend_summary ? t.g_st : t.kv_st;
+  a.list = at<int32_t>(ws, p.o_list);
+  a.cnt = at<int32_t>(ws, p.o_cnt);
+  a.gpre_out = at<int32_t>(ws, p.o_gpre);
+  a.po = at<float>(ws, p.o_po);
+  a.pl = at<float>(ws, p.o_pl);
+  a.n_list = p.M;
+  a.n_groups = c.batch * c.n_kv_heads;
+  a.Hk = c.n_kv_heads;
+  a.Hq = c.n_q_heads;
+  a.G = p.G;
+  int cs = 0;
+  while ((1 << cs) < c.chunk_size) ++cs;
+  a.chunk_shift = cs;
+  a.attend_summary = c.attend_summary;
+  a.scale_log2 = c.softmax_scale * 1.4426950408889634f;
+  const dim3 grid(p.attend_blocks);
+  if (c.kv_dtype == SD_BF16) {
+    if (c.head_dim == 128)
+      hipLaunchKernelGGL((k_attend<uint16_t, 128>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_attend<uint16_t, 64>), grid, dim3(256), 0, st, a);
+  } else {
+    if (c.head_dim == 128)
+      hipLaunchKernelGGL((k_attend<float, 128>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_attend<float, 64>), grid, dim3(256), 0, st, a);
+  }
+  return int(hipGetLastError());
+}
+
+int launch_combine(const Plan& p, char* ws, float* out, float* lse, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const sd_config& c = p.cfg;
+  const dim3 grid(c.n_q_heads, c.batch);
+  const int NG = c.batch * c.n_kv_heads;
+  if (c.head_dim == 128)
+    hipLaunchKernelGGL(k_combine<128>, grid, dim3(256), 0, st, at<float>(ws, p.o_po), at<float>(ws, p.o_pl),
+                       at<int32_t>(ws, p.o_gpre), NG, p.attend_blocks, p.G, c.n_q_heads, c.n_kv_heads, out, lse);
+  else
+    hipLaunchKernelGGL(k_combine<64>, grid, dim3(256), 0, st, at<float>(ws, p.o_po), at<float>(ws, p.o_pl),
+                       at<int32_t>(ws, p.o_gpre), NG, p.attend_blocks, p.G, c.n_q_heads, c.n_kv_heads, out, lse);
+  return int(hipGetLastError());
+}
+
+const char* hip_error_string(int code) { return hipGetErrorString(static_cast<hipError_t>(code)); }
+
+}  // namespace sd

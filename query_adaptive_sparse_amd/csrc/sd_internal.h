@@ -20,10 +20,13 @@ constexpr int kResolveCap = 4096;
 // Tokens per workgroup in the long-row passes.
 constexpr int kLongBlock = 8192;
 // Attention: tokens per MFMA tile and waves per workgroup.
-constexpr int kTile = 32;
+constexpr int kTile = 16;
 constexpr int kWaves = 4;
 constexpr int kMaxGroup = 8;
 constexpr int kMaxKvHeads = 64;
+// Attention: persistent workgroups (default) and the most (sequence, KV group) pairs per call.
+constexpr int kAttendBlocks = 512;
+constexpr int kMaxGroups = 4096;
 
 struct Plan {
   sd_config cfg;
@@ -37,13 +40,12 @@ struct Plan {
   bool long0;               // level-0 rows take the long-row (histogram) path
   int64_t words;            // bitmap words per row = ceil(M / 32)
   int32_t ranges;           // union compaction ranges per group
-  int32_t split_entries;    // list entries per split
-  int32_t max_splits;
+  int32_t attend_blocks;    // persistent attention workgroups
   int32_t score_blocks0;    // blocks per row of the long-row score pass (partial max/min)
   int32_t long_blocks;      // blocks per row of the long-row histogram passes
   // workspace byte offsets
   size_t o_status, o_qp, o_s0, o_s1, o_cand, o_bits, o_ubits, o_rcnt, o_list, o_cnt;
-  size_t o_po, o_pl, o_pmax, o_pmin, o_info, o_h1m, o_h1c, o_h2m, o_h2c, o_ckey, o_cidx, o_ccnt;
+  size_t o_gpre, o_po, o_pl, o_pmax, o_pmin, o_info, o_h1m, o_h1c, o_h2m, o_h2c, o_ckey, o_cidx, o_ccnt;
   size_t ws_bytes;
 };
 
@@ -60,7 +62,7 @@ struct RowInfo {
 // Kernel launchers (sd_kernels.hip). Each returns hipSuccess or the launch error.
 int launch_score(const Plan& p, const sd_tensors& t, int level, char* ws, void* stream);
 int launch_select(const Plan& p, int level, char* ws, void* stream);
-int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream);
+int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream);  // + kAttendBlocks
 int launch_combine(const Plan& p, char* ws, float* out, float* lse, void* stream);
 const char* hip_error_string(int code);
 

@@ -1,0 +1,205 @@
+// Score kernels: summary / meta-summary / candidate rows, proxy query and proxy scores.
+//
+// Compiled with -ffp-contract=off: every fused multiply-add is an explicit fma(), so fp64 score
+// arithmetic can be matched bit for bit by a sequential CPU evaluation.
+#include "sd_device.h"
+
+namespace sd {
+namespace {
+// ---------------------------------------------------------------------------------------------
+// Scores. One workgroup scores 64 rows of summary keys (or per-head candidate rows) against the
+// group's queries. The key tile is staged in LDS as fp32 (exact for bf16 and fp32 inputs); each
+// thread owns one (row, head) score and accumulates it in fp64 over d in index order. Each
+// product of two bf16 or two fp32 values is exact in fp64, so fma(q, k, acc) equals the CPU's
+// acc + q*k, step for step.
+// ---------------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, int64_t q_sb, int64_t q_sh,
+                                                    const T* __restrict__ keys, int64_t k_sb, int64_t k_sh,
+                                                    int64_t k_st, const int32_t* __restrict__ cand,
+                                                    int64_t n_rows, int64_t n_keys, int G, int Hq,
+                                                    uint64_t local_mask, double* __restrict__ out, int64_t out_len,
+                                                    uint32_t* __restrict__ status) {
+  constexpr int R = 64;
+  __shared__ float tile[R][D + 1];
+  __shared__ float qs[kMaxGroup][D];
+  const int b = blockIdx.z, y = blockIdx.y, tid = threadIdx.x;
+  if (status && blockIdx.x == 0 && y == 0 && b == 0 && tid < 4) status[tid] = 0;
+  const int g = cand ? y / G : y;
+  if ((local_mask >> g) & 1) return;
+  const int h0 = cand ? y : y * G;
+  const int nh = cand ? 1 : G;
+  const int64_t r0 = int64_t(blockIdx.x) * R;
+  for (int i = tid; i < nh * D; i += 256) {
+    const int j = i / D, dd = i - j * D;
+    qs[j][dd] = elem_f32<T>(q + b * q_sb + (h0 + j) * q_sh + dd);
+  }
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int PPR = D / EPV;
+  const T* kb = keys + b * k_sb + int64_t(g) * k_sh;
+  for (int i = tid; i < R * PPR; i += 256) {
+    const int r = i / PPR, pc = i - r * PPR;
+    const int64_t row = r0 + r;
+    if (row < n_rows) {
+      int64_t src = cand ? int64_t(cand[(int64_t(b) * Hq + h0) * out_len + row]) : row;
+      src = src < 0 ? 0 : (src < n_keys ? src : n_keys - 1);
+      const uint4 v = ld16(kb + src * k_st + pc * EPV);
+      const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int u = 0; u < EPV; ++u) tile[r][pc * EPV + u] = elem_f32<T>(e + u);
+    }
+  }
+  __syncthreads();
+  const int r = tid % R;
+  const int64_t row = r0 + r;
+  if (row >= n_rows) return;
+  for (int j = tid / R; j < nh; j += 256 / R) {
+    double acc = 0.0;
+    for (int i = 0; i < D; ++i) acc = fma(double(qs[j][i]), double(tile[r][i]), acc);
+    out[(int64_t(b) * Hq + h0 + j) * out_len + row] = acc;
+  }
+}
+
+// Projected query q_p = q P (d -> 16) per scored head, fp64, index order. A bf16 or fp32 query
+// times an fp32 projection entry is exact in fp64.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_proxy_query(const T* __restrict__ q, int64_t q_sb, int64_t q_sh,
+                                                     const float* __restrict__ proj, int G, int Hq,
+                                                     uint64_t local_mask, double* __restrict__ qp,
+                                                     uint32_t* __restrict__ status) {
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.x == 0 && b == 0 && threadIdx.x < 4) status[threadIdx.x] = 0;
+  const int h = t >> 4, j = t & 15;
+  if (h >= Hq) return;
+  const int g = h / G;
+  double acc = 0.0;
+  if (!((local_mask >> g) & 1)) {
+    const float* P = proj + int64_t(g) * D * 16;
+    const T* qh = q + b * q_sb + h * q_sh;
+    for (int i = 0; i < D; ++i) acc = fma(double(elem_f32<T>(qh + i)), double(P[i * 16 + j]), acc);
+  }
+  qp[(int64_t(b) * Hq + h) * 16 + j] = acc;
+}
+
+// Proxy scores s_t = q_p . k_p[t] over the 16 proxy dims, separate multiply and add in index
+// order (q_p has 53 significant bits, so the products round). One thread per token; the
+// group's G heads share the token's proxy key. Also writes per-block max / min per head.
+__global__ __launch_bounds__(256) void k_score_proxy(const uint16_t* __restrict__ kp, int64_t kp_sb,
+                                                     int64_t kp_sh, int64_t kp_st, const double* __restrict__ qp,
+                                                     int G, int Hq, int64_t N, uint64_t local_mask,
+                                                     double* __restrict__ s0, double* __restrict__ pmax,
+                                                     double* __restrict__ pmin, int nblk) {
+  const int b = blockIdx.z, g = blockIdx.y, tid = threadIdx.x;
+  if ((local_mask >> g) & 1) return;
+  __shared__ double qs[kMaxGroup][16];
+  __shared__ double rmax[kMaxGroup][4], rmin[kMaxGroup][4];
+  if (tid < G * 16) qs[tid >> 4][tid & 15] = qp[(int64_t(b) * Hq + g * G + (tid >> 4)) * 16 + (tid & 15)];
+  __syncthreads();
+  const int64_t t = int64_t(blockIdx.x) * 256 + tid;
+  const bool valid = t < N;
+  double kd[16];
+  if (valid) {
+    const uint16_t* row = kp + b * kp_sb + int64_t(g) * kp_sh + t * kp_st;
+    const uint4 a = ld16(row), c = ld16(row + 8);
+    const _Float16* ha = reinterpret_cast<const _Float16*>(&a);
+    const _Float16* hc = reinterpret_cast<const _Float16*>(&c);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      kd[j] = double(float(ha[j]));
+      kd[j + 8] = double(float(hc[j]));
+    }
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int j = 0; j < G; ++j) {
+    double acc = 0.0;
+    if (valid) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc = acc + qs[j][u] * kd[u];
+      s0[(int64_t(b) * Hq + g * G + j) * N + t] = acc;
+    }
+    const double mx = wave_max(valid ? acc : kNegInfD);
+    const double mn = wave_min(valid ? acc : kPosInfD);
+    if (lane == 0) {
+      rmax[j][wave] = mx;
+      rmin[j][wave] = mn;
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    const double mx = fmax(fmax(rmax[tid][0], rmax[tid][1]), fmax(rmax[tid][2], rmax[tid][3]));
+    const double mn = fmin(fmin(rmin[tid][0], rmin[tid][1]), fmin(rmin[tid][2], rmin[tid][3]));
+    pmax[(int64_t(b) * Hq + g * G + tid) * nblk + blockIdx.x] = mx;
+    pmin[(int64_t(b) * Hq + g * G + tid) * nblk + blockIdx.x] = mn;
+  }
+}
+
+// Per-256-entry max / min of score rows that take the long-row path on summary routing.
+__global__ __launch_bounds__(256) void k_row_minmax(const double* __restrict__ s0, int64_t len, int G, int Hq,
+                                                    uint64_t local_mask, double* __restrict__ pmax,
+                                                    double* __restrict__ pmin, int nblk) {
+  const int b = blockIdx.z, h = blockIdx.y, tid = threadIdx.x;
+  if ((local_mask >> (h / G)) & 1) return;
+  __shared__ double rmax[4], rmin[4];
+  const int64_t t = int64_t(blockIdx.x) * 256 + tid;
+  const int64_t row = int64_t(b) * Hq + h;
+  const double v = t < len ? s0[row * len + t] : 0.0;
+  const double mx = wave_max(t < len ? v : kNegInfD), mn = wave_min(t < len ? v : kPosInfD);
+  if ((tid & 63) == 0) {
+    rmax[tid >> 6] = mx;
+    rmin[tid >> 6] = mn;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    pmax[row * nblk + blockIdx.x] = fmax(fmax(rmax[0], rmax[1]), fmax(rmax[2], rmax[3]));
+    pmin[row * nblk + blockIdx.x] = fmin(fmin(rmin[0], rmin[1]), fmin(rmin[2], rmin[3]));
+  }
+}
+
+template <typename T, int D>
+int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStream_t st) {
+  const sd_config& c = p.cfg;
+  const int B = c.batch, Hq = c.n_q_heads, Hk = c.n_kv_heads;
+  uint32_t* status = at<uint32_t>(ws, p.o_status);
+  if (c.route == SD_ROUTE_PROXY) {
+    const int nb = (Hq * 16 + 255) / 256;
+    hipLaunchKernelGGL((k_proxy_query<T, D>), dim3(nb, B), dim3(256), 0, st, static_cast<const T*>(t.q), t.q_sb,
+                       t.q_sh, t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status);
+    hipLaunchKernelGGL(k_score_proxy, dim3(p.score_blocks0, Hk, B), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(t.kp), t.kp_sb, t.kp_sh, t.kp_st, at<double>(ws, p.o_qp),
+                       p.G, Hq, c.n_ctx, p.local_mask, at<double>(ws, p.o_s0), at<double>(ws, p.o_pmax),
+                       at<double>(ws, p.o_pmin), p.score_blocks0);
+    return int(hipGetLastError());
+  }
+  if (c.mode == SD_HIER_TOPK && level == 1) {
+    hipLaunchKernelGGL((k_score_rows<T, D>), dim3((p.len1 + 63) / 64, Hq, B), dim3(256), 0, st,
+                       static_cast<const T*>(t.q), t.q_sb, t.q_sh, static_cast<const T*>(t.kg), t.g_sb, t.g_sh,
+                       t.g_st, at<int32_t>(ws, p.o_cand), p.len1, p.M, p.G, Hq, p.local_mask, at<double>(ws, p.o_s1),
+                       p.len1, static_cast<uint32_t*>(nullptr));
+    return int(hipGetLastError());
+  }
+  const bool meta = c.mode == SD_HIER_TOPK;
+  hipLaunchKernelGGL((k_score_rows<T, D>), dim3((p.len0 + 63) / 64, Hk, B), dim3(256), 0, st,
+                     static_cast<const T*>(t.q), t.q_sb, t.q_sh, static_cast<const T*>(meta ? t.kmg : t.kg),
+                     meta ? t.mg_sb : t.g_sb, meta ? t.mg_sh : t.g_sh, meta ? t.mg_st : t.g_st,
+                     static_cast<const int32_t*>(nullptr), p.len0, p.len0, p.G, Hq, p.local_mask, at<double>(ws, p.o_s0),
+                     p.len0, status);
+  if (p.long0)
+    hipLaunchKernelGGL(k_row_minmax, dim3(p.score_blocks0, Hq, B), dim3(256), 0, st, at<double>(ws, p.o_s0),
+                       p.len0, p.G, Hq, p.local_mask, at<double>(ws, p.o_pmax), at<double>(ws, p.o_pmin),
+                       p.score_blocks0);
+  return int(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_score(const Plan& p, const sd_tensors& t, int level, char* ws, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const sd_config& c = p.cfg;
+  if (c.kv_dtype == SD_BF16)
+    return c.head_dim == 128 ? score_impl<uint16_t, 128>(p, t, level, ws, st)
+                             : score_impl<uint16_t, 64>(p, t, level, ws, st);
+  return c.head_dim == 128 ? score_impl<float, 128>(p, t, level, ws, st) : score_impl<float, 64>(p, t, level, ws, st);
+}
+
+}  // namespace sd

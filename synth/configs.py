@@ -48,7 +48,7 @@ class Workload:
     plant: str = ""            # synthetic structure recipe, see synth.gen
     plants_per_head: int = 0
     zipf_s: float = 0.0
-    split_entries: int = 0     # list entries per split-K work item (0 = library default)
+    attend_blocks: int = 0     # persistent attention workgroups (0 = library default)
     seed: int = 0
 
     # derived -------------------------------------------------------------
@@ -138,5 +138,5 @@ def library_params(w: Workload) -> dict:
         top_k=w.top_k, top_k_seg=w.top_k_seg, seg_size=w.seg_size, top_p=w.top_p,
         select_scale=w.select_scale, softmax_scale=w.softmax_scale,
         keep_first=w.keep_first, keep_last=w.keep_last, sink=w.sink, window=w.window,
-        attend_summary=w.attend_summary and w.mode != PROXY_TOPP, split_entries=w.split_entries,
+        attend_summary=w.attend_summary and w.mode != PROXY_TOPP, attend_blocks=w.attend_blocks,
         head_mode=[1 if g in w.local_kv_heads else 0 for g in range(w.n_kv_heads)])

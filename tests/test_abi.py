@@ -56,7 +56,7 @@ BAD = [
     (dict(select_scale=0.0), N.SD_EINVAL, "select_scale"),
     (dict(softmax_scale=-1.0), N.SD_EINVAL, "softmax_scale"),
     (dict(mode="topk", top_k=0), N.SD_EINVAL, "top_k"),
-    (dict(split_entries=4096), N.SD_EINVAL, "split_entries"),
+    (dict(attend_blocks=-1), N.SD_EINVAL, "attend_blocks"),
     (dict(keep_first=-1), N.SD_EINVAL, "keep_first"),
     (dict(head_mode=[0, 1, 0, 0, 0, 0, 0, 2]), N.SD_EINVAL, "head_mode"),
     (dict(head_mode=[0, 1, 0, 0, 0, 0, 0, 0]), N.SD_EINVAL, "chunk_size must be 1"),
