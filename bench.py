@@ -206,7 +206,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "context": w.n_ctx, "chunk": w.chunk_size, "mode": w.mode,
                    "top_p": w.top_p if w.mode in ("topp", "proxy") else None,
-                   "top_k": w.top_k or None, "attend_blocks": dec.params.get("attend_blocks") or 512},
+                   "top_k": w.top_k or None, "attend_blocks": dec.params.get("attend_blocks") or 256},
         "hbm_gbps": round(step_gbps, 1),
         "hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
         "step_bytes": nb["step"],

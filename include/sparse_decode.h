@@ -89,7 +89,7 @@ typedef struct {
   int32_t window;         /* ... and [N - window, N); needs C == 1 */
   int32_t attend_summary; /* 1: the hybrid context adds the selected chunks' summary K/V */
   int32_t attend_blocks;  /* persistent attention workgroups, each streaming an equal slice
-                             of all groups' tiles; 0 = library default (512: two per CU of a
+                             of all groups' tiles; 0 = library default (256: one per CU of a
                              256-CU MI355X) */
   const int8_t* head_mode;/* HOST array [n_kv_heads]: 0 = scored head, 1 = local head;
                              NULL = all scored. Copied at init. */

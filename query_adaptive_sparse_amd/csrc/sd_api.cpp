@@ -67,10 +67,11 @@ sd_status check_cfg(const sd_config& c) {
     const int64_t M = c.n_ctx / c.chunk_size;
     if (c.seg_size < 1 || M % c.seg_size) return fail(SD_EINVAL, "seg_size %d must divide the %lld chunks", c.seg_size, (long long)M);
     if (c.top_k_seg < 1) return fail(SD_EINVAL, "top_k_seg must be >= 1");
-    if (M / c.seg_size > sd::kSmallRowMax) return fail(SD_EUNSUPPORTED, "more than %d segments", sd::kSmallRowMax);
+    const int64_t lim = sd::small_row_limit(c.n_q_heads / c.n_kv_heads);
+    if (M / c.seg_size > lim) return fail(SD_EUNSUPPORTED, "more than %lld segments", (long long)lim);
     if (M > int64_t(32) * 4096) return fail(SD_EUNSUPPORTED, "two-level selection over more than %d chunks", 32 * 4096);
-    if (int64_t(std::min<int64_t>(c.top_k_seg, M / c.seg_size)) * c.seg_size > sd::kSmallRowMax)
-      return fail(SD_EUNSUPPORTED, "top_k_seg * seg_size > %d candidates", sd::kSmallRowMax);
+    if (int64_t(std::min<int64_t>(c.top_k_seg, M / c.seg_size)) * c.seg_size > lim)
+      return fail(SD_EUNSUPPORTED, "top_k_seg * seg_size > %lld candidates", (long long)lim);
   }
   if (!(c.softmax_scale > 0.0f) || !std::isfinite(c.softmax_scale)) return fail(SD_EINVAL, "softmax_scale must be finite and > 0");
   if (c.keep_first < 0 || c.keep_last < 0) return fail(SD_EINVAL, "keep_first / keep_last must be >= 0");
@@ -108,6 +109,7 @@ void plan_workspace(sd::Plan& p) {
     return o;
   };
   p.o_status = take(64);
+  p.o_arrive = take(size_t(B * Hk) * 4);
   p.o_qp = take(c.route == SD_ROUTE_PROXY ? size_t(B * Hq * 16) * 8 : 0);
   p.o_s0 = take(size_t(B * Hq * p.len0) * 8);
   p.o_s1 = take(size_t(B * Hq * p.len1) * 8);
@@ -195,7 +197,7 @@ sd_status sparse_decode_init(const sd_config* cfg, sd_handle** out, size_t* work
   p.levels = c.mode == SD_HIER_TOPK ? 2 : 1;
   p.len0 = c.mode == SD_HIER_TOPK ? p.S : p.M;
   p.len1 = c.mode == SD_HIER_TOPK ? int64_t(std::min(c.top_k_seg, p.S)) * c.seg_size : 0;
-  p.long0 = p.len0 > sd::kSmallRowMax;
+  p.long0 = p.len0 > sd::small_row_limit(p.G);
   p.words = (p.M + 31) / 32;
   p.ranges = int32_t((p.words + 1023) / 1024);
   p.attend_blocks = c.attend_blocks ? c.attend_blocks : sd::kAttendBlocks;

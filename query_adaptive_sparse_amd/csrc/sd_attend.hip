@@ -199,9 +199,9 @@ struct Attender {
       pr[i] = none ? 0.f : __builtin_amdgcn_exp2f(lg[i] - mn);
       s.l += pr[i];
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // LDS operations of one wave complete in order: the V tile written above is visible to the
+    // reads below without a wait; the barrier only keeps the compiler from reordering them.
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // ---- P V: P is the A operand (row = head slot, k = tokens 4c .. 4c+3), V the B operand
     if constexpr (CF::BF) {
       const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
@@ -229,9 +229,7 @@ struct Attender {
           s.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, vtf[(4 * c + i) * CF::kRowWords + 16 * nb + n], s.acc[nb], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
   // This wave's tiles of [u0, u1) (alternating with the other waves) through an NS-stage register
@@ -246,18 +244,19 @@ struct Attender {
     TileRegs<T, D> R[NS];
     auto tile = [&](int k) { return first + k * kWaves; };
     auto nv_of = [&](int t) { return min(kTile, limit - t * kTile); };
+    // Loads are issued unconditionally (past the end they repeat the wave's last tile, which is
+    // still cached), so the compiler can count the loads in flight exactly and wait only for the
+    // stage being computed.
+    auto clamp = [&](int k) { return tile(k < nt ? k : nt - 1); };
 #pragma unroll
-    for (int k = 0; k < NS - 1; ++k)
-      if (k < nt) issue(R[k], summary, tile(k) * kTile, nv_of(tile(k)), e0);
+    for (int k = 0; k < NS - 1; ++k) issue(R[k], summary, clamp(k) * kTile, nv_of(clamp(k)), e0);
     for (int k0 = 0; k0 < nt; k0 += NS) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const int k = k0 + j;
-        if (k < nt) {
-          const int kn = k + NS - 1;
-          if (kn < nt) issue(R[(j + NS - 1) % NS], summary, tile(kn) * kTile, nv_of(tile(kn)), e0);
-          compute(R[j], nv_of(tile(k)), s);
-        }
+        const int kn = k + NS - 1;
+        issue(R[(j + NS - 1) % NS], summary, clamp(kn) * kTile, nv_of(clamp(kn)), e0);
+        if (k < nt) compute(R[j], nv_of(tile(k)), s);
       }
     }
   }

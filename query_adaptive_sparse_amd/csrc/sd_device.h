@@ -69,6 +69,84 @@ __device__ __forceinline__ uint32_t edge_bits(int64_t w, int64_t n, int64_t firs
   return m;
 }
 
+// ---- wave-level reductions and scans on DPP (no LDS round trip). Each has a fixed association,
+// and reductions return one lane's value through readlane, so every lane holds the same bits.
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, true);
+  return __hiloint2double(hi, lo);
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
+  return __hiloint2double(hi, lo);
+}
+
+// Row-of-16 reduction: every lane of a row ends with the row's result.
+#define SD_ROW_REDUCE(v, OP)                      \
+  v = OP(v, dpp_f64<kDppQuadXor1>(v));            \
+  v = OP(v, dpp_f64<kDppQuadXor2>(v));            \
+  v = OP(v, dpp_f64<kDppRowRor4>(v));             \
+  v = OP(v, dpp_f64<kDppRowRor8>(v));
+
+__device__ __forceinline__ double dpp_add(double a, double b) { return a + b; }
+
+__device__ __forceinline__ double wave_max_dpp(double v) {
+  SD_ROW_REDUCE(v, fmax)
+  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+__device__ __forceinline__ double wave_min_dpp(double v) {
+  SD_ROW_REDUCE(v, fmin)
+  return fmin(fmin(readlane_f64(v, 0), readlane_f64(v, 16)), fmin(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  SD_ROW_REDUCE(v, dpp_add)
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+__device__ __forceinline__ int wave_min_i32_dpp(int v) {
+  v = min(v, dpp_i32<kDppQuadXor1>(v));
+  v = min(v, dpp_i32<kDppQuadXor2>(v));
+  v = min(v, dpp_i32<kDppRowRor4>(v));
+  v = min(v, dpp_i32<kDppRowRor8>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+// Inclusive scans across the wave: shifts within rows of 16, then the earlier rows' totals.
+__device__ __forceinline__ double wave_scan_dpp(double v, int lane) {
+  v += dpp_f64<kDppRowShr1>(v);
+  v += dpp_f64<kDppRowShr2>(v);
+  v += dpp_f64<kDppRowShr4>(v);
+  v += dpp_f64<kDppRowShr8>(v);
+  const double t0 = readlane_f64(v, 15), t1 = readlane_f64(v, 31), t2 = readlane_f64(v, 47);
+  const int r = lane >> 4;
+  const double off = r == 0 ? 0.0 : (r == 1 ? t0 : (r == 2 ? t0 + t1 : (t0 + t1) + t2));
+  return v + off;
+}
+__device__ __forceinline__ int wave_scan_i32_dpp(int v, int lane) {
+  v += dpp_i32<kDppRowShr1>(v);
+  v += dpp_i32<kDppRowShr2>(v);
+  v += dpp_i32<kDppRowShr4>(v);
+  v += dpp_i32<kDppRowShr8>(v);
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31),
+            t2 = __builtin_amdgcn_readlane(v, 47);
+  const int r = lane >> 4;
+  return v + (r == 0 ? 0 : (r == 1 ? t0 : (r == 2 ? t0 + t1 : t0 + t1 + t2)));
+}
+
 template <typename T>
 inline T* at(char* ws, size_t off) {
   return reinterpret_cast<T*>(ws + off);

@@ -10,7 +10,9 @@ namespace sd {
 
 // Rows up to this length are selected by one workgroup sorting them in LDS;
 // longer rows (token-level selection) take the histogram path.
-constexpr int kSmallRowMax = 4096;
+constexpr int kSmallRowMax = 2048;
+constexpr int64_t small_row_limit(int) { return kSmallRowMax; }
+
 // Histogram resolution of the long-row path: coarse bins over the row's score
 // range, then fine bins inside the crossing coarse bin.
 constexpr int kBins1 = 4096;
@@ -25,7 +27,7 @@ constexpr int kWaves = 4;
 constexpr int kMaxGroup = 8;
 constexpr int kMaxKvHeads = 64;
 // Attention: persistent workgroups (default) and the most (sequence, KV group) pairs per call.
-constexpr int kAttendBlocks = 512;
+constexpr int kAttendBlocks = 256;
 constexpr int kMaxGroups = 4096;
 
 struct Plan {
@@ -44,7 +46,7 @@ struct Plan {
   int32_t score_blocks0;    // blocks per row of the long-row score pass (partial max/min)
   int32_t long_blocks;      // blocks per row of the long-row histogram passes
   // workspace byte offsets
-  size_t o_status, o_qp, o_s0, o_s1, o_cand, o_bits, o_ubits, o_rcnt, o_list, o_cnt;
+  size_t o_status, o_arrive, o_qp, o_s0, o_s1, o_cand, o_bits, o_ubits, o_rcnt, o_list, o_cnt;
   size_t o_gpre, o_po, o_pl, o_pmax, o_pmin, o_info, o_h1m, o_h1c, o_h2m, o_h2c, o_ckey, o_cidx, o_ccnt;
   size_t ws_bytes;
 };

@@ -7,57 +7,63 @@
 namespace sd {
 namespace {
 // ---------------------------------------------------------------------------------------------
-// Scores. One workgroup scores 64 rows of summary keys (or per-head candidate rows) against the
-// group's queries. The key tile is staged in LDS as fp32 (exact for bf16 and fp32 inputs); each
-// thread owns one (row, head) score and accumulates it in fp64 over d in index order. Each
-// product of two bf16 or two fp32 values is exact in fp64, so fma(q, k, acc) equals the CPU's
-// acc + q*k, step for step.
+// Scores. One thread per (summary row, query head): the head slots of a row sit in adjacent lanes,
+// which load the row's 16-byte pieces together (one fetch from L1), and each thread accumulates
+// its dot product in fp64, one fma per dimension in index order. A product of two bf16 or two
+// fp32 values is exact in fp64, so fma(q, k, acc) equals the CPU's acc + q*k step for step.
+// Block (0, 0, 0) also clears the device status words and the per-group arrival counters of the
+// selection.
 // ---------------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, int64_t q_sb, int64_t q_sh,
                                                     const T* __restrict__ keys, int64_t k_sb, int64_t k_sh,
                                                     int64_t k_st, const int32_t* __restrict__ cand,
-                                                    int64_t n_rows, int64_t n_keys, int G, int Hq,
+                                                    int64_t n_rows, int64_t n_keys, int G, int Hq, int hs_shift,
                                                     uint64_t local_mask, double* __restrict__ out, int64_t out_len,
-                                                    uint32_t* __restrict__ status) {
-  constexpr int R = 64;
-  __shared__ float tile[R][D + 1];
-  __shared__ float qs[kMaxGroup][D];
+                                                    uint32_t* __restrict__ status, int32_t* __restrict__ arrivals,
+                                                    int n_groups) {
+  constexpr int EPV = 16 / int(sizeof(T));
+  constexpr int PPR = D / EPV;
+  constexpr int QW = D + 4;  // padded query row: the head slots' reads fall in distinct banks
+  __shared__ float qs[kMaxGroup * QW];
   const int b = blockIdx.z, y = blockIdx.y, tid = threadIdx.x;
-  if (status && blockIdx.x == 0 && y == 0 && b == 0 && tid < 4) status[tid] = 0;
+  if (status && blockIdx.x == 0 && y == 0 && b == 0) {
+    if (tid < 4) status[tid] = 0;
+    for (int i = tid; i < n_groups; i += 256) arrivals[i] = 0;
+  }
   const int g = cand ? y / G : y;
   if ((local_mask >> g) & 1) return;
   const int h0 = cand ? y : y * G;
   const int nh = cand ? 1 : G;
-  const int64_t r0 = int64_t(blockIdx.x) * R;
   for (int i = tid; i < nh * D; i += 256) {
     const int j = i / D, dd = i - j * D;
-    qs[j][dd] = elem_f32<T>(q + b * q_sb + (h0 + j) * q_sh + dd);
-  }
-  constexpr int EPV = 16 / sizeof(T);
-  constexpr int PPR = D / EPV;
-  const T* kb = keys + b * k_sb + int64_t(g) * k_sh;
-  for (int i = tid; i < R * PPR; i += 256) {
-    const int r = i / PPR, pc = i - r * PPR;
-    const int64_t row = r0 + r;
-    if (row < n_rows) {
-      int64_t src = cand ? int64_t(cand[(int64_t(b) * Hq + h0) * out_len + row]) : row;
-      src = src < 0 ? 0 : (src < n_keys ? src : n_keys - 1);
-      const uint4 v = ld16(kb + src * k_st + pc * EPV);
-      const T* e = reinterpret_cast<const T*>(&v);
-#pragma unroll
-      for (int u = 0; u < EPV; ++u) tile[r][pc * EPV + u] = elem_f32<T>(e + u);
-    }
+    qs[j * QW + dd] = elem_f32<T>(q + b * q_sb + (h0 + j) * q_sh + dd);
   }
   __syncthreads();
-  const int r = tid % R;
-  const int64_t row = r0 + r;
-  if (row >= n_rows) return;
-  for (int j = tid / R; j < nh; j += 256 / R) {
-    double acc = 0.0;
-    for (int i = 0; i < D; ++i) acc = fma(double(qs[j][i]), double(tile[r][i]), acc);
-    out[(int64_t(b) * Hq + h0 + j) * out_len + row] = acc;
+  const int j = tid & ((1 << hs_shift) - 1);
+  const int64_t row = int64_t(blockIdx.x) * (256 >> hs_shift) + (tid >> hs_shift);
+  if (row >= n_rows || j >= nh) return;
+  int64_t src = cand ? int64_t(cand[(int64_t(b) * Hq + h0) * out_len + row]) : row;
+  src = src < 0 ? 0 : (src < n_keys ? src : n_keys - 1);
+  const T* kr = keys + b * k_sb + int64_t(g) * k_sh + src * k_st;
+  uint4 piece[PPR];
+#pragma unroll
+  for (int pc = 0; pc < PPR; ++pc) piece[pc] = ld16(kr + pc * EPV);
+  const float* qj = qs + j * QW;
+  double acc = 0.0;
+#pragma unroll
+  for (int pc = 0; pc < PPR; ++pc) {
+    const T* e = reinterpret_cast<const T*>(&piece[pc]);
+#pragma unroll
+    for (int u4 = 0; u4 < EPV; u4 += 4) {
+      const float4 q4 = *reinterpret_cast<const float4*>(qj + pc * EPV + u4);
+      acc = fma(double(q4.x), double(elem_f32<T>(e + u4 + 0)), acc);
+      acc = fma(double(q4.y), double(elem_f32<T>(e + u4 + 1)), acc);
+      acc = fma(double(q4.z), double(elem_f32<T>(e + u4 + 2)), acc);
+      acc = fma(double(q4.w), double(elem_f32<T>(e + u4 + 3)), acc);
+    }
   }
+  out[(int64_t(b) * Hq + h0 + j) * out_len + row] = acc;
 }
 
 // Projected query q_p = q P (d -> 16) per scored head, fp64, index order. A bf16 or fp32 query
@@ -66,10 +72,14 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_proxy_query(const T* __restrict__ q, int64_t q_sb, int64_t q_sh,
                                                      const float* __restrict__ proj, int G, int Hq,
                                                      uint64_t local_mask, double* __restrict__ qp,
-                                                     uint32_t* __restrict__ status) {
+                                                     uint32_t* __restrict__ status, int32_t* __restrict__ arrivals,
+                                                     int n_groups) {
   const int b = blockIdx.y;
   const int t = blockIdx.x * 256 + threadIdx.x;
-  if (blockIdx.x == 0 && b == 0 && threadIdx.x < 4) status[threadIdx.x] = 0;
+  if (blockIdx.x == 0 && b == 0) {
+    if (threadIdx.x < 4) status[threadIdx.x] = 0;
+    for (int i = threadIdx.x; i < n_groups; i += 256) arrivals[i] = 0;
+  }
   const int h = t >> 4, j = t & 15;
   if (h >= Hq) return;
   const int g = h / G;
@@ -164,7 +174,8 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
   if (c.route == SD_ROUTE_PROXY) {
     const int nb = (Hq * 16 + 255) / 256;
     hipLaunchKernelGGL((k_proxy_query<T, D>), dim3(nb, B), dim3(256), 0, st, static_cast<const T*>(t.q), t.q_sb,
-                       t.q_sh, t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status);
+                       t.q_sh, t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status,
+                       at<int32_t>(ws, p.o_arrive), B * Hk);
     hipLaunchKernelGGL(k_score_proxy, dim3(p.score_blocks0, Hk, B), dim3(256), 0, st,
                        static_cast<const uint16_t*>(t.kp), t.kp_sb, t.kp_sh, t.kp_st, at<double>(ws, p.o_qp),
                        p.G, Hq, c.n_ctx, p.local_mask, at<double>(ws, p.o_s0), at<double>(ws, p.o_pmax),
@@ -172,18 +183,21 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
     return int(hipGetLastError());
   }
   if (c.mode == SD_HIER_TOPK && level == 1) {
-    hipLaunchKernelGGL((k_score_rows<T, D>), dim3((p.len1 + 63) / 64, Hq, B), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_score_rows<T, D>), dim3((p.len1 + 255) / 256, Hq, B), dim3(256), 0, st,
                        static_cast<const T*>(t.q), t.q_sb, t.q_sh, static_cast<const T*>(t.kg), t.g_sb, t.g_sh,
-                       t.g_st, at<int32_t>(ws, p.o_cand), p.len1, p.M, p.G, Hq, p.local_mask, at<double>(ws, p.o_s1),
-                       p.len1, static_cast<uint32_t*>(nullptr));
+                       t.g_st, at<int32_t>(ws, p.o_cand), p.len1, p.M, p.G, Hq, 0, p.local_mask, at<double>(ws, p.o_s1),
+                       p.len1, static_cast<uint32_t*>(nullptr), static_cast<int32_t*>(nullptr), 0);
     return int(hipGetLastError());
   }
   const bool meta = c.mode == SD_HIER_TOPK;
-  hipLaunchKernelGGL((k_score_rows<T, D>), dim3((p.len0 + 63) / 64, Hk, B), dim3(256), 0, st,
-                     static_cast<const T*>(t.q), t.q_sb, t.q_sh, static_cast<const T*>(meta ? t.kmg : t.kg),
+  int hs = 0;
+  while ((1 << hs) < p.G) ++hs;
+  const int64_t rows_per_block = 256 >> hs;
+  hipLaunchKernelGGL((k_score_rows<T, D>), dim3((p.len0 + rows_per_block - 1) / rows_per_block, Hk, B), dim3(256), 0,
+                     st, static_cast<const T*>(t.q), t.q_sb, t.q_sh, static_cast<const T*>(meta ? t.kmg : t.kg),
                      meta ? t.mg_sb : t.g_sb, meta ? t.mg_sh : t.g_sh, meta ? t.mg_st : t.g_st,
-                     static_cast<const int32_t*>(nullptr), p.len0, p.len0, p.G, Hq, p.local_mask, at<double>(ws, p.o_s0),
-                     p.len0, status);
+                     static_cast<const int32_t*>(nullptr), p.len0, p.len0, p.G, Hq, hs, p.local_mask, at<double>(ws, p.o_s0),
+                     p.len0, status, at<int32_t>(ws, p.o_arrive), B * Hk);
   if (p.long0)
     hipLaunchKernelGGL(k_row_minmax, dim3(p.score_blocks0, Hq, B), dim3(256), 0, st, at<double>(ws, p.o_s0),
                        p.len0, p.G, Hq, p.local_mask, at<double>(ws, p.o_pmax), at<double>(ws, p.o_pmin),

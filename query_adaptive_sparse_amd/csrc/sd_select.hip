@@ -13,11 +13,11 @@ constexpr int kSelThreads = 512;
 
 // Sort keys[0..Lp) (Lp a power of two) so that larger keys come first and equal keys by
 // smaller index: a bitonic network over LDS.
-template <typename Idx>
+template <typename Idx, int NT = kSelThreads>
 __device__ void bitonic_desc(uint64_t* keys, Idx* idx, int Lp) {
   for (int kk = 2; kk <= Lp; kk <<= 1) {
     for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < Lp; i += kSelThreads) {
+      for (int i = threadIdx.x; i < Lp; i += NT) {
         const int ixj = i ^ j;
         if (ixj > i) {
           const uint64_t ka = keys[i], kb = keys[ixj];
@@ -83,89 +83,400 @@ __device__ int block_first_crossing(int n, double base, double target, WF weight
 }
 
 // ---------------------------------------------------------------------------------------------
-// Selection of rows up to kSmallRowMax entries: one workgroup per (sequence, query head) sorts
-// the row by (score desc, index asc) in LDS, then takes the first k (top-k) or the shortest
-// prefix whose softmax mass reaches p * Z (top-p; masses and their prefix sums in fp64, fixed
-// reduction order). kind 0: bitmap of the row's entries. kind 1 (two-level, level 0): the kept
-// segments' chunks as ascending candidate lists. kind 2 (level 1): bitmap over the chunks named
-// by the candidate list.
+// Selection of rows up to kSmallRowMax entries, fused with the GQA union and the compaction.
+// One 256-thread workgroup per (sequence, query head); the row lives in registers, at most
+// kLaneEntries per lane:
+//   1. fp64 scores, their range and, for top-p, the masses w = exp(scale*s - scale*smax) and Z
+//      (fixed-order DPP reductions: every lane holds the same bits);
+//   2. a 256-bin histogram of the weights (mass, or 1 for top-k) over the bins of (smax - s)
+//      finds the bin where the running weight reaches the target (p*Z or k); if that bin holds
+//      more than kCandCap entries a second 256-bin level splits it;
+//   3. the crossing bin's entries are ranked in (score desc, index asc) order by counting and
+//      their weights walked from the weight of everything ahead of the bin to the first crossing.
+// Bins are monotone in the score, so every entry of an earlier bin precedes every entry of a
+// later bin in the order: the result equals the sorted-prefix rule. A crossing bin still holding
+// more than kCandCap entries after two levels (a mass of near-equal scores) falls back to a full
+// sort of the row in LDS.
+// The last workgroup of a group to finish (arrival counter; release / acquire fences at device
+// scope) ORs the group's per-head bitmaps with the forced or local entries and writes the
+// ascending list.
+// kind 0: flat rows. kind 1: two-level, level 0 (kept segments -> ascending candidate chunk
+// lists, no union). kind 2: two-level, level 1 (kept candidates -> chunk bitmaps -> union).
 // ---------------------------------------------------------------------------------------------
-constexpr int kLdsBitsWords = 4096;
+constexpr int kNBin = 256;
+constexpr int kCandCap = 256;
+constexpr int kSelT = 256;                          // threads per head
+constexpr int kSelW = kSelT / 64;                   // waves per head
+constexpr int kLaneEntries = kSmallRowMax / kSelT;  // 8
+constexpr int kUnionWordsMax = 4096;
 
-__global__ __launch_bounds__(kSelThreads) void k_select_small(
-    const double* __restrict__ s, int64_t len, int Hq, int G, uint64_t local_mask, int topp, int k, double p,
-    double scale, int kind, const int32_t* __restrict__ cand_in, int32_t* __restrict__ cand_out, int seg_size,
-    int64_t cand_len, uint32_t* __restrict__ bits, int64_t words) {
-  __shared__ uint64_t keys[kSmallRowMax];
-  __shared__ uint16_t idx[kSmallRowMax];
-  __shared__ double buf[kSelThreads];
-  __shared__ int ibuf;
-  __shared__ uint32_t lbits[kLdsBitsWords];
-  const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
-  const int64_t row = int64_t(b) * Hq + h;
-  const bool local = (local_mask >> (h / G)) & 1;
-  if (local) {
-    if (kind != 1)
-      for (int64_t w = tid; w < words; w += kSelThreads) bits[row * words + w] = 0;
-    return;
+struct GroupSelArgs {
+  const double* s;
+  int64_t len;  // row length (entries scored per head)
+  int Hq, Hk, G;
+  uint64_t local_mask;
+  int topp, k;
+  double p, scale;
+  int kind;
+  const int32_t* cand_in;  // kind 2: [B][Hq][len] chunk id of each candidate
+  int32_t* cand_out;       // kind 1: [B][Hq][cand_len]
+  int seg_size;
+  int64_t cand_len;
+  uint32_t* bits;  // per-head bitmaps [B][Hq][words]
+  int64_t words;
+  int32_t* list;      // [B][Hk][n_entries]
+  int32_t* cnt;       // [B][Hk]
+  int32_t* arrivals;  // [B][Hk], cleared by the score pass
+  int64_t n_entries;
+  int keep_first, keep_last, sink, window;
+};
+
+// Bin of a score: coarse bin of (smax - s) over the row's range, and its fine sub-bin.
+__device__ __forceinline__ void bins_of(double s, double smax, double binscale, int* c1, int* c2) {
+  double d = (smax - s) * binscale;
+  d = d >= 0.0 ? (d < double(kNBin) ? d : double(kNBin)) : 0.0;
+  int b = int(d);
+  b = b < kNBin - 1 ? b : kNBin - 1;
+  *c1 = b;
+  int f = int((d - double(b)) * double(kNBin));
+  *c2 = f < 0 ? 0 : (f < kNBin - 1 ? f : kNBin - 1);
+}
+
+__global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
+  __shared__ double hm[kNBin];
+  __shared__ uint32_t hc[kNBin];
+  __shared__ uint64_t ckey[kCandCap];
+  __shared__ double cw[kCandCap];
+  __shared__ double rw[kCandCap];
+  __shared__ uint16_t cidx[kCandCap];
+  __shared__ uint16_t ridx[kCandCap];
+  __shared__ uint32_t selb[kSmallRowMax / 32];
+  __shared__ uint32_t ubits[kUnionWordsMax];
+  __shared__ uint64_t fkey[kSmallRowMax];  // whole-row fallback sort
+  __shared__ uint16_t fidx[kSmallRowMax];
+  __shared__ double wred[kSelW], wred2[kSelW];
+  __shared__ int wcnt[kSelW];
+  __shared__ double res_d;
+  __shared__ int res_i, res_state, ncand, is_last;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int G = a.G, g = h / G;
+  const int L = int(a.len);
+  const bool local = (a.local_mask >> g) & 1;
+  const int64_t row = int64_t(b) * a.Hq + h;
+  const int words_row = (L + 31) / 32;
+
+  for (int w = tid; w < words_row; w += kSelT) selb[w] = 0;
+  for (int i = tid; i < kNBin; i += kSelT) {
+    hm[i] = 0.0;
+    hc[i] = 0;
   }
-  const int L = int(len);
-  int Lp = 2;
-  while (Lp < L) Lp <<= 1;
-  for (int i = tid; i < Lp; i += kSelThreads) {
-    keys[i] = i < L ? dkey(s[row * len + i]) : 0ull;
-    idx[i] = uint16_t(i);
+  if (tid == 0) ncand = 0;
+
+  // ---- 1. scores (unconditional, clamped loads), range, weights, target
+  double sv[kLaneEntries], wt[kLaneEntries];
+  const int EPL = (L + kSelT - 1) / kSelT;
+#pragma unroll
+  for (int k = 0; k < kLaneEntries; ++k) {
+    const int i = tid + kSelT * k;
+    sv[k] = local ? 0.0 : a.s[row * a.len + (i < L ? i : L - 1)];
   }
-  const int bw = kind == 1 ? (L + 31) / 32 : int(words);
-  for (int w = tid; w < bw; w += kSelThreads) lbits[w] = 0;
-  __syncthreads();
-  bitonic_desc<uint16_t>(keys, idx, Lp);
-  int n_sel;
-  if (!topp) {
-    n_sel = k < L ? k : L;
-  } else if (p >= 1.0) {
-    n_sel = L;
-  } else {
-    const double ellmax = scale * dkey_inv(keys[0]);
-    auto mass = [&](int i) { return exp(scale * dkey_inv(keys[i]) - ellmax); };
-    // Z over every entry, then the first prefix reaching p * Z
-    const int per = (L + kSelThreads - 1) / kSelThreads;
-    double local_z = 0.0;
-    for (int i = tid * per; i < min(L, tid * per + per); ++i) local_z += mass(i);
-    double Z;
-    block_excl_scan(local_z, buf, &Z);
-    const int pos = block_first_crossing(L, 0.0, p * Z, mass, buf, &ibuf);
-    n_sel = pos < 0 ? L : pos + 1;
-  }
-  for (int i = tid; i < n_sel; i += kSelThreads) {
-    int e = idx[i];
-    if (kind == 2) {
-      e = cand_in[row * len + e];
-      e = e < 0 ? 0 : (e < int(words) * 32 ? e : int(words) * 32 - 1);
+  double smax = kNegInfD, smin = kPosInfD;
+#pragma unroll
+  for (int k = 0; k < kLaneEntries; ++k) {
+    if (tid + kSelT * k < L) {
+      smax = fmax(smax, sv[k]);
+      smin = fmin(smin, sv[k]);
     }
-    atomicOr(&lbits[e >> 5], 1u << (e & 31));
+  }
+  smax = wave_max_dpp(smax);
+  smin = wave_min_dpp(smin);
+  if (lane == 0) {
+    wred[wv] = smax;
+    wred2[wv] = smin;
   }
   __syncthreads();
-  if (kind != 1) {
-    for (int64_t w = tid; w < words; w += kSelThreads) bits[row * words + w] = lbits[w];
+  smax = fmax(fmax(wred[0], wred[1]), fmax(wred[2], wred[3]));
+  smin = fmin(fmin(wred2[0], wred2[1]), fmin(wred2[2], wred2[3]));
+  __syncthreads();
+  const bool all = a.topp ? (a.p >= 1.0) : (a.k >= L);
+  const double ellmax = a.scale * smax;
+  const double range = smax - smin;
+  const double binscale = range > 0.0 ? double(kNBin) / range : 0.0;
+  const bool work = !local && !all;
+  double z = 0.0;
+#pragma unroll
+  for (int k = 0; k < kLaneEntries; ++k) {
+    wt[k] = 0.0;
+    if (work && k < EPL && tid + kSelT * k < L) {
+      wt[k] = a.topp ? exp(a.scale * sv[k] - ellmax) : 1.0;
+      z += wt[k];
+    }
+  }
+  double target = double(a.k);
+  if (a.topp) {
+    z = wave_sum_dpp(z);
+    if (lane == 0) wred[wv] = z;
+    __syncthreads();
+    target = a.p * ((wred[0] + wred[1]) + (wred[2] + wred[3]));
+  }
+
+  // ---- 2. histograms (two levels at most) and the crossing bin
+  // state: 0 = next level, 1 / 2 = resolved at that level, 3 = fallback, 4 = every entry,
+  // 5 = the whole crossing coarse bin, 6 = nothing to select (local head)
+  int state = local ? 6 : (all ? 4 : 0);
+  int b1 = 0, b2 = 0;
+  double before = 0.0;
+  for (int lv = 1; lv <= 2 && state == 0; ++lv) {
+#pragma unroll
+    for (int k = 0; k < kLaneEntries; ++k) {
+      if (k < EPL && tid + kSelT * k < L) {
+        int c1, c2;
+        bins_of(sv[k], smax, binscale, &c1, &c2);
+        if (lv == 2 && c1 != b1) continue;
+        const int bin = lv == 1 ? c1 : c2;
+        unsafeAtomicAdd(&hm[bin], wt[k]);
+        atomicAdd(&hc[bin], 1u);
+      }
+    }
+    __syncthreads();
+    if (wv == 0) {
+      double wl = 0.0;
+      for (int j = 0; j < 4; ++j) wl += hm[4 * lane + j];
+      const double incl = wave_scan_dpp(wl, lane);
+      double c = before + (incl - wl);
+      int hit = -1;
+      double before_hit = 0.0;
+      for (int j = 0; j < 4 && hit < 0; ++j) {
+        const double cn = c + hm[4 * lane + j];
+        if (cn >= target) {
+          hit = 4 * lane + j;
+          before_hit = c;
+        }
+        c = cn;
+      }
+      const uint64_t m = __ballot(hit >= 0);
+      const int first = m ? __ffsll((unsigned long long)m) - 1 : 0;
+      const int hb = __builtin_amdgcn_readlane(hit, first);  // first is wave-uniform
+      const double bb = readlane_f64(before_hit, first);
+      if (lane == 0) {
+        if (!m) {
+          // rounding left the target above the weight of the scanned bins: at level 1 every
+          // entry is kept; at level 2 the whole crossing coarse bin is
+          res_state = lv == 1 ? 4 : 5;
+        } else {
+          res_i = hb;
+          res_d = bb;
+          res_state = hc[hb] <= uint32_t(kCandCap) ? lv : (lv == 2 ? 3 : 0);
+        }
+      }
+    }
+    __syncthreads();
+    state = res_state;
+    if (state != 4 && state != 5) {
+      if (lv == 1) b1 = res_i; else b2 = res_i;
+      before = res_d;
+    }
+    if (state == 0) {
+      for (int i = tid; i < kNBin; i += kSelT) {
+        hm[i] = 0.0;
+        hc[i] = 0;
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- 3. mark entries ahead of the crossing bin (ballots), gather the crossing bin's entries
+  const bool marking = state == 1 || state == 2 || state == 4 || state == 5;
+#pragma unroll
+  for (int k = 0; k < kLaneEntries; ++k) {
+    if (k < EPL) {  // uniform across the workgroup
+      const int i = tid + kSelT * k;
+      bool sel = false, cand = false;
+      if (marking && i < L) {
+        sel = state == 4;
+        if (state != 4) {
+          int c1, c2;
+          bins_of(sv[k], smax, binscale, &c1, &c2);
+          if (state == 1) {
+            sel = c1 < b1;
+            cand = c1 == b1;
+          } else {
+            sel = c1 < b1 || (c1 == b1 && (state == 5 || c2 < b2));
+            cand = state == 2 && c1 == b1 && c2 == b2;
+          }
+        }
+      }
+      const uint64_t ms = __ballot(sel);
+      const int wbase = tid - lane + kSelT * k;  // first entry of this wave's 64
+      if (lane == 0 && wbase < L) selb[wbase >> 5] = uint32_t(ms);
+      if (lane == 1 && wbase + 32 < L) selb[(wbase >> 5) + 1] = uint32_t(ms >> 32);
+      const uint64_t mc = __ballot(cand);
+      if (mc) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&ncand, __popcll(mc));
+        base = __builtin_amdgcn_readlane(base, 0);
+        if (cand) {
+          const int pos = base + __builtin_amdgcn_mbcnt_hi(uint32_t(mc >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mc), 0));
+          ckey[pos] = dkey(sv[k]);
+          cidx[pos] = uint16_t(i);
+          cw[pos] = wt[k];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. order the candidates (ranks by counting) or, in the fallback, the whole row (sort),
+  // then walk their weights from the weight ahead of them to the first crossing
+  int n = 0;
+  const double* wo = rw;         // weights in order
+  const uint16_t* io = ridx;     // entries in order
+  if (state == 1 || state == 2) {
+    n = ncand;
+    for (int c = tid; c < n; c += kSelT) {
+      const uint64_t kc = ckey[c];
+      const uint16_t ic = cidx[c];
+      int r = 0;
+      for (int d = 0; d < n; ++d) {
+        const uint64_t kd = ckey[d];
+        r += (kd > kc || (kd == kc && cidx[d] < ic)) ? 1 : 0;
+      }
+      rw[r] = cw[c];
+      ridx[r] = ic;
+    }
+  } else if (state == 3) {
+    n = L;
+    int lp = 2;
+    while (lp < L) lp <<= 1;
+    for (int i = tid; i < lp; i += kSelT) {
+      fkey[i] = i < L ? dkey(a.s[row * a.len + i]) : 0ull;
+      fidx[i] = uint16_t(i < L ? i : 0xFFFF);
+    }
+    __syncthreads();
+    bitonic_desc<uint16_t, kSelT>(fkey, fidx, lp);
+    double* fw = reinterpret_cast<double*>(fkey);  // weights replace the keys in place
+    for (int i = tid; i < L; i += kSelT) fw[i] = a.topp ? exp(a.scale * dkey_inv(fkey[i]) - ellmax) : 1.0;
+    wo = fw;
+    io = fidx;
+    before = 0.0;
+  }
+  __syncthreads();
+  if (n > 0) {
+    const int per = (n + kSelT - 1) / kSelT;
+    const int i0 = tid * per;
+    double lw = 0.0;
+    for (int i = i0; i < min(n, i0 + per); ++i) lw += wo[i];
+    const double incl = wave_scan_dpp(lw, lane);
+    if (lane == 63) wred[wv] = incl;
+    __syncthreads();
+    double c = before + incl - lw;
+    for (int w = 0; w < wv; ++w) c += wred[w];
+    int cross = 0x7FFFFFFF;
+    for (int i = i0; i < min(n, i0 + per); ++i) {
+      c += wo[i];
+      if (c >= target) {
+        cross = i + 1;
+        break;
+      }
+    }
+    cross = wave_min_i32_dpp(cross);
+    if (lane == 0) wcnt[wv] = cross;
+    __syncthreads();
+    const int nsel = min(min(n, min(wcnt[0], wcnt[1])), min(wcnt[2], wcnt[3]));
+    for (int i = tid; i < nsel; i += kSelT) {
+      const int e = io[i];
+      atomicOr(&selb[e >> 5], 1u << (e & 31));
+    }
+  }
+  __syncthreads();
+
+  // ---- 5. per-head outputs
+  if (a.kind == 1) {
+    // kept segments in ascending order -> candidate chunk lists (first wave)
+    if (!local && wv == 0) {
+      int base = 0;
+      for (int w0 = 0; w0 < words_row; w0 += 64) {
+        const int w = w0 + lane;
+        const int pc = w < words_row ? __popc(selb[w]) : 0;
+        const int incl = wave_scan_i32_dpp(pc, lane);
+        int rank = base + incl - pc;
+        if (w < words_row) {
+          uint32_t m = selb[w];
+          while (m) {
+            const int bit = __ffs(m) - 1;
+            m &= m - 1;
+            const int seg = w * 32 + bit;
+            for (int j = 0; j < a.seg_size; ++j)
+              a.cand_out[row * a.cand_len + int64_t(rank) * a.seg_size + j] = seg * a.seg_size + j;
+            ++rank;
+          }
+        }
+        base += __builtin_amdgcn_readlane(incl, 63);
+      }
+    }
     return;
   }
-  // kind 1: kept segments in ascending order -> candidate chunk lists
-  const int per = (bw + kSelThreads - 1) / kSelThreads;
-  int cntl = 0;
-  for (int w = tid * per; w < min(bw, tid * per + per); ++w) cntl += __popc(lbits[w]);
-  double tot;
-  int rank = int(block_excl_scan(double(cntl), buf, &tot));
-  for (int w = tid * per; w < min(bw, tid * per + per); ++w) {
-    uint32_t m = lbits[w];
+  if (a.kind == 0) {
+    for (int w = tid; w < a.words; w += kSelT) a.bits[row * a.words + w] = (!local && w < words_row) ? selb[w] : 0u;
+  } else {
+    for (int w = tid; w < a.words; w += kSelT) a.bits[row * a.words + w] = 0u;
+    __syncthreads();  // the zeroing stores complete before the atomics below
+    if (!local)
+      for (int w = tid; w < words_row; w += kSelT) {
+        uint32_t m = selb[w];
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          m &= m - 1;
+          int e = a.cand_in[row * a.len + w * 32 + bit];
+          e = e < 0 ? 0 : (e < int(a.n_entries) ? e : int(a.n_entries) - 1);
+          atomicOr(&a.bits[row * a.words + (e >> 5)], 1u << (e & 31));
+        }
+      }
+  }
+
+  // ---- 6. the group's last workgroup builds the union and the ascending list
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  const int64_t grp = int64_t(b) * a.Hk + g;
+  if (tid == 0) is_last = atomicAdd(&a.arrivals[grp], 1) == G - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int uwords = int((a.n_entries + 31) / 32);
+  {
+    const int64_t first = local ? a.sink : a.keep_first;
+    const int64_t last = local ? a.window : a.keep_last;
+    for (int w = tid; w < uwords; w += kSelT) {
+      uint32_t u = edge_bits(w, a.n_entries, first, last);
+      if (!local)
+        for (int j = 0; j < G; ++j)
+          u |= __builtin_nontemporal_load(&a.bits[(int64_t(b) * a.Hq + g * G + j) * a.words + w]);
+      ubits[w] = u;
+    }
+  }
+  if (tid == 0) a.arrivals[grp] = 0;
+  __syncthreads();
+  const int per = (uwords + kSelT - 1) / kSelT;  // <= 16
+  const int w0 = tid * per;
+  int pc = 0;
+  for (int w = w0; w < min(uwords, w0 + per); ++w) pc += __popc(ubits[w]);
+  const int incl = wave_scan_i32_dpp(pc, lane);
+  if (lane == 63) wcnt[wv] = incl;
+  __syncthreads();
+  int pos = incl - pc;
+  for (int w = 0; w < wv; ++w) pos += wcnt[w];
+  int32_t* out = a.list + grp * a.n_entries;
+  for (int w = w0; w < min(uwords, w0 + per); ++w) {
+    uint32_t m = ubits[w];
     while (m) {
       const int bit = __ffs(m) - 1;
       m &= m - 1;
-      const int seg = w * 32 + bit;
-      for (int j = 0; j < seg_size; ++j) cand_out[row * cand_len + int64_t(rank) * seg_size + j] = seg * seg_size + j;
-      ++rank;
+      out[pos++] = w * 32 + bit;
     }
   }
+  if (tid == kSelT - 1) a.cnt[grp] = pos;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -571,40 +882,58 @@ int union_impl(const Plan& p, char* ws, hipStream_t st) {
   return int(hipGetLastError());
 }
 
+GroupSelArgs group_args(const Plan& p, char* ws, int level) {
+  const sd_config& c = p.cfg;
+  const bool hier = c.mode == SD_HIER_TOPK;
+  GroupSelArgs a;
+  a.s = at<double>(ws, hier && level == 1 ? p.o_s1 : p.o_s0);
+  a.len = hier && level == 1 ? p.len1 : p.len0;
+  a.Hq = c.n_q_heads;
+  a.Hk = c.n_kv_heads;
+  a.G = p.G;
+  a.local_mask = p.local_mask;
+  a.topp = c.mode == SD_TOPP;
+  a.k = hier && level == 0 ? c.top_k_seg : c.top_k;
+  a.p = c.top_p;
+  a.scale = c.mode == SD_TOPP ? c.select_scale : 1.0;
+  a.kind = hier ? (level == 0 ? 1 : 2) : 0;
+  a.cand_in = at<int32_t>(ws, p.o_cand);
+  a.cand_out = at<int32_t>(ws, p.o_cand);
+  a.seg_size = c.seg_size;
+  a.cand_len = p.len1;
+  a.bits = at<uint32_t>(ws, p.o_bits);
+  a.words = p.words;
+  a.list = at<int32_t>(ws, p.o_list);
+  a.cnt = at<int32_t>(ws, p.o_cnt);
+  a.arrivals = at<int32_t>(ws, p.o_arrive);
+  a.n_entries = p.M;
+  a.keep_first = c.keep_first;
+  a.keep_last = c.keep_last;
+  a.sink = c.sink;
+  a.window = c.window;
+  return a;
+}
+
 }  // namespace
 
 int launch_select(const Plan& p, int level, char* ws, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const sd_config& c = p.cfg;
   const int B = c.batch, Hq = c.n_q_heads;
-  const bool topp = c.mode == SD_TOPP;
-  const bool hier = c.mode == SD_HIER_TOPK;
-  if (hier && level == 0) {
-    hipLaunchKernelGGL(k_select_small, dim3(Hq, B), dim3(kSelThreads), 0, st, at<double>(ws, p.o_s0), p.len0, Hq,
-                       p.G, p.local_mask, 0, c.top_k_seg, 1.0, 1.0, 1, static_cast<const int32_t*>(nullptr),
-                       at<int32_t>(ws, p.o_cand), c.seg_size, p.len1, at<uint32_t>(ws, p.o_bits), p.words);
+  if (c.mode == SD_HIER_TOPK || !p.long0) {
+    // rows of at most kSmallRowMax entries: selection, union and compaction in one kernel
+    hipLaunchKernelGGL(k_select_head, dim3(Hq, B), dim3(kSelT), 0, st, group_args(p, ws, level));
     return int(hipGetLastError());
   }
-  if (hier) {
-    hipLaunchKernelGGL(k_select_small, dim3(Hq, B), dim3(kSelThreads), 0, st, at<double>(ws, p.o_s1), p.len1, Hq,
-                       p.G, p.local_mask, 0, c.top_k, 1.0, 1.0, 2, at<int32_t>(ws, p.o_cand),
-                       static_cast<int32_t*>(nullptr), c.seg_size, p.len1, at<uint32_t>(ws, p.o_bits), p.words);
-  } else if (!p.long0) {
-    hipLaunchKernelGGL(k_select_small, dim3(Hq, B), dim3(kSelThreads), 0, st, at<double>(ws, p.o_s0), p.len0, Hq,
-                       p.G, p.local_mask, topp ? 1 : 0, c.top_k, c.top_p, c.select_scale, 0,
-                       static_cast<const int32_t*>(nullptr), static_cast<int32_t*>(nullptr), 0, 0,
-                       at<uint32_t>(ws, p.o_bits), p.words);
-  } else {
-    const LongArgs a = long_args(p, ws);
-    const dim3 rows(Hq, B), blocks(p.long_blocks, Hq, B);
-    hipLaunchKernelGGL(k_long_prep, rows, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_long_hist<1>, blocks, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_long_find<1>, rows, dim3(kSelThreads), 0, st, a);
-    hipLaunchKernelGGL(k_long_hist<2>, blocks, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_long_find<2>, rows, dim3(kSelThreads), 0, st, a);
-    hipLaunchKernelGGL(k_long_collect, blocks, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_long_resolve, rows, dim3(kSelThreads), 0, st, a);
-  }
+  const LongArgs a = long_args(p, ws);
+  const dim3 rows(Hq, B), blocks(p.long_blocks, Hq, B);
+  hipLaunchKernelGGL(k_long_prep, rows, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_long_hist<1>, blocks, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_long_find<1>, rows, dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_hist<2>, blocks, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_long_find<2>, rows, dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_collect, blocks, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_long_resolve, rows, dim3(kSelThreads), 0, st, a);
   int e = int(hipGetLastError());
   if (e) return e;
   return union_impl(p, ws, st);

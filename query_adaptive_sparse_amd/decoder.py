@@ -91,7 +91,10 @@ class SparseDecoder:
     def __del__(self):
         h = getattr(self, "handle", None)
         if h is not None and h.value:
-            N.sparse_decode_destroy(h)
+            try:
+                N.sparse_decode_destroy(h)
+            except Exception:  # interpreter shutdown: the library may already be gone
+                pass
             self.handle = None
 
     @staticmethod

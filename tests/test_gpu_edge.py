@@ -1,0 +1,105 @@
+"""Degenerate and boundary cases of the HIP path against the oracle (needs an MI355X)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from synth import configs, gen
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, inp, **over):
+    print(f"[edge] {w.name} {over}", flush=True)
+    g = parity.run_gpu(w, inp, **over)
+    o = parity.oracle_step(w, inp)
+    rep = parity.compare(w, g, o)
+    print(f"[edge] {w.name}: {rep}", flush=True)
+    return g, o
+
+
+@pytest.mark.parametrize("n_ctx", [4096, 32768])
+def test_all_scores_equal_topk(n_ctx):
+    """Every summary key identical: all scores tie, top-k keeps the lowest indices. At 2048 chunks
+    the tie overflows both histogram levels and takes the whole-row sort."""
+    w = replace(configs.get("c2s"), name="tie_topk", n_ctx=n_ctx, top_k=37)
+    inp = gen.make_inputs(w, device="cuda")
+    inp["Kg"][:] = inp["Kg"][:, :, :1]
+    g, o = _run(w, inp)
+    for (b, gg), r in o["sel"].items():
+        for h, S in r["heads"].items():
+            assert S.tolist() == list(range(37))
+
+
+@pytest.mark.parametrize("n_ctx", [16384, 131072])
+def test_all_scores_equal_topp(n_ctx):
+    """All-equal masses: top-p keeps the shortest index prefix reaching p."""
+    w = replace(configs.get("c3s"), name="tie_topp", n_ctx=n_ctx, top_p=0.3, keep_first=0, keep_last=0)
+    inp = gen.make_inputs(w, device="cuda")
+    inp["Kg"][:] = inp["Kg"][:, :, :1]
+    _run(w, inp)
+
+
+def test_clustered_scores():
+    """Most scores packed in a narrow band far below a few large ones (second histogram level)."""
+    w = replace(configs.get("c3s"), name="cluster", top_p=0.9, keep_first=0, keep_last=0)
+    inp = gen.make_inputs(w, device="cuda")
+    Kg = inp["Kg"].float()
+    Kg = Kg * 1e-3
+    Kg[:, :, :4] = inp["Kg"][:, :, :4].float() * 50
+    inp["Kg"] = Kg.to(torch.bfloat16).contiguous()
+    _run(w, inp)
+
+
+@pytest.mark.parametrize("k", [1, 255, 256, 10_000])
+def test_topk_bounds(k):
+    w = replace(configs.get("c2s"), name=f"topk_{k}", top_k=k)
+    _run(w, gen.make_inputs(w, device="cuda"))
+
+
+@pytest.mark.parametrize("p", [1e-9, 0.5, 0.999999, 1.0])
+def test_topp_bounds(p):
+    w = replace(configs.get("c3s"), name=f"topp_{p}", top_p=p)
+    _run(w, gen.make_inputs(w, device="cuda"))
+
+
+def test_long_rows_topk():
+    """Top-k over rows longer than the short-row limit (histogram path with unit weights):
+    one summary row per token."""
+    w = replace(configs.get("c2s"), name="long_topk", chunk_size=1, n_ctx=8192, top_k=700)
+    _run(w, gen.make_inputs(w, device="cuda"))
+
+
+def test_long_rows_topp_summary():
+    """Top-p over long summary-routed rows (histogram path with softmax masses)."""
+    w = replace(configs.get("c3s"), name="long_topp", batch=1, kv_batch=1, chunk_size=2, n_ctx=16384,
+                keep_first=3, keep_last=5)
+    _run(w, gen.make_inputs(w, device="cuda"))
+
+
+def test_token_topp_short_rows():
+    """Token-level proxy top-p on rows short enough for the fused short-row kernel, mixed heads."""
+    w = replace(configs.get("c5s"), name="tok_short", n_ctx=2048, window=100, sink=7)
+    _run(w, gen.make_inputs(w, device="cuda"))
+
+
+def test_only_local_heads():
+    w = replace(configs.get("c5s"), name="local_only", n_ctx=16384, local_kv_heads=tuple(range(8)),
+                sink=3, window=1111)
+    _run(w, gen.make_inputs(w, device="cuda"))
+
+
+def test_single_group_two_level_all_segments():
+    """Two-level selection keeping every segment equals flat top-k."""
+    w = replace(configs.get("c4s"), name="hier_all", top_k_seg=32, top_k=40)
+    _run(w, gen.make_inputs(w, device="cuda"))
+
+
+@pytest.mark.parametrize("blocks", [1, 7, 4096])
+def test_attend_block_counts(blocks):
+    """The attention result does not depend on how the tile sequence is cut into workgroups."""
+    w = configs.get("c2s")
+    inp = gen.make_inputs(w, device="cuda")
+    _run(w, inp, attend_blocks=blocks)
