@@ -15,6 +15,9 @@
 // hi = bf16(p) (slots [0, G)) and lo = bf16(p - hi) (slots [G, 2G)) rows, which keeps fp32
 // accuracy. V goes through LDS (row-major, padded rows) to reach the B-operand layout. The next
 // tiles' K and V loads are issued before the current tile is computed (a ring of register stages).
+// K and V rows are read exactly once per call, so their loads are marked non-temporal: without
+// the hint they evict each other in the per-XCD L2s and some XCDs stream 10-20% slower than others,
+// which leaves the whole chip waiting on the slowest one at the end of the launch.
 #include "sd_device.h"
 
 namespace sd {
@@ -140,12 +143,12 @@ struct Attender {
   __device__ __forceinline__ void issue(TileRegs<T, D>& r, bool summary, int first, int nv, int e0) const {
     const T* kr = kb + row_of(summary, first, n, nv, e0) * st;
 #pragma unroll
-    for (int q = 0; q < CF::KQ; ++q) r.k[q] = ld16(kr + (CF::BF ? 32 * q + 8 * c : (D / 4) * c + 4 * q));
+    for (int q = 0; q < CF::KQ; ++q) r.k[q] = ld16_stream(kr + (CF::BF ? 32 * q + 8 * c : (D / 4) * c + 4 * q));
 #pragma unroll
     for (int kq = 0; kq < CF::VPL; ++kq) {
       const int pidx = kq * 64 + lane;
       const int x = pidx / CF::PPR, cp = pidx - x * CF::PPR;
-      r.v[kq] = ld16(vb + row_of(summary, first, x, nv, e0) * st + cp * CF::EPV);
+      r.v[kq] = ld16_stream(vb + row_of(summary, first, x, nv, e0) * st + cp * CF::EPV);
     }
   }
 

@@ -35,6 +35,13 @@ template <>
 __device__ __forceinline__ float elem_f32<uint16_t>(const uint16_t* p) { return bf2f(*p); }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Streaming 16-byte load, marked non-temporal: data read once per call (the gathered K / V rows)
+// should not displace reusable lines from the caches.
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Monotone map of fp64 to uint64: larger score -> larger key; -0 and +0 share a key.
 __device__ __forceinline__ uint64_t dkey(double s) {
