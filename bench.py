@@ -86,7 +86,8 @@ def algorithmic_bytes(w, counts: np.ndarray) -> dict:
 
 
 def cpu_baseline(w, inp, target_s=15.0, max_groups=0):
-    """The fp64 oracle (as it stands) on whole (sequence, KV group) units of the same workload."""
+    """The fp64 oracle (as it stands) on whole (sequence, KV group) units of the same workload:
+    units in a fixed random order, cycling over the step until about target_s of CPU time."""
     from oracle import HostSource, ref
     from threadpoolctl import threadpool_info
 
@@ -97,7 +98,8 @@ def cpu_baseline(w, inp, target_s=15.0, max_groups=0):
     host = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inp.items()}
     src = HostSource(host)
     done, t_total = 0, 0.0
-    for (b, g) in order:
+    while True:
+        b, g = order[done % len(order)]
         t0 = time.perf_counter()
         r = ref.select_group(w, src, b, g)
         ref.attend_group(w, src, b, g, r["union"])
@@ -109,9 +111,34 @@ def cpu_baseline(w, inp, target_s=15.0, max_groups=0):
     step_s = per_group * len(groups)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(w.batch / step_s, 4), "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {len(groups)} (sequence, KV group) units of {w.name}: selection + attention, "
-                      f"{t_total:.1f} s, scaled to a full step ({step_s:.1f} s)",
+            "sample": f"{done} (sequence, KV group) units of {w.name} ({len(groups)} per step, cycled): "
+                      f"selection + attention, {t_total:.1f} s, scaled to a full step ({step_s:.2f} s)",
             "cpu": _cpu_model()}
+
+
+COUNTER_PROFILE = os.path.join(ROOT, "profiles", "c3_128k_attend_counters.md")
+
+
+def counter_traffic(workload: str, attend_blocks: int):
+    """HBM bytes per attention launch from the committed FETCH_SIZE / WRITE_SIZE summary, scaled by
+    its copy calibration; None when the summary is for another workload or launch shape, or when
+    the attention sources have changed since the counters were taken."""
+    import hashlib
+    import re
+
+    try:
+        text = open(COUNTER_PROFILE).read()
+        rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
+        h = hashlib.sha256()
+        for s in rec["sources"]:
+            with open(os.path.join(ROOT, s), "rb") as f:
+                h.update(f.read())
+    except (OSError, AttributeError, KeyError, ValueError):
+        return None
+    if rec["workload"] != workload or rec["attend_blocks"] != attend_blocks or h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return int(round(rec["fetch_kib_per_dispatch"] * 1024 * rec["fetch_factor"]
+                     + rec["write_kib_per_dispatch"] * 1024 * rec["write_factor"]))
 
 
 def _cpu_model():
@@ -215,7 +242,8 @@ def main():
                       "combine": round(combine_ms, 4)},
         "roofline": {"kernel": "k_attend (gathered split-K attention)", "bound": "hbm",
                      "achieved": round(attend_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(attend_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(attend_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": counter_traffic(w.name, dec.params.get("attend_blocks") or 256),
                      "bytes_per_launch": nb["attend"], "avg_launch_ms": round(attend_ms, 5)},
         "status_flags": int(status[0]),
     }
