@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-groups", type=int, default=0, help="0 = size the sample to ~10-30 s")
     ap.add_argument("--attend-blocks", type=int, default=None)
+    ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
+                    help="before every timed step, overwrite a MIB MiB buffer (evicts the L2s and the "
+                         "256 MB Infinity Cache); steps are then timed by events only, flush excluded")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch device-to-device copies of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -188,10 +191,13 @@ def main():
     # timed steps; events bracket the stages on the stream the library launches on
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         e = ev[i]
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
         e[0].record()
         for level in range(dec.levels):
             dec.score_chunks(t, level)
@@ -204,6 +210,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
+    if scratch is not None:  # the flush is not part of the step
+        ms_per_step = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
     route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     attend_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     combine_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
@@ -233,7 +241,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "context": w.n_ctx, "chunk": w.chunk_size, "mode": w.mode,
                    "top_p": w.top_p if w.mode in ("topp", "proxy") else None,
-                   "top_k": w.top_k or None, "attend_blocks": dec.params.get("attend_blocks") or 256},
+                   "top_k": w.top_k or None, "attend_blocks": dec.params.get("attend_blocks") or 256,
+                   "cache_flush_mib": args.flush_mib},
         "hbm_gbps": round(step_gbps, 1),
         "hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
         "step_bytes": nb["step"],
