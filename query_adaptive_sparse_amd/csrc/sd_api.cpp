@@ -129,13 +129,11 @@ void plan_workspace(sd::Plan& p) {
   p.o_pmax = take(mm_rows * p.score_blocks0 * 8);
   p.o_pmin = take(mm_rows * p.score_blocks0 * 8);
   p.o_info = take(rows * sizeof(sd::RowInfo));
-  p.o_h1m = take(rows * sd::kBins1 * 8);
-  p.o_h1c = take(rows * sd::kBins1 * 4);
-  p.o_h2m = take(rows * sd::kBins2 * 8);
-  p.o_h2c = take(rows * sd::kBins2 * 4);
-  p.o_ckey = take(rows * sd::kResolveCap * 8);
-  p.o_cidx = take(rows * sd::kResolveCap * 4);
-  p.o_ccnt = take(rows * 4);
+  p.o_h1m = take(rows * p.long_blocks * sd::kBins1 * 8);
+  p.o_h1c = take(rows * p.long_blocks * sd::kBins1 * 4);
+  p.o_cbin = take(rows * ((p.len0 + 7) & ~int64_t(7)) * 2);
+  p.o_cidx = take(rows * p.long_blocks * sd::kResolveCap * 4);
+  p.o_ccnt = take(rows * p.long_blocks * 4);
   p.ws_bytes = off;
 }
 
@@ -201,7 +199,10 @@ sd_status sparse_decode_init(const sd_config* cfg, sd_handle** out, size_t* work
   p.words = (p.M + 31) / 32;
   p.ranges = int32_t((p.words + 1023) / 1024);
   p.attend_blocks = c.attend_blocks ? c.attend_blocks : sd::kAttendBlocks;
-  p.score_blocks0 = int32_t((p.len0 + 255) / 256);
+  p.score_blocks0 = int32_t((p.len0 + sd::kMinMaxBlock - 1) / sd::kMinMaxBlock);
+  p.n_scored = 0;
+  for (int g = 0; g < c.n_kv_heads; ++g)
+    if (!p.head_mode[g]) p.scored[p.n_scored++] = int8_t(g);
   p.long_blocks = int32_t((p.len0 + sd::kLongBlock - 1) / sd::kLongBlock);
   plan_workspace(p);
   *out = h;

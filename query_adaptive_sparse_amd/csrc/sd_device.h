@@ -132,6 +132,14 @@ __device__ __forceinline__ int wave_min_i32_dpp(int v) {
   return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
              min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
+__device__ __forceinline__ int wave_sum_i32_dpp(int v) {
+  v += dpp_i32<kDppQuadXor1>(v);
+  v += dpp_i32<kDppQuadXor2>(v);
+  v += dpp_i32<kDppRowRor4>(v);
+  v += dpp_i32<kDppRowRor8>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
 // Inclusive scans across the wave: shifts within rows of 16, then the earlier rows' totals.
 __device__ __forceinline__ double wave_scan_dpp(double v, int lane) {
   v += dpp_f64<kDppRowShr1>(v);

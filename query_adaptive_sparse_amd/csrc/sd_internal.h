@@ -13,14 +13,16 @@ namespace sd {
 constexpr int kSmallRowMax = 2048;
 constexpr int64_t small_row_limit(int) { return kSmallRowMax; }
 
-// Histogram resolution of the long-row path: coarse bins over the row's score
-// range, then fine bins inside the crossing coarse bin.
-constexpr int kBins1 = 4096;
+// Long-row path: coarse bins over the row's score range (per-slab partial histograms); the
+// crossing coarse bin's entries (at most kResolveCap of them, else a fine split first) are
+// resolved exactly in one workgroup.
+constexpr int kBins1 = 1024;
 constexpr int kBins2 = 4096;
-// Entries of the final fine bin resolved exactly per row (sorted in LDS).
 constexpr int kResolveCap = 4096;
-// Tokens per workgroup in the long-row passes.
-constexpr int kLongBlock = 8192;
+// Entries per workgroup ("slab") in the long-row histogram and marking passes.
+constexpr int kLongBlock = 32768;
+// Entries per partial max / min written by the score passes of long rows.
+constexpr int kMinMaxBlock = 2048;
 // Attention: tokens per MFMA tile and waves per workgroup.
 constexpr int kTile = 16;
 constexpr int kWaves = 4;
@@ -43,11 +45,13 @@ struct Plan {
   int64_t words;            // bitmap words per row = ceil(M / 32)
   int32_t ranges;           // union compaction ranges per group
   int32_t attend_blocks;    // persistent attention workgroups
-  int32_t score_blocks0;    // blocks per row of the long-row score pass (partial max/min)
-  int32_t long_blocks;      // blocks per row of the long-row histogram passes
+  int32_t score_blocks0;    // partial max / min per long row (kMinMaxBlock entries each)
+  int32_t long_blocks;      // slabs per long row (kLongBlock entries each)
+  int32_t n_scored;         // KV groups that are scored (not local)
+  int8_t scored[kMaxKvHeads];  // their indices, ascending
   // workspace byte offsets
   size_t o_status, o_arrive, o_qp, o_s0, o_s1, o_cand, o_bits, o_ubits, o_rcnt, o_list, o_cnt;
-  size_t o_gpre, o_po, o_pl, o_pmax, o_pmin, o_info, o_h1m, o_h1c, o_h2m, o_h2c, o_ckey, o_cidx, o_ccnt;
+  size_t o_gpre, o_po, o_pl, o_pmax, o_pmin, o_info, o_h1m, o_h1c, o_cbin, o_cidx, o_ccnt;
   size_t ws_bytes;
 };
 
@@ -55,9 +59,10 @@ struct Plan {
 struct RowInfo {
   double smax, smin, binscale;  // score range and coarse-bin scale
   double target;                // p * Z (top-p) or k (top-k)
-  double before1, before2;      // weight of everything ahead of the crossing bins
-  int32_t bin1, bin2;           // crossing coarse / fine bin
+  double before1;               // weight of everything ahead of the crossing coarse bin
+  int32_t bin1;                 // crossing coarse bin
   int32_t all;                  // 1: the whole row is selected
+  int32_t gather;               // 1: the crossing coarse bin holds <= kResolveCap entries
   int32_t pad;
 };
 

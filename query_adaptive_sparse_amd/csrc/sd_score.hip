@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, int
   __shared__ float qs[kMaxGroup * QW];
   const int b = blockIdx.z, y = blockIdx.y, tid = threadIdx.x;
   if (status && blockIdx.x == 0 && y == 0 && b == 0) {
-    if (tid < 4) status[tid] = 0;
+    if (tid < 16) status[tid] = 0;
     for (int i = tid; i < n_groups; i += 256) arrivals[i] = 0;
   }
   const int g = cand ? y / G : y;
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void k_proxy_query(const T* __restrict__ q, in
   const int b = blockIdx.y;
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (blockIdx.x == 0 && b == 0) {
-    if (threadIdx.x < 4) status[threadIdx.x] = 0;
+    if (threadIdx.x < 16) status[threadIdx.x] = 0;
     for (int i = threadIdx.x; i < n_groups; i += 256) arrivals[i] = 0;
   }
   const int h = t >> 4, j = t & 15;
@@ -93,68 +93,154 @@ __global__ __launch_bounds__(256) void k_proxy_query(const T* __restrict__ q, in
 }
 
 // Proxy scores s_t = q_p . k_p[t] over the 16 proxy dims, separate multiply and add in index
-// order (q_p has 53 significant bits, so the products round). One thread per token; the
-// group's G heads share the token's proxy key. Also writes per-block max / min per head.
-__global__ __launch_bounds__(256) void k_score_proxy(const uint16_t* __restrict__ kp, int64_t kp_sb,
-                                                     int64_t kp_sh, int64_t kp_st, const double* __restrict__ qp,
-                                                     int G, int Hq, int64_t N, uint64_t local_mask,
-                                                     double* __restrict__ s0, double* __restrict__ pmax,
-                                                     double* __restrict__ pmin, int nblk) {
-  const int b = blockIdx.z, g = blockIdx.y, tid = threadIdx.x;
-  if ((local_mask >> g) & 1) return;
+// order (q_p has 53 significant bits, so the products round). One 512-thread workgroup per
+// kMinMaxBlock tokens of one scored KV group; each thread takes 4 tokens 512 apart with all their
+// loads issued first, and the group's G heads share each token's proxy key. The workgroup projects
+// the group's queries itself (q_p = q P, fp64 in index order, the same arithmetic as
+// k_proxy_query) while the key loads are in flight, and writes its max and min per head.
+// Workgroup (0, 0, 0) clears the status words and the per-group arrival counters.
+struct ProxyArgs {
+  const uint16_t* kp;
+  int64_t kp_sb, kp_sh, kp_st;
+  const void* q;
+  int64_t q_sb, q_sh;
+  const float* proj;
+  int G, Hq;
+  int64_t N;
+  double* s0;
+  double* pmax;
+  double* pmin;
+  int nblk;
+  uint32_t* status;
+  int32_t* arrivals;
+  int n_groups;
+  int8_t scored[kMaxKvHeads];  // blockIdx.y -> KV group
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
+  const int b = blockIdx.z, g = a.scored[blockIdx.y], tid = threadIdx.x;
+  const int G = a.G;
   __shared__ double qs[kMaxGroup][16];
-  __shared__ double rmax[kMaxGroup][4], rmin[kMaxGroup][4];
-  if (tid < G * 16) qs[tid >> 4][tid & 15] = qp[(int64_t(b) * Hq + g * G + (tid >> 4)) * 16 + (tid & 15)];
-  __syncthreads();
-  const int64_t t = int64_t(blockIdx.x) * 256 + tid;
-  const bool valid = t < N;
-  double kd[16];
-  if (valid) {
-    const uint16_t* row = kp + b * kp_sb + int64_t(g) * kp_sh + t * kp_st;
-    const uint4 a = ld16(row), c = ld16(row + 8);
-    const _Float16* ha = reinterpret_cast<const _Float16*>(&a);
-    const _Float16* hc = reinterpret_cast<const _Float16*>(&c);
+  __shared__ double rmax[kMaxGroup][8], rmin[kMaxGroup][8];
+  if (blockIdx.x == 0 && blockIdx.y == 0 && b == 0) {
+    if (tid < 16) a.status[tid] = 0;
+    for (int i = tid; i < a.n_groups; i += 512) a.arrivals[i] = 0;
+  }
+  const int64_t t0 = int64_t(blockIdx.x) * kMinMaxBlock;
+  const uint16_t* kb = a.kp + b * a.kp_sb + int64_t(g) * a.kp_sh;
+  constexpr int TPT = kMinMaxBlock / 512;  // tokens per thread (512 threads)
+  uint4 raw[TPT][2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      kd[j] = double(float(ha[j]));
-      kd[j + 8] = double(float(hc[j]));
+  for (int k = 0; k < TPT; ++k) {
+    int64_t t = t0 + tid + 512 * k;
+    t = t < a.N ? t : a.N - 1;
+    raw[k][0] = ld16(kb + t * a.kp_st);
+    raw[k][1] = ld16(kb + t * a.kp_st + 8);
+  }
+  {
+    // stage the group's projection and queries in LDS (one parallel round of loads), then one
+    // thread per (head, proxy dim) runs the index-order fma chain
+    __shared__ float Ps[D * 16];
+    __shared__ float Qs[kMaxGroup][D];
+    const float* P = a.proj + int64_t(g) * D * 16;
+    for (int i = tid; i < D * 16; i += 512) Ps[i] = P[i];
+    for (int i = tid; i < G * D; i += 512) {
+      const int hh = i / D, e = i - hh * D;
+      Qs[hh][e] = elem_f32<T>(static_cast<const T*>(a.q) + b * a.q_sb + int64_t(g * G + hh) * a.q_sh + e);
+    }
+    __syncthreads();
+    if (tid < G * 16) {
+      const int hh = tid >> 4, j = tid & 15;
+      double acc = 0.0;
+#pragma unroll 16
+      for (int i = 0; i < D; ++i) acc = fma(double(Qs[hh][i]), double(Ps[i * 16 + j]), acc);
+      qs[hh][j] = acc;
+    }
+  }
+  __syncthreads();
+  double mx[kMaxGroup], mn[kMaxGroup];
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j) {
+    mx[j] = kNegInfD;
+    mn[j] = kPosInfD;
+  }
+  const int64_t row0 = int64_t(b) * a.Hq + g * G;
+#pragma unroll
+  for (int k = 0; k < TPT; ++k) {
+    const int64_t t = t0 + tid + 512 * k;
+    const bool valid = t < a.N;
+    double kd[16];
+    const _Float16* h0 = reinterpret_cast<const _Float16*>(&raw[k][0]);
+    const _Float16* h1 = reinterpret_cast<const _Float16*>(&raw[k][1]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      kd[u] = double(float(h0[u]));
+      kd[u + 8] = double(float(h1[u]));
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxGroup; ++j) {
+      if (j < G) {
+        double acc = 0.0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc = acc + qs[j][u] * kd[u];
+        if (valid) {
+          a.s0[(row0 + j) * a.N + t] = acc;
+          mx[j] = fmax(mx[j], acc);
+          mn[j] = fmin(mn[j], acc);
+        }
+      }
     }
   }
   const int lane = tid & 63, wave = tid >> 6;
-  for (int j = 0; j < G; ++j) {
-    double acc = 0.0;
-    if (valid) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) acc = acc + qs[j][u] * kd[u];
-      s0[(int64_t(b) * Hq + g * G + j) * N + t] = acc;
-    }
-    const double mx = wave_max(valid ? acc : kNegInfD);
-    const double mn = wave_min(valid ? acc : kPosInfD);
-    if (lane == 0) {
-      rmax[j][wave] = mx;
-      rmin[j][wave] = mn;
+  for (int j = 0; j < kMaxGroup; ++j) {
+    if (j < G) {
+      const double wx = wave_max_dpp(mx[j]), wn = wave_min_dpp(mn[j]);
+      if (lane == 0) {
+        rmax[j][wave] = wx;
+        rmin[j][wave] = wn;
+      }
     }
   }
   __syncthreads();
   if (tid < G) {
-    const double mx = fmax(fmax(rmax[tid][0], rmax[tid][1]), fmax(rmax[tid][2], rmax[tid][3]));
-    const double mn = fmin(fmin(rmin[tid][0], rmin[tid][1]), fmin(rmin[tid][2], rmin[tid][3]));
-    pmax[(int64_t(b) * Hq + g * G + tid) * nblk + blockIdx.x] = mx;
-    pmin[(int64_t(b) * Hq + g * G + tid) * nblk + blockIdx.x] = mn;
+    double x = rmax[tid][0], y = rmin[tid][0];
+    for (int w = 1; w < 8; ++w) {
+      x = fmax(x, rmax[tid][w]);
+      y = fmin(y, rmin[tid][w]);
+    }
+    a.pmax[(row0 + tid) * a.nblk + blockIdx.x] = x;
+    a.pmin[(row0 + tid) * a.nblk + blockIdx.x] = y;
   }
 }
 
-// Per-256-entry max / min of score rows that take the long-row path on summary routing.
+// Max / min of each kMinMaxBlock entries of score rows that take the long-row path on summary
+// routing (8 entries per thread, loads issued first).
 __global__ __launch_bounds__(256) void k_row_minmax(const double* __restrict__ s0, int64_t len, int G, int Hq,
                                                     uint64_t local_mask, double* __restrict__ pmax,
                                                     double* __restrict__ pmin, int nblk) {
   const int b = blockIdx.z, h = blockIdx.y, tid = threadIdx.x;
   if ((local_mask >> (h / G)) & 1) return;
   __shared__ double rmax[4], rmin[4];
-  const int64_t t = int64_t(blockIdx.x) * 256 + tid;
   const int64_t row = int64_t(b) * Hq + h;
-  const double v = t < len ? s0[row * len + t] : 0.0;
-  const double mx = wave_max(t < len ? v : kNegInfD), mn = wave_min(t < len ? v : kPosInfD);
+  const int64_t t0 = int64_t(blockIdx.x) * kMinMaxBlock;
+  double v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int64_t t = t0 + tid + 256 * k;
+    v[k] = s0[row * len + (t < len ? t : len - 1)];
+  }
+  double mx = kNegInfD, mn = kPosInfD;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (t0 + tid + 256 * k < len) {
+      mx = fmax(mx, v[k]);
+      mn = fmin(mn, v[k]);
+    }
+  }
+  mx = wave_max_dpp(mx);
+  mn = wave_min_dpp(mn);
   if ((tid & 63) == 0) {
     rmax[tid >> 6] = mx;
     rmin[tid >> 6] = mn;
@@ -172,14 +258,34 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
   const int B = c.batch, Hq = c.n_q_heads, Hk = c.n_kv_heads;
   uint32_t* status = at<uint32_t>(ws, p.o_status);
   if (c.route == SD_ROUTE_PROXY) {
-    const int nb = (Hq * 16 + 255) / 256;
-    hipLaunchKernelGGL((k_proxy_query<T, D>), dim3(nb, B), dim3(256), 0, st, static_cast<const T*>(t.q), t.q_sb,
-                       t.q_sh, t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status,
-                       at<int32_t>(ws, p.o_arrive), B * Hk);
-    hipLaunchKernelGGL(k_score_proxy, dim3(p.score_blocks0, Hk, B), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(t.kp), t.kp_sb, t.kp_sh, t.kp_st, at<double>(ws, p.o_qp),
-                       p.G, Hq, c.n_ctx, p.local_mask, at<double>(ws, p.o_s0), at<double>(ws, p.o_pmax),
-                       at<double>(ws, p.o_pmin), p.score_blocks0);
+    if (p.n_scored == 0) {  // every group is local: only the status words and counters need clearing
+      const int nb = (Hq * 16 + 255) / 256;
+      hipLaunchKernelGGL((k_proxy_query<T, D>), dim3(nb, B), dim3(256), 0, st, static_cast<const T*>(t.q), t.q_sb,
+                         t.q_sh, t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status,
+                         at<int32_t>(ws, p.o_arrive), B * Hk);
+    } else {
+      ProxyArgs pa;
+      pa.kp = static_cast<const uint16_t*>(t.kp);
+      pa.kp_sb = t.kp_sb;
+      pa.kp_sh = t.kp_sh;
+      pa.kp_st = t.kp_st;
+      pa.q = t.q;
+      pa.q_sb = t.q_sb;
+      pa.q_sh = t.q_sh;
+      pa.proj = t.proj;
+      pa.G = p.G;
+      pa.Hq = Hq;
+      pa.N = c.n_ctx;
+      pa.s0 = at<double>(ws, p.o_s0);
+      pa.pmax = at<double>(ws, p.o_pmax);
+      pa.pmin = at<double>(ws, p.o_pmin);
+      pa.nblk = p.score_blocks0;
+      pa.status = status;
+      pa.arrivals = at<int32_t>(ws, p.o_arrive);
+      pa.n_groups = B * Hk;
+      for (int i = 0; i < kMaxKvHeads; ++i) pa.scored[i] = i < p.n_scored ? p.scored[i] : 0;
+      hipLaunchKernelGGL((k_score_proxy<T, D>), dim3(p.score_blocks0, p.n_scored, B), dim3(512), 0, st, pa);
+    }
     return int(hipGetLastError());
   }
   if (c.mode == SD_HIER_TOPK && level == 1) {

@@ -480,12 +480,23 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Selection of long rows (token-level): the order is resolved through a coarse histogram of
-// (smax - s) over the row's score range, a fine histogram inside the coarse bin where the
-// running weight crosses the target, and an exact sort of the entries of the crossing fine bin.
-// Weight = softmax mass exp(scale*s - scale*smax) for top-p, 1 for top-k. Bins are monotone in
-// the score, so every entry of an earlier bin precedes every entry of a later one in the
-// (score desc, index asc) order.
+// Selection of long rows (more than kSmallRowMax entries: token-level proxy rows, or fine chunk
+// rows). The (score desc, index asc) order is resolved through a coarse histogram of the weights
+// over the bins of (smax - s) on the row's score range, then the entries of the coarse bin where
+// the running weight crosses the target. Weight = softmax mass exp(scale*s - scale*smax) for
+// top-p, 1 for top-k. Bins are monotone in the score, so every entry of an earlier bin precedes
+// every entry of a later one in the order. Passes:
+//   hist     per slab of kLongBlock entries: coarse bin of every entry (kept, 2 bytes), partial
+//            coarse histogram (no atomics across workgroups);
+//   find1    per row: bin totals (slab partials in slab order), Z and the target, the crossing
+//            coarse bin and the weight ahead of it;
+//   mark     per slab: bitmap words of the entries of earlier coarse bins, and the indices of the
+//            crossing bin's entries in the slab's own region of the resolution buffer;
+//   resolve  per row: the crossing bin's entries split by a sub-bin histogram of their interval;
+//            earlier sub-bins are selected, the crossing sub-bin's entries are ranked and walked to
+//            the first crossing.
+// A crossing coarse bin of more than kResolveCap entries (heavily tied scores) is split inside the
+// resolve workgroup by a fine histogram over one more pass of the row (slow, and only then).
 // ---------------------------------------------------------------------------------------------
 struct LongArgs {
   const double* s0;
@@ -495,227 +506,264 @@ struct LongArgs {
   int topp, k;
   double p, scale;
   RowInfo* info;
-  const double* pmax;
+  const double* pmax;  // [row][nblk] partial max / min of the scores
   const double* pmin;
   int nblk;
-  double* h1m;
+  int nb1;             // slabs per row
+  double* h1m;         // [row][slab][kBins1] partial coarse histograms
   uint32_t* h1c;
-  double* h2m;
-  uint32_t* h2c;
-  uint64_t* ckey;
-  int32_t* cidx;
-  int32_t* ccnt;
+  uint16_t* cbin;      // [row][cstride] coarse bin of every entry
+  int64_t cstride;     // len rounded up to a multiple of 8 (16-byte aligned rows)
+  int32_t* cidx;       // [row][slab][kResolveCap] indices of the crossing bin's entries
+  int32_t* ccnt;       // [row][slab] their counts
   uint32_t* bits;
   int64_t words;
   uint32_t* status;
 };
 
-__device__ __forceinline__ void long_bins(double s, const RowInfo& ri, int* b1, int* b2) {
-  double delta = (ri.smax - s) * ri.binscale;
-  delta = delta >= 0.0 ? (delta < double(kBins1) ? delta : double(kBins1)) : 0.0;  // NaN -> 0
-  int c1 = int(delta);
-  c1 = c1 < kBins1 - 1 ? c1 : kBins1 - 1;
-  *b1 = c1;
-  const double f = delta - double(c1);
-  int c2 = int(f * double(kBins2));
-  c2 = c2 < 0 ? 0 : (c2 < kBins2 - 1 ? c2 : kBins2 - 1);
-  *b2 = c2;
+__device__ __forceinline__ double coarse_pos(double s, double smax, double binscale) {
+  const double d = (smax - s) * binscale;
+  return d >= 0.0 ? (d < double(kBins1) ? d : double(kBins1)) : 0.0;  // NaN -> 0
+}
+__device__ __forceinline__ int coarse_bin(double d) {
+  const int c = int(d);
+  return c < kBins1 - 1 ? c : kBins1 - 1;
+}
+__device__ __forceinline__ int fine_bin(double d, int c1) {
+  const int c2 = int((d - double(c1)) * double(kBins2));
+  return c2 < 0 ? 0 : (c2 < kBins2 - 1 ? c2 : kBins2 - 1);
+}
+__device__ __forceinline__ double long_weight(const LongArgs& a, double smax, double s) {
+  return a.topp ? exp(a.scale * s - a.scale * smax) : 1.0;
 }
 
-__device__ __forceinline__ double long_weight(const LongArgs& a, const RowInfo& ri, double s) {
-  return a.topp ? exp(a.scale * s - a.scale * ri.smax) : 1.0;
+// Inclusive scan of one double per thread over an NT-thread workgroup, in thread order; `wtot`
+// holds NT/64 doubles of LDS. Returns the inclusive value; *total = the workgroup's sum.
+template <int NT = 256>
+__device__ __forceinline__ double block_scan(double v, double* wtot, double* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const double incl = wave_scan_dpp(v, lane);
+  if (lane == 63) wtot[wv] = incl;
+  __syncthreads();
+  double before = 0.0;
+  for (int w = 0; w < wv; ++w) before += wtot[w];
+  double tot = 0.0;
+  for (int w = 0; w < NT / 64; ++w) tot += wtot[w];
+  *total = tot;
+  __syncthreads();
+  return before + incl;
 }
 
-__global__ __launch_bounds__(256) void k_long_prep(LongArgs a) {
-  const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+constexpr int kLongThreads = 1024;
+__global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
+  constexpr int NT = kLongThreads;
+  const int b = blockIdx.z, h = blockIdx.y, slab = blockIdx.x, tid = threadIdx.x;
   if ((a.local_mask >> (h / a.G)) & 1) return;
   const int64_t row = int64_t(b) * a.Hq + h;
-  __shared__ double rmax[4], rmin[4];
+  __shared__ double hm[kBins1];
+  __shared__ uint32_t hc[kBins1];
+  __shared__ double rmax[NT / 64], rmin[NT / 64];
+  for (int i = tid; i < kBins1; i += NT) {
+    hm[i] = 0.0;
+    hc[i] = 0;
+  }
+  // the row's score range from the score pass's partials (every workgroup gets the same bits)
   double mx = kNegInfD, mn = kPosInfD;
-  for (int i = tid; i < a.nblk; i += 256) {
+  for (int i = tid; i < a.nblk; i += NT) {
     mx = fmax(mx, a.pmax[row * a.nblk + i]);
     mn = fmin(mn, a.pmin[row * a.nblk + i]);
   }
-  mx = wave_max(mx);
-  mn = wave_min(mn);
+  mx = wave_max_dpp(mx);
+  mn = wave_min_dpp(mn);
   if ((tid & 63) == 0) {
     rmax[tid >> 6] = mx;
     rmin[tid >> 6] = mn;
   }
-  for (int i = tid; i < kBins1; i += 256) {
-    a.h1m[row * kBins1 + i] = 0.0;
-    a.h1c[row * kBins1 + i] = 0;
+  __syncthreads();
+  double smax = rmax[0], smin = rmin[0];
+  for (int w = 1; w < NT / 64; ++w) {
+    smax = fmax(smax, rmax[w]);
+    smin = fmin(smin, rmin[w]);
   }
-  for (int i = tid; i < kBins2; i += 256) {
-    a.h2m[row * kBins2 + i] = 0.0;
-    a.h2c[row * kBins2 + i] = 0;
+  const double range = smax - smin;
+  const double binscale = range > 0.0 ? double(kBins1) / range : 0.0;
+  const bool all = a.topp ? (a.p >= 1.0) : (int64_t(a.k) >= a.len);
+  if (slab == 0 && tid == 0) {
+    RowInfo ri = {};
+    ri.smax = smax;
+    ri.smin = smin;
+    ri.binscale = binscale;
+    ri.all = all;
+    a.info[row] = ri;
+  }
+  if (all) return;
+  const int64_t t0 = int64_t(slab) * kLongBlock;
+  const int64_t t1 = t0 + kLongBlock < a.len ? t0 + kLongBlock : a.len;
+  const double* sr = a.s0 + row * a.len;
+  uint16_t* br = a.cbin + row * a.cstride;
+  // kLongBlock / (8 NT) batches of 8 entries per thread; the next batch's loads are issued before
+  // the current batch is binned (clamped, so every load is unconditional)
+  constexpr int kIters = kLongBlock / (NT * 8);
+  double sv[2][8];
+  auto load = [&](double* dst, int it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t t = t0 + int64_t(it) * (NT * 8) + tid + NT * k;
+      dst[k] = sr[t < t1 ? t : t1 - 1];
+    }
+  };
+  load(sv[0], 0);
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    if (it + 1 < kIters) load(sv[(it + 1) & 1], it + 1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t t = t0 + int64_t(it) * (NT * 8) + tid + NT * k;
+      if (t < t1) {
+        const double v = sv[it & 1][k];
+        const int c = coarse_bin(coarse_pos(v, smax, binscale));
+        br[t] = uint16_t(c);
+        unsafeAtomicAdd(&hm[c], long_weight(a, smax, v));
+        atomicAdd(&hc[c], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t o = (row * a.nb1 + slab) * kBins1;
+  for (int i = tid; i < kBins1; i += NT) {
+    a.h1m[o + i] = hm[i];
+    a.h1c[o + i] = hc[i];
+  }
+}
+
+// Per row: coarse bin totals (slab partials summed in slab order), Z and the target, the crossing
+// coarse bin, the weight ahead of it, and whether its entries fit the resolution buffer.
+constexpr int kFindThreads = kBins1;
+__global__ __launch_bounds__(kFindThreads) void k_long_find1(LongArgs a) {
+  const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+  if ((a.local_mask >> (h / a.G)) & 1) return;
+  const int64_t row = int64_t(b) * a.Hq + h;
+  __shared__ double wtot[kFindThreads / 64];
+  __shared__ int hit_bin;
+  __shared__ double hit_before;
+  __shared__ uint32_t hit_count;
+  RowInfo ri = a.info[row];
+  if (ri.all) return;
+  double m = 0.0;
+  uint32_t cn = 0;
+  const int64_t o = row * a.nb1 * kBins1 + tid;
+#pragma unroll 8
+  for (int sl = 0; sl < a.nb1; ++sl) {
+    m += a.h1m[o + int64_t(sl) * kBins1];
+    cn += a.h1c[o + int64_t(sl) * kBins1];
+  }
+  double Z;
+  const double incl = block_scan<kFindThreads>(m, wtot, &Z);
+  const double target = a.topp ? a.p * Z : double(a.k);
+  if (tid == 0) hit_bin = 0x7FFFFFFF;
+  __syncthreads();
+  const double excl = incl - m;
+  if (excl + m >= target) atomicMin(&hit_bin, tid);
+  __syncthreads();
+  const int bin1 = hit_bin;
+  if (bin1 == tid) {
+    hit_before = excl;
+    hit_count = cn;
   }
   __syncthreads();
   if (tid == 0) {
-    RowInfo ri = {};
-    ri.smax = fmax(fmax(rmax[0], rmax[1]), fmax(rmax[2], rmax[3]));
-    ri.smin = fmin(fmin(rmin[0], rmin[1]), fmin(rmin[2], rmin[3]));
-    const double range = ri.smax - ri.smin;
-    ri.binscale = range > 0.0 ? double(kBins1) / range : 0.0;
-    ri.all = a.topp ? (a.p >= 1.0) : (int64_t(a.k) >= a.len);
-    ri.target = a.topp ? 0.0 : double(a.k);
+    if (bin1 == 0x7FFFFFFF) {
+      ri.all = 1;  // rounding left the target above the total weight: keep every entry
+    } else {
+      ri.bin1 = bin1;
+      ri.before1 = hit_before;
+      ri.target = target;
+      ri.gather = hit_count <= uint32_t(kResolveCap);
+    }
     a.info[row] = ri;
-    a.ccnt[row] = 0;
   }
 }
 
-// level 1: coarse histogram of every entry; level 2: fine histogram of the crossing coarse bin,
-// plus the bitmap of the row (entries of earlier coarse bins are selected).
-template <int LEVEL>
-__global__ __launch_bounds__(256) void k_long_hist(LongArgs a) {
-  const int b = blockIdx.z, h = blockIdx.y, tid = threadIdx.x;
+// Per slab: the row's bitmap (entries of coarse bins ahead of the crossing bin, or every entry
+// when the whole row is kept; zero for local heads) and, in gather mode, the indices of the
+// crossing bin's entries in the slab's region of the resolution buffer. Each lane takes 8
+// consecutive entries (one 16-byte load of their bins, all of a slab's loads issued at once) and
+// writes their 8 bits as one byte of the bitmap.
+__global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
+  constexpr int NT = kLongThreads;
+  const int b = blockIdx.z, h = blockIdx.y, slab = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63;
   const int64_t row = int64_t(b) * a.Hq + h;
+  const int64_t t0 = int64_t(slab) * kLongBlock;
+  const int64_t t1 = t0 + kLongBlock < a.len ? t0 + kLongBlock : a.len;
+  uint32_t* bw = a.bits + row * a.words;
   if ((a.local_mask >> (h / a.G)) & 1) {
-    // local heads select nothing themselves: their bitmap rows are zero
-    if (LEVEL == 2) {
-      const int64_t w0 = int64_t(blockIdx.x) * (kLongBlock / 32);
-      for (int64_t w = w0 + tid; w < w0 + kLongBlock / 32 && w < a.words; w += 256) a.bits[row * a.words + w] = 0;
-    }
+    for (int64_t w = (t0 >> 5) + tid; w < ((t1 + 31) >> 5); w += NT) bw[w] = 0u;
     return;
   }
-  const RowInfo ri = a.info[row];
-  constexpr int NB = LEVEL == 1 ? kBins1 : kBins2;
-  __shared__ double hm[NB];
-  __shared__ uint32_t hc[NB];
-  for (int i = tid; i < NB; i += 256) {
-    hm[i] = 0.0;
-    hc[i] = 0;
-  }
+  __shared__ int scnt;
+  if (tid == 0) scnt = 0;
   __syncthreads();
-  const int64_t t0 = int64_t(blockIdx.x) * kLongBlock;
-  const int64_t t1 = t0 + kLongBlock < a.len ? t0 + kLongBlock : a.len;
-  const double* sr = a.s0 + row * a.len;
-  for (int64_t base = t0; base < t0 + kLongBlock; base += 256) {
-    const int64_t t = base + tid;
-    bool sel = false;
-    if (t < t1) {
-      const double s = sr[t];
-      int b1, b2;
-      long_bins(s, ri, &b1, &b2);
-      if (LEVEL == 1) {
-        if (!ri.all) {
-          atomicAdd(&hm[b1], long_weight(a, ri, s));
-          atomicAdd(&hc[b1], 1u);
-        }
-      } else {
-        sel = ri.all || b1 < ri.bin1;
-        if (!ri.all && b1 == ri.bin1) {
-          atomicAdd(&hm[b2], long_weight(a, ri, s));
-          atomicAdd(&hc[b2], 1u);
-        }
-      }
-    }
-    if (LEVEL == 2 && base < a.len) {
-      const uint64_t m = __ballot(sel);
-      const int lane = tid & 63;
-      const int64_t w = (base + (tid & ~63)) >> 5;
-      if (lane == 0 && w < a.words) a.bits[row * a.words + w] = uint32_t(m);
-      if (lane == 1 && w + 1 < a.words) a.bits[row * a.words + w + 1] = uint32_t(m >> 32);
-    }
-  }
-  __syncthreads();
-  if (ri.all) return;
-  double* gm = LEVEL == 1 ? a.h1m + row * kBins1 : a.h2m + row * kBins2;
-  uint32_t* gc = LEVEL == 1 ? a.h1c + row * kBins1 : a.h2c + row * kBins2;
-  for (int i = tid; i < NB; i += 256) {
-    if (hc[i]) {
-      unsafeAtomicAdd(&gm[i], hm[i]);
-      atomicAdd(&gc[i], hc[i]);
-    }
-  }
-}
-
-// Find the bin where the running weight crosses the target (one workgroup per row).
-template <int LEVEL>
-__global__ __launch_bounds__(kSelThreads) void k_long_find(LongArgs a) {
-  const int b = blockIdx.y, h = blockIdx.x;
-  if ((a.local_mask >> (h / a.G)) & 1) return;
-  const int64_t row = int64_t(b) * a.Hq + h;
-  __shared__ double buf[kSelThreads];
-  __shared__ int ibuf;
-  RowInfo ri = a.info[row];
-  if (ri.all) return;
-  constexpr int NB = LEVEL == 1 ? kBins1 : kBins2;
-  const double* gm = LEVEL == 1 ? a.h1m + row * kBins1 : a.h2m + row * kBins2;
-  double base = 0.0;
-  if (LEVEL == 1) {
-    if (a.topp) {
-      double Z;
-      const int per = NB / kSelThreads;
-      double local = 0.0;
-      for (int i = threadIdx.x * per; i < threadIdx.x * per + per; ++i) local += gm[i];
-      block_excl_scan(local, buf, &Z);
-      ri.target = a.p * Z;
-    }
-  } else {
-    base = ri.before1;
-  }
-  auto weight = [&](int i) { return gm[i]; };
-  const int pos = block_first_crossing(NB, base, ri.target, weight, buf, &ibuf);
-  // weight ahead of the crossing bin, in the same association as the crossing search
-  double before;
-  {
-    const int per = (NB + kSelThreads - 1) / kSelThreads;
-    const int i0 = threadIdx.x * per;
-    double local = 0.0;
-    for (int i = i0; i < min(NB, i0 + per); ++i) local += (pos >= 0 && i < pos) ? gm[i] : 0.0;
-    double tot;
-    block_excl_scan(local, buf, &tot);
-    before = base + tot;
-  }
-  if (threadIdx.x == 0) {
-    if (pos < 0) {
-      // rounding left the target above the total weight: keep every entry
-      ri.all = 1;
-    } else if (LEVEL == 1) {
-      ri.bin1 = pos;
-      ri.before1 = before;
-    } else {
-      ri.bin2 = pos;
-      ri.before2 = before;
-    }
-    a.info[row] = ri;
-  }
-}
-
-// Entries of the crossing coarse bin: earlier fine bins are selected outright; the crossing fine
-// bin's entries are gathered for the exact resolution.
-__global__ __launch_bounds__(256) void k_long_collect(LongArgs a) {
-  const int b = blockIdx.z, h = blockIdx.y, tid = threadIdx.x;
-  if ((a.local_mask >> (h / a.G)) & 1) return;
-  const int64_t row = int64_t(b) * a.Hq + h;
   const RowInfo ri = a.info[row];
-  if (ri.all) return;
-  const int64_t t0 = int64_t(blockIdx.x) * kLongBlock;
-  const int64_t t1 = t0 + kLongBlock < a.len ? t0 + kLongBlock : a.len;
-  const double* sr = a.s0 + row * a.len;
-  for (int64_t t = t0 + tid; t < t1; t += 256) {
-    const double s = sr[t];
-    int b1, b2;
-    long_bins(s, ri, &b1, &b2);
-    if (b1 != ri.bin1) continue;
-    if (b2 < ri.bin2) {
-      atomicOr(&a.bits[row * a.words + (t >> 5)], 1u << (t & 31));
-    } else if (b2 == ri.bin2) {
-      const int pos = atomicAdd(&a.ccnt[row], 1);
-      if (pos < kResolveCap) {
-        a.ckey[row * kResolveCap + pos] = dkey(s);
-        a.cidx[row * kResolveCap + pos] = int32_t(t);
-      } else {
-        atomicOr(&a.status[0], 1u);
+  const bool gather = !ri.all && ri.gather;
+  const uint16_t* br = a.cbin + row * a.cstride;
+  uint8_t* bb = reinterpret_cast<uint8_t*>(bw);
+  int32_t* out = a.cidx + (row * a.nb1 + slab) * kResolveCap;
+  constexpr int kVec = kLongBlock / (NT * 8);  // 16-byte pieces per lane
+  // piece v of lane tid covers entries t0 + 8 * (tid + NT v) .. + 7; pieces past the slab load
+  // the slab's last piece again (rows are padded to a multiple of 8 entries) and are masked
+  uint4 pc[kVec];
+#pragma unroll
+  for (int v = 0; v < kVec; ++v) {
+    int64_t e = t0 + 8 * (int64_t(tid) + NT * v);
+    const int64_t last = (t1 - 1) & ~int64_t(7);
+    e = e < last ? e : last;
+    pc[v] = ri.all ? make_uint4(0, 0, 0, 0) : ld16(br + e);
+  }
+#pragma unroll
+  for (int v = 0; v < kVec; ++v) {
+    const int64_t e0 = t0 + 8 * (int64_t(tid) + NT * v);
+    const uint16_t* cb = reinterpret_cast<const uint16_t*>(&pc[v]);
+    uint32_t sel = 0, cand = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool valid = e0 + u < t1;
+      sel |= (valid && (ri.all || cb[u] < ri.bin1)) ? (1u << u) : 0u;
+      cand |= (gather && valid && cb[u] == ri.bin1) ? (1u << u) : 0u;
+    }
+    if (e0 < ((t1 + 31) & ~int64_t(31))) bb[e0 >> 3] = uint8_t(sel);  // whole words, zero past the row
+    const int nc = __popc(cand);
+    const int incl = wave_scan_i32_dpp(nc, lane);
+    const int wtot = __builtin_amdgcn_readlane(incl, 63);
+    if (wtot) {
+      int p0 = 0;
+      if (lane == 0) p0 = atomicAdd(&scnt, wtot);
+      p0 = __builtin_amdgcn_readlane(p0, 0);
+      int pos = p0 + incl - nc;
+      while (cand) {
+        const int u = __ffs(cand) - 1;
+        cand &= cand - 1;
+        if (pos < kResolveCap) out[pos] = int32_t(e0 + u);
+        ++pos;
       }
     }
   }
+  __syncthreads();
+  if (tid == 0) a.ccnt[row * a.nb1 + slab] = scnt < kResolveCap ? scnt : kResolveCap;
 }
 
-// Exact resolution of the crossing fine bin: sort its entries, walk the running weight from the
-// weight of everything ahead of the bin, select up to the first crossing.
-__global__ __launch_bounds__(kSelThreads) void k_long_resolve(LongArgs a) {
+// Exact resolution of the crossing bin's entries. They span one interval of the bin axis; a
+// kSub-bin histogram of that interval (monotone in the score) finds the sub-bin where the running
+// weight, started at the weight ahead of the interval, crosses the target. Entries of earlier
+// sub-bins are selected; the crossing sub-bin's entries are ranked by counting in (score desc,
+// index asc) order and walked to the first crossing. A crossing sub-bin of more than kSubCap
+// entries is resolved by sorting every gathered entry instead.
+constexpr int kSub = 1024;
+constexpr int kSubCap = 256;
+constexpr int kResolveThreads = 512;
+
+__global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
+  constexpr int NT = kResolveThreads;
   const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
   if ((a.local_mask >> (h / a.G)) & 1) return;
   const int64_t row = int64_t(b) * a.Hq + h;
@@ -723,25 +771,253 @@ __global__ __launch_bounds__(kSelThreads) void k_long_resolve(LongArgs a) {
   if (ri.all) return;
   __shared__ uint64_t keys[kResolveCap];
   __shared__ int32_t idx[kResolveCap];
+  __shared__ uint16_t sub[kResolveCap];
+  __shared__ double hm[kSub];
+  __shared__ uint32_t hc[kSub];
+  __shared__ uint64_t xkey[kSubCap];
+  __shared__ int32_t xidx[kSubCap];
+  __shared__ double xw[kSubCap];
+  __shared__ int32_t ridx[kSubCap];
+  __shared__ double wtot[NT / 64];
   __shared__ double buf[kSelThreads];
-  __shared__ int ibuf;
-  int n = a.ccnt[row];
-  n = n < kResolveCap ? n : kResolveCap;
-  int Lp = 2;
-  while (Lp < n) Lp <<= 1;
-  for (int i = tid; i < Lp; i += kSelThreads) {
-    keys[i] = i < n ? a.ckey[row * kResolveCap + i] : 0ull;
-    idx[i] = i < n ? a.cidx[row * kResolveCap + i] : 0x7FFFFFFF;
+  __shared__ int soff[NT + 1];
+  __shared__ int hit_bin, nx, ibuf;
+  __shared__ double hit_before;
+  const double* sr = a.s0 + row * a.len;
+  uint32_t* bw = a.bits + row * a.words;
+  int n;
+  double before, dlo, sscale;
+  if (ri.gather) {
+    // ---- the crossing bin's entries, slab after slab (slab s owns soff[s] .. soff[s+1])
+    const int per = (a.nb1 + NT - 1) / NT;  // slabs per thread
+    double local = 0.0;
+    for (int s = tid * per; s < min(a.nb1, tid * per + per); ++s) local += double(a.ccnt[row * a.nb1 + s]);
+    double tot;
+    const double incl = block_scan<NT>(local, wtot, &tot);
+    // soff holds the first position of every thread's first slab; slabs inside a thread's range
+    // are walked in order below
+    soff[tid] = int(incl - local);
+    if (tid == NT - 1) soff[NT] = int(tot);
+    __syncthreads();
+    n = int(tot) < kResolveCap ? int(tot) : kResolveCap;
+    if (n == 0) return;
+    constexpr int PER = kResolveCap / NT;
+    int32_t tv[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + NT * k;
+      const int j = i < n ? i : n - 1;
+      // owner thread range: last thread u with soff[u] <= j
+      int lo = 0, hi = NT;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (soff[mid] <= j) lo = mid; else hi = mid;
+      }
+      int s = lo * per, off = j - soff[lo];
+      while (s + 1 < a.nb1 && off >= a.ccnt[row * a.nb1 + s]) {  // at most `per` steps
+        off -= a.ccnt[row * a.nb1 + s];
+        ++s;
+      }
+      tv[k] = a.cidx[(row * a.nb1 + s) * kResolveCap + off];
+    }
+    double sv[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) sv[k] = sr[tv[k]];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + NT * k;
+      if (i < n) {
+        keys[i] = dkey(sv[k]);
+        idx[i] = tv[k];
+      }
+    }
+    before = ri.before1;
+    dlo = double(ri.bin1);
+    sscale = double(kSub);
+  } else {
+    // ---- crossing coarse bin too full: fine histogram of its entries over one pass of the row
+    double* fm = reinterpret_cast<double*>(keys);    // kBins2 doubles
+    uint32_t* fc = reinterpret_cast<uint32_t*>(idx);  // kBins2 counts
+    for (int i = tid; i < kBins2; i += NT) {
+      fm[i] = 0.0;
+      fc[i] = 0;
+    }
+    if (tid == 0) {
+      nx = 0;
+      hit_bin = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    const uint16_t* br = a.cbin + row * a.cstride;
+    for (int64_t t = tid; t < a.len; t += NT) {
+      if (br[t] == ri.bin1) {
+        const double s = sr[t];
+        const int f = fine_bin(coarse_pos(s, ri.smax, ri.binscale), ri.bin1);
+        unsafeAtomicAdd(&fm[f], long_weight(a, ri.smax, s));
+        atomicAdd(&fc[f], 1u);
+      }
+    }
+    __syncthreads();
+    constexpr int FPER = kBins2 / NT;
+    double m[FPER];
+    double local = 0.0;
+#pragma unroll
+    for (int j = 0; j < FPER; ++j) {
+      m[j] = fm[FPER * tid + j];
+      local += m[j];
+    }
+    double tot;
+    const double incl = block_scan<NT>(local, wtot, &tot);
+    double c = ri.before1 + (incl - local);
+    const double c0 = c;
+#pragma unroll
+    for (int j = 0; j < FPER; ++j) {
+      const double cn = c + m[j];
+      if (cn >= ri.target) {
+        atomicMin(&hit_bin, FPER * tid + j);
+        break;
+      }
+      c = cn;
+    }
+    __syncthreads();
+    const int bin2 = hit_bin == 0x7FFFFFFF ? kBins2 : hit_bin;  // none: keep the whole coarse bin
+    if (bin2 < kBins2 && bin2 / FPER == tid) {
+      double cb = c0;
+      for (int j = 0; j < bin2 - FPER * tid; ++j) cb += m[j];
+      hit_before = cb;
+    }
+    __syncthreads();  // the fine histogram is dead from here: keys / idx take the candidates
+    for (int64_t t = tid; t < a.len; t += NT) {
+      if (br[t] == ri.bin1) {
+        const double s = sr[t];
+        const int f = fine_bin(coarse_pos(s, ri.smax, ri.binscale), ri.bin1);
+        if (f < bin2) {
+          atomicOr(&bw[t >> 5], 1u << (t & 31));
+        } else if (f == bin2) {
+          const int q = atomicAdd(&nx, 1);
+          if (q < kResolveCap) {
+            keys[q] = dkey(s);
+            idx[q] = int32_t(t);
+          } else {
+            atomicOr(&a.status[0], 1u);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    n = nx < kResolveCap ? nx : kResolveCap;
+    if (n == 0) return;
+    before = hit_before;
+    dlo = double(ri.bin1) + double(bin2) / double(kBins2);
+    sscale = double(kSub) * double(kBins2);
+  }
+  // ---- sub-bin histogram of the gathered entries
+  for (int i = tid; i < kSub; i += NT) {
+    hm[i] = 0.0;
+    hc[i] = 0;
+  }
+  if (tid == 0) {
+    nx = 0;
+    hit_bin = 0x7FFFFFFF;
   }
   __syncthreads();
-  bitonic_desc<int32_t>(keys, idx, Lp);
-  auto weight = [&](int i) { return long_weight(a, ri, dkey_inv(keys[i])); };
-  const int pos = block_first_crossing(n, ri.before2, ri.target, weight, buf, &ibuf);
-  const int n_sel = pos < 0 ? n : pos + 1;
-  for (int i = tid; i < n_sel; i += kSelThreads) {
-    const int t = idx[i];
-    atomicOr(&a.bits[row * a.words + (t >> 5)], 1u << (t & 31));
+  for (int i = tid; i < n; i += NT) {
+    const double s = dkey_inv(keys[i]);
+    const double x = (coarse_pos(s, ri.smax, ri.binscale) - dlo) * sscale;
+    int sb = x >= 0.0 ? (x < double(kSub) ? int(x) : kSub - 1) : 0;
+    sb = sb < kSub - 1 ? sb : kSub - 1;
+    sub[i] = uint16_t(sb);
+    unsafeAtomicAdd(&hm[sb], long_weight(a, ri.smax, s));
+    atomicAdd(&hc[sb], 1u);
   }
+  __syncthreads();
+  constexpr int SPER = kSub / NT;
+  double m[SPER];
+  double local = 0.0;
+#pragma unroll
+  for (int j = 0; j < SPER; ++j) {
+    m[j] = hm[SPER * tid + j];
+    local += m[j];
+  }
+  double tot;
+  const double incl = block_scan<NT>(local, wtot, &tot);
+  double c = before + (incl - local);
+  const double c0 = c;
+#pragma unroll
+  for (int j = 0; j < SPER; ++j) {
+    const double cn = c + m[j];
+    if (cn >= ri.target) {
+      atomicMin(&hit_bin, SPER * tid + j);
+      break;
+    }
+    c = cn;
+  }
+  __syncthreads();
+  const int hb = hit_bin;
+  if (hb != 0x7FFFFFFF && hb / SPER == tid) {
+    double cb = c0;
+    for (int j = 0; j < hb - SPER * tid; ++j) cb += m[j];
+    hit_before = cb;
+  }
+  __syncthreads();
+  if (hb == 0x7FFFFFFF) {
+    // rounding: the target lies beyond the gathered entries; keep all of them
+    for (int i = tid; i < n; i += NT) atomicOr(&bw[idx[i] >> 5], 1u << (idx[i] & 31));
+    return;
+  }
+  if (hc[hb] <= uint32_t(kSubCap)) {
+    for (int i = tid; i < n; i += NT) {
+      const int sb = sub[i];
+      if (sb < hb) {
+        atomicOr(&bw[idx[i] >> 5], 1u << (idx[i] & 31));
+      } else if (sb == hb) {
+        const int q = atomicAdd(&nx, 1);
+        xkey[q] = keys[i];
+        xidx[q] = idx[i];
+      }
+    }
+    __syncthreads();
+    const int nc = nx;
+    for (int q = tid; q < nc; q += NT) {
+      const uint64_t kq = xkey[q];
+      const int32_t iq = xidx[q];
+      int r = 0;
+      for (int u = 0; u < nc; ++u) {
+        const uint64_t ku = xkey[u];
+        r += (ku > kq || (ku == kq && xidx[u] < iq)) ? 1 : 0;
+      }
+      xw[r] = long_weight(a, ri.smax, dkey_inv(kq));
+      ridx[r] = iq;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double cw = hit_before;
+      int ns = nc;
+      for (int r = 0; r < nc; ++r) {
+        cw += xw[r];
+        if (cw >= ri.target) {
+          ns = r + 1;
+          break;
+        }
+      }
+      ibuf = ns;
+    }
+    __syncthreads();
+    for (int r = tid; r < ibuf; r += NT) atomicOr(&bw[ridx[r] >> 5], 1u << (ridx[r] & 31));
+    return;
+  }
+  // near-equal scores fill the crossing sub-bin: sort every gathered entry and walk them all
+  int Lp = 2;
+  while (Lp < n) Lp <<= 1;
+  for (int i = n + tid; i < Lp; i += NT) {
+    keys[i] = 0ull;
+    idx[i] = 0x7FFFFFFF;
+  }
+  __syncthreads();
+  bitonic_desc<int32_t, NT>(keys, idx, Lp);
+  auto weight = [&](int i) { return long_weight(a, ri.smax, dkey_inv(keys[i])); };
+  const int pos = block_first_crossing(n, before, ri.target, weight, buf, &ibuf);
+  const int n_sel = pos < 0 ? n : pos + 1;
+  for (int i = tid; i < n_sel; i += NT) atomicOr(&bw[idx[i] >> 5], 1u << (idx[i] & 31));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -793,10 +1069,15 @@ __global__ __launch_bounds__(256) void k_union_write(UnionArgs a) {
   const int64_t grp = int64_t(b) * a.Hk + g;
   __shared__ int sbase;
   __shared__ int scan[256];
-  if (tid == 0) {
+  __shared__ int wpart[4];
+  {
+    // counts of the earlier ranges, summed by the whole workgroup
     int s = 0;
-    for (int i = 0; i < r; ++i) s += a.rcnt[grp * a.ranges + i];
-    sbase = s;
+    for (int i = tid; i < r; i += 256) s += a.rcnt[grp * a.ranges + i];
+    s = wave_sum_i32_dpp(s);
+    if ((tid & 63) == 0) wpart[tid >> 6] = s;
+    __syncthreads();
+    if (tid == 0) sbase = wpart[0] + wpart[1] + wpart[2] + wpart[3];
   }
   // each thread owns 4 consecutive words
   const int64_t w0 = int64_t(r) * kUnionWordsPerBlock + tid * 4;
@@ -844,11 +1125,11 @@ LongArgs long_args(const Plan& p, char* ws) {
   a.pmax = at<double>(ws, p.o_pmax);
   a.pmin = at<double>(ws, p.o_pmin);
   a.nblk = p.score_blocks0;
+  a.nb1 = p.long_blocks;
   a.h1m = at<double>(ws, p.o_h1m);
   a.h1c = at<uint32_t>(ws, p.o_h1c);
-  a.h2m = at<double>(ws, p.o_h2m);
-  a.h2c = at<uint32_t>(ws, p.o_h2c);
-  a.ckey = at<uint64_t>(ws, p.o_ckey);
+  a.cbin = at<uint16_t>(ws, p.o_cbin);
+  a.cstride = (p.len0 + 7) & ~int64_t(7);
   a.cidx = at<int32_t>(ws, p.o_cidx);
   a.ccnt = at<int32_t>(ws, p.o_ccnt);
   a.bits = at<uint32_t>(ws, p.o_bits);
@@ -927,13 +1208,10 @@ int launch_select(const Plan& p, int level, char* ws, void* stream) {
   }
   const LongArgs a = long_args(p, ws);
   const dim3 rows(Hq, B), blocks(p.long_blocks, Hq, B);
-  hipLaunchKernelGGL(k_long_prep, rows, dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_long_hist<1>, blocks, dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_long_find<1>, rows, dim3(kSelThreads), 0, st, a);
-  hipLaunchKernelGGL(k_long_hist<2>, blocks, dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_long_find<2>, rows, dim3(kSelThreads), 0, st, a);
-  hipLaunchKernelGGL(k_long_collect, blocks, dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_long_resolve, rows, dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_hist, blocks, dim3(kLongThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_find1, rows, dim3(kFindThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_mark, blocks, dim3(kLongThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_resolve, rows, dim3(kResolveThreads), 0, st, a);
   int e = int(hipGetLastError());
   if (e) return e;
   return union_impl(p, ws, st);
