@@ -411,13 +411,16 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
 }
 
 // LSE combine. One workgroup per (sequence, query head): the partials of the head's group are
-// the pool slots (b + group) of the persistent workgroups b whose tile slice meets the group.
+// the pool slots (k + group) of the persistent workgroups k whose tile slice meets the group.
+// Their lse values are read in one parallel round (max, then weights exp(lse - max) in LDS, 256
+// partials at a time); each thread then accumulates one output dimension over a fixed subset of
+// the partials with independent loads. Summation order is fixed: the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ po, const float* __restrict__ pl,
                                                  const int32_t* __restrict__ gpre, int n_groups, int nb_attend,
                                                  int G, int Hq, int Hk, float* __restrict__ out,
                                                  float* __restrict__ lse) {
-  constexpr int DPL = D / 64;  // dims per lane
+  constexpr int NGRP = 256 / D;  // thread groups, each covering all D dims
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int gid = b * Hk + h / G, hh = h % G;
@@ -425,43 +428,57 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ po, c
   const int64_t T = gpre[n_groups];
   const int64_t t0 = gpre[gid], t1 = gpre[gid + 1];
   __shared__ float red[4];
-  __shared__ float ored[4][D];
-  __shared__ float lred[4];
+  __shared__ float wj[256];
+  __shared__ int64_t sj[256];
+  __shared__ float part[NGRP][D];
   if (t0 == t1) {
     for (int d = tid; d < D; d += 256) out[hrow * D + d] = 0.f;
     if (tid == 0) lse[hrow] = kNegInf;
     return;
   }
   const int64_t NB = nb_attend;
-  const int bfirst = int(((t0 + 1) * NB - 1) / T);
-  const int blast = int((t1 * NB - 1) / T);
-  auto nonempty = [&](int k) { return (int64_t(k) * T) / NB < (int64_t(k + 1) * T) / NB; };
+  const int k0 = int(((t0 + 1) * NB - 1) / T);
+  const int nt = int((t1 * NB - 1) / T) - k0 + 1;
+  auto live = [&](int k) { return (int64_t(k) * T) / NB < (int64_t(k + 1) * T) / NB; };
+  // max over the partials' lse
   float M = kNegInf;
-  for (int k = bfirst + tid; k <= blast; k += 256)
-    if (nonempty(k)) M = fmaxf(M, pl[(int64_t(k) + gid) * G + hh]);
+  for (int j = tid; j < nt; j += 256)
+    if (live(k0 + j)) M = fmaxf(M, pl[(int64_t(k0 + j) + gid) * G + hh]);
   for (int o = 32; o; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   if (lane == 0) red[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float acc[DPL], wsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-#pragma unroll 4
-  for (int k = bfirst + wave; k <= blast; k += 4) {
-    if (!nonempty(k)) continue;
-    const int64_t slot = int64_t(k) + gid;
-    const float w = __expf(pl[slot * G + hh] - M);
-    wsum += w;
-    const float* src = po + (slot * G + hh) * D + lane * DPL;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[i] += w * src[i];
+  const int grp = tid / D, d = tid - grp * D;
+  float acc = 0.f, wsum = 0.f;
+  for (int c0 = 0; c0 < nt; c0 += 256) {
+    const int n = min(256, nt - c0);
+    __syncthreads();  // the previous chunk's weights are consumed
+    if (tid < n) {
+      const int k = k0 + c0 + tid;
+      const int64_t slot = int64_t(k) + gid;
+      sj[tid] = slot;
+      wj[tid] = live(k) ? __expf(pl[slot * G + hh] - M) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int j = grp; j < n; j += NGRP) {
+      // an empty slice's slot is never written: its weight is 0 and its contents are skipped
+      const float w = wj[j];
+      const float v = po[(sj[j] * G + hh) * D + d];
+      acc += w != 0.f ? w * v : 0.f;
+    }
+    if (tid == 0)
+      for (int j = 0; j < n; ++j) wsum += wj[j];
   }
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) ored[wave][lane * DPL + i] = acc[i];
-  if (lane == 0) lred[wave] = wsum;
+  part[grp][d] = acc;
+  if (tid == 0) red[0] = wsum;
   __syncthreads();
-  const float L = lred[0] + lred[1] + lred[2] + lred[3];
-  for (int d = tid; d < D; d += 256) out[hrow * D + d] = (ored[0][d] + ored[1][d] + ored[2][d] + ored[3][d]) / L;
+  const float L = red[0];
+  for (int e = tid; e < D; e += 256) {
+    float o = 0.f;
+    for (int g2 = 0; g2 < NGRP; ++g2) o += part[g2][e];
+    out[hrow * D + e] = o / L;
+  }
   if (tid == 0) lse[hrow] = M + __logf(L);
 }
 

@@ -1039,74 +1039,98 @@ struct UnionArgs {
   int keep_first, keep_last, sink, window;
 };
 
+// Per range of kUnionWordsPerBlock words: the union words (OR of the group's per-head words and
+// the forced / local edge bits) and their popcount. Every load is issued first.
 __global__ __launch_bounds__(256) void k_union_count(UnionArgs a) {
   const int b = blockIdx.z, g = blockIdx.y, r = blockIdx.x, tid = threadIdx.x;
   const bool local = (a.local_mask >> g) & 1;
   const int64_t w0 = int64_t(r) * kUnionWordsPerBlock;
   const int64_t grp = int64_t(b) * a.Hk + g;
-  int c = 0;
-  for (int64_t w = w0 + tid; w < w0 + kUnionWordsPerBlock && w < a.words; w += 256) {
-    uint32_t u;
-    if (local) {
-      u = edge_bits(w, a.n, a.sink, a.window);
-    } else {
-      u = edge_bits(w, a.n, a.keep_first, a.keep_last);
-      for (int j = 0; j < a.G; ++j) u |= a.bits[(int64_t(b) * a.Hq + g * a.G + j) * a.words + w];
-      if (w == a.words - 1 && (a.n & 31)) u &= (1u << (a.n & 31)) - 1u;
+  constexpr int PER = kUnionWordsPerBlock / 256;
+  uint32_t u[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) u[i] = 0u;
+  if (!local) {
+    for (int j = 0; j < a.G; ++j) {
+      const uint32_t* src = a.bits + (int64_t(b) * a.Hq + g * a.G + j) * a.words;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int64_t w = w0 + tid + 256 * i;
+        u[i] |= src[w < a.words ? w : a.words - 1];
+      }
     }
-    a.ubits[grp * a.words + w] = u;
-    c += __popc(u);
   }
-  for (int o = 32; o; o >>= 1) c += __shfl_xor(c, o);
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t w = w0 + tid + 256 * i;
+    if (w < a.words) {
+      uint32_t x = local ? edge_bits(w, a.n, a.sink, a.window) : (u[i] | edge_bits(w, a.n, a.keep_first, a.keep_last));
+      if (w == a.words - 1 && (a.n & 31)) x &= (1u << (a.n & 31)) - 1u;
+      a.ubits[grp * a.words + w] = x;
+      c += __popc(x);
+    }
+  }
+  c = wave_sum_i32_dpp(c);
   __shared__ int part[4];
   if ((tid & 63) == 0) part[tid >> 6] = c;
   __syncthreads();
   if (tid == 0) a.rcnt[grp * a.ranges + r] = part[0] + part[1] + part[2] + part[3];
 }
 
+// Per range: the set bits of the union words in ascending order, after the earlier ranges'
+// entries. Wave w takes words [256 w, 256 w + 256) of the range in 4 rounds of 64 (one word per
+// lane); a round's entries are expanded into LDS and copied out with coalesced stores.
 __global__ __launch_bounds__(256) void k_union_write(UnionArgs a) {
   const int b = blockIdx.z, g = blockIdx.y, r = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int64_t grp = int64_t(b) * a.Hk + g;
-  __shared__ int sbase;
-  __shared__ int scan[256];
-  __shared__ int wpart[4];
-  {
-    // counts of the earlier ranges, summed by the whole workgroup
-    int s = 0;
-    for (int i = tid; i < r; i += 256) s += a.rcnt[grp * a.ranges + i];
-    s = wave_sum_i32_dpp(s);
-    if ((tid & 63) == 0) wpart[tid >> 6] = s;
-    __syncthreads();
-    if (tid == 0) sbase = wpart[0] + wpart[1] + wpart[2] + wpart[3];
-  }
-  // each thread owns 4 consecutive words
-  const int64_t w0 = int64_t(r) * kUnionWordsPerBlock + tid * 4;
-  uint32_t u[4];
-  int c = 0;
-  for (int i = 0; i < 4; ++i) {
-    const int64_t w = w0 + i;
+  constexpr int ROUNDS = kUnionWordsPerBlock / 256;
+  __shared__ int wpart[4], wtot[4];
+  __shared__ int32_t stage[4][64 * 32];
+  const int64_t wbase = int64_t(r) * kUnionWordsPerBlock + wave * (64 * ROUNDS);
+  uint32_t u[ROUNDS];
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i) {
+    const int64_t w = wbase + 64 * i + lane;
     u[i] = w < a.words ? a.ubits[grp * a.words + w] : 0u;
-    c += __popc(u[i]);
   }
-  scan[tid] = c;
+  // counts of the earlier ranges, summed by the whole workgroup
+  int s = 0;
+  for (int i = tid; i < r; i += 256) s += a.rcnt[grp * a.ranges + i];
+  s = wave_sum_i32_dpp(s);
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i) mine += __popc(u[i]);
+  mine = wave_sum_i32_dpp(mine);
+  if (lane == 0) {
+    wpart[wave] = s;
+    wtot[wave] = mine;
+  }
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int add = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  int pos = sbase + scan[tid] - c;
+  int pos = wpart[0] + wpart[1] + wpart[2] + wpart[3];
+  for (int w = 0; w < wave; ++w) pos += wtot[w];
   int32_t* out = a.list + grp * a.n;
-  for (int i = 0; i < 4; ++i) {
+  int32_t* st = stage[wave];
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i) {
+    const int c = __popc(u[i]);
+    const int incl = wave_scan_i32_dpp(c, lane);
+    const int n = __builtin_amdgcn_readlane(incl, 63);
+    int o = incl - c;
     uint32_t m = u[i];
+    const int32_t wi = int32_t((wbase + 64 * i + lane) * 32);
     while (m) {
       const int bit = __ffs(m) - 1;
       m &= m - 1;
-      out[pos++] = int32_t((w0 + i) * 32 + bit);
+      st[o++] = wi + bit;
     }
+    __builtin_amdgcn_wave_barrier();
+    for (int e = lane; e < n; e += 64) out[pos + e] = st[e];
+    __builtin_amdgcn_wave_barrier();
+    pos += n;
   }
-  if (r == a.ranges - 1 && tid == 255) a.cnt[grp] = sbase + scan[255];
+  if (r == a.ranges - 1 && wave == 3 && lane == 0) a.cnt[grp] = pos;
 }
 
 LongArgs long_args(const Plan& p, char* ws) {
