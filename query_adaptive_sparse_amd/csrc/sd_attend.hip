@@ -14,7 +14,7 @@
 // slots as M. P arrives from the logit layout with no data movement; for bf16 it is split into
 // hi = bf16(p) (slots [0, G)) and lo = bf16(p - hi) (slots [G, 2G)) rows, which keeps fp32
 // accuracy. V goes through LDS (row-major, padded rows) to reach the B-operand layout. The next
-// tiles' K and V loads are issued before the current tile is computed (a ring of register stages).
+// tile's K and V loads are issued before the current tile is computed (a ring of register stages).
 // K and V rows are read exactly once per call, so their loads are marked non-temporal: without
 // the hint they evict each other in the per-XCD L2s and some XCDs stream 10-20% slower than others,
 // which leaves the whole chip waiting on the slowest one at the end of the launch.
@@ -54,9 +54,11 @@ struct Cfg {
   static constexpr int kVtWords = kTile * kRowWords;
   static constexpr int kMergeWords = 16 * D + 32;
   static constexpr int kWaveWords = kVtWords > kMergeWords ? kVtWords : kMergeWords;
-  // register stages of the load pipeline: ~128 VGPRs of tiles in flight per wave
-  static constexpr int kRegsPerStage = 4 * (KQ + VPL);
-  static constexpr int NS = 128 / kRegsPerStage >= 4 ? 4 : (128 / kRegsPerStage >= 2 ? 128 / kRegsPerStage : 2);
+  // register stages of the load pipeline: about 8 KB of K / V in flight per wave beyond the tile
+  // being computed. With non-temporal loads, deeper rings measured slower on MI355X (more requests
+  // queued per wave, same bandwidth): 2 stages for 8 KB tiles (bf16, d = 128), 3 for 4 KB tiles.
+  static constexpr int kTileBytes = 2 * kTile * D * int(sizeof(T));
+  static constexpr int NS = 1 + (8192 / kTileBytes > 1 ? 8192 / kTileBytes : 1);
 };
 
 template <typename T, int D>
