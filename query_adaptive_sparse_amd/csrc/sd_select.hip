@@ -885,7 +885,62 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
       for (int j = 0; j < bin2 - FPER * tid; ++j) cb += m[j];
       hit_before = cb;
     }
-    __syncthreads();  // the fine histogram is dead from here: keys / idx take the candidates
+    __syncthreads();
+    const uint32_t cnt2 = bin2 < kBins2 ? fc[bin2] : 0u;
+    if (cnt2 > uint32_t(kResolveCap)) {
+      // The crossing fine bin holds more entries than the buffer. Resolvable here when they all
+      // carry one score (exact ties): their order is then the index order and their weights are
+      // equal. Entries are taken in contiguous per-thread index ranges, so a thread-order scan of
+      // their counts ranks them by index.
+      __shared__ double tmin[NT / 64], tmax[NT / 64];
+      const int64_t per = (a.len + NT - 1) / NT;
+      const int64_t r0 = int64_t(tid) * per, r1 = r0 + per < a.len ? r0 + per : a.len;
+      double lo = kPosInfD, hi = kNegInfD;
+      int mine = 0;
+      for (int64_t t = r0; t < r1; ++t) {
+        if (br[t] == ri.bin1) {
+          const double sc = sr[t];
+          const int f = fine_bin(coarse_pos(sc, ri.smax, ri.binscale), ri.bin1);
+          if (f < bin2) {
+            atomicOr(&bw[t >> 5], 1u << (t & 31));
+          } else if (f == bin2) {
+            lo = fmin(lo, sc);
+            hi = fmax(hi, sc);
+            ++mine;
+          }
+        }
+      }
+      lo = wave_min_dpp(lo);
+      hi = wave_max_dpp(hi);
+      if ((tid & 63) == 0) {
+        tmin[tid >> 6] = lo;
+        tmax[tid >> 6] = hi;
+      }
+      __syncthreads();
+      for (int w = 0; w < NT / 64; ++w) {
+        lo = fmin(lo, tmin[w]);
+        hi = fmax(hi, tmax[w]);
+      }
+      if (lo != hi) {  // near-equal but distinct scores beyond the buffer: not resolved
+        if (tid == 0) atomicOr(&a.status[0], 1u);
+        return;
+      }
+      const double wt = long_weight(a, ri.smax, lo);
+      auto same = [&](int) { return wt; };
+      const int pos = block_first_crossing(int(cnt2), hit_before, ri.target, same, buf, &ibuf);
+      const int take = pos < 0 ? int(cnt2) : pos + 1;
+      double tot;
+      const int rank0 = int(block_scan<NT>(double(mine), wtot, &tot)) - mine;
+      int rank = rank0;
+      for (int64_t t = r0; t < r1 && rank < take; ++t) {
+        if (br[t] == ri.bin1 && fine_bin(coarse_pos(sr[t], ri.smax, ri.binscale), ri.bin1) == bin2) {
+          atomicOr(&bw[t >> 5], 1u << (t & 31));
+          ++rank;
+        }
+      }
+      return;
+    }
+    // the fine histogram is dead from here: keys / idx take the candidates
     for (int64_t t = tid; t < a.len; t += NT) {
       if (br[t] == ri.bin1) {
         const double s = sr[t];

@@ -103,3 +103,24 @@ def test_attend_block_counts(blocks):
     w = configs.get("c2s")
     inp = gen.make_inputs(w, device="cuda")
     _run(w, inp, attend_blocks=blocks)
+
+
+@pytest.mark.parametrize("kind", ["proxy_topp", "summary_topp", "topk"])
+def test_long_rows_all_tied(kind):
+    """Long rows whose scores all tie: the crossing bin holds the whole row (more entries than the
+    resolution buffer), and the selection is the lowest indices reaching the target."""
+    if kind == "proxy_topp":
+        w = replace(configs.get("c5s"), name="tie_long_proxy")
+        inp = gen.make_inputs(w, device="cuda")
+        inp["Kp"][:] = inp["Kp"][:, :, :1]
+    elif kind == "summary_topp":
+        w = replace(configs.get("c3s"), name="tie_long_summary", batch=1, kv_batch=1, chunk_size=2, n_ctx=16384,
+                    keep_first=0, keep_last=0)
+        inp = gen.make_inputs(w, device="cuda")
+        inp["Kg"][:] = inp["Kg"][:, :, :1]
+    else:
+        w = replace(configs.get("c2s"), name="tie_long_topk", chunk_size=1, n_ctx=8192, top_k=5000)
+        inp = gen.make_inputs(w, device="cuda")
+        inp["Kg"][:] = inp["Kg"][:, :, :1]
+    g, o = _run(w, inp)
+    assert int(g["sel"]["status"][0]) == 0, "overflow flag set"
