@@ -81,7 +81,7 @@ sd_status check_cfg(const sd_config& c) {
     return fail(SD_EUNSUPPORTED, "batch * n_kv_heads > %d", sd::kMaxGroups);
   {
     const int64_t M = c.n_ctx / c.chunk_size;
-    const int64_t tiles = int64_t(c.batch) * c.n_kv_heads * ((c.n_ctx + 15) / 16 + (M + 15) / 16);
+    const int64_t tiles = int64_t(c.batch) * c.n_kv_heads * ((c.n_ctx + 15) / 16 + (M + 15) / 16 + 64);
     if (tiles >= (int64_t(1) << 30)) return fail(SD_EUNSUPPORTED, "too many attention tiles per call");
   }
   if (c.chunk_size & (c.chunk_size - 1)) return fail(SD_EUNSUPPORTED, "chunk_size must be a power of two (got %d)", c.chunk_size);

@@ -75,6 +75,21 @@ struct SoftmaxState {
 };
 
 constexpr int kListLds = 4096;
+// Cost of starting a segment (a group's raw tiles, or its summary tiles) in tiles of streaming:
+// the load ring refills and the query and list slice are reloaded. Each segment start counts as
+// this many extra tiles when the tile sequence is cut into equal slices, so a slice that starts a
+// segment carries fewer tiles (workgroups whose slice crossed a group boundary measured ~7 us
+// slower at 128K context without it).
+constexpr int kSegmentCost = 16;
+
+// Extent of a group in the sliced sequence: [kSegmentCost virtual tiles, raw tiles,
+// kSegmentCost virtual tiles, summary tiles]; an empty group has none.
+__device__ __forceinline__ int group_extent(int cnt, int cs, int attend_summary) {
+  if (cnt <= 0) return 0;
+  const int traw = ((cnt << cs) + kTile - 1) / kTile;
+  const int tsum = attend_summary ? (cnt + kTile - 1) / kTile : 0;
+  return kSegmentCost + traw + (tsum ? kSegmentCost + tsum : 0);
+}
 
 template <typename T, int D>
 struct Attender {
@@ -278,14 +293,13 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   const int NG = a.n_groups;
   const int cs = a.chunk_shift;
 
-  // ---- tiles per group, exclusive prefix in gpre[0..NG]
+  // ---- extent of every group (tiles plus segment costs), exclusive prefix in gpre[0..NG]
   {
     const int per = (NG + 255) / 256;
     const int g0 = tid * per;
     int sum = 0;
     for (int gg = g0; gg < min(NG, g0 + per); ++gg) {
-      const int cnt = a.cnt[gg];
-      sum += ((cnt << cs) + kTile - 1) / kTile + (a.attend_summary ? (cnt + kTile - 1) / kTile : 0);
+      sum += group_extent(a.cnt[gg], cs, a.attend_summary);
     }
     sbuf[tid] = sum;
     __syncthreads();
@@ -298,8 +312,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
     int run = sbuf[tid] - sum;
     for (int gg = g0; gg < min(NG, g0 + per); ++gg) {
       gpre[gg] = run;
-      const int cnt = a.cnt[gg];
-      run += ((cnt << cs) + kTile - 1) / kTile + (a.attend_summary ? (cnt + kTile - 1) / kTile : 0);
+      run += group_extent(a.cnt[gg], cs, a.attend_summary);
     }
     if (tid == 255) gpre[NG] = sbuf[255];
     __syncthreads();
@@ -339,14 +352,16 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
     for (int nb = 0; nb < D / 16; ++nb) st.acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int32_t* glist = a.list + int64_t(gi) * a.n_list;
 
-    // raw tiles [max(s0, 0), min(s1, traw)), in slices whose list entries fit the LDS buffer
+    // raw tiles [r0, r1) (the group's extent puts them at [kSegmentCost, kSegmentCost + traw)), in
+    // pieces whose list entries fit the LDS buffer
     {
-      // a slice of u tiles spans at most (u * kTile) / C + 2 list entries
+      const int r0 = max(s0, kSegmentCost) - kSegmentCost, r1 = min(s1, kSegmentCost + traw) - kSegmentCost;
+      // a piece of u tiles spans at most (u * kTile) / C + 2 list entries
       const int64_t tps = (int64_t(kListLds - 2) << cs) / kTile;
       const int tiles_per_slice = int(tps < 1 ? 1 : (tps > (1 << 30) ? (1 << 30) : tps));
       at.set_kind(false);
-      for (int u0 = s0; u0 < min(s1, traw); u0 += tiles_per_slice) {
-        const int u1 = min(min(s1, traw), u0 + tiles_per_slice);
+      for (int u0 = r0; u0 < r1; u0 += tiles_per_slice) {
+        const int u1 = min(r1, u0 + tiles_per_slice);
         const int e0 = (u0 * kTile) >> cs;
         const int e1 = min(cnt, ((u1 * kTile - 1) >> cs) + 1);
         __syncthreads();
@@ -355,18 +370,20 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
         at.run(false, u0, u1, ntok, e0, st);
       }
     }
-    // summary tiles
+    // summary tiles [q0, q1) (at [2 kSegmentCost + traw, extent) of the group's extent)
     if (a.attend_summary) {
+      const int base = 2 * kSegmentCost + traw;
+      const int q0 = max(s0, base) - base, q1 = s1 - base;
       at.set_kind(true);
       const int tiles_per_slice = kListLds / kTile;
-      for (int u0 = max(s0, traw); u0 < s1; u0 += tiles_per_slice) {
-        const int u1 = min(s1, u0 + tiles_per_slice);
-        const int e0 = (u0 - traw) * kTile;
-        const int e1 = min(cnt, (u1 - traw) * kTile);
+      for (int u0 = q0; u0 < q1; u0 += tiles_per_slice) {
+        const int u1 = min(q1, u0 + tiles_per_slice);
+        const int e0 = u0 * kTile;
+        const int e1 = min(cnt, u1 * kTile);
         __syncthreads();
         for (int i = tid; i < e1 - e0; i += 256) lst[i] = glist[e0 + i];
         __syncthreads();
-        at.run(true, u0 - traw, u1 - traw, cnt, e0, st);
+        at.run(true, u0, u1, cnt, e0, st);
       }
     }
 
@@ -405,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
         if (CF::BF) o += ww[(hh + G) * D + dd];
         O += o * f;
       }
-      a.po[(slot * G + hh) * D + dd] = O / Ls;
+      a.po[(slot * G + hh) * D + dd] = Ls > 0.f ? O / Ls : 0.f;  // no tiles of the group: empty partial
       if (dd == 0) a.pl[slot * G + hh] = (M + __log2f(Ls)) * 0.6931471805599453f;
     }
     __syncthreads();
