@@ -261,7 +261,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "context": w.n_ctx, "chunk": w.chunk_size, "mode": w.mode,
                    "top_p": w.top_p if w.mode in ("topp", "proxy") else None,
-                   "top_k": w.top_k or None, "attend_blocks": dec.params.get("attend_blocks") or 256,
+                   "top_k": w.top_k or None, "attend_blocks": dec.attend_blocks,
                    "cache_flush_mib": args.flush_mib},
         "hbm_gbps": round(step_gbps, 1),
         "hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
@@ -273,7 +273,7 @@ def main():
         "roofline": {"kernel": "k_attend (gathered split-K attention)", "bound": "hbm",
                      "achieved": round(attend_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attend_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": counter_traffic(w.name, dec.params.get("attend_blocks") or 256),
+                     "traffic": counter_traffic(w.name, dec.attend_blocks),
                      "bytes_per_launch": nb["attend"], "avg_launch_ms": round(attend_ms, 5)},
         "status_flags": int(status[0]),
     }

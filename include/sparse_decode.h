@@ -90,7 +90,7 @@ typedef struct {
   int32_t attend_summary; /* 1: the hybrid context adds the selected chunks' summary K/V */
   int32_t attend_blocks;  /* persistent attention workgroups, each streaming an equal slice
                              of all groups' tiles; 0 = library default (256: one per CU of a
-                             256-CU MI355X) */
+                             256-CU MI355X). See sparse_decode_attend_blocks(). */
   const int8_t* head_mode;/* HOST array [n_kv_heads]: 0 = scored head, 1 = local head;
                              NULL = all scored. Copied at init. */
 } sd_config;
@@ -140,8 +140,12 @@ typedef struct {
  * shape or parameter), SD_EUNSUPPORTED (head_dim not 64/128, group > 8). */
 sd_status sparse_decode_init(const sd_config* cfg, sd_handle** out, size_t* workspace_bytes);
 
-/* 1 for flat selection, 2 for two-level (SD_HIER_TOPK). */
+/* 1 for flat selection, 2 for two-level (SD_HIER_TOPK). 0 for a NULL handle. */
 int32_t sparse_decode_num_levels(const sd_handle* h);
+
+/* Persistent attention workgroups the handle launches (attend_blocks, or the
+ * library default when it was 0). 0 for a NULL handle. Host only. */
+int32_t sparse_decode_attend_blocks(const sd_handle* h);
 
 /* Step 1: scores of `level` (0: summary / meta-summary / proxy scores of every
  * entry; 1: chunk scores of the level-0 candidates) into the workspace. */

@@ -212,6 +212,8 @@ sd_status sparse_decode_init(const sd_config* cfg, sd_handle** out, size_t* work
 
 int32_t sparse_decode_num_levels(const sd_handle* h) { return h ? h->plan.levels : 0; }
 
+int32_t sparse_decode_attend_blocks(const sd_handle* h) { return h ? h->plan.attend_blocks : 0; }
+
 sd_status sparse_decode_score_chunks(const sd_handle* h, const sd_tensors* t, int level, void* ws, void* stream) {
   if (!h) return fail(SD_EINVAL, "score: NULL handle");
   const sd::Plan& p = h->plan;

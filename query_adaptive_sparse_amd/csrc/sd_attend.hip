@@ -429,29 +429,34 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   }
 }
 
-// LSE combine. One workgroup per (sequence, query head): the partials of the head's group are
-// the pool slots (k + group) of the persistent workgroups k whose tile slice meets the group.
-// Their lse values are read in one parallel round (max, then weights exp(lse - max) in LDS, 256
-// partials at a time); each thread then accumulates one output dimension over a fixed subset of
-// the partials with independent loads. Summation order is fixed: the result is deterministic.
+// LSE combine. One workgroup of kCombineThreads per (sequence, query head): the partials of the
+// head's group are the pool slots (k + group) of the persistent workgroups k whose tile slice
+// meets the group. Their lse values are read in one parallel round (max, then weights
+// exp(lse - max) in LDS, kCombineThreads partials at a time); each thread then accumulates one
+// output dimension over a fixed subset of the partials with independent loads. Summation order
+// is fixed: the result is deterministic.
+constexpr int kCombineThreads = 1024;
+
 template <int D>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ po, const float* __restrict__ pl,
-                                                 const int32_t* __restrict__ gpre, int n_groups, int nb_attend,
-                                                 int G, int Hq, int Hk, float* __restrict__ out,
-                                                 float* __restrict__ lse) {
-  constexpr int NGRP = 256 / D;  // thread groups, each covering all D dims
+__global__ __launch_bounds__(kCombineThreads) void k_combine(const float* __restrict__ po, const float* __restrict__ pl,
+                                                             const int32_t* __restrict__ gpre, int n_groups,
+                                                             int nb_attend, int G, int Hq, int Hk,
+                                                             float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int NT = kCombineThreads;
+  constexpr int NW = NT / 64;
+  constexpr int NGRP = NT / D;  // thread groups, each covering all D dims
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int gid = b * Hk + h / G, hh = h % G;
   const int64_t hrow = int64_t(b) * Hq + h;
   const int64_t T = gpre[n_groups];
   const int64_t t0 = gpre[gid], t1 = gpre[gid + 1];
-  __shared__ float red[4];
-  __shared__ float wj[256];
-  __shared__ int64_t sj[256];
+  __shared__ float red[NW];
+  __shared__ float wj[NT];
+  __shared__ int64_t sj[NT];
   __shared__ float part[NGRP][D];
   if (t0 == t1) {
-    for (int d = tid; d < D; d += 256) out[hrow * D + d] = 0.f;
+    for (int d = tid; d < D; d += NT) out[hrow * D + d] = 0.f;
     if (tid == 0) lse[hrow] = kNegInf;
     return;
   }
@@ -461,17 +466,18 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ po, c
   auto live = [&](int k) { return (int64_t(k) * T) / NB < (int64_t(k + 1) * T) / NB; };
   // max over the partials' lse
   float M = kNegInf;
-  for (int j = tid; j < nt; j += 256)
+  for (int j = tid; j < nt; j += NT)
     if (live(k0 + j)) M = fmaxf(M, pl[(int64_t(k0 + j) + gid) * G + hh]);
   for (int o = 32; o; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   if (lane == 0) red[wave] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  M = red[0];
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
   const int grp = tid / D, d = tid - grp * D;
   float acc = 0.f, wsum = 0.f;
-  for (int c0 = 0; c0 < nt; c0 += 256) {
-    const int n = min(256, nt - c0);
-    __syncthreads();  // the previous chunk's weights are consumed
+  for (int c0 = 0; c0 < nt; c0 += NT) {
+    const int n = min(NT, nt - c0);
+    __syncthreads();  // the previous chunk's weights (and red) are consumed
     if (tid < n) {
       const int k = k0 + c0 + tid;
       const int64_t slot = int64_t(k) + gid;
@@ -490,10 +496,11 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ po, c
       for (int j = 0; j < n; ++j) wsum += wj[j];
   }
   part[grp][d] = acc;
+  __syncthreads();
   if (tid == 0) red[0] = wsum;
   __syncthreads();
   const float L = red[0];
-  for (int e = tid; e < D; e += 256) {
+  for (int e = tid; e < D; e += NT) {
     float o = 0.f;
     for (int g2 = 0; g2 < NGRP; ++g2) o += part[g2][e];
     out[hrow * D + e] = o / L;
@@ -556,10 +563,10 @@ int launch_combine(const Plan& p, char* ws, float* out, float* lse, void* stream
   const dim3 grid(c.n_q_heads, c.batch);
   const int NG = c.batch * c.n_kv_heads;
   if (c.head_dim == 128)
-    hipLaunchKernelGGL(k_combine<128>, grid, dim3(256), 0, st, at<float>(ws, p.o_po), at<float>(ws, p.o_pl),
+    hipLaunchKernelGGL(k_combine<128>, grid, dim3(kCombineThreads), 0, st, at<float>(ws, p.o_po), at<float>(ws, p.o_pl),
                        at<int32_t>(ws, p.o_gpre), NG, p.attend_blocks, p.G, c.n_q_heads, c.n_kv_heads, out, lse);
   else
-    hipLaunchKernelGGL(k_combine<64>, grid, dim3(256), 0, st, at<float>(ws, p.o_po), at<float>(ws, p.o_pl),
+    hipLaunchKernelGGL(k_combine<64>, grid, dim3(kCombineThreads), 0, st, at<float>(ws, p.o_po), at<float>(ws, p.o_pl),
                        at<int32_t>(ws, p.o_gpre), NG, p.attend_blocks, p.G, c.n_q_heads, c.n_kv_heads, out, lse);
   return int(hipGetLastError());
 }

@@ -28,7 +28,8 @@ constexpr int kTile = 16;
 constexpr int kWaves = 4;
 constexpr int kMaxGroup = 8;
 constexpr int kMaxKvHeads = 64;
-// Attention: persistent workgroups (default) and the most (sequence, KV group) pairs per call.
+// Attention: persistent workgroups (default: one per CU of a 256-CU MI355X) and the most
+// (sequence, KV group) pairs per call.
 constexpr int kAttendBlocks = 256;
 constexpr int kMaxGroups = 4096;
 
@@ -69,7 +70,7 @@ struct RowInfo {
 // Kernel launchers (sd_kernels.hip). Each returns hipSuccess or the launch error.
 int launch_score(const Plan& p, const sd_tensors& t, int level, char* ws, void* stream);
 int launch_select(const Plan& p, int level, char* ws, void* stream);
-int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream);  // + kAttendBlocks
+int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream);
 int launch_combine(const Plan& p, char* ws, float* out, float* lse, void* stream);
 const char* hip_error_string(int code);
 

@@ -90,7 +90,7 @@ __device__ int block_first_crossing(int n, double base, double target, WF weight
 //      (fixed-order DPP reductions: every lane holds the same bits);
 //   2. a 256-bin histogram of the weights (mass, or 1 for top-k) over the bins of (smax - s)
 //      finds the bin where the running weight reaches the target (p*Z or k); if that bin holds
-//      more than kCandCap entries a second 256-bin level splits it;
+//      more than kRankDirect entries a second 256-bin level splits it;
 //   3. the crossing bin's entries are ranked in (score desc, index asc) order by counting and
 //      their weights walked from the weight of everything ahead of the bin to the first crossing.
 // Bins are monotone in the score, so every entry of an earlier bin precedes every entry of a
@@ -105,6 +105,9 @@ __device__ int block_first_crossing(int n, double base, double target, WF weight
 // ---------------------------------------------------------------------------------------------
 constexpr int kNBin = 256;
 constexpr int kCandCap = 256;
+// A crossing coarse bin of more entries than this is split by the second level before ranking
+// (ranking by counting costs n^2 LDS reads).
+constexpr int kRankDirect = 16;
 constexpr int kSelT = 256;                          // threads per head
 constexpr int kSelW = kSelT / 64;                   // waves per head
 constexpr int kLaneEntries = kSmallRowMax / kSelT;  // 8
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
         } else {
           res_i = hb;
           res_d = bb;
-          res_state = hc[hb] <= uint32_t(kCandCap) ? lv : (lv == 2 ? 3 : 0);
+          res_state = hc[hb] <= uint32_t(lv == 1 ? kRankDirect : kCandCap) ? lv : (lv == 2 ? 3 : 0);
         }
       }
     }

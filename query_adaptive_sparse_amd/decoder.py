@@ -79,6 +79,7 @@ class SparseDecoder:
         self.cfg, self._hm = make_config(**params)
         self.handle, self.ws_bytes = N.sparse_decode_init(self.cfg)
         self.levels = N.sparse_decode_num_levels(self.handle)
+        self.attend_blocks = N.sparse_decode_attend_blocks(self.handle)
         self.device = torch.device(device)
         self.ws = None
 

@@ -19,7 +19,8 @@ SD_ROUTE_SUMMARY, SD_ROUTE_PROXY = 0, 1
 
 STATUS_NAMES = {0: "SD_OK", 1: "SD_EINVAL", 2: "SD_EUNSUPPORTED", 3: "SD_EWORKSPACE", 4: "SD_EHIP"}
 
-EXPORTS = ("sparse_decode_init", "sparse_decode_num_levels", "sparse_decode_score_chunks", "sparse_decode_select",
+EXPORTS = ("sparse_decode_init", "sparse_decode_num_levels", "sparse_decode_attend_blocks",
+           "sparse_decode_score_chunks", "sparse_decode_select",
            "sparse_decode_attend", "sparse_decode_combine", "sparse_decode_selection_view",
            "sparse_decode_last_error", "sparse_decode_destroy")
 
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.sparse_decode_init.restype = st
         L.sparse_decode_num_levels.argtypes = [vp]
         L.sparse_decode_num_levels.restype = i32
+        L.sparse_decode_attend_blocks.argtypes = [vp]
+        L.sparse_decode_attend_blocks.restype = i32
         L.sparse_decode_score_chunks.argtypes = [vp, ctypes.POINTER(sd_tensors), ctypes.c_int, vp, vp]
         L.sparse_decode_score_chunks.restype = st
         L.sparse_decode_select.argtypes = [vp, ctypes.c_int, vp, vp]
@@ -118,6 +121,10 @@ def sparse_decode_init(cfg: sd_config):
 
 def sparse_decode_num_levels(handle) -> int:
     return lib().sparse_decode_num_levels(handle)
+
+
+def sparse_decode_attend_blocks(handle) -> int:
+    return lib().sparse_decode_attend_blocks(handle)
 
 
 def sparse_decode_score_chunks(handle, tensors: sd_tensors, level: int, ws: int, stream: int):

@@ -128,3 +128,14 @@ def test_workspace_grows_with_batch():
     _, a = _init(**_params("c3s", batch=1, kv_batch=1))
     _, b = _init(**_params("c3s", batch=2, kv_batch=2))
     assert b > a
+
+
+def test_attend_blocks_default_and_override():
+    """One persistent attention workgroup per CU by default; an explicit count is kept."""
+    cases = [(dict(), 256), (dict(attend_blocks=7), 7), (dict(dtype="f32", head_dim=64), 256),
+             (dict(attend_blocks=4096), 4096)]
+    for kw, want in cases:
+        h, _ = _init(**_params("c3s", **kw))
+        assert N.sparse_decode_attend_blocks(h) == want, kw
+        N.sparse_decode_destroy(h)
+    assert N.sparse_decode_attend_blocks(None) == 0
