@@ -80,8 +80,9 @@ def algorithmic_bytes(w, counts: np.ndarray) -> dict:
         sum_k_sel = U * d * e
     else:
         routing = w.kv_batch * w.n_kv_heads * w.n_chunks * d * e  # every summary key
-        sum_v = U * d * e if w.attend_summary else 0
-        sum_k_sel = U * d * e if w.attend_summary else 0
+        n_sum = B * w.n_kv_heads * w.n_chunks if w.all_summaries else U  # summary rows attended
+        sum_v = n_sum * d * e if w.attend_summary else 0
+        sum_k_sel = n_sum * d * e if w.attend_summary else 0
     q_out = B * Hq * d * (e + 4)
     step = routing + raw_kv + sum_v + q_out
     attend = raw_kv + sum_v + sum_k_sel + B * Hq * d * e + U * 4  # + list
@@ -105,7 +106,7 @@ def cpu_baseline(w, inp, target_s=15.0, max_groups=0):
         b, g = order[done % len(order)]
         t0 = time.perf_counter()
         r = ref.select_group(w, src, b, g)
-        ref.attend_group(w, src, b, g, r["union"])
+        ref.attend_group(w, src, b, g, r["union"], r["heads"])
         t_total += time.perf_counter() - t0
         done += 1
         if (max_groups and done >= max_groups) or (not max_groups and t_total >= target_s):

@@ -87,10 +87,17 @@ typedef struct {
   int32_t keep_last;      /* chunks [M - keep_last, M) always in the union */
   int32_t sink;           /* local KV heads: tokens [0, sink) ... */
   int32_t window;         /* ... and [N - window, N); needs C == 1 */
-  int32_t attend_summary; /* 1: the hybrid context adds the selected chunks' summary K/V */
+  int32_t attend_summary; /* summary K/V in the hybrid context: 0 none, 1 the selected
+                             chunks' ([SSA] technical detail), 2 every chunk's (variant:
+                             the query meets all summaries) */
   int32_t attend_blocks;  /* persistent attention workgroups, each streaming an equal slice
                              of all groups' tiles; 0 = library default (256: one per CU of a
                              256-CU MI355X). See sparse_decode_attend_blocks(). */
+  int32_t head_masks;     /* 0: every head of a group attends to the whole group union; 1
+                             (variant): the union is still loaded once, but head h attends
+                             only to its own selection plus the forced chunks (local groups
+                             unmasked; summaries of unselected chunks under attend_summary 2
+                             stay visible to every head) */
   const int8_t* head_mode;/* HOST array [n_kv_heads]: 0 = scored head, 1 = local head;
                              NULL = all scored. Copied at init. */
 } sd_config;

@@ -37,6 +37,12 @@ Readings where the pages are silent (each is a fixed choice of this oracle):
   group union.
 * Proxy scoring: the same d x r projection maps the query and the keys;
   ``q_p = q P`` in fp64, score ``q_p . k_p``.
+* Variant "all summaries": the summary K/V of every chunk join the context,
+  not only the selected chunks' ([SSA] 기술 상세 has the query interact with
+  all summaries first); they are attended by every head of the group.
+* Variant "per-head masks": the group still loads the union once, but head h
+  attends only to the raw (and selected-summary) rows of its own selection plus
+  the forced sink / recent chunks; local groups are unmasked.
 
 Arithmetic: inputs arrive as fp64 (their bf16 / fp16 / fp32 values are exact in
 fp64). Scores are summed in index order, one rounding per multiply and per
@@ -227,17 +233,41 @@ def select_group(w, src, b: int, g: int) -> dict:
     return res
 
 
-def attend_group(w, src, b: int, g: int, U: np.ndarray):
-    """Every query head of group g attends to the hybrid context of union U."""
+def attend_group(w, src, b: int, g: int, U: np.ndarray, heads=None):
+    """The query heads of group g attend to the hybrid context of union U: raw
+    rows of U's chunks, then (``attend_summary``) the summary rows of U, or of
+    every chunk with ``all_summaries``. With ``head_masks`` and a scored group,
+    head h attends only to its own selection ``heads[h]`` plus the forced
+    chunks (summary rows of every chunk stay visible to all heads)."""
     G = w.n_q_heads // w.n_kv_heads
     bk = b if w.kv_batch > 1 else 0
-    rows = hybrid_rows(U, w.chunk_size)
-    Kc, Vc = src.kv_rows(bk, g, rows)
-    if w.attend_summary and w.mode != PROXY_TOPP:
-        Kc = np.concatenate([Kc, src.Kg[bk, g][U]], axis=0)
-        Vc = np.concatenate([Vc, src.Vg[bk, g][U]], axis=0)
+    n_ent = w.n_ctx // w.chunk_size
+    summaries = w.attend_summary and w.mode != PROXY_TOPP
+    all_sum = summaries and getattr(w, "all_summaries", False)
+    masked = getattr(w, "head_masks", False) and g not in tuple(w.local_kv_heads)
     qh = src.q[b, g * G:(g + 1) * G]
-    return attend(qh, Kc, Vc, w.softmax_scale)
+
+    def context(S):
+        rows = hybrid_rows(S, w.chunk_size)
+        Kc, Vc = src.kv_rows(bk, g, rows)
+        if summaries:
+            srows = np.arange(n_ent) if all_sum else np.asarray(S, dtype=np.int64)
+            Kc = np.concatenate([Kc, src.Kg[bk, g][srows]], axis=0)
+            Vc = np.concatenate([Vc, src.Vg[bk, g][srows]], axis=0)
+        return Kc, Vc
+
+    if not masked:
+        Kc, Vc = context(U)
+        return attend(qh, Kc, Vc, w.softmax_scale)
+    forced = edge_entries(n_ent, w.keep_first, w.keep_last)
+    o = np.zeros((G, w.head_dim))
+    lse = np.zeros(G)
+    for j in range(G):
+        S = group_union([heads[g * G + j], forced])
+        Kc, Vc = context(S)
+        oj, lj = attend(qh[j:j + 1], Kc, Vc, w.softmax_scale)
+        o[j], lse[j] = oj[0], lj[0]
+    return o, lse
 
 
 def decode_step(w, src, groups=None, attend_groups=None) -> dict:
@@ -258,7 +288,7 @@ def decode_step(w, src, groups=None, attend_groups=None) -> dict:
     for b, g in attend_groups:
         if (b, g) not in sel:
             sel[(b, g)] = select_group(w, src, b, g)
-        o, l = attend_group(w, src, b, g, sel[(b, g)]["union"])
+        o, l = attend_group(w, src, b, g, sel[(b, g)]["union"], sel[(b, g)]["heads"])
         out[b, g * G:(g + 1) * G] = o
         lse[b, g * G:(g + 1) * G] = l
     return {"sel": sel, "out": out, "lse": lse}

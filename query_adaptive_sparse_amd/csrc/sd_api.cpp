@@ -77,6 +77,8 @@ sd_status check_cfg(const sd_config& c) {
   if (c.keep_first < 0 || c.keep_last < 0) return fail(SD_EINVAL, "keep_first / keep_last must be >= 0");
   if (c.sink < 0 || c.window < 0) return fail(SD_EINVAL, "sink / window must be >= 0");
   if (c.attend_blocks < 0 || c.attend_blocks > 65536) return fail(SD_EINVAL, "attend_blocks must be in [0, 65536]");
+  if (c.attend_summary < 0 || c.attend_summary > 2) return fail(SD_EINVAL, "attend_summary must be 0, 1 or 2");
+  if (c.head_masks != 0 && c.head_masks != 1) return fail(SD_EINVAL, "head_masks must be 0 or 1");
   if (int64_t(c.batch) * c.n_kv_heads > sd::kMaxGroups)
     return fail(SD_EUNSUPPORTED, "batch * n_kv_heads > %d", sd::kMaxGroups);
   {

@@ -37,9 +37,16 @@ struct AttendArgs {
   int32_t* gpre_out;  // [n_groups + 1] tile prefix over groups, for the combine
   float* po;          // [attend_blocks + n_groups][G][D] partial outputs
   float* pl;          // [attend_blocks + n_groups][G] partial lse (natural log)
-  int64_t n_list;     // list row stride (entries)
-  int n_groups, Hk, Hq, G, chunk_shift, attend_summary;
+  int64_t n_list;     // list row stride (entries) = entries per row (M)
+  int n_groups, Hk, Hq, G, chunk_shift;
+  int attend_summary;  // 0 none, 1 the listed chunks' summaries, 2 every chunk's
   float scale_log2;
+  // per-head masks (variant): head h sees only its own entries plus the forced ones
+  int head_masks;
+  const uint32_t* bits;  // per-head bitmaps [B][Hq][words]
+  int64_t words;
+  int keep_first, keep_last;
+  uint64_t local_mask;
 };
 
 template <typename T, int D>
@@ -84,11 +91,27 @@ constexpr int kSegmentCost = 16;
 
 // Extent of a group in the sliced sequence: [kSegmentCost virtual tiles, raw tiles,
 // kSegmentCost virtual tiles, summary tiles]; an empty group has none.
-__device__ __forceinline__ int group_extent(int cnt, int cs, int attend_summary) {
+__device__ __forceinline__ int summary_tiles(int cnt, int attend_summary, int64_t M) {
+  return attend_summary == 2 ? int((M + kTile - 1) / kTile) : (attend_summary ? (cnt + kTile - 1) / kTile : 0);
+}
+__device__ __forceinline__ int group_extent(int cnt, int cs, int attend_summary, int64_t M) {
   if (cnt <= 0) return 0;
   const int traw = ((cnt << cs) + kTile - 1) / kTile;
-  const int tsum = attend_summary ? (cnt + kTile - 1) / kTile : 0;
+  const int tsum = summary_tiles(cnt, attend_summary, M);
   return kSegmentCost + traw + (tsum ? kSegmentCost + tsum : 0);
+}
+
+// Heads of group `gid` whose own selection holds entry e (bit j = head j of the group): every head
+// for a forced entry or a local group.
+__device__ __forceinline__ uint32_t head_mask_of(const AttendArgs& a, int gid, int e) {
+  const int b = gid / a.Hk, g = gid - b * a.Hk;
+  if (((a.local_mask >> g) & 1) || e < a.keep_first || int64_t(e) >= a.n_list - a.keep_last) return 0xFFu;
+  uint32_t m = 0;
+  for (int j = 0; j < a.G; ++j) {
+    const uint32_t w = a.bits[(int64_t(b) * a.Hq + g * a.G + j) * a.words + (e >> 5)];
+    m |= ((w >> (e & 31)) & 1u) << j;
+  }
+  return m;
 }
 
 template <typename T, int D>
@@ -97,6 +120,7 @@ struct Attender {
   const AttendArgs& a;
   const int lane, wave, n, c;
   const int32_t* lst;   // LDS list slice
+  const uint8_t* lmask; // LDS head masks of the slice's entries (per-head-mask variant)
   uint32_t* vt;         // this wave's LDS region
   // current group
   int gid, G, hs;
@@ -108,8 +132,9 @@ struct Attender {
   uint4 qf[CF::BF ? CF::QF : 1];
   float qf32[CF::BF ? 1 : CF::QF];
 
-  __device__ Attender(const AttendArgs& args, const int32_t* l, uint32_t* v)
-      : a(args), lane(threadIdx.x & 63), wave(threadIdx.x >> 6), n(lane & 15), c(lane >> 4), lst(l), vt(v) {}
+  __device__ Attender(const AttendArgs& args, const int32_t* l, const uint8_t* lm, uint32_t* v)
+      : a(args), lane(threadIdx.x & 63), wave(threadIdx.x >> 6), n(lane & 15), c(lane >> 4), lst(l), lmask(lm),
+        vt(v) {}
 
   __device__ void load_query(int group) {
     gid = group;
@@ -151,7 +176,7 @@ struct Attender {
   // summary tiles: list entry first + x. `e0` is the first list entry held in the LDS slice.
   __device__ __forceinline__ int64_t row_of(bool summary, int first, int x, int nv, int e0) const {
     x = x < nv ? x : 0;  // padded positions read a valid row; their logits are masked
-    if (summary) return lst[first + x - e0];
+    if (summary) return a.attend_summary == 2 ? first + x : lst[first + x - e0];
     const int cs = a.chunk_shift;
     const int v = first + x;
     return (int64_t(lst[(v >> cs) - e0]) << cs) | (v & ((1 << cs) - 1));
@@ -169,7 +194,8 @@ struct Attender {
     }
   }
 
-  __device__ __forceinline__ void compute(const TileRegs<T, D>& r, int nv, SoftmaxState<D>& s) {
+  __device__ __forceinline__ void compute(const TileRegs<T, D>& r, int nv, SoftmaxState<D>& s, bool summary,
+                                          int first, int e0) {
     // ---- logits: S^T[token][slot]; lane (n, c) gets tokens 4c + i of head slot n
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (CF::BF) {
@@ -196,6 +222,15 @@ struct Attender {
     float lg[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) lg[i] = 4 * c + i < nv ? sacc[i] * a.scale_log2 : kNegInf;
+    if (a.head_masks && !(summary && a.attend_summary == 2) && hs >= 0) {
+      // per-head masks: a token whose entry is outside this head's own set is not attended
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int x = 4 * c + i < nv ? 4 * c + i : 0;
+        const int ei = summary ? first + x - e0 : ((first + x) >> a.chunk_shift) - e0;
+        if (!((lmask[ei] >> hs) & 1)) lg[i] = kNegInf;
+      }
+    }
     float mt = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -276,7 +311,7 @@ struct Attender {
         const int k = k0 + j;
         const int kn = k + NS - 1;
         issue(R[(j + NS - 1) % NS], summary, clamp(kn) * kTile, nv_of(clamp(kn)), e0);
-        if (k < nt) compute(R[j], nv_of(tile(k)), s);
+        if (k < nt) compute(R[j], nv_of(tile(k)), s, summary, tile(k) * kTile, e0);
       }
     }
   }
@@ -287,6 +322,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   using CF = Cfg<T, D>;
   __shared__ int32_t gpre[kMaxGroups + 1];
   __shared__ int32_t lst[kListLds];
+  __shared__ uint8_t lmask[kListLds];
   __shared__ uint32_t wlds[kWaves * CF::kWaveWords];
   __shared__ int32_t sbuf[256];
   const int tid = threadIdx.x;
@@ -299,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
     const int g0 = tid * per;
     int sum = 0;
     for (int gg = g0; gg < min(NG, g0 + per); ++gg) {
-      sum += group_extent(a.cnt[gg], cs, a.attend_summary);
+      sum += group_extent(a.cnt[gg], cs, a.attend_summary, a.n_list);
     }
     sbuf[tid] = sum;
     __syncthreads();
@@ -312,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
     int run = sbuf[tid] - sum;
     for (int gg = g0; gg < min(NG, g0 + per); ++gg) {
       gpre[gg] = run;
-      run += group_extent(a.cnt[gg], cs, a.attend_summary);
+      run += group_extent(a.cnt[gg], cs, a.attend_summary, a.n_list);
     }
     if (tid == 255) gpre[NG] = sbuf[255];
     __syncthreads();
@@ -334,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
 
   const int wave = tid >> 6;
   uint32_t* vt = wlds + wave * CF::kWaveWords;
-  Attender<T, D> at(a, lst, vt);
+  Attender<T, D> at(a, lst, lmask, vt);
   const int lane = tid & 63, n = lane & 15, c = lane >> 4;
 
   for (int gi = lo; gi < NG && gpre[gi] < b1; ++gi) {
@@ -365,25 +401,38 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
         const int e0 = (u0 * kTile) >> cs;
         const int e1 = min(cnt, ((u1 * kTile - 1) >> cs) + 1);
         __syncthreads();
-        for (int i = tid; i < e1 - e0; i += 256) lst[i] = glist[e0 + i];
+        for (int i = tid; i < e1 - e0; i += 256) {
+          const int e = glist[e0 + i];
+          lst[i] = e;
+          if (a.head_masks) lmask[i] = uint8_t(head_mask_of(a, gi, e));
+        }
         __syncthreads();
         at.run(false, u0, u1, ntok, e0, st);
       }
     }
-    // summary tiles [q0, q1) (at [2 kSegmentCost + traw, extent) of the group's extent)
+    // summary tiles [q0, q1) (at [2 kSegmentCost + traw, extent) of the group's extent): the listed
+    // chunks' summary rows, or (attend_summary 2) every chunk's, addressed directly
     if (a.attend_summary) {
+      const int tsum = summary_tiles(cnt, a.attend_summary, a.n_list);
+      const int nsum = a.attend_summary == 2 ? int(a.n_list) : cnt;
       const int base = 2 * kSegmentCost + traw;
-      const int q0 = max(s0, base) - base, q1 = s1 - base;
+      const int q0 = max(s0, base) - base, q1 = min(s1 - base, tsum);
       at.set_kind(true);
-      const int tiles_per_slice = kListLds / kTile;
+      const int tiles_per_slice = a.attend_summary == 2 ? (1 << 30) : kListLds / kTile;
       for (int u0 = q0; u0 < q1; u0 += tiles_per_slice) {
         const int u1 = min(q1, u0 + tiles_per_slice);
         const int e0 = u0 * kTile;
-        const int e1 = min(cnt, u1 * kTile);
-        __syncthreads();
-        for (int i = tid; i < e1 - e0; i += 256) lst[i] = glist[e0 + i];
-        __syncthreads();
-        at.run(true, u0, u1, cnt, e0, st);
+        if (a.attend_summary == 1) {
+          const int e1 = min(cnt, u1 * kTile);
+          __syncthreads();
+          for (int i = tid; i < e1 - e0; i += 256) {
+            const int e = glist[e0 + i];
+            lst[i] = e;
+            if (a.head_masks) lmask[i] = uint8_t(head_mask_of(a, gi, e));
+          }
+          __syncthreads();
+        }
+        at.run(true, u0, u1, nsum, e0, st);
       }
     }
 
@@ -542,6 +591,12 @@ int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream) {
   a.chunk_shift = cs;
   a.attend_summary = c.attend_summary;
   a.scale_log2 = c.softmax_scale * 1.4426950408889634f;
+  a.head_masks = c.head_masks;
+  a.bits = at<uint32_t>(ws, p.o_bits);
+  a.words = p.words;
+  a.keep_first = c.keep_first;
+  a.keep_last = c.keep_last;
+  a.local_mask = p.local_mask;
   const dim3 grid(p.attend_blocks);
   if (c.kv_dtype == SD_BF16) {
     if (c.head_dim == 128)

@@ -17,8 +17,8 @@ _MODES = {"topk": N.SD_TOPK, "topp": N.SD_TOPP, "hier": N.SD_HIER_TOPK}
 
 def make_config(*, batch, kv_batch, n_q_heads, n_kv_heads, head_dim, n_ctx, chunk_size, dtype, mode,
                 route="summary", route_dim=0, top_k=0, top_k_seg=0, seg_size=0, top_p=1.0, select_scale=1.0,
-                softmax_scale=1.0, keep_first=0, keep_last=0, sink=0, window=0, attend_summary=True,
-                attend_blocks=0, head_mode=None):
+                softmax_scale=1.0, keep_first=0, keep_last=0, sink=0, window=0, attend_summary=1,
+                attend_blocks=0, head_masks=False, head_mode=None):
     """An sd_config plus the host array it points to (keep both alive)."""
     cfg = N.sd_config()
     cfg.batch, cfg.kv_batch = batch, kv_batch
@@ -31,8 +31,9 @@ def make_config(*, batch, kv_batch, n_q_heads, n_kv_heads, head_dim, n_ctx, chun
     cfg.top_k, cfg.top_k_seg = top_k, top_k_seg
     cfg.top_p, cfg.select_scale, cfg.softmax_scale = top_p, select_scale, softmax_scale
     cfg.keep_first, cfg.keep_last, cfg.sink, cfg.window = keep_first, keep_last, sink, window
-    cfg.attend_summary = int(bool(attend_summary))
+    cfg.attend_summary = int(attend_summary)  # 0 none, 1 selected chunks', 2 every chunk's
     cfg.attend_blocks = attend_blocks
+    cfg.head_masks = int(bool(head_masks))
     hm = None
     if head_mode is not None:
         hm = (ctypes.c_int8 * len(head_mode))(*[int(x) for x in head_mode])

@@ -35,7 +35,7 @@ class sd_config(ctypes.Structure):
         ("top_p", ctypes.c_double), ("select_scale", ctypes.c_double), ("softmax_scale", ctypes.c_float),
         ("keep_first", ctypes.c_int32), ("keep_last", ctypes.c_int32),
         ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
-        ("attend_summary", ctypes.c_int32), ("attend_blocks", ctypes.c_int32),
+        ("attend_summary", ctypes.c_int32), ("attend_blocks", ctypes.c_int32), ("head_masks", ctypes.c_int32),
         ("head_mode", ctypes.POINTER(ctypes.c_int8)),
     ]
 

@@ -45,6 +45,8 @@ class Workload:
     sink: int = 0
     window: int = 0
     attend_summary: bool = True
+    all_summaries: bool = False  # variant: every chunk's summary K/V joins the context
+    head_masks: bool = False     # variant: each head attends to its own selection + forced chunks
     plant: str = ""            # synthetic structure recipe, see synth.gen
     plants_per_head: int = 0
     zipf_s: float = 0.0
@@ -118,7 +120,12 @@ C1S = replace(C1, name="c1s", seed=11)
 
 SMALL = {w.name: w for w in (C1S, C2S, C3S, C4S, C5S)}
 
-ALL = {**FULL, **SMALL}
+# Context variants of the 128K workload (the same selection; what the heads attend to differs).
+C3_HEADMASK = replace(C3, name="c3_topp_llama31_8b_128k_headmask", head_masks=True)
+C3_ALLSUM = replace(C3, name="c3_topp_llama31_8b_128k_allsum", all_summaries=True)
+VARIANTS = {w.name: w for w in (C3_HEADMASK, C3_ALLSUM)}
+
+ALL = {**FULL, **SMALL, **VARIANTS}
 
 # The workload the throughput metric is quoted on: 128K context, top-p decode.
 BENCH = C3
@@ -138,5 +145,6 @@ def library_params(w: Workload) -> dict:
         top_k=w.top_k, top_k_seg=w.top_k_seg, seg_size=w.seg_size, top_p=w.top_p,
         select_scale=w.select_scale, softmax_scale=w.softmax_scale,
         keep_first=w.keep_first, keep_last=w.keep_last, sink=w.sink, window=w.window,
-        attend_summary=w.attend_summary and w.mode != PROXY_TOPP, attend_blocks=w.attend_blocks,
+        attend_summary=(2 if w.all_summaries else 1) if (w.attend_summary and w.mode != PROXY_TOPP) else 0,
+        head_masks=w.head_masks, attend_blocks=w.attend_blocks,
         head_mode=[1 if g in w.local_kv_heads else 0 for g in range(w.n_kv_heads)])

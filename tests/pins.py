@@ -252,7 +252,8 @@ def _tiny_workload(mode, **kw):
     base = dict(name="pin", batch=2, kv_batch=2, n_q_heads=6, n_kv_heads=2, head_dim=16, n_ctx=96,
                 chunk_size=8, mode=mode, top_k=3, top_k_seg=2, seg_size=4, top_p=0.9,
                 select_scale=0.25, softmax_scale=0.25, keep_first=0, keep_last=0, route_dim=4,
-                local_kv_heads=(), sink=0, window=0, attend_summary=True)
+                local_kv_heads=(), sink=0, window=0, attend_summary=True, all_summaries=False,
+                head_masks=False)
     base.update(kw)
     return SimpleNamespace(**base)
 
@@ -362,7 +363,56 @@ def pin_step_selection(ref, seed=8):
             assert S.tolist() == _brute_topk(s, w.top_k), (b, h)
 
 
+def pin_variants(ref, seed=9):
+    """The two context variants against dense attention with masks built here from their
+    definitions (torch SDPA, fp64): with per-head masks head h sees the raw and summary rows of its
+    own set plus the forced chunks (local groups: the sink + window); with all summaries every head
+    sees the union's raw rows plus every chunk's summary. With one head per group and no forced
+    chunks the per-head masks change nothing."""
+    rng = np.random.default_rng(seed)
+    cases = [
+        _tiny_workload("topk", keep_first=1, keep_last=2, head_masks=True, all_summaries=False),
+        _tiny_workload("topp", top_p=0.7, head_masks=True, all_summaries=False),
+        _tiny_workload("hier", head_masks=True, all_summaries=False),
+        _tiny_workload("proxy", chunk_size=1, top_p=0.6, attend_summary=False, head_masks=True,
+                       all_summaries=False, local_kv_heads=(1,), sink=3, window=9),
+        _tiny_workload("topp", top_p=0.7, keep_last=1, head_masks=False, all_summaries=True),
+        _tiny_workload("topk", keep_first=2, head_masks=True, all_summaries=True),
+    ]
+    for w in cases:
+        src = _Src(w, rng)
+        res = ref.decode_step(w, src)
+        G = w.n_q_heads // w.n_kv_heads
+        M = w.n_ctx // w.chunk_size
+        forced = [e for e in range(M) if e < w.keep_first or e >= M - w.keep_last]
+        summ = w.attend_summary and w.mode != "proxy"
+        for (b, g), r in res["sel"].items():
+            Kc, Vc = src.K[b, g], src.V[b, g]
+            if summ:
+                Kc = np.concatenate([Kc, src.Kg[b, g]])
+                Vc = np.concatenate([Vc, src.Vg[b, g]])
+            for j in range(G):
+                h = g * G + j
+                if g in w.local_kv_heads:
+                    chunks = [e for e in range(M) if e < w.sink or e >= M - w.window]
+                elif w.head_masks:
+                    chunks = sorted(set(r["heads"][h].tolist()) | set(forced))
+                else:
+                    chunks = r["union"].tolist()
+                mask = [c * w.chunk_size + t for c in chunks for t in range(w.chunk_size)]
+                if summ:
+                    mask += [w.n_ctx + e for e in (range(M) if w.all_summaries else chunks)]
+                o2, l2 = _sdpa(src.q[b, h][None], Kc, Vc, w.softmax_scale, mask=np.array(mask))
+                assert np.allclose(res["out"][b, h], o2[0], rtol=1e-11, atol=1e-11), (w.mode, b, h)
+                assert np.allclose(res["lse"][b, h], l2[0], rtol=1e-11, atol=1e-11), (w.mode, b, h)
+    w1 = _tiny_workload("topp", n_q_heads=2, n_kv_heads=2, top_p=0.8, head_masks=True, all_summaries=False)
+    w0 = _tiny_workload("topp", n_q_heads=2, n_kv_heads=2, top_p=0.8, head_masks=False, all_summaries=False)
+    src = _Src(w1, np.random.default_rng(seed + 1))
+    a, c = ref.decode_step(w1, src), ref.decode_step(w0, src)
+    assert np.array_equal(a["out"], c["out"]) and np.array_equal(a["lse"], c["lse"]), "G = 1 masks"
+
+
 ALL_PINS = [pin_golden_scores, pin_golden_proxy, pin_golden_topk, pin_golden_topp, pin_golden_two_level,
             pin_golden_union, pin_golden_attention, pin_scores_exact, pin_bruteforce, pin_topp_minimal,
             pin_reductions, pin_union, pin_masked_dense, pin_dense_limits, pin_step_masked,
-            pin_step_selection]
+            pin_step_selection, pin_variants]

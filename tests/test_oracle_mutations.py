@@ -31,12 +31,16 @@ MUTATIONS = {
     "attention_values_are_keys": ("o = (e.T @ Vc) / L[:, None]", "o = (e.T @ Kc) / L[:, None]"),
     "attention_lse_drops_max": ("return o, mx + np.log(L)\n\n\ndef lse_combine", "return o, np.log(L)\n\n\ndef lse_combine"),
     "combine_unweighted": ("o = (w[..., None] * o_parts).sum(axis=0) / L[..., None]", "o = o_parts.mean(axis=0)"),
-    "hybrid_drops_summary": ("Kc = np.concatenate([Kc, src.Kg[bk, g][U]], axis=0)", "Kc = Kc"),
+    "hybrid_drops_summary": ("Kc = np.concatenate([Kc, src.Kg[bk, g][srows]], axis=0)", "Kc = Kc"),
     "hybrid_wrong_rows": ("(U[:, None] * chunk_size + np.arange(chunk_size)[None, :])",
                           "(U[:, None] + np.arange(chunk_size)[None, :])"),
     "forced_not_added": ("U = group_union([U, edge_entries(n_ent, w.keep_first, w.keep_last)])", "U = U"),
     "union_first_head_only": ("per_head.append(sel)", "per_head.append(sel) if not per_head else None"),
-    "wrong_kv_group": ("qh = src.q[b, g * G:(g + 1) * G]\n    return attend", "qh = src.q[b, (g * G + 1) % w.n_q_heads:(g * G + 1) % w.n_q_heads + G]\n    return attend"),
+    "wrong_kv_group": ("qh = src.q[b, g * G:(g + 1) * G]\n", "qh = src.q[b, (g * G + 1) % w.n_q_heads:(g * G + 1) % w.n_q_heads + G]\n"),
+    "head_mask_drops_forced": ("S = group_union([heads[g * G + j], forced])", "S = heads[g * G + j]"),
+    "head_mask_wrong_head": ("S = group_union([heads[g * G + j], forced])", "S = group_union([heads[g * G + (j + 1) % G], forced])"),
+    "head_mask_ignored": ("masked = getattr(w, \"head_masks\", False) and", "masked = False and"),
+    "all_summaries_only_selected": ("srows = np.arange(n_ent) if all_sum else", "srows = np.asarray(S, dtype=np.int64) if all_sum else"),
 }
 
 
