@@ -62,7 +62,7 @@ typedef enum {
 } sd_status;
 
 enum { SD_F32 = 0, SD_BF16 = 1 };                       /* q / K / V / summary dtype */
-enum { SD_TOPK = 0, SD_TOPP = 1, SD_HIER_TOPK = 2 };    /* selection rule */
+enum { SD_TOPK = 0, SD_TOPP = 1, SD_HIER_TOPK = 2, SD_COVERAGE = 3 };  /* selection rule */
 enum { SD_ROUTE_SUMMARY = 0, SD_ROUTE_PROXY = 1 };      /* what is scored */
 
 typedef struct {
@@ -77,11 +77,17 @@ typedef struct {
   int32_t route;          /* SD_ROUTE_SUMMARY or SD_ROUTE_PROXY (needs C == 1) */
   int32_t route_dim;      /* proxy rank r (SD_ROUTE_PROXY): 16 */
   int32_t kv_dtype;       /* SD_F32 or SD_BF16 */
-  int32_t mode;           /* SD_TOPK, SD_TOPP or SD_HIER_TOPK */
+  int32_t mode;           /* SD_TOPK, SD_TOPP, SD_HIER_TOPK or SD_COVERAGE */
   int32_t top_k;          /* SD_TOPK / SD_HIER_TOPK: chunks kept per head, >= 1 */
   int32_t top_k_seg;      /* SD_HIER_TOPK: segments kept per head, >= 1 */
   double top_p;           /* SD_TOPP: mass to reach, in (0, 1]; 1 keeps all */
-  double select_scale;    /* SD_TOPP: logit = select_scale * score, > 0 */
+  double select_scale;    /* SD_TOPP / SD_COVERAGE: logit = select_scale * score, > 0 */
+  double tau;             /* SD_COVERAGE ([TSA] dynamic token coverage), in [0, 1): per
+                             sequence, importance = the scored heads' softmax probabilities
+                             summed per chunk; the ascending tail is cut until the cut mass
+                             exceeds tau x total; budget = max(1, chunks - cut), and every
+                             head keeps its own top-budget chunks. Summary routing, at most
+                             2048 chunks per row. */
   float softmax_scale;    /* attention logit scale, > 0 (1/sqrt(d)) */
   int32_t keep_first;     /* chunks [0, keep_first) always in the union */
   int32_t keep_last;      /* chunks [M - keep_last, M) always in the union */

@@ -18,6 +18,10 @@ Sources (cited by page title and section):
   section "1. Key Terms & Definitions": retrieval heads keep the full KV cache; a
   16-dim low-dimensional projection scores token importance; dynamic top-p picks
   a per-query variable budget that secures attention mass instead of a fixed k.
+* [TSA] Technical summary of "Token Sparse Attention", section 2 "Dynamic Token
+  Coverage": token importance is the column sum of a proxy attention map; the
+  budget comes from cutting the ascending-importance tail until the cut mass
+  exceeds a coverage threshold tau; each head then keeps its own top-k.
 * [HiLS] Review of "Hierarchical Sparse Attention Done Right", section 1: a
   landmark token's key summarises its chunk; GQA extended to group-wise chunk
   selection.
@@ -37,6 +41,13 @@ Readings where the pages are silent (each is a fixed choice of this oracle):
   group union.
 * Proxy scoring: the same d x r projection maps the query and the keys;
   ``q_p = q P`` in fp64, score ``q_p . k_p``.
+* Coverage budget (decode form of [TSA]): the proxy attention map is the
+  current query's per-head softmax over the chunk scores (``select_scale``);
+  importance = the sum of the sequence's scored heads' probabilities; the
+  ascending order breaks equal importance by the higher index first; the cut
+  removes the shortest ascending prefix whose mass exceeds ``tau`` times the
+  total; the budget ``k = max(1, entries - removed)`` is shared by every head of
+  the sequence, each of which then keeps its own top-k.
 * Variant "all summaries": the summary K/V of every chunk join the context,
   not only the selected chunks' ([SSA] 기술 상세 has the query interact with
   all summaries first); they are attended by every head of the group.
@@ -54,7 +65,7 @@ import math
 
 import numpy as np
 
-TOPK, TOPP, HIER, PROXY_TOPP = "topk", "topp", "hier", "proxy"
+TOPK, TOPP, HIER, PROXY_TOPP, COVERAGE = "topk", "topp", "hier", "proxy", "coverage"
 
 
 # --------------------------------------------------------------------------- scores
@@ -121,6 +132,34 @@ def select_top_p(s: np.ndarray, p: float, scale: float):
     above = abs(c[n_sel - 1] - target)
     below = abs(c[n_sel - 2] - target) if n_sel >= 2 else abs(target)
     return np.sort(o[:n_sel]), min(above, below) / Z
+
+
+def coverage_importance(score_rows, scale: float) -> np.ndarray:
+    """[TSA] dynamic token coverage, scoring: every head's attention distribution over the
+    entries (softmax of ``scale * s``), summed over the heads in order."""
+    imp = np.zeros(score_rows[0].shape[0], dtype=np.float64)
+    for s in score_rows:
+        ell = scale * s
+        mass = np.exp(ell - ell.max())
+        imp = imp + mass / math.fsum(mass.tolist())
+    return imp
+
+
+def coverage_budget(imp: np.ndarray, tau: float):
+    """[TSA] dynamic token coverage, budget: entries in ascending importance (equal importance:
+    higher index first; the cumulative masses, hence the budget, do not depend on how ties are
+    ordered); cut the tail until the cut mass exceeds ``tau`` times the total; the budget is what
+    remains, at least 1. Returns (budget, margin of the cut decision / total)."""
+    n = imp.shape[0]
+    order = np.lexsort((-np.arange(n), imp))
+    c = np.cumsum(imp[order])
+    T = math.fsum(imp.tolist())
+    thr = tau * T
+    hit = np.nonzero(c > thr)[0]
+    removed = int(hit[0]) + 1 if hit.size else n
+    above = abs(c[removed - 1] - thr)
+    below = abs(c[removed - 2] - thr) if removed >= 2 else abs(thr)
+    return max(1, n - removed), min(above, below) / T
 
 
 def candidates(segments: np.ndarray, seg_size: int) -> np.ndarray:
@@ -190,6 +229,15 @@ def hybrid_rows(U: np.ndarray, chunk_size: int) -> np.ndarray:
 
 
 # ------------------------------------------------------------------------ the step
+def sequence_budget(w, src, b: int):
+    """Coverage budget of sequence b from all its scored heads' chunk scores."""
+    G = w.n_q_heads // w.n_kv_heads
+    bk = b if w.kv_batch > 1 else 0
+    rows = [chunk_scores(src.q[b, g * G + j], src.Kg[bk, g])
+            for g in range(w.n_kv_heads) if g not in tuple(w.local_kv_heads) for j in range(G)]
+    return coverage_budget(coverage_importance(rows, w.select_scale), w.tau)
+
+
 def select_group(w, src, b: int, g: int) -> dict:
     """Per-head selections and the group union for sequence b, KV group g."""
     G = w.n_q_heads // w.n_kv_heads
@@ -216,6 +264,12 @@ def select_group(w, src, b: int, g: int) -> dict:
                 s, lambda c: chunk_scores(q, src.Kg[bk, g][c]), w.top_k_seg, w.top_k, w.seg_size)
             res["segments"][h] = segs
             res["cand"][h] = (cand, s2)
+        elif w.mode == COVERAGE:
+            s = chunk_scores(q, src.Kg[bk, g])
+            k_b, mg = sequence_budget(w, src, b)
+            sel = select_top_k(s, k_b)
+            res["margin"] = min(res["margin"], mg)
+            res["budget"] = k_b
         elif w.mode == PROXY_TOPP:
             qp = proxy_query(q, src.P[g])
             s = proxy_scores(qp, src.Kp[bk, g])

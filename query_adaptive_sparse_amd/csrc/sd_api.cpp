@@ -48,7 +48,8 @@ sd_status check_cfg(const sd_config& c) {
   if (c.chunk_size < 1 || c.n_ctx % c.chunk_size)
     return fail(SD_EINVAL, "chunk_size %d must be >= 1 and divide n_ctx %lld", c.chunk_size, (long long)c.n_ctx);
   if (c.route != SD_ROUTE_SUMMARY && c.route != SD_ROUTE_PROXY) return fail(SD_EINVAL, "route %d unknown", c.route);
-  if (c.mode != SD_TOPK && c.mode != SD_TOPP && c.mode != SD_HIER_TOPK) return fail(SD_EINVAL, "mode %d unknown", c.mode);
+  if (c.mode != SD_TOPK && c.mode != SD_TOPP && c.mode != SD_HIER_TOPK && c.mode != SD_COVERAGE)
+    return fail(SD_EINVAL, "mode %d unknown", c.mode);
   if (c.route == SD_ROUTE_PROXY) {
     if (c.chunk_size != 1) return fail(SD_EINVAL, "proxy routing scores tokens: chunk_size must be 1");
     if (c.route_dim != 16) return fail(SD_EUNSUPPORTED, "route_dim must be 16 (got %d)", c.route_dim);
@@ -57,6 +58,14 @@ sd_status check_cfg(const sd_config& c) {
   }
   if (c.mode == SD_TOPK || c.mode == SD_HIER_TOPK) {
     if (c.top_k < 1) return fail(SD_EINVAL, "top_k must be >= 1 (got %d)", c.top_k);
+  }
+  if (c.mode == SD_COVERAGE) {
+    if (!(c.tau >= 0.0) || !(c.tau < 1.0)) return fail(SD_EINVAL, "tau must be in [0, 1) (got %g)", c.tau);
+    if (!(c.select_scale > 0.0) || !std::isfinite(c.select_scale))
+      return fail(SD_EINVAL, "select_scale must be finite and > 0 (got %g)", c.select_scale);
+    if (c.route != SD_ROUTE_SUMMARY) return fail(SD_EUNSUPPORTED, "the coverage budget routes on summary keys");
+    if (c.n_ctx / c.chunk_size > sd::kSmallRowMax)
+      return fail(SD_EUNSUPPORTED, "the coverage budget handles at most %d chunks per row", sd::kSmallRowMax);
   }
   if (c.mode == SD_TOPP) {
     if (!(c.top_p > 0.0) || !(c.top_p <= 1.0)) return fail(SD_EINVAL, "top_p must be in (0, 1] (got %g)", c.top_p);
@@ -111,6 +120,7 @@ void plan_workspace(sd::Plan& p) {
     return o;
   };
   p.o_status = take(64);
+  p.o_budget = take(size_t(B) * 4);  // coverage budget per sequence
   p.o_arrive = take(size_t(B * Hk) * 4);
   p.o_qp = take(c.route == SD_ROUTE_PROXY ? size_t(B * Hq * 16) * 8 : 0);
   p.o_s0 = take(size_t(B * Hq * p.len0) * 8);

@@ -119,6 +119,7 @@ struct GroupSelArgs {
   int Hq, Hk, G;
   uint64_t local_mask;
   int topp, k;
+  const int32_t* kbudget;  // per-sequence top-k (coverage budget), or NULL: k
   double p, scale;
   int kind;
   const int32_t* cand_in;  // kind 2: [B][Hq][len] chunk id of each candidate
@@ -203,7 +204,8 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
   smax = fmax(fmax(wred[0], wred[1]), fmax(wred[2], wred[3]));
   smin = fmin(fmin(wred2[0], wred2[1]), fmin(wred2[2], wred2[3]));
   __syncthreads();
-  const bool all = a.topp ? (a.p >= 1.0) : (a.k >= L);
+  const int kk = a.kbudget ? a.kbudget[b] : a.k;
+  const bool all = a.topp ? (a.p >= 1.0) : (kk >= L);
   const double ellmax = a.scale * smax;
   const double range = smax - smin;
   const double binscale = range > 0.0 ? double(kNBin) / range : 0.0;
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
       z += wt[k];
     }
   }
-  double target = double(a.k);
+  double target = double(kk);
   if (a.topp) {
     z = wave_sum_dpp(z);
     if (lane == 0) wred[wv] = z;
@@ -1079,6 +1081,102 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Coverage budget (dynamic token coverage, decode form): per sequence, every scored head's softmax
+// of select_scale * s over its row, summed per entry (the column sums of the proxy attention map);
+// the entries in ascending importance; the shortest ascending prefix whose mass exceeds tau x the
+// total is cut; budget = max(1, entries - cut), used by every head of the sequence as its top-k.
+// One 1024-thread workgroup per sequence, rows of at most kSmallRowMax entries.
+// ---------------------------------------------------------------------------------------------
+struct CoverageArgs {
+  const double* s;
+  int64_t len;
+  int Hq, G;
+  uint64_t local_mask;
+  double scale, tau;
+  int32_t* budget;  // [B]
+};
+
+constexpr int kCoverThreads = 1024;
+
+__global__ __launch_bounds__(kCoverThreads) void k_coverage(CoverageArgs a) {
+  constexpr int NT = kCoverThreads, NW = NT / 64;
+  constexpr int PT = kSmallRowMax / NT;  // entries per thread
+  __shared__ double hmax[kMaxKvHeads * kMaxGroup], hz[kMaxKvHeads * kMaxGroup];
+  __shared__ uint64_t keys[kSmallRowMax];
+  __shared__ uint16_t idx[kSmallRowMax];
+  __shared__ double wtot[NW];
+  __shared__ int hit;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int L = int(a.len);
+  const double* sb = a.s + int64_t(b) * a.Hq * a.len;
+  // ---- per head: max and Z of the masses (a wave per head; local heads score nothing)
+  for (int h = wv; h < a.Hq; h += NW) {
+    if ((a.local_mask >> (h / a.G)) & 1) {
+      if (lane == 0) hz[h] = 0.0;
+      continue;
+    }
+    const double* row = sb + int64_t(h) * a.len;
+    double mx = kNegInfD;
+    for (int i = lane; i < L; i += 64) mx = fmax(mx, row[i]);
+    mx = wave_max_dpp(mx);
+    double z = 0.0;
+    for (int i = lane; i < L; i += 64) z += exp(a.scale * row[i] - a.scale * mx);
+    z = wave_sum_dpp(z);
+    if (lane == 0) {
+      hmax[h] = mx;
+      hz[h] = z;
+    }
+  }
+  __syncthreads();
+  // ---- importance per entry (heads summed in order), sorted ascending (keys complemented)
+  int Lp = 2;
+  while (Lp < L) Lp <<= 1;
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    const int m = tid + NT * k;
+    if (m < L) {
+      double imp = 0.0;
+      for (int h = 0; h < a.Hq; ++h)
+        if (hz[h] > 0.0) imp += exp(a.scale * sb[int64_t(h) * a.len + m] - a.scale * hmax[h]) / hz[h];
+      keys[m] = ~dkey(imp);
+      idx[m] = uint16_t(m);
+    } else if (m < Lp) {
+      keys[m] = 0ull;  // padding sorts last
+      idx[m] = 0xFFFF;
+    }
+  }
+  __syncthreads();
+  bitonic_desc<uint16_t, NT>(keys, idx, Lp);
+  // ---- the cut: first sorted position where the running mass exceeds tau x total
+  double w[PT];
+  double local = 0.0;
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    const int i = PT * tid + k;
+    w[k] = i < L ? dkey_inv(~keys[i]) : 0.0;
+    local += w[k];
+  }
+  if (tid == 0) hit = 0x7FFFFFFF;
+  double total;
+  const double incl = block_scan<NT>(local, wtot, &total);
+  const double thr = a.tau * total;
+  double c = incl - local;
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    c += w[k];
+    if (PT * tid + k < L && c > thr) {
+      atomicMin(&hit, PT * tid + k);
+      break;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int removed = hit == 0x7FFFFFFF ? L : hit + 1;
+    a.budget[b] = L - removed > 1 ? L - removed : 1;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // GQA union and compaction: per (sequence, KV group) the OR of the group's per-head bitmaps plus
 // forced sink / recent entries (scored groups) or the sink + window (local groups), then the set
 // bits in ascending order. Ranges of 1024 words per workgroup; counts, then writes.
@@ -1257,6 +1355,7 @@ GroupSelArgs group_args(const Plan& p, char* ws, int level) {
   a.local_mask = p.local_mask;
   a.topp = c.mode == SD_TOPP;
   a.k = hier && level == 0 ? c.top_k_seg : c.top_k;
+  a.kbudget = c.mode == SD_COVERAGE ? at<int32_t>(ws, p.o_budget) : nullptr;
   a.p = c.top_p;
   a.scale = c.mode == SD_TOPP ? c.select_scale : 1.0;
   a.kind = hier ? (level == 0 ? 1 : 2) : 0;
@@ -1283,6 +1382,18 @@ int launch_select(const Plan& p, int level, char* ws, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const sd_config& c = p.cfg;
   const int B = c.batch, Hq = c.n_q_heads;
+  if (c.mode == SD_COVERAGE) {
+    CoverageArgs ca;
+    ca.s = at<double>(ws, p.o_s0);
+    ca.len = p.len0;
+    ca.Hq = Hq;
+    ca.G = p.G;
+    ca.local_mask = p.local_mask;
+    ca.scale = c.select_scale;
+    ca.tau = c.tau;
+    ca.budget = at<int32_t>(ws, p.o_budget);
+    hipLaunchKernelGGL(k_coverage, dim3(B), dim3(kCoverThreads), 0, st, ca);
+  }
   if (c.mode == SD_HIER_TOPK || !p.long0) {
     // rows of at most kSmallRowMax entries: selection, union and compaction in one kernel
     hipLaunchKernelGGL(k_select_head, dim3(Hq, B), dim3(kSelT), 0, st, group_args(p, ws, level));

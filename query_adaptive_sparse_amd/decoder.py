@@ -12,11 +12,11 @@ import torch
 from . import native as N
 
 _DTYPES = {torch.float32: N.SD_F32, torch.bfloat16: N.SD_BF16}
-_MODES = {"topk": N.SD_TOPK, "topp": N.SD_TOPP, "hier": N.SD_HIER_TOPK}
+_MODES = {"topk": N.SD_TOPK, "topp": N.SD_TOPP, "hier": N.SD_HIER_TOPK, "coverage": N.SD_COVERAGE}
 
 
 def make_config(*, batch, kv_batch, n_q_heads, n_kv_heads, head_dim, n_ctx, chunk_size, dtype, mode,
-                route="summary", route_dim=0, top_k=0, top_k_seg=0, seg_size=0, top_p=1.0, select_scale=1.0,
+                route="summary", route_dim=0, top_k=0, top_k_seg=0, seg_size=0, top_p=1.0, select_scale=1.0, tau=0.0,
                 softmax_scale=1.0, keep_first=0, keep_last=0, sink=0, window=0, attend_summary=1,
                 attend_blocks=0, head_masks=False, head_mode=None):
     """An sd_config plus the host array it points to (keep both alive)."""
@@ -29,7 +29,7 @@ def make_config(*, batch, kv_batch, n_q_heads, n_kv_heads, head_dim, n_ctx, chun
     cfg.kv_dtype = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else {"f32": N.SD_F32, "bf16": N.SD_BF16}[dtype]
     cfg.mode = _MODES[mode]
     cfg.top_k, cfg.top_k_seg = top_k, top_k_seg
-    cfg.top_p, cfg.select_scale, cfg.softmax_scale = top_p, select_scale, softmax_scale
+    cfg.top_p, cfg.select_scale, cfg.tau, cfg.softmax_scale = top_p, select_scale, tau, softmax_scale
     cfg.keep_first, cfg.keep_last, cfg.sink, cfg.window = keep_first, keep_last, sink, window
     cfg.attend_summary = int(attend_summary)  # 0 none, 1 selected chunks', 2 every chunk's
     cfg.attend_blocks = attend_blocks

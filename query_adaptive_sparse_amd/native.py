@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_HERE, "_lib", "libsparse_decode.so")
 
 SD_OK, SD_EINVAL, SD_EUNSUPPORTED, SD_EWORKSPACE, SD_EHIP = range(5)
 SD_F32, SD_BF16 = 0, 1
-SD_TOPK, SD_TOPP, SD_HIER_TOPK = 0, 1, 2
+SD_TOPK, SD_TOPP, SD_HIER_TOPK, SD_COVERAGE = 0, 1, 2, 3
 SD_ROUTE_SUMMARY, SD_ROUTE_PROXY = 0, 1
 
 STATUS_NAMES = {0: "SD_OK", 1: "SD_EINVAL", 2: "SD_EUNSUPPORTED", 3: "SD_EWORKSPACE", 4: "SD_EHIP"}
@@ -32,7 +32,8 @@ class sd_config(ctypes.Structure):
         ("n_ctx", ctypes.c_int64), ("chunk_size", ctypes.c_int32), ("seg_size", ctypes.c_int32),
         ("route", ctypes.c_int32), ("route_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
         ("mode", ctypes.c_int32), ("top_k", ctypes.c_int32), ("top_k_seg", ctypes.c_int32),
-        ("top_p", ctypes.c_double), ("select_scale", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+        ("top_p", ctypes.c_double), ("select_scale", ctypes.c_double), ("tau", ctypes.c_double),
+        ("softmax_scale", ctypes.c_float),
         ("keep_first", ctypes.c_int32), ("keep_last", ctypes.c_int32),
         ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
         ("attend_summary", ctypes.c_int32), ("attend_blocks", ctypes.c_int32), ("head_masks", ctypes.c_int32),

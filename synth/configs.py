@@ -18,6 +18,7 @@ TOPK = "topk"          # per-head top-k over chunk summary scores
 TOPP = "topp"          # per-head dynamic top-p over the softmax of chunk scores
 HIER = "hier"          # two-level: top-k segments (meta summaries) -> top-k chunks
 PROXY_TOPP = "proxy"   # per-token top-p on rank-r proxy-key scores; local heads
+COVERAGE = "coverage"  # per-sequence coverage budget (tau), then per-head top-k
 
 
 @dataclass(frozen=True)
@@ -36,6 +37,7 @@ class Workload:
     top_k_seg: int = 0
     seg_size: int = 0          # summaries per meta-summary (HIER)
     top_p: float = 1.0
+    tau: float = 0.0           # coverage threshold (COVERAGE): tail mass cut from the importance
     select_scale: float = 1.0  # logit scale of the top-p softmax
     softmax_scale: float = 1.0
     keep_first: int = 0        # forced leading chunks (attention sink)
@@ -122,8 +124,11 @@ SMALL = {w.name: w for w in (C1S, C2S, C3S, C4S, C5S)}
 
 # Context variants of the 128K workload (the same selection; what the heads attend to differs).
 C3_HEADMASK = replace(C3, name="c3_topp_llama31_8b_128k_headmask", head_masks=True)
+# The coverage budget rule on the 128K workload: cut 20% of the head-summed importance mass.
+C3_COVERAGE = replace(C3, name="c3_coverage_llama31_8b_128k", mode=COVERAGE, tau=0.2, top_p=1.0)
 C3_ALLSUM = replace(C3, name="c3_topp_llama31_8b_128k_allsum", all_summaries=True)
-VARIANTS = {w.name: w for w in (C3_HEADMASK, C3_ALLSUM)}
+C3S_COVERAGE = replace(C3_COVERAGE, name="c3s_coverage", batch=2, kv_batch=2, n_ctx=16384, seed=16)
+VARIANTS = {w.name: w for w in (C3_HEADMASK, C3_ALLSUM, C3_COVERAGE, C3S_COVERAGE)}
 
 ALL = {**FULL, **SMALL, **VARIANTS}
 
@@ -137,12 +142,12 @@ def get(name: str) -> Workload:
 
 def library_params(w: Workload) -> dict:
     """Keyword arguments of query_adaptive_sparse_amd.SparseDecoder for workload ``w``."""
-    mode = {TOPK: "topk", TOPP: "topp", HIER: "hier", PROXY_TOPP: "topp"}[w.mode]
+    mode = {TOPK: "topk", TOPP: "topp", HIER: "hier", PROXY_TOPP: "topp", COVERAGE: "coverage"}[w.mode]
     return dict(
         batch=w.batch, kv_batch=w.kv_batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
         head_dim=w.head_dim, n_ctx=w.n_ctx, chunk_size=w.chunk_size, dtype=w.dtype, mode=mode,
         route="proxy" if w.mode == PROXY_TOPP else "summary", route_dim=w.route_dim,
-        top_k=w.top_k, top_k_seg=w.top_k_seg, seg_size=w.seg_size, top_p=w.top_p,
+        top_k=w.top_k, top_k_seg=w.top_k_seg, seg_size=w.seg_size, top_p=w.top_p, tau=w.tau,
         select_scale=w.select_scale, softmax_scale=w.softmax_scale,
         keep_first=w.keep_first, keep_last=w.keep_last, sink=w.sink, window=w.window,
         attend_summary=(2 if w.all_summaries else 1) if (w.attend_summary and w.mode != PROXY_TOPP) else 0,

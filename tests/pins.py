@@ -253,7 +253,7 @@ def _tiny_workload(mode, **kw):
                 chunk_size=8, mode=mode, top_k=3, top_k_seg=2, seg_size=4, top_p=0.9,
                 select_scale=0.25, softmax_scale=0.25, keep_first=0, keep_last=0, route_dim=4,
                 local_kv_heads=(), sink=0, window=0, attend_summary=True, all_summaries=False,
-                head_masks=False)
+                head_masks=False, tau=0.0)
     base.update(kw)
     return SimpleNamespace(**base)
 
@@ -412,7 +412,58 @@ def pin_variants(ref, seed=9):
     assert np.array_equal(a["out"], c["out"]) and np.array_equal(a["lse"], c["lse"]), "G = 1 masks"
 
 
+def _brute_coverage(score_rows, scale, tau):
+    """Budget by the definition, every quantity re-derived: probabilities with math.exp and
+    math.fsum, importance summed per entry over the heads, the cut walked one entry at a time."""
+    n = len(score_rows[0])
+    imp = [0.0] * n
+    for s in score_rows:
+        mx = max(scale * x for x in s)
+        e = [math.exp(scale * x - mx) for x in s]
+        Z = math.fsum(e)
+        for m in range(n):
+            imp[m] += e[m] / Z
+    T = math.fsum(imp)
+    order = sorted(range(n), key=lambda m: (imp[m], -m))
+    cut, removed = 0.0, 0
+    for m in order:
+        cut += imp[m]
+        removed += 1
+        if cut > tau * T:
+            break
+    return max(1, n - removed)
+
+
+def pin_coverage(ref, seed=10):
+    """Coverage budget: equals the definition walked entry by entry; tau = 0 removes exactly one
+    entry; the budget never grows with tau; in a step every scored head keeps exactly its own
+    top-budget entries (brute force over its scores)."""
+    rng = np.random.default_rng(seed)
+    for t in range(30):
+        n, H = int(rng.integers(2, 40)), int(rng.integers(1, 6))
+        rows = [rng.standard_normal(n) * rng.choice([0.3, 3.0]) for _ in range(H)]
+        scale, tau = float(rng.choice([0.5, 1.0, 2.0])), float(rng.uniform(0, 0.95))
+        k, _ = ref.coverage_budget(ref.coverage_importance(rows, scale), tau)
+        assert k == _brute_coverage(rows, scale, tau), (t, k)
+        k0, _ = ref.coverage_budget(ref.coverage_importance(rows, scale), 0.0)
+        assert k0 == n - 1, "tau = 0"
+        ks = [ref.coverage_budget(ref.coverage_importance(rows, scale), x)[0] for x in (0.1, 0.3, 0.6, 0.9)]
+        assert ks == sorted(ks, reverse=True), "budget grows with tau"
+    w = _tiny_workload("coverage", n_ctx=96, chunk_size=8, tau=0.2, keep_last=1)
+    src = _Src(w, rng)
+    res = ref.decode_step(w, src)
+    G = w.n_q_heads // w.n_kv_heads
+    for b in range(w.batch):
+        rows = [np.array([math.fsum((src.q[b, h] * k).tolist()) for k in src.Kg[b, h // G]]) for h in range(w.n_q_heads)]
+        k = _brute_coverage(rows, w.select_scale, w.tau)
+        for g in range(w.n_kv_heads):
+            r = res["sel"][(b, g)]
+            for j in range(G):
+                h = g * G + j
+                assert r["heads"][h].tolist() == _brute_topk(rows[h], k), (b, h)
+
+
 ALL_PINS = [pin_golden_scores, pin_golden_proxy, pin_golden_topk, pin_golden_topp, pin_golden_two_level,
             pin_golden_union, pin_golden_attention, pin_scores_exact, pin_bruteforce, pin_topp_minimal,
             pin_reductions, pin_union, pin_masked_dense, pin_dense_limits, pin_step_masked,
-            pin_step_selection, pin_variants]
+            pin_step_selection, pin_variants, pin_coverage]

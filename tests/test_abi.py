@@ -83,6 +83,29 @@ def test_init_rejects_proxy_and_hier_shapes():
     assert e.value.status == N.SD_EINVAL
 
 
+COVERAGE_BAD = [
+    (dict(tau=-0.1), N.SD_EINVAL, "tau"),
+    (dict(tau=1.0), N.SD_EINVAL, "tau"),
+    (dict(tau=float("nan")), N.SD_EINVAL, "tau"),
+    (dict(select_scale=0.0), N.SD_EINVAL, "select_scale"),
+    (dict(n_ctx=4096 * 16, chunk_size=16), N.SD_EUNSUPPORTED, "chunks per row"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", COVERAGE_BAD, ids=[b[2] + str(i) for i, b in enumerate(COVERAGE_BAD)])
+def test_init_rejects_coverage(kw, status, msg):
+    with pytest.raises(N.SparseDecodeError) as e:
+        _init(**_params("c3s_coverage", **kw))
+    assert e.value.status == status
+    assert msg in str(e.value)
+
+
+def test_init_coverage_needs_summary_route():
+    with pytest.raises(N.SparseDecodeError) as e:
+        _init(**_params("c5s", mode="coverage", tau=0.1))
+    assert e.value.status == N.SD_EUNSUPPORTED
+
+
 def test_init_null_arguments():
     L = N.lib()
     h = ctypes.c_void_p()

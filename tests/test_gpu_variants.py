@@ -1,5 +1,5 @@
-"""The two context variants through the HIP path against the oracle (needs an MI355X):
-per-head masks inside the loaded union, and every chunk's summary K/V in the context."""
+"""The variants through the HIP path against the oracle (needs an MI355X): per-head masks
+inside the loaded union, every chunk's summary K/V in the context, and the coverage budget."""
 from dataclasses import replace
 
 import numpy as np
@@ -15,7 +15,13 @@ REDUCED = [("c1s", dict(head_masks=True)), ("c2s", dict(head_masks=True)), ("c3s
            ("c4s", dict(head_masks=True)), ("c5s", dict(head_masks=True)),
            ("c1s", dict(all_summaries=True)), ("c2s", dict(all_summaries=True)), ("c3s", dict(all_summaries=True)),
            ("c4s", dict(all_summaries=True)), ("c3s", dict(head_masks=True, all_summaries=True)),
-           ("c2s", dict(head_masks=True, chunk_size=1, n_ctx=8192, top_k=700))]
+           ("c2s", dict(head_masks=True, chunk_size=1, n_ctx=8192, top_k=700)),
+           # coverage budget: tau 0 keeps all but one entry, tau near 1 clamps the budget to 1
+           ("c1s", dict(mode="coverage", tau=0.3)), ("c2s", dict(mode="coverage", tau=0.1)),
+           ("c3s", dict(mode="coverage", tau=0.0)), ("c3s", dict(mode="coverage", tau=0.999)),
+           ("c3s", dict(mode="coverage", tau=0.5, head_masks=True, all_summaries=True)),
+           ("c2s", dict(mode="coverage", tau=0.15, chunk_size=1, n_ctx=2048, local_kv_heads=(1, 3), sink=16,
+                        window=100))]
 
 
 @pytest.mark.parametrize("name,kw", REDUCED, ids=[f"{n}-" + "-".join(k for k in kw) for n, kw in REDUCED])
@@ -26,6 +32,8 @@ def test_variant_reduced(name, kw):
     g = parity.run_gpu(w, inp)
     o = parity.oracle_step(w, inp)
     rep = parity.compare(w, g, o)
+    if w.mode == "coverage":
+        rep["budgets"] = sorted({r["budget"] for r in o["sel"].values() if "budget" in r})
     print(f"[variant] {w.name}: {rep}", flush=True)
 
 

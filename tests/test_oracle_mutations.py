@@ -40,6 +40,9 @@ MUTATIONS = {
     "head_mask_drops_forced": ("S = group_union([heads[g * G + j], forced])", "S = heads[g * G + j]"),
     "head_mask_wrong_head": ("S = group_union([heads[g * G + j], forced])", "S = group_union([heads[g * G + (j + 1) % G], forced])"),
     "head_mask_ignored": ("masked = getattr(w, \"head_masks\", False) and", "masked = False and"),
+    "coverage_cut_inclusive": ("hit = np.nonzero(c > thr)[0]", "hit = np.nonzero(c >= thr)[0] + 1"),
+    "coverage_unnormalized": ("imp = imp + mass / math.fsum(mass.tolist())", "imp = imp + mass"),
+    "coverage_descending": ("order = np.lexsort((-np.arange(n), imp))", "order = np.lexsort((-np.arange(n), -imp))"),
     "all_summaries_only_selected": ("srows = np.arange(n_ent) if all_sum else", "srows = np.asarray(S, dtype=np.int64) if all_sum else"),
 }
 
