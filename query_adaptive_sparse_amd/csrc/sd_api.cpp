@@ -121,7 +121,11 @@ void plan_workspace(sd::Plan& p) {
   };
   p.o_status = take(64);
   p.o_budget = take(size_t(B) * 4);  // coverage budget per sequence
-  p.o_arrive = take(size_t(B * Hk) * 4);
+  p.o_cmass = take(c.mode == SD_COVERAGE ? size_t(B * Hq * p.len0) * 8 : 0);  // per-head softmax masses
+  p.o_cimp = take(c.mode == SD_COVERAGE ? size_t(B * p.len0) * 8 : 0);        // importance per entry
+  p.o_csort = take(c.mode == SD_COVERAGE ? size_t(B * p.len0) * 8 : 0);       // importance, ascending
+  p.n_arrive = int64_t(B) * Hk;
+  p.o_arrive = take(size_t(p.n_arrive) * 4);
   p.o_qp = take(c.route == SD_ROUTE_PROXY ? size_t(B * Hq * 16) * 8 : 0);
   p.o_s0 = take(size_t(B * Hq * p.len0) * 8);
   p.o_s1 = take(size_t(B * Hq * p.len1) * 8);

@@ -52,7 +52,8 @@ struct Plan {
   int8_t scored[kMaxKvHeads];  // their indices, ascending
   // workspace byte offsets
   size_t o_status, o_arrive, o_qp, o_s0, o_s1, o_cand, o_bits, o_ubits, o_rcnt, o_list, o_cnt;
-  size_t o_gpre, o_po, o_pl, o_pmax, o_pmin, o_info, o_h1m, o_h1c, o_cbin, o_cidx, o_ccnt, o_budget;
+  size_t o_gpre, o_po, o_pl, o_pmax, o_pmin, o_info, o_h1m, o_h1c, o_cbin, o_cidx, o_ccnt, o_budget, o_cmass, o_cimp, o_csort;
+  int64_t n_arrive;  // arrival counters: one per (sequence, KV group)
   size_t ws_bytes;
 };
 

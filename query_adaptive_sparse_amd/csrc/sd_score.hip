@@ -262,7 +262,7 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
       const int nb = (Hq * 16 + 255) / 256;
       hipLaunchKernelGGL((k_proxy_query<T, D>), dim3(nb, B), dim3(256), 0, st, static_cast<const T*>(t.q), t.q_sb,
                          t.q_sh, t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status,
-                         at<int32_t>(ws, p.o_arrive), B * Hk);
+                         at<int32_t>(ws, p.o_arrive), p.n_arrive);
     } else {
       ProxyArgs pa;
       pa.kp = static_cast<const uint16_t*>(t.kp);
@@ -282,7 +282,7 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
       pa.nblk = p.score_blocks0;
       pa.status = status;
       pa.arrivals = at<int32_t>(ws, p.o_arrive);
-      pa.n_groups = B * Hk;
+      pa.n_groups = p.n_arrive;
       for (int i = 0; i < kMaxKvHeads; ++i) pa.scored[i] = i < p.n_scored ? p.scored[i] : 0;
       hipLaunchKernelGGL((k_score_proxy<T, D>), dim3(p.score_blocks0, p.n_scored, B), dim3(512), 0, st, pa);
     }
@@ -303,7 +303,7 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
                      st, static_cast<const T*>(t.q), t.q_sb, t.q_sh, static_cast<const T*>(meta ? t.kmg : t.kg),
                      meta ? t.mg_sb : t.g_sb, meta ? t.mg_sh : t.g_sh, meta ? t.mg_st : t.g_st,
                      static_cast<const int32_t*>(nullptr), p.len0, p.len0, p.G, Hq, hs, p.local_mask, at<double>(ws, p.o_s0),
-                     p.len0, status, at<int32_t>(ws, p.o_arrive), B * Hk);
+                     p.len0, status, at<int32_t>(ws, p.o_arrive), p.n_arrive);
   if (p.long0)
     hipLaunchKernelGGL(k_row_minmax, dim3(p.score_blocks0, Hq, B), dim3(256), 0, st, at<double>(ws, p.o_s0),
                        p.len0, p.G, Hq, p.local_mask, at<double>(ws, p.o_pmax), at<double>(ws, p.o_pmin),

@@ -1085,7 +1085,14 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
 // of select_scale * s over its row, summed per entry (the column sums of the proxy attention map);
 // the entries in ascending importance; the shortest ascending prefix whose mass exceeds tau x the
 // total is cut; budget = max(1, entries - cut), used by every head of the sequence as its top-k.
-// One 1024-thread workgroup per sequence, rows of at most kSmallRowMax entries.
+// Four short launches, each spread over many workgroups:
+//   k_cov_mass        per (head, sequence): the head's softmax masses (zero for a local head);
+//   k_cov_importance  per (slice, sequence): the masses summed per entry in head order;
+//   k_cov_rank        per (slice, sequence): each entry's ascending rank, counted against every
+//                     entry of the sequence (ties by index), and its importance scattered to
+//                     that sorted position;
+//   k_cov_budget      per sequence: the running sum in sorted order and the first crossing.
+// Rows of at most kSmallRowMax entries.
 // ---------------------------------------------------------------------------------------------
 struct CoverageArgs {
   const double* s;
@@ -1093,67 +1100,121 @@ struct CoverageArgs {
   int Hq, G;
   uint64_t local_mask;
   double scale, tau;
-  int32_t* budget;  // [B]
+  double* mass;    // [B][Hq][len]
+  double* imp;     // [B][len]
+  double* sorted;  // [B][len] importance in ascending order
+  int32_t* budget; // [B]
 };
 
-constexpr int kCoverThreads = 1024;
+constexpr int kCovThreads = 256;
+constexpr int kCovRankEntries = 32;   // entries ranked per workgroup
+constexpr int kCovRankPerThread = 4;  // entries per thread (each key read serves all of them)
 
-__global__ __launch_bounds__(kCoverThreads) void k_coverage(CoverageArgs a) {
-  constexpr int NT = kCoverThreads, NW = NT / 64;
-  constexpr int PT = kSmallRowMax / NT;  // entries per thread
-  __shared__ double hmax[kMaxKvHeads * kMaxGroup], hz[kMaxKvHeads * kMaxGroup];
-  __shared__ uint64_t keys[kSmallRowMax];
-  __shared__ uint16_t idx[kSmallRowMax];
-  __shared__ double wtot[NW];
-  __shared__ int hit;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+__global__ __launch_bounds__(kCovThreads) void k_cov_mass(CoverageArgs a) {
+  constexpr int NT = kCovThreads, PT = kSmallRowMax / NT;
+  __shared__ double wred[NT / 64];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int L = int(a.len);
-  const double* sb = a.s + int64_t(b) * a.Hq * a.len;
-  // ---- per head: max and Z of the masses (a wave per head; local heads score nothing)
-  for (int h = wv; h < a.Hq; h += NW) {
-    if ((a.local_mask >> (h / a.G)) & 1) {
-      if (lane == 0) hz[h] = 0.0;
-      continue;
-    }
-    const double* row = sb + int64_t(h) * a.len;
-    double mx = kNegInfD;
-    for (int i = lane; i < L; i += 64) mx = fmax(mx, row[i]);
-    mx = wave_max_dpp(mx);
-    double z = 0.0;
-    for (int i = lane; i < L; i += 64) z += exp(a.scale * row[i] - a.scale * mx);
-    z = wave_sum_dpp(z);
-    if (lane == 0) {
-      hmax[h] = mx;
-      hz[h] = z;
-    }
+  const int64_t row = int64_t(b) * a.Hq + h;
+  double* mr = a.mass + row * a.len;
+  if ((a.local_mask >> (h / a.G)) & 1) {
+    // a local head scores nothing: zero masses keep the per-entry sum branch-free and exact
+    for (int m = tid; m < L; m += NT) mr[m] = 0.0;
+    return;
   }
-  __syncthreads();
-  // ---- importance per entry (heads summed in order), sorted ascending (keys complemented)
-  int Lp = 2;
-  while (Lp < L) Lp <<= 1;
+  const double* sr = a.s + row * a.len;
+  double v[PT];
+  double mx = kNegInfD;
 #pragma unroll
   for (int k = 0; k < PT; ++k) {
     const int m = tid + NT * k;
-    if (m < L) {
-      double imp = 0.0;
-      for (int h = 0; h < a.Hq; ++h)
-        if (hz[h] > 0.0) imp += exp(a.scale * sb[int64_t(h) * a.len + m] - a.scale * hmax[h]) / hz[h];
-      keys[m] = ~dkey(imp);
-      idx[m] = uint16_t(m);
-    } else if (m < Lp) {
-      keys[m] = 0ull;  // padding sorts last
-      idx[m] = 0xFFFF;
-    }
+    v[k] = m < L ? sr[m] : kNegInfD;
+    mx = fmax(mx, v[k]);
   }
+  mx = wave_max_dpp(mx);
+  if (lane == 0) wred[wv] = mx;
   __syncthreads();
-  bitonic_desc<uint16_t, NT>(keys, idx, Lp);
-  // ---- the cut: first sorted position where the running mass exceeds tau x total
+  mx = fmax(fmax(wred[0], wred[1]), fmax(wred[2], wred[3]));
+  __syncthreads();
+  double z = 0.0;
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    v[k] = tid + NT * k < L ? exp(a.scale * v[k] - a.scale * mx) : 0.0;
+    z += v[k];
+  }
+  z = wave_sum_dpp(z);
+  if (lane == 0) wred[wv] = z;
+  __syncthreads();
+  z = (wred[0] + wred[1]) + (wred[2] + wred[3]);
+#pragma unroll
+  for (int k = 0; k < PT; ++k)
+    if (tid + NT * k < L) mr[tid + NT * k] = v[k] / z;
+}
+
+__global__ __launch_bounds__(kCovThreads) void k_cov_importance(CoverageArgs a) {
+  const int b = blockIdx.y, m = blockIdx.x * kCovThreads + threadIdx.x;
+  if (m >= a.len) return;
+  const double* mb = a.mass + int64_t(b) * a.Hq * a.len + m;
+  double imp = 0.0;
+#pragma unroll 8
+  for (int h = 0; h < a.Hq; ++h) imp += mb[int64_t(h) * a.len];
+  a.imp[int64_t(b) * a.len + m] = imp;
+}
+
+__global__ __launch_bounds__(kCovThreads) void k_cov_rank(CoverageArgs a) {
+  constexpr int NT = kCovThreads, E = kCovRankEntries, EPT = kCovRankPerThread;
+  constexpr int EG = E / EPT, S = NT / EG;  // entry groups, key slices
+  __shared__ uint64_t keys[kSmallRowMax];
+  __shared__ int part[S][E];
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int L = int(a.len);
+  const double* ib = a.imp + int64_t(b) * a.len;
+  for (int j = tid; j < L; j += NT) keys[j] = dkey(ib[j]);
+  __syncthreads();
+  // thread: entries e0 + EG i (i < EPT) against keys slice, slice + S, ... (consecutive slices
+  // of a wave read consecutive keys)
+  const int eg = tid % EG, slice = tid / EG;
+  const int e0 = blockIdx.x * E + eg;
+  uint64_t ke[EPT];
+  int cnt[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = e0 + EG * i;
+    ke[i] = e < L ? keys[e] : 0ull;
+    cnt[i] = 0;
+  }
+#pragma unroll 4
+  for (int j = slice; j < L; j += S) {
+    const uint64_t kj = keys[j];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) cnt[i] += (kj < ke[i]) | ((kj == ke[i]) & (j < e0 + EG * i));
+  }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) part[slice][eg + EG * i] = cnt[i];
+  __syncthreads();
+  const int e = blockIdx.x * E + tid;
+  if (tid < E && e < L) {
+    int r = 0;
+#pragma unroll 8
+    for (int q = 0; q < S; ++q) r += part[q][tid];
+    a.sorted[int64_t(b) * a.len + r] = ib[e];
+  }
+}
+
+constexpr int kCovBudgetThreads = 1024;
+__global__ __launch_bounds__(kCovBudgetThreads) void k_cov_budget(CoverageArgs a) {
+  constexpr int NT = kCovBudgetThreads, PT = kSmallRowMax / NT;
+  __shared__ double wtot[NT / 64];
+  __shared__ int hit;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int L = int(a.len);
+  const double* sb = a.sorted + int64_t(b) * a.len;
   double w[PT];
   double local = 0.0;
 #pragma unroll
   for (int k = 0; k < PT; ++k) {
     const int i = PT * tid + k;
-    w[k] = i < L ? dkey_inv(~keys[i]) : 0.0;
+    w[k] = i < L ? sb[i] : 0.0;
     local += w[k];
   }
   if (tid == 0) hit = 0x7FFFFFFF;
@@ -1382,7 +1443,7 @@ int launch_select(const Plan& p, int level, char* ws, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const sd_config& c = p.cfg;
   const int B = c.batch, Hq = c.n_q_heads;
-  if (c.mode == SD_COVERAGE) {
+  if (c.mode == SD_COVERAGE && p.n_scored > 0) {
     CoverageArgs ca;
     ca.s = at<double>(ws, p.o_s0);
     ca.len = p.len0;
@@ -1391,8 +1452,15 @@ int launch_select(const Plan& p, int level, char* ws, void* stream) {
     ca.local_mask = p.local_mask;
     ca.scale = c.select_scale;
     ca.tau = c.tau;
+    ca.mass = at<double>(ws, p.o_cmass);
+    ca.imp = at<double>(ws, p.o_cimp);
+    ca.sorted = at<double>(ws, p.o_csort);
     ca.budget = at<int32_t>(ws, p.o_budget);
-    hipLaunchKernelGGL(k_coverage, dim3(B), dim3(kCoverThreads), 0, st, ca);
+    const int L = int(p.len0);
+    hipLaunchKernelGGL(k_cov_mass, dim3(Hq, B), dim3(kCovThreads), 0, st, ca);
+    hipLaunchKernelGGL(k_cov_importance, dim3((L + kCovThreads - 1) / kCovThreads, B), dim3(kCovThreads), 0, st, ca);
+    hipLaunchKernelGGL(k_cov_rank, dim3((L + kCovRankEntries - 1) / kCovRankEntries, B), dim3(kCovThreads), 0, st, ca);
+    hipLaunchKernelGGL(k_cov_budget, dim3(B), dim3(kCovBudgetThreads), 0, st, ca);
   }
   if (c.mode == SD_HIER_TOPK || !p.long0) {
     // rows of at most kSmallRowMax entries: selection, union and compaction in one kernel
