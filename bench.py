@@ -65,7 +65,7 @@ def algorithmic_bytes(w, counts: np.ndarray) -> dict:
     counts[b, g] = entries in group (b, g)'s union (chunks, or tokens at chunk 1).
     """
     e = w.elem_bytes
-    d, C, B, Hq = w.head_dim, w.chunk_size, w.batch, w.n_q_heads
+    d, C, B, Hq = w.head_dim, w.chunk_size, w.batch, w.n_q_heads * w.n_queries  # query rows per sequence
     U = int(counts.sum())
     raw_kv = U * C * d * e * 2                        # selected raw K and V
     if w.mode == "proxy":
@@ -114,7 +114,7 @@ def cpu_baseline(w, inp, target_s=15.0, max_groups=0):
     per_group = t_total / done
     step_s = per_group * len(groups)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(w.batch / step_s, 4), "unit": "queries/s", "cores": threads, "kind": "oracle",
+    return {"value": round(w.batch * w.n_queries / step_s, 4), "unit": "queries/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} (sequence, KV group) units of {w.name} ({len(groups)} per step, cycled): "
                       f"selection + attention, {t_total:.1f} s, scaled to a full step ({step_s:.2f} s)",
             "cpu": _cpu_model()}
@@ -180,8 +180,8 @@ def main():
     dec.alloc_workspace()
     t = make_tensors(inp["q"], inp["K"], inp["V"], Kg=inp.get("Kg"), Vg=inp.get("Vg"), Kmg=inp.get("Kmg"),
                      Kp=inp.get("Kp"), P=inp.get("P"))
-    out = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
-    lse = torch.empty(w.batch, w.n_q_heads, dtype=torch.float32, device=dev)
+    out = torch.empty(w.batch, w.n_queries, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    lse = torch.empty(w.batch, w.n_queries, w.n_q_heads, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -242,7 +242,7 @@ def main():
     counts = sel["count"].cpu().numpy()
     status = sel["status"].cpu().numpy()
     nb = algorithmic_bytes(w, counts)
-    qps = w.batch / (ms_per_step * 1e-3)
+    qps = w.batch * w.n_queries / (ms_per_step * 1e-3)  # a query: one token of one sequence, all heads
     step_gbps = nb["step"] / (ms_per_step * 1e-3) / 1e9
     attend_gbps = nb["attend"] / (attend_ms * 1e-3) / 1e9
 
@@ -259,7 +259,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded counter-based N(0,1) inputs with a planted Zipf chunk-mass profile)",
-        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+        "config": {"workload": w.name, "batch": w.batch, "n_queries": w.n_queries, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "context": w.n_ctx, "chunk": w.chunk_size, "mode": w.mode,
                    "top_p": w.top_p if w.mode in ("topp", "proxy") else None,
                    "top_k": w.top_k or None, "attend_blocks": dec.attend_blocks,

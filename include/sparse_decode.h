@@ -2,7 +2,8 @@
  * sparse_decode.h -- C ABI of the query-adaptive sparse decode attention library
  * for AMD Instinct MI355X (gfx950).
  *
- * One decode step, for every sequence b and query head h (KV group g = h / G):
+ * One decode step, for every sequence b, query token t (T adjacent tokens per
+ * sequence, usually 1) and query head h (KV group g = h / G):
  *   1. score   relevance of each chunk summary key to the query, s = q . k_g
  *              (AI Trends summary of SSA, aitrends.kr/articles/69798, sections
  *              "방법론" and "기술 상세"); for H-SSA also meta-summary scores first
@@ -66,10 +67,18 @@ enum { SD_TOPK = 0, SD_TOPP = 1, SD_HIER_TOPK = 2, SD_COVERAGE = 3 };  /* select
 enum { SD_ROUTE_SUMMARY = 0, SD_ROUTE_PROXY = 1 };      /* what is scored */
 
 typedef struct {
-  int32_t batch;          /* decode queries B (one per sequence), >= 1 */
-  int32_t kv_batch;       /* KV caches: 1 (every query reads cache 0) or B */
+  int32_t batch;          /* sequences B, >= 1 */
+  int32_t n_queries;      /* T adjacent query tokens per sequence (0 or 1: one). With T > 1
+                             (multi-query decode: speculative or batched positions; review of
+                             "Hierarchical Sparse Attention Done Right", section 3 and its
+                             kernel figure: adjacent queries share the union of their chunks)
+                             every (token, head) selects on its own and the union per KV group
+                             runs over all T x G of them; each attends that union. The T
+                             queries read the same cache: it holds their past, not their own
+                             keys. T x G <= 16 (8 with SD_ROUTE_PROXY). */
+  int32_t kv_batch;       /* KV caches: 1 (every sequence reads cache 0) or B */
   int32_t n_q_heads;      /* Hq */
-  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0 and G = Hq / Hkv <= 8 */
+  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0 and G = Hq / Hkv, T x G <= 16 */
   int32_t head_dim;       /* d: 64 or 128 */
   int64_t n_ctx;          /* N tokens in the cache, 1 <= N < 2^31 */
   int32_t chunk_size;     /* C tokens per chunk, N % C == 0; 1 = token-level */
@@ -110,7 +119,7 @@ typedef struct {
 
 /* Input tensors (device pointers) and their element strides. The last
  * dimension of every tensor is contiguous. Unused tensors may be NULL.
- *   q    [B][Hq][d]            kv_dtype   strides q_sb, q_sh
+ *   q    [B][T][Hq][d]         kv_dtype   strides q_sb, q_st (ignored when T = 1), q_sh
  *   k, v [Bkv][Hkv][N][d]      kv_dtype   strides kv_sb (0 allowed), kv_sh, kv_st
  *   kg, vg [Bkv][Hkv][M][d]    kv_dtype   summary key / value per chunk; g_sb, g_sh, g_st
  *   kmg  [Bkv][Hkv][S][d]      kv_dtype   meta-summary key per segment; mg_sb, mg_sh, mg_st
@@ -119,7 +128,7 @@ typedef struct {
  * Row strides (kv_st, g_st, mg_st) must keep every row 16-byte aligned, and
  * every base pointer must be 16-byte aligned. */
 typedef struct {
-  const void* q;   int64_t q_sb, q_sh;
+  const void* q;   int64_t q_sb, q_sh, q_st;
   const void* k;   const void* v;   int64_t kv_sb, kv_sh, kv_st;
   const void* kg;  const void* vg;  int64_t g_sb, g_sh, g_st;
   const void* kmg; int64_t mg_sb, mg_sh, mg_st;
@@ -127,11 +136,13 @@ typedef struct {
   const float* proj;
 } sd_tensors;
 
-/* Device pointers into a workspace, for inspection after a step.
- *   scores0   fp64 [B][Hq][len0]  level-0 scores (chunks, segments or tokens)
- *   scores1   fp64 [B][Hq][len1]  level-1 candidate scores (two-level only)
- *   cand1     int32 [B][Hq][len1] level-1 candidate chunk ids, ascending
- *   head_bits u32 [B][Hq][words]  per-head selection bitmap, bit e of word e/32
+/* Device pointers into a workspace, for inspection after a step. Per-query
+ * rows come T x Hq per sequence, ordered by KV group, then query token, then
+ * head in the group: row g (T G) + t G + j is token t, head g G + j.
+ *   scores0   fp64 [B][T Hq][len0]  level-0 scores (chunks, segments or tokens)
+ *   scores1   fp64 [B][T Hq][len1]  level-1 candidate scores (two-level only)
+ *   cand1     int32 [B][T Hq][len1] level-1 candidate chunk ids, ascending
+ *   head_bits u32 [B][T Hq][words]  per-head selection bitmap, bit e of word e/32
  *                                 (forced and local entries are not included)
  *   list      int32 [B][Hkv][n_entries] group union, ascending; first cnt valid
  *   count     int32 [B][Hkv]      union size
@@ -150,7 +161,7 @@ typedef struct {
 
 /* Validate and copy `cfg`, create a handle, report the workspace size in bytes.
  * Host only: touches no GPU. Errors: SD_EINVAL (null pointer, inconsistent
- * shape or parameter), SD_EUNSUPPORTED (head_dim not 64/128, group > 8). */
+ * shape or parameter), SD_EUNSUPPORTED (head_dim not 64/128, T x G > 16). */
 sd_status sparse_decode_init(const sd_config* cfg, sd_handle** out, size_t* workspace_bytes);
 
 /* 1 for flat selection, 2 for two-level (SD_HIER_TOPK). 0 for a NULL handle. */
@@ -172,8 +183,9 @@ sd_status sparse_decode_select(const sd_handle* h, int level, void* ws, void* st
 /* Step 3: split-K partial attention over each group's list (workspace). */
 sd_status sparse_decode_attend(const sd_handle* h, const sd_tensors* t, void* ws, void* stream);
 
-/* Step 4: merge the partials into out fp32 [B][Hq][d] and lse_out fp32 [B][Hq]
- * (natural log of the softmax normaliser), both contiguous device buffers. */
+/* Step 4: merge the partials into out fp32 [B][T][Hq][d] and lse_out fp32
+ * [B][T][Hq] (natural log of the softmax normaliser), both contiguous device
+ * buffers. */
 sd_status sparse_decode_combine(const sd_handle* h, void* ws, float* out, float* lse_out,
                                 void* stream);
 

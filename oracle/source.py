@@ -24,7 +24,9 @@ class HostSource:
     def __init__(self, inputs: dict):
         self._K = inputs["K"]
         self._V = inputs["V"]
-        self.q = _f64(inputs["q"])
+        q = _f64(inputs["q"])
+        # [B][T][Hq][d] (T adjacent query tokens) -> [B][T * Hq][d], row t * Hq + h
+        self.q = q.reshape(q.shape[0], -1, q.shape[-1]) if q.ndim == 4 else q
         self.Kg = _f64(inputs.get("Kg"))
         self.Vg = _f64(inputs.get("Vg"))
         self.Kmg = _f64(inputs.get("Kmg"))

@@ -24,7 +24,8 @@ Sources (cited by page title and section):
   exceeds a coverage threshold tau; each head then keeps its own top-k.
 * [HiLS] Review of "Hierarchical Sparse Attention Done Right", section 1: a
   landmark token's key summarises its chunk; GQA extended to group-wise chunk
-  selection.
+  selection. Section 3 and the kernel figure: adjacent query tokens are grouped
+  and their chunks' union is processed together.
 
 Readings where the pages are silent (each is a fixed choice of this oracle):
 
@@ -51,6 +52,10 @@ Readings where the pages are silent (each is a fixed choice of this oracle):
 * Variant "all summaries": the summary K/V of every chunk join the context,
   not only the selected chunks' ([SSA] 기술 상세 has the query interact with
   all summaries first); they are attended by every head of the group.
+* Multi-query decode ([HiLS] section 3, kernel figure): a sequence may carry T
+  adjacent query tokens; each (token, head) selects on its own, the group union
+  runs over all T x G of them, and every one attends that union. The T tokens
+  read the same cache (their past); their own keys are not in it.
 * Variant "per-head masks": the group still loads the union once, but head h
   attends only to the raw (and selected-summary) rows of its own selection plus
   the forced sink / recent chunks; local groups are unmasked.
@@ -229,18 +234,27 @@ def hybrid_rows(U: np.ndarray, chunk_size: int) -> np.ndarray:
 
 
 # ------------------------------------------------------------------------ the step
-def sequence_budget(w, src, b: int):
-    """Coverage budget of sequence b from all its scored heads' chunk scores."""
+def group_queries(w, g: int) -> list:
+    """Query rows of KV group g: every query token t of the sequence (T adjacent
+    tokens, usually one) and every head g*G + j of the group, as indices
+    ``t * Hq + h`` into the sequence's [T * Hq] query rows ([HiLS] section 3:
+    adjacent query tokens share one union of chunks)."""
     G = w.n_q_heads // w.n_kv_heads
+    T = getattr(w, "n_queries", 1)
+    return [t * w.n_q_heads + g * G + j for t in range(T) for j in range(G)]
+
+
+def sequence_budget(w, src, b: int):
+    """Coverage budget of sequence b from all its scored query rows' chunk scores."""
     bk = b if w.kv_batch > 1 else 0
-    rows = [chunk_scores(src.q[b, g * G + j], src.Kg[bk, g])
-            for g in range(w.n_kv_heads) if g not in tuple(w.local_kv_heads) for j in range(G)]
+    rows = [chunk_scores(src.q[b, qi], src.Kg[bk, g])
+            for g in range(w.n_kv_heads) if g not in tuple(w.local_kv_heads) for qi in group_queries(w, g)]
     return coverage_budget(coverage_importance(rows, w.select_scale), w.tau)
 
 
 def select_group(w, src, b: int, g: int) -> dict:
-    """Per-head selections and the group union for sequence b, KV group g."""
-    G = w.n_q_heads // w.n_kv_heads
+    """Per-query-row selections (keyed by row ``t * Hq + h``) and the group union
+    for sequence b, KV group g."""
     bk = b if w.kv_batch > 1 else 0
     n_ent = w.n_ctx // w.chunk_size
     res = {"heads": {}, "scores": {}, "margin": math.inf, "segments": {}, "cand": {}}
@@ -248,8 +262,7 @@ def select_group(w, src, b: int, g: int) -> dict:
         res["union"] = edge_entries(n_ent, w.sink, w.window)
         return res
     per_head = []
-    for j in range(G):
-        h = g * G + j
+    for h in group_queries(w, g):
         q = src.q[b, h]
         if w.mode == TOPK:
             s = chunk_scores(q, src.Kg[bk, g])
@@ -293,13 +306,13 @@ def attend_group(w, src, b: int, g: int, U: np.ndarray, heads=None):
     every chunk with ``all_summaries``. With ``head_masks`` and a scored group,
     head h attends only to its own selection ``heads[h]`` plus the forced
     chunks (summary rows of every chunk stay visible to all heads)."""
-    G = w.n_q_heads // w.n_kv_heads
+    rows_q = group_queries(w, g)
     bk = b if w.kv_batch > 1 else 0
     n_ent = w.n_ctx // w.chunk_size
     summaries = w.attend_summary and w.mode != PROXY_TOPP
     all_sum = summaries and getattr(w, "all_summaries", False)
     masked = getattr(w, "head_masks", False) and g not in tuple(w.local_kv_heads)
-    qh = src.q[b, g * G:(g + 1) * G]
+    qh = src.q[b, rows_q]
 
     def context(S):
         rows = hybrid_rows(S, w.chunk_size)
@@ -314,10 +327,10 @@ def attend_group(w, src, b: int, g: int, U: np.ndarray, heads=None):
         Kc, Vc = context(U)
         return attend(qh, Kc, Vc, w.softmax_scale)
     forced = edge_entries(n_ent, w.keep_first, w.keep_last)
-    o = np.zeros((G, w.head_dim))
-    lse = np.zeros(G)
-    for j in range(G):
-        S = group_union([heads[g * G + j], forced])
+    o = np.zeros((len(rows_q), w.head_dim))
+    lse = np.zeros(len(rows_q))
+    for j, qi in enumerate(rows_q):
+        S = group_union([heads[qi], forced])
         Kc, Vc = context(S)
         oj, lj = attend(qh[j:j + 1], Kc, Vc, w.softmax_scale)
         o[j], lse[j] = oj[0], lj[0]
@@ -327,15 +340,15 @@ def attend_group(w, src, b: int, g: int, U: np.ndarray, heads=None):
 def decode_step(w, src, groups=None, attend_groups=None) -> dict:
     """One decode step: selections for ``groups`` (default all (b, g)), attention
     for ``attend_groups`` (default the same). Returns per-(b, g) results and
-    output / lse arrays (NaN where not computed)."""
+    output / lse arrays [B][T * Hq] (NaN where not computed)."""
     B, Hq, Hk, d = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
-    G = Hq // Hk
+    T = getattr(w, "n_queries", 1)
     if groups is None:
         groups = [(b, g) for b in range(B) for g in range(Hk)]
     if attend_groups is None:
         attend_groups = groups
-    out = np.full((B, Hq, d), np.nan)
-    lse = np.full((B, Hq), np.nan)
+    out = np.full((B, T * Hq, d), np.nan)
+    lse = np.full((B, T * Hq), np.nan)
     sel = {}
     for b, g in groups:
         sel[(b, g)] = select_group(w, src, b, g)
@@ -343,6 +356,6 @@ def decode_step(w, src, groups=None, attend_groups=None) -> dict:
         if (b, g) not in sel:
             sel[(b, g)] = select_group(w, src, b, g)
         o, l = attend_group(w, src, b, g, sel[(b, g)]["union"], sel[(b, g)]["heads"])
-        out[b, g * G:(g + 1) * G] = o
-        lse[b, g * G:(g + 1) * G] = l
+        out[b, group_queries(w, g)] = o
+        lse[b, group_queries(w, g)] = l
     return {"sel": sel, "out": out, "lse": lse}

@@ -40,8 +40,17 @@ sd_status check_cfg(const sd_config& c) {
                 c.n_kv_heads);
   if (c.n_kv_heads > sd::kMaxKvHeads)
     return fail(SD_EUNSUPPORTED, "n_kv_heads > %d", sd::kMaxKvHeads);
-  if (c.n_q_heads / c.n_kv_heads > sd::kMaxGroup)
-    return fail(SD_EUNSUPPORTED, "group size %d > %d", c.n_q_heads / c.n_kv_heads, sd::kMaxGroup);
+  if (c.n_queries < 0) return fail(SD_EINVAL, "n_queries must be >= 0 (got %d)", c.n_queries);
+  {
+    const int64_t T = c.n_queries > 1 ? c.n_queries : 1;
+    const int64_t rows = T * (c.n_q_heads / c.n_kv_heads);
+    if (rows > sd::kMaxGroup)
+      return fail(SD_EUNSUPPORTED, "query rows per KV group (n_queries x group size) %lld > %d", (long long)rows,
+                  sd::kMaxGroup);
+    if (c.route == SD_ROUTE_PROXY && rows > sd::kMaxProxyGroup)
+      return fail(SD_EUNSUPPORTED, "proxy routing: query rows per KV group %lld > %d", (long long)rows,
+                  sd::kMaxProxyGroup);
+  }
   if (c.head_dim != 64 && c.head_dim != 128) return fail(SD_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c.head_dim);
   if (c.kv_dtype != SD_F32 && c.kv_dtype != SD_BF16) return fail(SD_EINVAL, "kv_dtype %d unknown", c.kv_dtype);
   if (c.n_ctx < 1 || c.n_ctx >= (int64_t(1) << 31)) return fail(SD_EINVAL, "n_ctx out of range (%lld)", (long long)c.n_ctx);
@@ -166,6 +175,7 @@ sd_status check_tensors(const sd::Plan& p, const sd_tensors* t, bool for_score, 
   const int es = c.kv_dtype == SD_F32 ? 4 : 2;
   auto row_ok = [&](int64_t st) { return st >= c.head_dim && (st * es) % 16 == 0; };
   if ((t->q_sh * es) % 16 || (t->q_sb * es) % 16 || t->q_sh < c.head_dim) return fail(SD_EINVAL, "q strides must keep 16-byte aligned rows");
+  if (p.T > 1 && ((t->q_st * es) % 16 || t->q_st < c.head_dim)) return fail(SD_EINVAL, "q token stride must keep 16-byte aligned rows");
   if (for_score) {
     if (c.route == SD_ROUTE_PROXY) {
       if (!t->kp || !aligned16(t->kp)) return fail(SD_EINVAL, "proxy routing needs kp (16-byte aligned)");
@@ -204,6 +214,10 @@ sd_status sparse_decode_init(const sd_config* cfg, sd_handle** out, size_t* work
     p.head_mode[g] = cfg->head_mode ? cfg->head_mode[g] : 0;
     if (p.head_mode[g]) p.local_mask |= uint64_t(1) << g;
   }
+  p.T = cfg->n_queries > 1 ? cfg->n_queries : 1;
+  p.Gq = cfg->n_q_heads / cfg->n_kv_heads;
+  p.Hq_user = cfg->n_q_heads;
+  p.cfg.n_q_heads = p.T * cfg->n_q_heads;  // query rows per sequence (see Plan)
   const sd_config& c = p.cfg;
   p.G = c.n_q_heads / c.n_kv_heads;
   p.M = c.n_ctx / c.chunk_size;

@@ -25,7 +25,7 @@ namespace {
 
 struct AttendArgs {
   const void* q;
-  int64_t q_sb, q_sh;
+  QRows qm;
   const void* k;
   const void* v;
   int64_t kv_sb, kv_sh, kv_st;
@@ -40,6 +40,10 @@ struct AttendArgs {
   int64_t n_list;     // list row stride (entries) = entries per row (M)
   int n_groups, Hk, Hq, G, chunk_shift;
   int attend_summary;  // 0 none, 1 the listed chunks' summaries, 2 every chunk's
+  // bf16 P.V: with at most 8 query rows per group, the hi and lo halves of P share one MFMA in
+  // rows [0, G) and [G, 2G); with more rows they go through two MFMAs into one accumulator
+  // (the kernel's SPLIT instance)
+  int pv_split;
   float scale_log2;
   // per-head masks (variant): head h sees only its own entries plus the forced ones
   int head_masks;
@@ -105,7 +109,7 @@ __device__ __forceinline__ int group_extent(int cnt, int cs, int attend_summary,
 // for a forced entry or a local group.
 __device__ __forceinline__ uint32_t head_mask_of(const AttendArgs& a, int gid, int e) {
   const int b = gid / a.Hk, g = gid - b * a.Hk;
-  if (((a.local_mask >> g) & 1) || e < a.keep_first || int64_t(e) >= a.n_list - a.keep_last) return 0xFFu;
+  if (((a.local_mask >> g) & 1) || e < a.keep_first || int64_t(e) >= a.n_list - a.keep_last) return 0xFFFFu;
   uint32_t m = 0;
   for (int j = 0; j < a.G; ++j) {
     const uint32_t w = a.bits[(int64_t(b) * a.Hq + g * a.G + j) * a.words + (e >> 5)];
@@ -114,13 +118,13 @@ __device__ __forceinline__ uint32_t head_mask_of(const AttendArgs& a, int gid, i
   return m;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool SPLIT>
 struct Attender {
   using CF = Cfg<T, D>;
   const AttendArgs& a;
   const int lane, wave, n, c;
   const int32_t* lst;   // LDS list slice
-  const uint8_t* lmask; // LDS head masks of the slice's entries (per-head-mask variant)
+  const uint16_t* lmask; // LDS head masks of the slice's entries (per-head-mask variant)
   uint32_t* vt;         // this wave's LDS region
   // current group
   int gid, G, hs;
@@ -132,17 +136,17 @@ struct Attender {
   uint4 qf[CF::BF ? CF::QF : 1];
   float qf32[CF::BF ? 1 : CF::QF];
 
-  __device__ Attender(const AttendArgs& args, const int32_t* l, const uint8_t* lm, uint32_t* v)
+  __device__ Attender(const AttendArgs& args, const int32_t* l, const uint16_t* lm, uint32_t* v)
       : a(args), lane(threadIdx.x & 63), wave(threadIdx.x >> 6), n(lane & 15), c(lane >> 4), lst(l), lmask(lm),
         vt(v) {}
 
   __device__ void load_query(int group) {
     gid = group;
     G = a.G;
-    hs = n < G ? n : (n < 2 * G ? n - G : -1);
-    lo_row = CF::BF && n >= G && n < 2 * G;
+    hs = n < G ? n : (!SPLIT && n < 2 * G ? n - G : -1);
+    lo_row = CF::BF && !SPLIT && n >= G && n < 2 * G;
     const int b = group / a.Hk, g = group - b * a.Hk;
-    const T* qrow = reinterpret_cast<const T*>(a.q) + b * a.q_sb + int64_t(g * G + (hs < 0 ? 0 : hs)) * a.q_sh;
+    const T* qrow = reinterpret_cast<const T*>(a.q) + q_offset(a.qm, b, g * G + (hs < 0 ? 0 : hs));
     if constexpr (CF::BF) {
 #pragma unroll
       for (int j = 0; j < CF::QF; ++j) qf[j] = hs >= 0 ? ld16(qrow + 32 * j + 8 * c) : make_uint4(0, 0, 0, 0);
@@ -260,19 +264,34 @@ struct Attender {
     // ---- P V: P is the A operand (row = head slot, k = tokens 4c .. 4c+3), V the B operand
     if constexpr (CF::BF) {
       const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
-      u16x4 pa;
+      u16x4 pa, pl;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint16_t hi = f2bf(pr[i]);
-        pa[i] = hs < 0 ? uint16_t(0) : (lo_row ? f2bf(pr[i] - bf2f(hi)) : hi);
+        const uint16_t lo = f2bf(pr[i] - bf2f(hi));
+        pa[i] = hs < 0 ? uint16_t(0) : (lo_row ? lo : hi);
+        pl[i] = hs < 0 ? uint16_t(0) : lo;
       }
+      if constexpr (!SPLIT) {
 #pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb) {
-        u16x4 vbf;
+        for (int nb = 0; nb < D / 16; ++nb) {
+          u16x4 vbf;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vbf[i] = vt16[(4 * c + i) * (2 * CF::kRowWords) + 16 * nb + n];
-        s.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, pa),
-                                                               __builtin_bit_cast(bf16x4, vbf), s.acc[nb], 0, 0, 0);
+          for (int i = 0; i < 4; ++i) vbf[i] = vt16[(4 * c + i) * (2 * CF::kRowWords) + 16 * nb + n];
+          s.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, pa),
+                                                                 __builtin_bit_cast(bf16x4, vbf), s.acc[nb], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) {
+          u16x4 vbf;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vbf[i] = vt16[(4 * c + i) * (2 * CF::kRowWords) + 16 * nb + n];
+          s.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, pa),
+                                                                 __builtin_bit_cast(bf16x4, vbf), s.acc[nb], 0, 0, 0);
+          s.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, pl),
+                                                                 __builtin_bit_cast(bf16x4, vbf), s.acc[nb], 0, 0, 0);
+        }
       }
     } else {
       const float* vtf = reinterpret_cast<const float*>(vt);
@@ -317,12 +336,12 @@ struct Attender {
   }
 };
 
-template <typename T, int D>
+template <typename T, int D, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   using CF = Cfg<T, D>;
   __shared__ int32_t gpre[kMaxGroups + 1];
   __shared__ int32_t lst[kListLds];
-  __shared__ uint8_t lmask[kListLds];
+  __shared__ uint16_t lmask[kListLds];
   __shared__ uint32_t wlds[kWaves * CF::kWaveWords];
   __shared__ int32_t sbuf[256];
   const int tid = threadIdx.x;
@@ -370,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
 
   const int wave = tid >> 6;
   uint32_t* vt = wlds + wave * CF::kWaveWords;
-  Attender<T, D> at(a, lst, lmask, vt);
+  Attender<T, D, SPLIT> at(a, lst, lmask, vt);
   const int lane = tid & 63, n = lane & 15, c = lane >> 4;
 
   for (int gi = lo; gi < NG && gpre[gi] < b1; ++gi) {
@@ -404,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
         for (int i = tid; i < e1 - e0; i += 256) {
           const int e = glist[e0 + i];
           lst[i] = e;
-          if (a.head_masks) lmask[i] = uint8_t(head_mask_of(a, gi, e));
+          if (a.head_masks) lmask[i] = uint16_t(head_mask_of(a, gi, e));
         }
         __syncthreads();
         at.run(false, u0, u1, ntok, e0, st);
@@ -428,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
           for (int i = tid; i < e1 - e0; i += 256) {
             const int e = glist[e0 + i];
             lst[i] = e;
-            if (a.head_masks) lmask[i] = uint8_t(head_mask_of(a, gi, e));
+            if (a.head_masks) lmask[i] = uint16_t(head_mask_of(a, gi, e));
           }
           __syncthreads();
         }
@@ -442,7 +461,8 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
     __syncthreads();  // every wave is done with its V tile; reuse the LDS regions
     float* mw = reinterpret_cast<float*>(vt);  // [16][D] acc rows, then m[16], l[16]
     const int G = a.G;
-    const int nslots = CF::BF ? 2 * G : G;
+    const bool lo_rows = CF::BF && !SPLIT;
+    const int nslots = lo_rows ? 2 * G : G;
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb)
 #pragma unroll
@@ -468,7 +488,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
         const float f = __builtin_amdgcn_exp2f(mw_ - M);
         Ls += ww[16 * D + 16 + hh] * f;
         float o = ww[hh * D + dd];
-        if (CF::BF) o += ww[(hh + G) * D + dd];
+        if (lo_rows) o += ww[(hh + G) * D + dd];
         O += o * f;
       }
       a.po[(slot * G + hh) * D + dd] = Ls > 0.f ? O / Ls : 0.f;  // no tiles of the group: empty partial
@@ -478,7 +498,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   }
 }
 
-// LSE combine. One workgroup of kCombineThreads per (sequence, query head): the partials of the
+// LSE combine. One workgroup of kCombineThreads per (sequence, query row): the partials of the
 // head's group are the pool slots (k + group) of the persistent workgroups k whose tile slice
 // meets the group. Their lse values are read in one parallel round (max, then weights
 // exp(lse - max) in LDS, kCombineThreads partials at a time); each thread then accumulates one
@@ -489,7 +509,7 @@ constexpr int kCombineThreads = 1024;
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void k_combine(const float* __restrict__ po, const float* __restrict__ pl,
                                                              const int32_t* __restrict__ gpre, int n_groups,
-                                                             int nb_attend, int G, int Hq, int Hk,
+                                                             int nb_attend, int G, int Hq, int Hk, int Gq,
                                                              float* __restrict__ out, float* __restrict__ lse) {
   constexpr int NT = kCombineThreads;
   constexpr int NW = NT / 64;
@@ -497,7 +517,12 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float* __rest
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int gid = b * Hk + h / G, hh = h % G;
-  const int64_t hrow = int64_t(b) * Hq + h;
+  // query row h = g G + t Gq + j (token t, head g Gq + j) -> output row [b][t][g Gq + j]
+  int64_t hrow = int64_t(b) * Hq + h;
+  if (G != Gq) {
+    const int tq = hh / Gq, HqU = Hq / (G / Gq);
+    hrow = (int64_t(b) * (G / Gq) + tq) * HqU + (h / G) * Gq + (hh - tq * Gq);
+  }
   const int64_t T = gpre[n_groups];
   const int64_t t0 = gpre[gid], t1 = gpre[gid + 1];
   __shared__ float red[NW];
@@ -564,8 +589,7 @@ int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream) {
   const sd_config& c = p.cfg;
   AttendArgs a;
   a.q = t.q;
-  a.q_sb = t.q_sb;
-  a.q_sh = t.q_sh;
+  a.qm = QRows{t.q_sb, t.q_st, t.q_sh, p.G, p.Gq};
   a.k = t.k;
   a.v = t.v;
   a.kv_sb = t.kv_sb;
@@ -590,6 +614,7 @@ int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream) {
   while ((1 << cs) < c.chunk_size) ++cs;
   a.chunk_shift = cs;
   a.attend_summary = c.attend_summary;
+  a.pv_split = c.kv_dtype == SD_BF16 && 2 * p.G > 16;
   a.scale_log2 = c.softmax_scale * 1.4426950408889634f;
   a.head_masks = c.head_masks;
   a.bits = at<uint32_t>(ws, p.o_bits);
@@ -599,15 +624,22 @@ int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream) {
   a.local_mask = p.local_mask;
   const dim3 grid(p.attend_blocks);
   if (c.kv_dtype == SD_BF16) {
-    if (c.head_dim == 128)
-      hipLaunchKernelGGL((k_attend<uint16_t, 128>), grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_attend<uint16_t, 64>), grid, dim3(256), 0, st, a);
+    if (c.head_dim == 128) {
+      if (a.pv_split)
+        hipLaunchKernelGGL((k_attend<uint16_t, 128, true>), grid, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_attend<uint16_t, 128, false>), grid, dim3(256), 0, st, a);
+    } else {
+      if (a.pv_split)
+        hipLaunchKernelGGL((k_attend<uint16_t, 64, true>), grid, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_attend<uint16_t, 64, false>), grid, dim3(256), 0, st, a);
+    }
   } else {
     if (c.head_dim == 128)
-      hipLaunchKernelGGL((k_attend<float, 128>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_attend<float, 128, false>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((k_attend<float, 64>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_attend<float, 64, false>), grid, dim3(256), 0, st, a);
   }
   return int(hipGetLastError());
 }
@@ -619,10 +651,10 @@ int launch_combine(const Plan& p, char* ws, float* out, float* lse, void* stream
   const int NG = c.batch * c.n_kv_heads;
   if (c.head_dim == 128)
     hipLaunchKernelGGL(k_combine<128>, grid, dim3(kCombineThreads), 0, st, at<float>(ws, p.o_po), at<float>(ws, p.o_pl),
-                       at<int32_t>(ws, p.o_gpre), NG, p.attend_blocks, p.G, c.n_q_heads, c.n_kv_heads, out, lse);
+                       at<int32_t>(ws, p.o_gpre), NG, p.attend_blocks, p.G, c.n_q_heads, c.n_kv_heads, p.Gq, out, lse);
   else
     hipLaunchKernelGGL(k_combine<64>, grid, dim3(kCombineThreads), 0, st, at<float>(ws, p.o_po), at<float>(ws, p.o_pl),
-                       at<int32_t>(ws, p.o_gpre), NG, p.attend_blocks, p.G, c.n_q_heads, c.n_kv_heads, out, lse);
+                       at<int32_t>(ws, p.o_gpre), NG, p.attend_blocks, p.G, c.n_q_heads, c.n_kv_heads, p.Gq, out, lse);
   return int(hipGetLastError());
 }
 

@@ -162,6 +162,17 @@ __device__ __forceinline__ int wave_scan_i32_dpp(int v, int lane) {
   return v + (r == 0 ? 0 : (r == 1 ? t0 : (r == 2 ? t0 + t1 : t0 + t1 + t2)));
 }
 
+// Element offset of query row r of sequence b. Rows are ordered by KV group, then query token,
+// then head: r = g Gr + t Gq + j (Gr = T Gq rows per group) is token t, head g Gq + j.
+struct QRows {
+  int64_t sb, st, sh;
+  int Gr, Gq;
+};
+__device__ __forceinline__ int64_t q_offset(const QRows& m, int b, int r) {
+  const int g = r / m.Gr, rr = r - g * m.Gr, t = rr / m.Gq, j = rr - t * m.Gq;
+  return int64_t(b) * m.sb + int64_t(t) * m.st + int64_t(g * m.Gq + j) * m.sh;
+}
+
 template <typename T>
 inline T* at(char* ws, size_t off) {
   return reinterpret_cast<T*>(ws + off);

@@ -26,7 +26,9 @@ constexpr int kMinMaxBlock = 2048;
 // Attention: tokens per MFMA tile and waves per workgroup.
 constexpr int kTile = 16;
 constexpr int kWaves = 4;
-constexpr int kMaxGroup = 8;
+// Query rows per KV group (T query tokens x G heads), and the limit of the proxy score kernel.
+constexpr int kMaxGroup = 16;
+constexpr int kMaxProxyGroup = 8;
 constexpr int kMaxKvHeads = 64;
 // Attention: persistent workgroups (default: one per CU of a 256-CU MI355X) and the most
 // (sequence, KV group) pairs per call.
@@ -37,7 +39,11 @@ struct Plan {
   sd_config cfg;
   int8_t head_mode[kMaxKvHeads];
   uint64_t local_mask;      // bit g set: KV head g is a local (sink + window) head
-  int32_t G;                // query heads per KV head
+  // T query tokens per sequence run as T x Hq query rows: cfg.n_q_heads holds T x Hq and G the
+  // rows per KV group, T x Gq, ordered token-major inside the group (row g G + t Gq + j is token
+  // t, head g Gq + j)
+  int32_t G;                // query rows per KV head
+  int32_t T, Gq, Hq_user;   // query tokens per sequence, heads per KV head, heads
   int64_t M;                // chunks = n_ctx / chunk_size (selection entries)
   int32_t S;                // segments (two-level)
   int32_t levels;

@@ -15,7 +15,7 @@ namespace {
 // selection.
 // ---------------------------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, int64_t q_sb, int64_t q_sh,
+__global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRows qm,
                                                     const T* __restrict__ keys, int64_t k_sb, int64_t k_sh,
                                                     int64_t k_st, const int32_t* __restrict__ cand,
                                                     int64_t n_rows, int64_t n_keys, int G, int Hq, int hs_shift,
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, int
   const int nh = cand ? 1 : G;
   for (int i = tid; i < nh * D; i += 256) {
     const int j = i / D, dd = i - j * D;
-    qs[j * QW + dd] = elem_f32<T>(q + b * q_sb + (h0 + j) * q_sh + dd);
+    qs[j * QW + dd] = elem_f32<T>(q + q_offset(qm, b, h0 + j) + dd);
   }
   __syncthreads();
   const int j = tid & ((1 << hs_shift) - 1);
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, int
 // Projected query q_p = q P (d -> 16) per scored head, fp64, index order. A bf16 or fp32 query
 // times an fp32 projection entry is exact in fp64.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_proxy_query(const T* __restrict__ q, int64_t q_sb, int64_t q_sh,
+__global__ __launch_bounds__(256) void k_proxy_query(const T* __restrict__ q, QRows qm,
                                                      const float* __restrict__ proj, int G, int Hq,
                                                      uint64_t local_mask, double* __restrict__ qp,
                                                      uint32_t* __restrict__ status, int32_t* __restrict__ arrivals,
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void k_proxy_query(const T* __restrict__ q, in
   double acc = 0.0;
   if (!((local_mask >> g) & 1)) {
     const float* P = proj + int64_t(g) * D * 16;
-    const T* qh = q + b * q_sb + h * q_sh;
+    const T* qh = q + q_offset(qm, b, h);
     for (int i = 0; i < D; ++i) acc = fma(double(elem_f32<T>(qh + i)), double(P[i * 16 + j]), acc);
   }
   qp[(int64_t(b) * Hq + h) * 16 + j] = acc;
@@ -103,7 +103,7 @@ struct ProxyArgs {
   const uint16_t* kp;
   int64_t kp_sb, kp_sh, kp_st;
   const void* q;
-  int64_t q_sb, q_sh;
+  QRows qm;
   const float* proj;
   int G, Hq;
   int64_t N;
@@ -121,8 +121,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
   const int b = blockIdx.z, g = a.scored[blockIdx.y], tid = threadIdx.x;
   const int G = a.G;
-  __shared__ double qs[kMaxGroup][16];
-  __shared__ double rmax[kMaxGroup][8], rmin[kMaxGroup][8];
+  __shared__ double qs[kMaxProxyGroup][16];
+  __shared__ double rmax[kMaxProxyGroup][8], rmin[kMaxProxyGroup][8];
   if (blockIdx.x == 0 && blockIdx.y == 0 && b == 0) {
     if (tid < 16) a.status[tid] = 0;
     for (int i = tid; i < a.n_groups; i += 512) a.arrivals[i] = 0;
@@ -142,12 +142,12 @@ __global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
     // stage the group's projection and queries in LDS (one parallel round of loads), then one
     // thread per (head, proxy dim) runs the index-order fma chain
     __shared__ float Ps[D * 16];
-    __shared__ float Qs[kMaxGroup][D];
+    __shared__ float Qs[kMaxProxyGroup][D];
     const float* P = a.proj + int64_t(g) * D * 16;
     for (int i = tid; i < D * 16; i += 512) Ps[i] = P[i];
     for (int i = tid; i < G * D; i += 512) {
       const int hh = i / D, e = i - hh * D;
-      Qs[hh][e] = elem_f32<T>(static_cast<const T*>(a.q) + b * a.q_sb + int64_t(g * G + hh) * a.q_sh + e);
+      Qs[hh][e] = elem_f32<T>(static_cast<const T*>(a.q) + q_offset(a.qm, b, g * G + hh) + e);
     }
     __syncthreads();
     if (tid < G * 16) {
@@ -159,9 +159,9 @@ __global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
     }
   }
   __syncthreads();
-  double mx[kMaxGroup], mn[kMaxGroup];
+  double mx[kMaxProxyGroup], mn[kMaxProxyGroup];
 #pragma unroll
-  for (int j = 0; j < kMaxGroup; ++j) {
+  for (int j = 0; j < kMaxProxyGroup; ++j) {
     mx[j] = kNegInfD;
     mn[j] = kPosInfD;
   }
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
       kd[u + 8] = double(float(h1[u]));
     }
 #pragma unroll
-    for (int j = 0; j < kMaxGroup; ++j) {
+    for (int j = 0; j < kMaxProxyGroup; ++j) {
       if (j < G) {
         double acc = 0.0;
 #pragma unroll
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
   }
   const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int j = 0; j < kMaxGroup; ++j) {
+  for (int j = 0; j < kMaxProxyGroup; ++j) {
     if (j < G) {
       const double wx = wave_max_dpp(mx[j]), wn = wave_min_dpp(mn[j]);
       if (lane == 0) {
@@ -257,11 +257,12 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
   const sd_config& c = p.cfg;
   const int B = c.batch, Hq = c.n_q_heads, Hk = c.n_kv_heads;
   uint32_t* status = at<uint32_t>(ws, p.o_status);
+  const QRows qm{t.q_sb, t.q_st, t.q_sh, p.G, p.Gq};
   if (c.route == SD_ROUTE_PROXY) {
     if (p.n_scored == 0) {  // every group is local: only the status words and counters need clearing
       const int nb = (Hq * 16 + 255) / 256;
-      hipLaunchKernelGGL((k_proxy_query<T, D>), dim3(nb, B), dim3(256), 0, st, static_cast<const T*>(t.q), t.q_sb,
-                         t.q_sh, t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status,
+      hipLaunchKernelGGL((k_proxy_query<T, D>), dim3(nb, B), dim3(256), 0, st, static_cast<const T*>(t.q), qm,
+                         t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status,
                          at<int32_t>(ws, p.o_arrive), p.n_arrive);
     } else {
       ProxyArgs pa;
@@ -270,8 +271,7 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
       pa.kp_sh = t.kp_sh;
       pa.kp_st = t.kp_st;
       pa.q = t.q;
-      pa.q_sb = t.q_sb;
-      pa.q_sh = t.q_sh;
+      pa.qm = qm;
       pa.proj = t.proj;
       pa.G = p.G;
       pa.Hq = Hq;
@@ -290,7 +290,7 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
   }
   if (c.mode == SD_HIER_TOPK && level == 1) {
     hipLaunchKernelGGL((k_score_rows<T, D>), dim3((p.len1 + 255) / 256, Hq, B), dim3(256), 0, st,
-                       static_cast<const T*>(t.q), t.q_sb, t.q_sh, static_cast<const T*>(t.kg), t.g_sb, t.g_sh,
+                       static_cast<const T*>(t.q), qm, static_cast<const T*>(t.kg), t.g_sb, t.g_sh,
                        t.g_st, at<int32_t>(ws, p.o_cand), p.len1, p.M, p.G, Hq, 0, p.local_mask, at<double>(ws, p.o_s1),
                        p.len1, static_cast<uint32_t*>(nullptr), static_cast<int32_t*>(nullptr), 0);
     return int(hipGetLastError());
@@ -300,7 +300,7 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
   while ((1 << hs) < p.G) ++hs;
   const int64_t rows_per_block = 256 >> hs;
   hipLaunchKernelGGL((k_score_rows<T, D>), dim3((p.len0 + rows_per_block - 1) / rows_per_block, Hk, B), dim3(256), 0,
-                     st, static_cast<const T*>(t.q), t.q_sb, t.q_sh, static_cast<const T*>(meta ? t.kmg : t.kg),
+                     st, static_cast<const T*>(t.q), qm, static_cast<const T*>(meta ? t.kmg : t.kg),
                      meta ? t.mg_sb : t.g_sb, meta ? t.mg_sh : t.g_sh, meta ? t.mg_st : t.g_st,
                      static_cast<const int32_t*>(nullptr), p.len0, p.len0, p.G, Hq, hs, p.local_mask, at<double>(ws, p.o_s0),
                      p.len0, status, at<int32_t>(ws, p.o_arrive), p.n_arrive);

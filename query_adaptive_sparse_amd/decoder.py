@@ -15,13 +15,13 @@ _DTYPES = {torch.float32: N.SD_F32, torch.bfloat16: N.SD_BF16}
 _MODES = {"topk": N.SD_TOPK, "topp": N.SD_TOPP, "hier": N.SD_HIER_TOPK, "coverage": N.SD_COVERAGE}
 
 
-def make_config(*, batch, kv_batch, n_q_heads, n_kv_heads, head_dim, n_ctx, chunk_size, dtype, mode,
+def make_config(*, batch, kv_batch, n_q_heads, n_kv_heads, head_dim, n_ctx, chunk_size, dtype, mode, n_queries=1,
                 route="summary", route_dim=0, top_k=0, top_k_seg=0, seg_size=0, top_p=1.0, select_scale=1.0, tau=0.0,
                 softmax_scale=1.0, keep_first=0, keep_last=0, sink=0, window=0, attend_summary=1,
                 attend_blocks=0, head_masks=False, head_mode=None):
     """An sd_config plus the host array it points to (keep both alive)."""
     cfg = N.sd_config()
-    cfg.batch, cfg.kv_batch = batch, kv_batch
+    cfg.batch, cfg.n_queries, cfg.kv_batch = batch, n_queries, kv_batch
     cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim = n_q_heads, n_kv_heads, head_dim
     cfg.n_ctx, cfg.chunk_size, cfg.seg_size = n_ctx, chunk_size, seg_size
     cfg.route = N.SD_ROUTE_PROXY if route == "proxy" else N.SD_ROUTE_SUMMARY
@@ -46,10 +46,13 @@ def _ptr(t):
 
 
 def make_tensors(q, K, V, Kg=None, Vg=None, Kmg=None, Kp=None, P=None) -> N.sd_tensors:
-    """sd_tensors from torch tensors (q [B][Hq][d]; K, V [Bkv][Hkv][N][d]; ...)."""
+    """sd_tensors from torch tensors (q [B][Hq][d] or [B][T][Hq][d]; K, V [Bkv][Hkv][N][d]; ...)."""
     t = N.sd_tensors()
     t.q = _ptr(q)
-    t.q_sb, t.q_sh = q.stride(0), q.stride(1)
+    if q.dim() == 4:
+        t.q_sb, t.q_st, t.q_sh = q.stride(0), q.stride(1), q.stride(2)
+    else:
+        t.q_sb, t.q_st, t.q_sh = q.stride(0), 0, q.stride(1)
 
     def sb(x):
         return 0 if x.shape[0] == 1 else x.stride(0)
@@ -132,6 +135,12 @@ class SparseDecoder:
         base = ws.data_ptr()
         p = self.params
         B, Hq, Hk = p["batch"], p["n_q_heads"], p["n_kv_heads"]
+        T = p.get("n_queries", 1) or 1
+        G = Hq // Hk
+        # the library orders a sequence's T x Hq query rows by KV group, then token, then head;
+        # rows here come token-major (row t * Hq + h), like the outputs
+        perm = torch.tensor([(h // G) * T * G + t * G + h % G for t in range(T) for h in range(Hq)],
+                            device=ws.device)
 
         def view(ptr, dtype, shape):
             n = 1
@@ -141,14 +150,17 @@ class SparseDecoder:
             es = torch.tensor([], dtype=dtype).element_size()
             return ws[off:off + n * es].view(dtype).view(*shape)
 
+        def rows(x):
+            return x if T == 1 else x.index_select(1, perm)
+
         out = {
-            "scores0": view(v.scores0, torch.float64, (B, Hq, v.len0)),
-            "head_bits": view(v.head_bits, torch.int32, (B, Hq, v.words)),
+            "scores0": rows(view(v.scores0, torch.float64, (B, T * Hq, v.len0))),
+            "head_bits": rows(view(v.head_bits, torch.int32, (B, T * Hq, v.words))),
             "list": view(v.list, torch.int32, (B, Hk, v.n_entries)),
             "count": view(v.count, torch.int32, (B, Hk)),
             "status": view(v.status, torch.int32, (4,)),
         }
         if v.len1:
-            out["scores1"] = view(v.scores1, torch.float64, (B, Hq, v.len1))
-            out["cand1"] = view(v.cand1, torch.int32, (B, Hq, v.len1))
+            out["scores1"] = rows(view(v.scores1, torch.float64, (B, T * Hq, v.len1)))
+            out["cand1"] = rows(view(v.cand1, torch.int32, (B, T * Hq, v.len1)))
         return out

@@ -27,7 +27,7 @@ EXPORTS = ("sparse_decode_init", "sparse_decode_num_levels", "sparse_decode_atte
 
 class sd_config(ctypes.Structure):
     _fields_ = [
-        ("batch", ctypes.c_int32), ("kv_batch", ctypes.c_int32),
+        ("batch", ctypes.c_int32), ("n_queries", ctypes.c_int32), ("kv_batch", ctypes.c_int32),
         ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("n_ctx", ctypes.c_int64), ("chunk_size", ctypes.c_int32), ("seg_size", ctypes.c_int32),
         ("route", ctypes.c_int32), ("route_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
@@ -43,7 +43,7 @@ class sd_config(ctypes.Structure):
 
 class sd_tensors(ctypes.Structure):
     _fields_ = [
-        ("q", ctypes.c_void_p), ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64), ("q_st", ctypes.c_int64),
         ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("kv_sb", ctypes.c_int64), ("kv_sh", ctypes.c_int64), ("kv_st", ctypes.c_int64),
         ("kg", ctypes.c_void_p), ("vg", ctypes.c_void_p),

@@ -24,7 +24,7 @@ COVERAGE = "coverage"  # per-sequence coverage budget (tau), then per-head top-k
 @dataclass(frozen=True)
 class Workload:
     name: str
-    batch: int                 # decode queries (one per sequence)
+    batch: int                 # sequences
     kv_batch: int              # distinct KV caches; 1 = every query reads one cache
     n_q_heads: int
     n_kv_heads: int
@@ -53,6 +53,7 @@ class Workload:
     plants_per_head: int = 0
     zipf_s: float = 0.0
     attend_blocks: int = 0     # persistent attention workgroups (0 = library default)
+    n_queries: int = 1         # adjacent query tokens per sequence (multi-query decode)
     seed: int = 0
 
     # derived -------------------------------------------------------------
@@ -128,7 +129,11 @@ C3_HEADMASK = replace(C3, name="c3_topp_llama31_8b_128k_headmask", head_masks=Tr
 C3_COVERAGE = replace(C3, name="c3_coverage_llama31_8b_128k", mode=COVERAGE, tau=0.2, top_p=1.0)
 C3_ALLSUM = replace(C3, name="c3_topp_llama31_8b_128k_allsum", all_summaries=True)
 C3S_COVERAGE = replace(C3_COVERAGE, name="c3s_coverage", batch=2, kv_batch=2, n_ctx=16384, seed=16)
-VARIANTS = {w.name: w for w in (C3_HEADMASK, C3_ALLSUM, C3_COVERAGE, C3S_COVERAGE)}
+# Multi-query decode: 4 adjacent query tokens per sequence share each KV group's union (4 tokens x
+# 4 heads = 16 query rows per group).
+C3_MQ4 = replace(C3, name="c3_mq4_llama31_8b_128k", n_queries=4)
+C3S_MQ4 = replace(C3_MQ4, name="c3s_mq4", batch=2, kv_batch=2, n_ctx=16384, seed=17)
+VARIANTS = {w.name: w for w in (C3_HEADMASK, C3_ALLSUM, C3_COVERAGE, C3S_COVERAGE, C3_MQ4, C3S_MQ4)}
 
 ALL = {**FULL, **SMALL, **VARIANTS}
 
@@ -144,7 +149,7 @@ def library_params(w: Workload) -> dict:
     """Keyword arguments of query_adaptive_sparse_amd.SparseDecoder for workload ``w``."""
     mode = {TOPK: "topk", TOPP: "topp", HIER: "hier", PROXY_TOPP: "topp", COVERAGE: "coverage"}[w.mode]
     return dict(
-        batch=w.batch, kv_batch=w.kv_batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+        batch=w.batch, n_queries=w.n_queries, kv_batch=w.kv_batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
         head_dim=w.head_dim, n_ctx=w.n_ctx, chunk_size=w.chunk_size, dtype=w.dtype, mode=mode,
         route="proxy" if w.mode == PROXY_TOPP else "summary", route_dim=w.route_dim,
         top_k=w.top_k, top_k_seg=w.top_k_seg, seg_size=w.seg_size, top_p=w.top_p, tau=w.tau,

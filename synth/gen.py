@@ -165,7 +165,9 @@ def make_inputs(w: Workload, device="cpu", seed: int | None = None) -> dict:
     B, Bk, Hq, Hk, d, N = w.batch, w.kv_batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx
     G, M = w.group, w.n_chunks
     out = {"workload": w, "seed": seed}
-    out["q"] = normal((B, Hq, d), seed, T_Q, dt, device)
+    T = w.n_queries
+    # q [B][Hq][d], or [B][T][Hq][d] for T adjacent query tokens per sequence
+    out["q"] = normal((B, Hq, d) if T == 1 else (B, T, Hq, d), seed, T_Q, dt, device)
     out["K"] = normal((Bk, Hk, N, d), seed, T_K, dt, device)
     out["V"] = normal((Bk, Hk, N, d), seed, T_V, dt, device)
     mode = torch.zeros(Hk, dtype=torch.int8)
@@ -183,7 +185,8 @@ def make_inputs(w: Workload, device="cpu", seed: int | None = None) -> dict:
     # summary (gist / landmark) keys and values: built on the host, small
     Kg = normal((Bk, Hk, M, d), seed, T_KG, dt, "cpu")
     Vg = normal((Bk, Hk, M, d), seed, T_VG, dt, "cpu")
-    qc = out["q"].to("cpu")
+    # per sequence, every query row [T * Hq][d], row t * Hq + h; head plants use token 0
+    qc = out["q"].to("cpu").reshape(B, T * Hq, d)
     if w.plant == "gist_align":
         n_p = w.plants_per_head
         for b in range(Bk):
@@ -201,9 +204,10 @@ def make_inputs(w: Workload, device="cpu", seed: int | None = None) -> dict:
                 pi[permutation(seed, T_PERM, b * Hk + g, M)] = torch.arange(M, dtype=torch.float64)
                 ell = -w.zipf_s * torch.log(pi + 1.0)
                 ell = ell - ell.mean()
-                Q = qc[b, g * G:(g + 1) * G].double()               # [G, d]
+                # the group's T x G query rows
+                Q = torch.stack([qc[b, t * Hq + g * G + j] for t in range(T) for j in range(G)]).double()
                 gram = Q @ Q.T
-                wv = Q.T @ torch.linalg.solve(gram, torch.ones(G, dtype=torch.float64))
+                wv = Q.T @ torch.linalg.solve(gram, torch.ones(Q.shape[0], dtype=torch.float64))
                 zg = z[b, g]
                 zperp = zg - (Q.T @ torch.linalg.solve(gram, Q @ zg.T)).T
                 Kg[b, g] = (zperp + math.sqrt(d) * ell[:, None] * wv[None, :]).to(Kg.dtype)

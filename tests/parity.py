@@ -32,12 +32,15 @@ def run_gpu(w, inp, **overrides):
     params.update(overrides)
     dec = SparseDecoder(device="cuda", **params)
     t = lib_tensors(inp)
-    out = torch.full((w.batch, w.n_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
-    lse = torch.full((w.batch, w.n_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+    T = w.n_queries
+    # out [B][T][Hq][d] (T query tokens per sequence), compared as [B][T * Hq][d]
+    out = torch.full((w.batch, T, w.n_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((w.batch, T, w.n_q_heads), float("nan"), dtype=torch.float32, device="cuda")
     dec.step(t, out, lse)
     torch.cuda.synchronize()
     sel = {k: v.cpu() for k, v in dec.selection().items()}
-    return {"out": out.cpu().numpy(), "lse": lse.cpu().numpy(), "sel": sel, "decoder": dec}
+    return {"out": out.cpu().numpy().reshape(w.batch, T * w.n_q_heads, w.head_dim),
+            "lse": lse.cpu().numpy().reshape(w.batch, T * w.n_q_heads), "sel": sel, "decoder": dec}
 
 
 def bits_to_set(words: torch.Tensor) -> np.ndarray:

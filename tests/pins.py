@@ -262,7 +262,7 @@ class _Src:
     def __init__(self, w, rng):
         B, Hq, Hk, d, N = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx
         M = N // w.chunk_size
-        self.q = rng.standard_normal((B, Hq, d))
+        self.q = rng.standard_normal((B, getattr(w, "n_queries", 1) * Hq, d))  # rows t * Hq + h
         self.K = rng.standard_normal((w.kv_batch, Hk, N, d))
         self.V = rng.standard_normal((w.kv_batch, Hk, N, d))
         self.Kg = rng.standard_normal((w.kv_batch, Hk, M, d))
@@ -463,7 +463,52 @@ def pin_coverage(ref, seed=10):
                 assert r["heads"][h].tolist() == _brute_topk(rows[h], k), (b, h)
 
 
+class _TokenView:
+    """The same caches, with query token t's rows of every sequence as a one-token step."""
+
+    def __init__(self, src, t, Hq):
+        self.__dict__.update({k: v for k, v in src.__dict__.items() if k != "q"})
+        self.q = src.q[:, t * Hq:(t + 1) * Hq]
+        self._src = src
+
+    def kv_rows(self, bk, g, rows):
+        return self._src.kv_rows(bk, g, rows)
+
+
+def pin_multi_query(ref, seed=11):
+    """T adjacent query tokens per sequence: each token's rows select exactly what the same
+    queries select in a one-token step; the group union is the union over the tokens'
+    one-token unions; every (token, head) output is dense attention masked to that union
+    (torch SDPA, fp64)."""
+    rng = np.random.default_rng(seed)
+    for w in (_tiny_workload("topk", n_queries=3, keep_last=1), _tiny_workload("topp", n_queries=2, top_p=0.7),
+              _tiny_workload("hier", n_queries=2),
+              _tiny_workload("proxy", n_queries=3, chunk_size=1, top_p=0.6, attend_summary=False)):
+        T, Hq, G = w.n_queries, w.n_q_heads, w.n_q_heads // w.n_kv_heads
+        w1 = SimpleNamespace(**{**vars(w), "n_queries": 1})
+        src = _Src(w, rng)
+        res = ref.decode_step(w, src)
+        views = [_TokenView(src, t, Hq) for t in range(T)]
+        for (b, g), r in res["sel"].items():
+            singles = [ref.select_group(w1, views[t], b, g) for t in range(T)]
+            assert r["union"].tolist() == ref.group_union([x["union"] for x in singles]).tolist(), (w.mode, b, g)
+            for t in range(T):
+                for j in range(G):
+                    h = g * G + j
+                    assert r["heads"][t * Hq + h].tolist() == singles[t]["heads"][h].tolist(), (w.mode, b, t, h)
+            U = r["union"]
+            rows = (U[:, None] * w.chunk_size + np.arange(w.chunk_size)).ravel()
+            mask, Kc, Vc = rows, src.K[b, g], src.V[b, g]
+            if w.attend_summary and w.mode != "proxy":
+                Kc, Vc = np.concatenate([Kc, src.Kg[b, g]]), np.concatenate([Vc, src.Vg[b, g]])
+                mask = np.concatenate([rows, w.n_ctx + U])
+            qi = [t * Hq + g * G + j for t in range(T) for j in range(G)]
+            o2, l2 = _sdpa(src.q[b, qi], Kc, Vc, w.softmax_scale, mask=mask)
+            assert np.allclose(res["out"][b, qi], o2, rtol=1e-11, atol=1e-11), w.mode
+            assert np.allclose(res["lse"][b, qi], l2, rtol=1e-11, atol=1e-11), w.mode
+
+
 ALL_PINS = [pin_golden_scores, pin_golden_proxy, pin_golden_topk, pin_golden_topp, pin_golden_two_level,
             pin_golden_union, pin_golden_attention, pin_scores_exact, pin_bruteforce, pin_topp_minimal,
             pin_reductions, pin_union, pin_masked_dense, pin_dense_limits, pin_step_masked,
-            pin_step_selection, pin_variants, pin_coverage]
+            pin_step_selection, pin_variants, pin_coverage, pin_multi_query]

@@ -47,7 +47,7 @@ BAD = [
     (dict(batch=0), N.SD_EINVAL, "batch"),
     (dict(kv_batch=3), N.SD_EINVAL, "kv_batch"),
     (dict(n_kv_heads=5), N.SD_EINVAL, "multiple"),
-    (dict(n_q_heads=80, n_kv_heads=8), N.SD_EUNSUPPORTED, "group size"),
+    (dict(n_q_heads=136, n_kv_heads=8), N.SD_EUNSUPPORTED, "query rows per KV group"),
     (dict(head_dim=96), N.SD_EUNSUPPORTED, "head_dim"),
     (dict(n_ctx=16384 + 7), N.SD_EINVAL, "divide"),
     (dict(chunk_size=48, n_ctx=48 * 100), N.SD_EUNSUPPORTED, "power of two"),
@@ -104,6 +104,34 @@ def test_init_coverage_needs_summary_route():
     with pytest.raises(N.SparseDecodeError) as e:
         _init(**_params("c5s", mode="coverage", tau=0.1))
     assert e.value.status == N.SD_EUNSUPPORTED
+
+
+MULTI_BAD = [
+    (dict(n_queries=-1), N.SD_EINVAL, "n_queries"),
+    (dict(n_queries=5), N.SD_EUNSUPPORTED, "query rows per KV group"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", MULTI_BAD, ids=[b[2] + str(i) for i, b in enumerate(MULTI_BAD)])
+def test_init_rejects_multi_query(kw, status, msg):
+    with pytest.raises(N.SparseDecodeError) as e:
+        _init(**_params("c3s", **kw))
+    assert e.value.status == status
+    assert msg in str(e.value)
+
+
+def test_init_multi_query_limits():
+    # 16 rows per group on summary routing; proxy routing stops at 8
+    h, n1 = _init(**_params("c3s", n_queries=4))
+    N.sparse_decode_destroy(h)
+    h, n0 = _init(**_params("c3s"))
+    N.sparse_decode_destroy(h)
+    assert n1 > n0  # four query rows per head: per-row scores and bitmaps grow
+    h, _ = _init(**_params("c5s", n_queries=2))
+    N.sparse_decode_destroy(h)
+    with pytest.raises(N.SparseDecodeError) as e:
+        _init(**_params("c5s", n_queries=3))
+    assert e.value.status == N.SD_EUNSUPPORTED and "proxy" in str(e.value)
 
 
 def test_init_null_arguments():

@@ -1,5 +1,6 @@
 """The variants through the HIP path against the oracle (needs an MI355X): per-head masks
-inside the loaded union, every chunk's summary K/V in the context, and the coverage budget."""
+inside the loaded union, every chunk's summary K/V in the context, the coverage budget, and
+multi-query decode (several adjacent query tokens per sequence)."""
 from dataclasses import replace
 
 import numpy as np
@@ -21,7 +22,13 @@ REDUCED = [("c1s", dict(head_masks=True)), ("c2s", dict(head_masks=True)), ("c3s
            ("c3s", dict(mode="coverage", tau=0.0)), ("c3s", dict(mode="coverage", tau=0.999)),
            ("c3s", dict(mode="coverage", tau=0.5, head_masks=True, all_summaries=True)),
            ("c2s", dict(mode="coverage", tau=0.15, chunk_size=1, n_ctx=2048, local_kv_heads=(1, 3), sink=16,
-                        window=100))]
+                        window=100)),
+           # multi-query decode: T adjacent tokens per sequence; T x G rows per group up to 16
+           # (8 rows: hi / lo halves of P in one MFMA; more: two MFMAs)
+           ("c1s", dict(n_queries=2)), ("c1s", dict(n_queries=4)), ("c2s", dict(n_queries=2)),
+           ("c3s", dict(n_queries=3)), ("c4s", dict(n_queries=2)), ("c5s", dict(n_queries=2)),
+           ("c3s", dict(n_queries=4, head_masks=True)), ("c3s", dict(n_queries=2, mode="coverage", tau=0.3)),
+           ("c1s", dict(n_queries=16, n_q_heads=1))]
 
 
 @pytest.mark.parametrize("name,kw", REDUCED, ids=[f"{n}-" + "-".join(k for k in kw) for n, kw in REDUCED])

@@ -36,9 +36,12 @@ MUTATIONS = {
                           "(U[:, None] + np.arange(chunk_size)[None, :])"),
     "forced_not_added": ("U = group_union([U, edge_entries(n_ent, w.keep_first, w.keep_last)])", "U = U"),
     "union_first_head_only": ("per_head.append(sel)", "per_head.append(sel) if not per_head else None"),
-    "wrong_kv_group": ("qh = src.q[b, g * G:(g + 1) * G]\n", "qh = src.q[b, (g * G + 1) % w.n_q_heads:(g * G + 1) % w.n_q_heads + G]\n"),
-    "head_mask_drops_forced": ("S = group_union([heads[g * G + j], forced])", "S = heads[g * G + j]"),
-    "head_mask_wrong_head": ("S = group_union([heads[g * G + j], forced])", "S = group_union([heads[g * G + (j + 1) % G], forced])"),
+    "wrong_kv_group": ("qh = src.q[b, rows_q]\n", "qh = src.q[b, [(x + 1) % w.n_q_heads for x in rows_q]]\n"),
+    "head_mask_drops_forced": ("S = group_union([heads[qi], forced])", "S = heads[qi]"),
+    "head_mask_wrong_head": ("S = group_union([heads[qi], forced])", "S = group_union([heads[rows_q[(j + 1) % len(rows_q)]], forced])"),
+    "multi_query_first_token_only": ("T = getattr(w, \"n_queries\", 1)\n    return", "T = 1\n    return"),
+    "multi_query_rows_head_major": ("return [t * w.n_q_heads + g * G + j for t in range(T) for j in range(G)]",
+                                    "return [(g * G + j) * T + t for t in range(T) for j in range(G)]"),
     "head_mask_ignored": ("masked = getattr(w, \"head_masks\", False) and", "masked = False and"),
     "coverage_cut_inclusive": ("hit = np.nonzero(c > thr)[0]", "hit = np.nonzero(c >= thr)[0] + 1"),
     "coverage_unnormalized": ("imp = imp + mass / math.fsum(mass.tolist())", "imp = imp + mass"),
