@@ -7,25 +7,31 @@
 namespace sd {
 namespace {
 // ---------------------------------------------------------------------------------------------
-// Scores. One thread per (summary row, query head): the head slots of a row sit in adjacent lanes,
-// which load the row's 16-byte pieces together (one fetch from L1), and each thread accumulates
-// its dot product in fp64, one fma per dimension in index order. A product of two bf16 or two
-// fp32 values is exact in fp64, so fma(q, k, acc) equals the CPU's acc + q*k step for step.
+// Scores. A workgroup scores kScoreRows summary rows (or candidate rows) for the query rows
+// ("slots") of one KV group: it stages the slots' queries in LDS as fp64 (exact) and the key rows
+// in LDS (one coalesced pass), then 4 lanes share a row and each runs HPT slots' dot products,
+// one fp64 fma per dimension in index order. A product of two bf16 or two fp32 values is exact in
+// fp64, so fma(q, k, acc) equals the CPU's acc + q*k step for step. A lane converts each key
+// element once for its HPT independent chains, which also hides the fma latency.
 // Block (0, 0, 0) also clears the device status words and the per-group arrival counters of the
 // selection.
 // ---------------------------------------------------------------------------------------------
-template <typename T, int D>
+constexpr int kScoreRows = 64;
+
+template <typename T, int D, int HPT>
 __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRows qm,
                                                     const T* __restrict__ keys, int64_t k_sb, int64_t k_sh,
                                                     int64_t k_st, const int32_t* __restrict__ cand,
-                                                    int64_t n_rows, int64_t n_keys, int G, int Hq, int hs_shift,
+                                                    int64_t n_rows, int64_t n_keys, int G, int Hq,
                                                     uint64_t local_mask, double* __restrict__ out, int64_t out_len,
                                                     uint32_t* __restrict__ status, int32_t* __restrict__ arrivals,
                                                     int n_groups) {
   constexpr int EPV = 16 / int(sizeof(T));
-  constexpr int PPR = D / EPV;
-  constexpr int QW = D + 4;  // padded query row: the head slots' reads fall in distinct banks
-  __shared__ float qs[kMaxGroup * QW];
+  constexpr int PPR = D / EPV;                          // 16-byte pieces per row
+  constexpr int QW = D + 2;                             // padded fp64 query row
+  constexpr int KW = (D * int(sizeof(T)) + 16) / 16;    // padded key row, in 16-byte pieces
+  __shared__ double qs[kMaxGroup * QW];
+  __shared__ uint4 ks[kScoreRows * KW];
   const int b = blockIdx.z, y = blockIdx.y, tid = threadIdx.x;
   if (status && blockIdx.x == 0 && y == 0 && b == 0) {
     if (tid < 16) status[tid] = 0;
@@ -35,35 +41,60 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRo
   if ((local_mask >> g) & 1) return;
   const int h0 = cand ? y : y * G;
   const int nh = cand ? 1 : G;
+  const int64_t r0 = int64_t(blockIdx.x) * kScoreRows;
+  // key rows of this workgroup, 16 bytes per thread per step (rows past the end repeat the last),
+  // loaded first; the queries are staged while they are in flight
+  constexpr int KPT = kScoreRows * PPR / 256;
+  uint4 kreg[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int i = tid + 256 * k, r = i / PPR, pc = i - r * PPR;
+    int64_t row = r0 + r < n_rows ? r0 + r : n_rows - 1;
+    int64_t src = cand ? int64_t(cand[(int64_t(b) * Hq + h0) * out_len + row]) : row;
+    src = src < 0 ? 0 : (src < n_keys ? src : n_keys - 1);
+    kreg[k] = ld16(keys + b * k_sb + int64_t(g) * k_sh + src * k_st + pc * EPV);
+  }
   for (int i = tid; i < nh * D; i += 256) {
     const int j = i / D, dd = i - j * D;
-    qs[j * QW + dd] = elem_f32<T>(q + q_offset(qm, b, h0 + j) + dd);
+    qs[j * QW + dd] = double(elem_f32<T>(q + q_offset(qm, b, h0 + j) + dd));
+  }
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int i = tid + 256 * k, r = i / PPR, pc = i - r * PPR;
+    ks[r * KW + pc] = kreg[k];
   }
   __syncthreads();
-  const int j = tid & ((1 << hs_shift) - 1);
-  const int64_t row = int64_t(blockIdx.x) * (256 >> hs_shift) + (tid >> hs_shift);
-  if (row >= n_rows || j >= nh) return;
-  int64_t src = cand ? int64_t(cand[(int64_t(b) * Hq + h0) * out_len + row]) : row;
-  src = src < 0 ? 0 : (src < n_keys ? src : n_keys - 1);
-  const T* kr = keys + b * k_sb + int64_t(g) * k_sh + src * k_st;
-  uint4 piece[PPR];
+  const int r = tid >> 2, j0 = (tid & 3) * HPT;
+  const int64_t row = r0 + r;
+  if (row >= n_rows || j0 >= nh) return;
+  const uint4* kr = ks + r * KW;
+  double acc[HPT];
+  const double* qrow[HPT];
 #pragma unroll
-  for (int pc = 0; pc < PPR; ++pc) piece[pc] = ld16(kr + pc * EPV);
-  const float* qj = qs + j * QW;
-  double acc = 0.0;
-#pragma unroll
+  for (int u = 0; u < HPT; ++u) {
+    acc[u] = 0.0;
+    qrow[u] = qs + min(j0 + u, nh - 1) * QW;  // slots past the group read a valid row; not stored
+  }
+#pragma unroll 2
   for (int pc = 0; pc < PPR; ++pc) {
-    const T* e = reinterpret_cast<const T*>(&piece[pc]);
+    const uint4 piece = kr[pc];
+    const T* e = reinterpret_cast<const T*>(&piece);
+    double kd[EPV];
 #pragma unroll
-    for (int u4 = 0; u4 < EPV; u4 += 4) {
-      const float4 q4 = *reinterpret_cast<const float4*>(qj + pc * EPV + u4);
-      acc = fma(double(q4.x), double(elem_f32<T>(e + u4 + 0)), acc);
-      acc = fma(double(q4.y), double(elem_f32<T>(e + u4 + 1)), acc);
-      acc = fma(double(q4.z), double(elem_f32<T>(e + u4 + 2)), acc);
-      acc = fma(double(q4.w), double(elem_f32<T>(e + u4 + 3)), acc);
+    for (int x = 0; x < EPV; ++x) kd[x] = double(elem_f32<T>(e + x));
+#pragma unroll
+    for (int u = 0; u < HPT; ++u) {
+#pragma unroll
+      for (int x = 0; x < EPV; x += 2) {
+        const double2 q2 = *reinterpret_cast<const double2*>(qrow[u] + pc * EPV + x);
+        acc[u] = fma(q2.x, kd[x], acc[u]);
+        acc[u] = fma(q2.y, kd[x + 1], acc[u]);
+      }
     }
   }
-  out[(int64_t(b) * Hq + h0 + j) * out_len + row] = acc;
+#pragma unroll
+  for (int u = 0; u < HPT; ++u)
+    if (j0 + u < nh) out[(int64_t(b) * Hq + h0 + j0 + u) * out_len + row] = acc[u];
 }
 
 // Projected query q_p = q P (d -> 16) per scored head, fp64, index order. A bf16 or fp32 query
@@ -289,21 +320,29 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
     return int(hipGetLastError());
   }
   if (c.mode == SD_HIER_TOPK && level == 1) {
-    hipLaunchKernelGGL((k_score_rows<T, D>), dim3((p.len1 + 255) / 256, Hq, B), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_score_rows<T, D, 1>), dim3((p.len1 + kScoreRows - 1) / kScoreRows, Hq, B), dim3(256), 0, st,
                        static_cast<const T*>(t.q), qm, static_cast<const T*>(t.kg), t.g_sb, t.g_sh,
-                       t.g_st, at<int32_t>(ws, p.o_cand), p.len1, p.M, p.G, Hq, 0, p.local_mask, at<double>(ws, p.o_s1),
+                       t.g_st, at<int32_t>(ws, p.o_cand), p.len1, p.M, p.G, Hq, p.local_mask, at<double>(ws, p.o_s1),
                        p.len1, static_cast<uint32_t*>(nullptr), static_cast<int32_t*>(nullptr), 0);
     return int(hipGetLastError());
   }
   const bool meta = c.mode == SD_HIER_TOPK;
-  int hs = 0;
-  while ((1 << hs) < p.G) ++hs;
-  const int64_t rows_per_block = 256 >> hs;
-  hipLaunchKernelGGL((k_score_rows<T, D>), dim3((p.len0 + rows_per_block - 1) / rows_per_block, Hk, B), dim3(256), 0,
-                     st, static_cast<const T*>(t.q), qm, static_cast<const T*>(meta ? t.kmg : t.kg),
-                     meta ? t.mg_sb : t.g_sb, meta ? t.mg_sh : t.g_sh, meta ? t.mg_st : t.g_st,
-                     static_cast<const int32_t*>(nullptr), p.len0, p.len0, p.G, Hq, hs, p.local_mask, at<double>(ws, p.o_s0),
-                     p.len0, status, at<int32_t>(ws, p.o_arrive), p.n_arrive);
+  // query slots per lane (4 lanes per row): 1 up to 4 query rows per group, 2 up to 8, 4 up to 16
+  const int hpt = p.G <= 4 ? 1 : (p.G <= 8 ? 2 : 4);
+  const dim3 grid((p.len0 + kScoreRows - 1) / kScoreRows, Hk, B);
+  const T* keys = static_cast<const T*>(meta ? t.kmg : t.kg);
+  const int64_t ksb = meta ? t.mg_sb : t.g_sb, ksh = meta ? t.mg_sh : t.g_sh, kst = meta ? t.mg_st : t.g_st;
+#define SD_SCORE_ROWS(HPT)                                                                                       \
+  hipLaunchKernelGGL((k_score_rows<T, D, HPT>), grid, dim3(256), 0, st, static_cast<const T*>(t.q), qm, keys, ksb, \
+                     ksh, kst, static_cast<const int32_t*>(nullptr), p.len0, p.len0, p.G, Hq, p.local_mask,          \
+                     at<double>(ws, p.o_s0), p.len0, status, at<int32_t>(ws, p.o_arrive), p.n_arrive)
+  if (hpt == 1)
+    SD_SCORE_ROWS(1);
+  else if (hpt == 2)
+    SD_SCORE_ROWS(2);
+  else
+    SD_SCORE_ROWS(4);
+#undef SD_SCORE_ROWS
   if (p.long0)
     hipLaunchKernelGGL(k_row_minmax, dim3(p.score_blocks0, Hq, B), dim3(256), 0, st, at<double>(ws, p.o_s0),
                        p.len0, p.G, Hq, p.local_mask, at<double>(ws, p.o_pmax), at<double>(ws, p.o_pmin),
