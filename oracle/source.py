@@ -38,3 +38,24 @@ class HostSource:
         Kr = self._K[bk, g].index_select(0, idx)
         Vr = self._V[bk, g].index_select(0, idx)
         return _f64(Kr), _f64(Vr)
+
+
+class PrefillSource:
+    """Inputs of one prefill step as the oracle reads them: Q [B][Hq][L][d] and K, V
+    [B][Hkv][L][d] on any device; rows are widened to fp64 on demand."""
+
+    def __init__(self, inputs: dict):
+        self._Q, self._K, self._V = inputs["Q"], inputs["K"], inputs["V"]
+
+    def _rows(self, t, b, h, rows):
+        idx = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=t.device)
+        return _f64(t[b, h].index_select(0, idx))
+
+    def q_rows(self, b: int, h: int, rows) -> np.ndarray:
+        return self._rows(self._Q, b, h, rows)
+
+    def k_all(self, b: int, g: int) -> np.ndarray:
+        return _f64(self._K[b, g])
+
+    def kv_rows(self, b: int, g: int, rows):
+        return self._rows(self._K, b, g, rows), self._rows(self._V, b, g, rows)

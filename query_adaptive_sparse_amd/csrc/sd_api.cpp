@@ -311,6 +311,118 @@ sd_status sparse_decode_selection_view(const sd_handle* h, void* ws, sd_selectio
   return ok();
 }
 
+// ---- Token-Sparse prefill
+sd_status sparse_prefill_init(const sp_config* cfg, sp_handle** out, size_t* workspace_bytes) {
+  if (!cfg || !out || !workspace_bytes) return fail(SD_EINVAL, "prefill init: NULL argument");
+  *out = nullptr;
+  const sp_config& c = *cfg;
+  if (c.batch < 1) return fail(SD_EINVAL, "batch must be >= 1 (got %d)", c.batch);
+  if (c.n_q_heads < 1 || c.n_kv_heads < 1 || c.n_q_heads % c.n_kv_heads)
+    return fail(SD_EINVAL, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", c.n_q_heads, c.n_kv_heads);
+  if (c.head_dim != 128) return fail(SD_EUNSUPPORTED, "prefill: head_dim must be 128 (got %d)", c.head_dim);
+  if (c.kv_dtype != SD_BF16) return fail(SD_EUNSUPPORTED, "prefill: kv_dtype must be SD_BF16");
+  if (c.window < 1) return fail(SD_EINVAL, "window must be >= 1 (got %d)", c.window);
+  if (c.window > sd::kPfMaxWindow) return fail(SD_EUNSUPPORTED, "window must be <= %d (got %d)", sd::kPfMaxWindow, c.window);
+  if (c.seq_len < c.window || c.seq_len >= (int64_t(1) << 31))
+    return fail(SD_EINVAL, "seq_len must be in [window, 2^31) (got %lld)", (long long)c.seq_len);
+  if (!(c.tau >= 0.0) || !(c.tau < 1.0)) return fail(SD_EINVAL, "tau must be in [0, 1) (got %g)", c.tau);
+  if (!(c.softmax_scale > 0.0) || !std::isfinite(c.softmax_scale))
+    return fail(SD_EINVAL, "softmax_scale must be finite and > 0 (got %g)", c.softmax_scale);
+  if (int64_t(c.batch) * c.n_q_heads * c.seq_len * c.window >= (int64_t(1) << 40))
+    return fail(SD_EUNSUPPORTED, "batch x heads x seq_len x window too large");
+  sp_handle* h = new (std::nothrow) sp_handle();
+  if (!h) return fail(SD_EINVAL, "prefill init: out of host memory");
+  sd::PrefillPlan& p = h->plan;
+  p.cfg = c;
+  p.G = c.n_q_heads / c.n_kv_heads;
+  p.L = c.seq_len;
+  p.words = (p.L + 31) / 32;
+  p.nslab = int32_t((p.L + sd::kPfSlab - 1) / sd::kPfSlab);
+  p.nkb = int32_t((p.L + sd::kPfKeyBlock - 1) / sd::kPfKeyBlock);
+  const int64_t B = c.batch, Hq = c.n_q_heads, L = p.L, W = c.window;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + std::max<size_t>(bytes, 1));
+    return o;
+  };
+  p.o_status = take(64);
+  p.o_S = take(size_t(B * Hq * L * W) * 8);
+  p.o_pmq = take(size_t(B * Hq * p.nkb * W) * 8);
+  p.o_M = take(size_t(B * Hq * W) * 8);
+  p.o_zq = take(size_t(B * Hq * p.nslab * W) * 8);
+  p.o_imp = take(size_t(B * Hq * L) * 8);
+  p.o_pmax = take(size_t(B * Hq * p.nslab) * 8);
+  p.o_pmin = take(size_t(B * Hq * p.nslab) * 8);
+  p.o_gimp = take(size_t(B * L) * 8);
+  p.o_gpmax = take(size_t(B * p.nslab) * 8);
+  p.o_gpmin = take(size_t(B * p.nslab) * 8);
+  p.o_long = take(sd::long_rows_scratch(B * Hq, L));
+  p.o_bbits = take(size_t(B * p.words) * 4);
+  p.o_budget = take(size_t(B) * 4);
+  p.o_bits = take(size_t(B * Hq * p.words) * 4);
+  p.o_list = take(size_t(B * Hq * L) * 4);
+  p.ws_bytes = off;
+  *out = h;
+  *workspace_bytes = p.ws_bytes;
+  return ok();
+}
+
+namespace {
+sd_status check_prefill_tensors(const sd::PrefillPlan& p, const sp_tensors* t) {
+  if (!t) return fail(SD_EINVAL, "prefill: tensors is NULL");
+  if (!t->q || !t->k || !t->v || !aligned16(t->q) || !aligned16(t->k) || !aligned16(t->v))
+    return fail(SD_EINVAL, "prefill: q, k and v must be non-NULL 16-byte aligned pointers");
+  const int64_t d = p.cfg.head_dim;
+  auto ok8 = [](int64_t x) { return x >= 0 && x % 8 == 0; };
+  if (!ok8(t->q_sb) || !ok8(t->q_sh) || !ok8(t->q_st) || t->q_st < d)
+    return fail(SD_EINVAL, "prefill: q strides must keep 16-byte aligned rows");
+  if (!ok8(t->kv_sb) || !ok8(t->kv_sh) || !ok8(t->kv_st) || t->kv_st < d)
+    return fail(SD_EINVAL, "prefill: k / v strides must keep 16-byte aligned rows");
+  return SD_OK;
+}
+}  // namespace
+
+sd_status sparse_prefill_select(const sp_handle* h, const sp_tensors* t, void* ws, void* stream) {
+  if (!h) return fail(SD_EINVAL, "prefill select: NULL handle");
+  if (!ws) return fail(SD_EWORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(SD_EWORKSPACE, "workspace not 256-byte aligned");
+  sd_status st = check_prefill_tensors(h->plan, t);
+  if (st != SD_OK) return st;
+  int e = sd::launch_prefill_select(h->plan, *t, static_cast<char*>(ws), stream);
+  if (e) return fail(SD_EHIP, "prefill select: HIP error %d (%s)", e, sd::hip_error_string(e));
+  return ok();
+}
+
+sd_status sparse_prefill_attend(const sp_handle* h, const sp_tensors* t, void* ws, float* out, void* stream) {
+  if (!h) return fail(SD_EINVAL, "prefill attend: NULL handle");
+  if (!ws) return fail(SD_EWORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(SD_EWORKSPACE, "workspace not 256-byte aligned");
+  sd_status st = check_prefill_tensors(h->plan, t);
+  if (st != SD_OK) return st;
+  if (!out || !aligned16(out)) return fail(SD_EINVAL, "prefill attend: out must be a non-NULL 16-byte aligned pointer");
+  int e = sd::launch_prefill_attend(h->plan, *t, static_cast<char*>(ws), out, stream);
+  if (e) return fail(SD_EHIP, "prefill attend: HIP error %d (%s)", e, sd::hip_error_string(e));
+  return ok();
+}
+
+sd_status sparse_prefill_view(const sp_handle* h, void* ws, sp_view* v) {
+  if (!h || !v) return fail(SD_EINVAL, "prefill view: NULL argument");
+  if (!ws) return fail(SD_EWORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(SD_EWORKSPACE, "workspace not 256-byte aligned");
+  const sd::PrefillPlan& p = h->plan;
+  char* w = static_cast<char*>(ws);
+  v->importance = reinterpret_cast<const double*>(w + p.o_imp);
+  v->budget = reinterpret_cast<const int32_t*>(w + p.o_budget);
+  v->head_bits = reinterpret_cast<const uint32_t*>(w + p.o_bits);
+  v->words = p.words;
+  v->list = reinterpret_cast<const int32_t*>(w + p.o_list);
+  v->status = reinterpret_cast<const uint32_t*>(w + p.o_status);
+  return ok();
+}
+
+void sparse_prefill_destroy(sp_handle* h) { delete h; }
+
 const char* sparse_decode_last_error(void) { return g_err; }
 
 void sparse_decode_destroy(sd_handle* h) { delete h; }

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/sparse_decode.h"
+#include "../../include/sparse_prefill.h"
 
 namespace sd {
 
@@ -74,15 +75,61 @@ struct RowInfo {
   int32_t pad;
 };
 
-// Kernel launchers (sd_kernels.hip). Each returns hipSuccess or the launch error.
+// Kernel launchers (sd_score.hip, sd_select.hip, sd_attend.hip). Each returns hipSuccess or the
+// launch error.
 int launch_score(const Plan& p, const sd_tensors& t, int level, char* ws, void* stream);
 int launch_select(const Plan& p, int level, char* ws, void* stream);
 int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream);
 int launch_combine(const Plan& p, char* ws, float* out, float* lse, void* stream);
 const char* hip_error_string(int code);
 
+// Long-row selection (histogram passes) over caller-given fp64 rows s [B][H][len]: top-k (k, or
+// kbudget[b] for every row of sequence b when non-null) with unit weights, or top-p of the
+// weights exp(scale (s - smax)), or (ident) of the values themselves as masses (s >= 0).
+// pmax / pmin hold each row's max / min per kMinMaxBlock entries. Writes the selection bitmaps
+// bits [B][H][words] (whole words) and raises status[0] for an incomplete row.
+struct LongRows {
+  const double* s;
+  int64_t len;
+  int B, H;
+  int topp, ident, k;
+  const int32_t* kbudget;
+  double p, scale;
+  const double* pmax;
+  const double* pmin;
+  int nblk;
+  char* scratch;  // long_rows_scratch(B * H, len) bytes, 256-byte aligned
+  uint32_t* bits;
+  int64_t words;
+  uint32_t* status;
+};
+size_t long_rows_scratch(int64_t rows, int64_t len);
+int launch_long_rows(const LongRows& r, void* stream);
+
+// ---- Token-Sparse prefill
+constexpr int kPfSlab = kMinMaxBlock;  // keys per importance workgroup (and per partial max / min)
+constexpr int kPfKeyBlock = 64;        // keys per proxy-score workgroup
+constexpr int kPfMaxWindow = 64;
+constexpr int kPfQueryBlock = 64;      // compact queries per attention workgroup
+
+struct PrefillPlan {
+  sp_config cfg;
+  int32_t G;
+  int64_t L, words;
+  int32_t nslab, nkb;  // importance slabs, proxy-score key blocks
+  size_t o_status, o_S, o_pmq, o_M, o_zq, o_imp, o_pmax, o_pmin, o_gimp, o_gpmax, o_gpmin;
+  size_t o_long, o_bbits, o_budget, o_bits, o_list;
+  size_t ws_bytes;
+};
+int launch_prefill_select(const PrefillPlan& p, const sp_tensors& t, char* ws, void* stream);
+int launch_prefill_attend(const PrefillPlan& p, const sp_tensors& t, char* ws, float* out, void* stream);
+
 }  // namespace sd
 
 struct sd_handle {
   sd::Plan plan;
+};
+
+struct sp_handle {
+  sd::PrefillPlan plan;
 };

@@ -509,6 +509,8 @@ struct LongArgs {
   int Hq, G;
   uint64_t local_mask;
   int topp, k;
+  int ident;               // top-p of the values themselves (masses), not of exp weights
+  const int32_t* kbudget;  // top-k per sequence (row / Hq), or NULL: k
   double p, scale;
   RowInfo* info;
   const double* pmax;  // [row][nblk] partial max / min of the scores
@@ -539,8 +541,9 @@ __device__ __forceinline__ int fine_bin(double d, int c1) {
   return c2 < 0 ? 0 : (c2 < kBins2 - 1 ? c2 : kBins2 - 1);
 }
 __device__ __forceinline__ double long_weight(const LongArgs& a, double smax, double s) {
-  return a.topp ? exp(a.scale * s - a.scale * smax) : 1.0;
+  return a.topp ? (a.ident ? s : exp(a.scale * s - a.scale * smax)) : 1.0;
 }
+__device__ __forceinline__ int long_k(const LongArgs& a, int b) { return a.kbudget ? a.kbudget[b] : a.k; }
 
 // Inclusive scan of one double per thread over an NT-thread workgroup, in thread order; `wtot`
 // holds NT/64 doubles of LDS. Returns the inclusive value; *total = the workgroup's sum.
@@ -592,7 +595,7 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
   }
   const double range = smax - smin;
   const double binscale = range > 0.0 ? double(kBins1) / range : 0.0;
-  const bool all = a.topp ? (a.p >= 1.0) : (int64_t(a.k) >= a.len);
+  const bool all = a.topp ? (a.p >= 1.0) : (int64_t(long_k(a, b)) >= a.len);
   if (slab == 0 && tid == 0) {
     RowInfo ri = {};
     ri.smax = smax;
@@ -664,7 +667,7 @@ __global__ __launch_bounds__(kFindThreads) void k_long_find1(LongArgs a) {
   }
   double Z;
   const double incl = block_scan<kFindThreads>(m, wtot, &Z);
-  const double target = a.topp ? a.p * Z : double(a.k);
+  const double target = a.topp ? a.p * Z : double(long_k(a, b));
   if (tid == 0) hit_bin = 0x7FFFFFFF;
   __syncthreads();
   const double excl = incl - m;
@@ -1360,6 +1363,8 @@ LongArgs long_args(const Plan& p, char* ws) {
   a.local_mask = p.local_mask;
   a.topp = c.mode == SD_TOPP;
   a.k = c.top_k;
+  a.ident = 0;
+  a.kbudget = nullptr;
   a.p = c.top_p;
   a.scale = c.mode == SD_TOPP ? c.select_scale : 1.0;
   a.info = at<RowInfo>(ws, p.o_info);
@@ -1476,6 +1481,70 @@ int launch_select(const Plan& p, int level, char* ws, void* stream) {
   int e = int(hipGetLastError());
   if (e) return e;
   return union_impl(p, ws, st);
+}
+
+// ---- long-row selection over caller-given rows (the prefill path's budget and per-head top-k)
+namespace {
+struct LongScratch {
+  size_t info, h1m, h1c, cbin, cidx, ccnt, total;
+};
+LongScratch long_scratch_layout(int64_t rows, int64_t len) {
+  const int64_t nb1 = (len + kLongBlock - 1) / kLongBlock;
+  LongScratch l;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + (bytes > 0 ? bytes : 1) + 255) & ~size_t(255);
+    return o;
+  };
+  l.info = take(size_t(rows) * sizeof(RowInfo));
+  l.h1m = take(size_t(rows * nb1 * kBins1) * 8);
+  l.h1c = take(size_t(rows * nb1 * kBins1) * 4);
+  l.cbin = take(size_t(rows * ((len + 7) & ~int64_t(7))) * 2);
+  l.cidx = take(size_t(rows * nb1 * kResolveCap) * 4);
+  l.ccnt = take(size_t(rows * nb1) * 4);
+  l.total = off;
+  return l;
+}
+}  // namespace
+
+size_t long_rows_scratch(int64_t rows, int64_t len) { return long_scratch_layout(rows, len).total; }
+
+int launch_long_rows(const LongRows& r, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const LongScratch l = long_scratch_layout(int64_t(r.B) * r.H, r.len);
+  LongArgs a;
+  a.s0 = r.s;
+  a.len = r.len;
+  a.Hq = r.H;
+  a.G = 1;
+  a.local_mask = 0;
+  a.topp = r.topp;
+  a.k = r.k;
+  a.ident = r.ident;
+  a.kbudget = r.kbudget;
+  a.p = r.p;
+  a.scale = r.scale;
+  a.info = reinterpret_cast<RowInfo*>(r.scratch + l.info);
+  a.pmax = r.pmax;
+  a.pmin = r.pmin;
+  a.nblk = r.nblk;
+  a.nb1 = int((r.len + kLongBlock - 1) / kLongBlock);
+  a.h1m = reinterpret_cast<double*>(r.scratch + l.h1m);
+  a.h1c = reinterpret_cast<uint32_t*>(r.scratch + l.h1c);
+  a.cbin = reinterpret_cast<uint16_t*>(r.scratch + l.cbin);
+  a.cstride = (r.len + 7) & ~int64_t(7);
+  a.cidx = reinterpret_cast<int32_t*>(r.scratch + l.cidx);
+  a.ccnt = reinterpret_cast<int32_t*>(r.scratch + l.ccnt);
+  a.bits = r.bits;
+  a.words = r.words;
+  a.status = r.status;
+  const dim3 rows(r.H, r.B), blocks(a.nb1, r.H, r.B);
+  hipLaunchKernelGGL(k_long_hist, blocks, dim3(kLongThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_find1, rows, dim3(kFindThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_mark, blocks, dim3(kLongThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_resolve, rows, dim3(kResolveThreads), 0, st, a);
+  return int(hipGetLastError());
 }
 
 }  // namespace sd

@@ -1,4 +1,4 @@
-"""ctypes binding of libsparse_decode.so (include/sparse_decode.h), same names.
+"""ctypes binding of libsparse_decode.so (include/sparse_decode.h, include/sparse_prefill.h), same names.
 
 Argument marshalling only: structs mirror the C ABI, functions forward to the
 library and raise on a non-OK status. The library must be built
@@ -22,7 +22,9 @@ STATUS_NAMES = {0: "SD_OK", 1: "SD_EINVAL", 2: "SD_EUNSUPPORTED", 3: "SD_EWORKSP
 EXPORTS = ("sparse_decode_init", "sparse_decode_num_levels", "sparse_decode_attend_blocks",
            "sparse_decode_score_chunks", "sparse_decode_select",
            "sparse_decode_attend", "sparse_decode_combine", "sparse_decode_selection_view",
-           "sparse_decode_last_error", "sparse_decode_destroy")
+           "sparse_decode_last_error", "sparse_decode_destroy",
+           "sparse_prefill_init", "sparse_prefill_select", "sparse_prefill_attend", "sparse_prefill_view",
+           "sparse_prefill_destroy")
 
 
 class sd_config(ctypes.Structure):
@@ -66,6 +68,30 @@ class sd_selection_view(ctypes.Structure):
     ]
 
 
+class sp_config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("seq_len", ctypes.c_int64), ("window", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32), ("tau", ctypes.c_double), ("softmax_scale", ctypes.c_double),
+    ]
+
+
+class sp_tensors(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64), ("q_st", ctypes.c_int64),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("kv_sb", ctypes.c_int64), ("kv_sh", ctypes.c_int64), ("kv_st", ctypes.c_int64),
+    ]
+
+
+class sp_view(ctypes.Structure):
+    _fields_ = [
+        ("importance", ctypes.c_void_p), ("budget", ctypes.c_void_p),
+        ("head_bits", ctypes.c_void_p), ("words", ctypes.c_int64),
+        ("list", ctypes.c_void_p), ("status", ctypes.c_void_p),
+    ]
+
+
 class SparseDecodeError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
@@ -103,6 +129,16 @@ def lib() -> ctypes.CDLL:
         L.sparse_decode_last_error.restype = ctypes.c_char_p
         L.sparse_decode_destroy.argtypes = [vp]
         L.sparse_decode_destroy.restype = None
+        L.sparse_prefill_init.argtypes = [ctypes.POINTER(sp_config), ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_size_t)]
+        L.sparse_prefill_init.restype = st
+        L.sparse_prefill_select.argtypes = [vp, ctypes.POINTER(sp_tensors), vp, vp]
+        L.sparse_prefill_select.restype = st
+        L.sparse_prefill_attend.argtypes = [vp, ctypes.POINTER(sp_tensors), vp, vp, vp]
+        L.sparse_prefill_attend.restype = st
+        L.sparse_prefill_view.argtypes = [vp, vp, ctypes.POINTER(sp_view)]
+        L.sparse_prefill_view.restype = st
+        L.sparse_prefill_destroy.argtypes = [vp]
+        L.sparse_prefill_destroy.restype = None
         _lib = L
     return _lib
 
@@ -156,3 +192,29 @@ def sparse_decode_last_error() -> str:
 
 def sparse_decode_destroy(handle):
     lib().sparse_decode_destroy(handle)
+
+
+def sparse_prefill_init(cfg: sp_config):
+    """Returns (handle, workspace_bytes)."""
+    h = ctypes.c_void_p()
+    n = ctypes.c_size_t()
+    _check(lib().sparse_prefill_init(ctypes.byref(cfg), ctypes.byref(h), ctypes.byref(n)))
+    return h, n.value
+
+
+def sparse_prefill_select(handle, tensors: sp_tensors, ws: int, stream: int):
+    _check(lib().sparse_prefill_select(handle, ctypes.byref(tensors), ws, stream))
+
+
+def sparse_prefill_attend(handle, tensors: sp_tensors, ws: int, out: int, stream: int):
+    _check(lib().sparse_prefill_attend(handle, ctypes.byref(tensors), ws, out, stream))
+
+
+def sparse_prefill_view(handle, ws: int) -> sp_view:
+    v = sp_view()
+    _check(lib().sparse_prefill_view(handle, ws, ctypes.byref(v)))
+    return v
+
+
+def sparse_prefill_destroy(handle):
+    lib().sparse_prefill_destroy(handle)

@@ -141,8 +141,40 @@ ALL = {**FULL, **SMALL, **VARIANTS}
 BENCH = C3
 
 
-def get(name: str) -> Workload:
-    return ALL[name]
+# ---------------------------------------------------------------------------------------------
+# Token-Sparse prefill (compress -> attend -> scatter) workloads.
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    seq_len: int               # L tokens of the prompt
+    window: int                # W most recent queries of the proxy attention map
+    tau: float                 # coverage threshold of the global budget
+    softmax_scale: float
+    dtype: str = "bf16"
+    beta: float = 4.0          # plant: every query of a KV group gets beta * u_g ...
+    zipf_s: float = 1.1        # ... and key j gets gamma_j * u_g, a Zipf(s) logit profile
+    seed: int = 0
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+
+# The 128K prompt of the Llama-3.1-8B shape (the page's 128K setting); 20% of the importance mass
+# of the proxy map is cut.
+P1 = PrefillWorkload(name="p1_tsa_llama31_8b_128k", batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                     seq_len=131072, window=64, tau=0.2, softmax_scale=_inv_sqrt(128), seed=31)
+P1S = replace(P1, name="p1s", seq_len=4096, window=64, seed=32)
+P1T = replace(P1, name="p1t", batch=2, n_q_heads=8, n_kv_heads=2, seq_len=1024, window=32, tau=0.3, seed=33)
+PREFILL = {w.name: w for w in (P1, P1S, P1T)}
+
+
+def get(name: str):
+    return ALL[name] if name in ALL else PREFILL[name]
 
 
 def library_params(w: Workload) -> dict:

@@ -27,7 +27,15 @@ the generator, not of the method):
 * proxy keys: ``Kp = fp16(K @ P)`` with ``P`` an N(0,1) d x r matrix per KV head,
   summed in fp64 in index order with separate multiply and add.
 
-No function here computes anything the decode path computes.
+Prefill inputs (``make_prefill_inputs``): Q [B][Hq][L][d], K and V [B][Hkv][L][d],
+N(0,1) as above; per (sequence, KV group) a unit direction ``u_g`` (normal draw,
+normalised) is added as ``beta * u_g`` to every query of the group and as
+``gamma_j * u_g`` to key j, with ``gamma_j = sqrt(d) * l_j / beta`` and ``l_j`` the
+centred Zipf(s) logit profile of a seeded permutation, so each head's attention
+mass over the keys is Zipf-like. The plant is added in fp64 and rounded once to
+bf16 on the device that generates the inputs; the oracle reads those tensors.
+
+No function here computes anything the decode or prefill path computes.
 """
 from __future__ import annotations
 
@@ -37,13 +45,14 @@ from functools import lru_cache
 import numpy as np
 import torch
 
-from .configs import HIER, PROXY_TOPP, Workload
+from .configs import HIER, PROXY_TOPP, PrefillWorkload, Workload
 
 _M32 = 0xFFFFFFFF
 
 # array tags
 T_Q, T_K, T_V, T_KG, T_VG, T_KMG, T_P = 1, 2, 3, 4, 5, 6, 7
 T_PERM, T_OFF, T_Z = 8, 9, 10
+T_PQ, T_PK, T_PV, T_PU, T_PPERM = 11, 12, 13, 14, 15  # prefill
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "f64": torch.float64}
 
@@ -229,3 +238,31 @@ def make_inputs(w: Workload, device="cpu", seed: int | None = None) -> dict:
     out["Kg"] = Kg.to(device)
     out["Vg"] = Vg.to(device)
     return out
+
+
+def make_prefill_inputs(w: PrefillWorkload, device="cpu", seed: int | None = None) -> dict:
+    """Q, K, V of one prefill step of workload ``w`` as tensors on ``device``."""
+    seed = w.seed if seed is None else seed
+    B, Hq, Hk, d, L, G = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.seq_len, w.group
+    dt = _DT[w.dtype]
+    U = normal((B, Hk, d), seed, T_PU, "f64", "cpu")
+    U = U / torch.sqrt((U * U).sum(dim=-1, keepdim=True))
+    Q = torch.empty((B, Hq, L, d), dtype=dt, device=device)
+    K = torch.empty((B, Hk, L, d), dtype=dt, device=device)
+    V = normal((B, Hk, L, d), seed, T_PV, w.dtype, device)
+    for b in range(B):
+        for g in range(Hk):
+            u = U[b, g].to(device)
+            for j in range(G):
+                h = g * G + j
+                flat = torch.arange((b * Hq + h) * L * d, (b * Hq + h + 1) * L * d, dtype=torch.int64, device=device)
+                z = normal_at(seed, T_PQ, flat, "f64").view(L, d)
+                Q[b, h] = (z + w.beta * u[None, :]).to(dt)
+            pi = torch.empty(L, dtype=torch.float64)
+            pi[permutation(seed, T_PPERM, b * Hk + g, L)] = torch.arange(L, dtype=torch.float64)
+            ell = -w.zipf_s * torch.log(pi + 1.0)
+            gamma = ((ell - ell.mean()) * math.sqrt(d) / w.beta).to(device)
+            flat = torch.arange((b * Hk + g) * L * d, (b * Hk + g + 1) * L * d, dtype=torch.int64, device=device)
+            z = normal_at(seed, T_PK, flat, "f64").view(L, d)
+            K[b, g] = (z + gamma[:, None] * u[None, :]).to(dt)
+    return {"workload": w, "seed": seed, "Q": Q, "K": K, "V": V}

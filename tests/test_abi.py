@@ -10,12 +10,12 @@ from query_adaptive_sparse_amd import native as N
 from query_adaptive_sparse_amd.decoder import make_config
 from synth import configs
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sparse_decode.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
 
 def test_header_symbols_exported():
-    src = open(HEADER).read()
-    declared = sorted(set(re.findall(r"\b(sparse_decode_\w+)\s*\(", src)))
+    src = "".join(open(os.path.join(INCLUDE, f)).read() for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h"))
+    declared = sorted(set(re.findall(r"\b(sparse_(?:decode|prefill)_\w+)\s*\(", src)))
     assert declared, "no declarations found"
     lib = ctypes.CDLL(N.LIB_PATH)
     for name in declared:
@@ -190,3 +190,66 @@ def test_attend_blocks_default_and_override():
         assert N.sparse_decode_attend_blocks(h) == want, kw
         N.sparse_decode_destroy(h)
     assert N.sparse_decode_attend_blocks(None) == 0
+
+
+# ---- Token-Sparse prefill entry points
+def _prefill_cfg(**kw):
+    w = configs.get("p1s")
+    base = dict(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
+                seq_len=w.seq_len, window=w.window, tau=w.tau, softmax_scale=w.softmax_scale, kv_dtype=N.SD_BF16)
+    base.update(kw)
+    cfg = N.sp_config()
+    for k, v in base.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+@pytest.mark.parametrize("name", sorted(configs.PREFILL))
+def test_prefill_init_every_workload(name):
+    w = configs.get(name)
+    h, n = N.sparse_prefill_init(_prefill_cfg(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                                              seq_len=w.seq_len, window=w.window, tau=w.tau))
+    # the fp64 proxy scores dominate: B Hq L W x 8 bytes
+    assert n >= w.batch * w.n_q_heads * w.seq_len * w.window * 8 and n % 256 == 0
+    N.sparse_prefill_destroy(h)
+
+
+PREFILL_BAD = [
+    (dict(batch=0), N.SD_EINVAL, "batch"),
+    (dict(n_kv_heads=5), N.SD_EINVAL, "multiple"),
+    (dict(head_dim=64), N.SD_EUNSUPPORTED, "head_dim"),
+    (dict(kv_dtype=N.SD_F32), N.SD_EUNSUPPORTED, "kv_dtype"),
+    (dict(window=0), N.SD_EINVAL, "window"),
+    (dict(window=65), N.SD_EUNSUPPORTED, "window"),
+    (dict(seq_len=16, window=32), N.SD_EINVAL, "seq_len"),
+    (dict(tau=1.0), N.SD_EINVAL, "tau"),
+    (dict(tau=-0.5), N.SD_EINVAL, "tau"),
+    (dict(softmax_scale=0.0), N.SD_EINVAL, "softmax_scale"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", PREFILL_BAD, ids=[b[2] + str(i) for i, b in enumerate(PREFILL_BAD)])
+def test_prefill_init_rejects(kw, status, msg):
+    with pytest.raises(N.SparseDecodeError) as e:
+        N.sparse_prefill_init(_prefill_cfg(**kw))
+    assert e.value.status == status
+    assert msg in str(e.value)
+
+
+def test_prefill_calls_reject_before_enqueue():
+    h, _ = N.sparse_prefill_init(_prefill_cfg())
+    L = N.lib()
+    t = N.sp_tensors()
+    assert L.sparse_prefill_select(None, ctypes.byref(t), 256, None) == N.SD_EINVAL
+    assert L.sparse_prefill_select(h, ctypes.byref(t), None, None) == N.SD_EWORKSPACE
+    assert L.sparse_prefill_select(h, ctypes.byref(t), 0x1001, None) == N.SD_EWORKSPACE
+    assert L.sparse_prefill_select(h, ctypes.byref(t), 256, None) == N.SD_EINVAL   # null tensors
+    t.q, t.k, t.v = 0x1000, 0x2000, 0x3000
+    t.q_st, t.kv_st = 100, 128                                                    # q rows not 16-byte aligned
+    assert L.sparse_prefill_select(h, ctypes.byref(t), 256, None) == N.SD_EINVAL
+    t.q_st = 128
+    assert L.sparse_prefill_attend(h, ctypes.byref(t), 256, None, None) == N.SD_EINVAL  # null out
+    v = N.sp_view()
+    assert L.sparse_prefill_view(h, 256, ctypes.byref(v)) == N.SD_OK
+    assert v.words == (configs.get("p1s").seq_len + 31) // 32
+    N.sparse_prefill_destroy(h)
