@@ -110,7 +110,7 @@ int launch_long_rows(const LongRows& r, void* stream);
 constexpr int kPfSlab = kMinMaxBlock;  // keys per importance workgroup (and per partial max / min)
 constexpr int kPfKeyBlock = 64;        // keys per proxy-score workgroup
 constexpr int kPfMaxWindow = 64;
-constexpr int kPfQueryBlock = 64;      // compact queries per attention workgroup
+constexpr int kPfQueryBlock = 128;     // compact queries per attention workgroup
 
 struct PrefillPlan {
   sp_config cfg;

@@ -19,7 +19,7 @@
 // Attention:
 //   k_pf_attend      64 compact queries per workgroup (16 per wave), heaviest blocks first; the
 //                    workgroup gathers 64 compact keys' K and V rows per step into LDS (K pieces
-//                    XOR-swizzled per row, V rows padded), each wave runs q.K^T on the bf16 MFMA,
+//                    XOR-swizzled per row, V rows as they are), each wave runs q.K^T on the bf16 MFMA,
 //                    the causal mask in compact order, an online softmax and P.V (hi and lo
 //                    halves of P on two MFMAs), then writes its rows to their positions;
 //   k_pf_zero        positions a head did not keep get zero rows.
@@ -111,17 +111,32 @@ __global__ __launch_bounds__(256) void k_pf_scores(PfScoreArgs a) {
         fmax(fmax(wmax[0][tid], wmax[1][tid]), fmax(wmax[2][tid], wmax[3][tid]));
 }
 
-// Every window query's max over its visible keys (the block maxima reduced in block order).
-__global__ __launch_bounds__(256) void k_pf_rowmax(const double* __restrict__ pmq, int nkb, int W, double* __restrict__ M) {
+// Every window query's max over its visible keys: the block maxima, 16 parts of the blocks per
+// query with 8 loads in flight per thread (max is exact, so the order does not matter).
+__global__ __launch_bounds__(1024) void k_pf_rowmax(const double* __restrict__ pmq, int nkb, int W, double* __restrict__ M) {
   const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x, tid = threadIdx.x;
-  __shared__ double red[4][kPfMaxWindow];
+  __shared__ double red[16][kPfMaxWindow];
   const int qi = tid & 63, part = tid >> 6;
   double m = kNegInfD;
-  if (qi < W)
-    for (int kb = part; kb < nkb; kb += 4) m = fmax(m, pmq[((int64_t(b) * Hq + h) * nkb + kb) * W + qi]);
+  if (qi < W) {
+    const double* pq = pmq + (int64_t(b) * Hq + h) * nkb * W + qi;
+    int kb = part;
+    for (; kb + 16 * 7 < nkb; kb += 16 * 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pq[int64_t(kb + 16 * u) * W];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) m = fmax(m, v[u]);
+    }
+    for (; kb < nkb; kb += 16) m = fmax(m, pq[int64_t(kb) * W]);
+  }
   red[part][qi] = m;
   __syncthreads();
-  if (tid < W) M[(int64_t(b) * Hq + h) * W + tid] = fmax(fmax(red[0][tid], red[1][tid]), fmax(red[2][tid], red[3][tid]));
+  if (tid < W) {
+    double r = red[0][tid];
+    for (int p = 1; p < 16; ++p) r = fmax(r, red[p][tid]);
+    M[(int64_t(b) * Hq + h) * W + tid] = r;
+  }
 }
 
 struct PfImpArgs {
@@ -179,8 +194,24 @@ __global__ __launch_bounds__(256) void k_pf_importance(PfImpArgs a) {
   for (int64_t j = j0 + tid; j < j1; j += 256) {
     const double* sp = a.S + (row * a.L + j) * a.W;
     const int64_t q0 = j - (a.L - a.W);  // first window query that sees key j
+    const int qa = q0 > 0 ? int(q0) : 0;
     double v = 0.0;
-    for (int qi = q0 > 0 ? int(q0) : 0; qi < a.W; ++qi) v += exp(a.scale * sp[qi] - ms[qi]) / zs[qi];
+    if (qa == 0 && (a.W & 7) == 0) {
+      // every query sees the key: 8 scores per step, loaded together
+      for (int q8 = 0; q8 < a.W; q8 += 8) {
+        double sv[8];
+#pragma unroll
+        for (int u = 0; u < 8; u += 2) {
+          const double2 d2 = *reinterpret_cast<const double2*>(sp + q8 + u);
+          sv[u] = d2.x;
+          sv[u + 1] = d2.y;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += exp(a.scale * sv[u] - ms[q8 + u]) / zs[q8 + u];
+      }
+    } else {
+      for (int qi = qa; qi < a.W; ++qi) v += exp(a.scale * sp[qi] - ms[qi]) / zs[qi];
+    }
     a.imp[row * a.L + j] = v;
     mx = fmax(mx, v);
     mn = fmin(mn, v);
@@ -271,8 +302,11 @@ __global__ __launch_bounds__(1024) void k_pf_lists(const uint32_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Compressed causal attention. Wave w of query block qb owns compact queries
-// 64 qb + 16 w + n (n = lane % 16); per step the workgroup holds 64 compact keys in LDS.
+// Compressed causal attention. A workgroup owns 128 compact queries (wave w: queries
+// 128 qb + 32 w + 16 t + n for its two query tiles t); per step it stages 64 compact keys' K and V
+// rows in LDS and every wave computes its 32 x 64 logits (each K fragment read serves both query
+// tiles), one online-softmax update per tile and step, and P.V (each V operand read serves both
+// query tiles and both halves of P).
 // ---------------------------------------------------------------------------------------------
 struct PfAttnArgs {
   const uint16_t* q;
@@ -288,14 +322,24 @@ struct PfAttnArgs {
   float scale_log2;
 };
 
-constexpr int kPPR = kD / 8;        // 16-byte pieces per row
-constexpr int kVRowW = kD / 2 + 4;  // padded V row in LDS (32-bit words)
+constexpr int kPPR = kD / 8;   // 16-byte pieces per row
+constexpr int kKeyTile = 64;   // compact keys staged per step
+constexpr int kQTiles = 2;     // 16-query tiles per wave
+// V rows are staged as they are (key-major), pitch 72 words: the B operand of P.V (4 consecutive
+// keys of one dimension) is one LDS transpose read. ds_read_b64_tr_b16 works on groups of 16
+// lanes: lane i of a group receives element i % 4 of the 8 bytes addressed by the group's lanes
+// i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12. So lane j of group c addresses key 4 c + j / 4 of the
+// sub-tile, dimensions 16 nb + 4 (j % 4) .. + 3, and lane n then holds V[4 c + 0..3][16 nb + n].
+// With a pitch of 8 (mod 64) words the 16 addresses of a group, and those of its neighbour group,
+// fall in distinct banks.
+constexpr int kVPitchW = kD / 2 + 8;  // 32-bit words per staged V row
 
 __device__ __forceinline__ int pf_kswz(int x) { return x & 15; }
 
 __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
-  __shared__ uint4 kst[kPfQueryBlock * kPPR];
-  __shared__ uint32_t vst[kPfQueryBlock * kVRowW];
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  __shared__ uint4 kstb[2][kKeyTile * kPPR];
+  __shared__ uint32_t vstb[2][kKeyTile * kVPitchW];
   const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, n = lane & 15, c = lane >> 4;
   const int kk = min(max(a.budget[b], 1), int(a.L));
@@ -312,106 +356,180 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
   };
   const uint16_t* kbase = a.k + b * a.kv_sb + g * a.kv_sh;
   const uint16_t* vbase = a.v + b * a.kv_sb + g * a.kv_sh;
-  // this lane's query (B operand of q.K^T: query n, dimensions 32 j + 8 c .. + 7)
-  const int qi = qb * kPfQueryBlock + 16 * wave + n;
-  const int64_t qrow = pos_of(qi < kk ? qi : kk - 1);
-  uint4 qf[kD / 32];
+  const int q0w = qb * kPfQueryBlock + 32 * wave;  // first query of this wave
+  // query fragments (B operand of q.K^T: query n, dimensions 32 j + 8 c .. + 7) per query tile
+  uint4 qf[kQTiles][kD / 32];
 #pragma unroll
-  for (int j = 0; j < kD / 32; ++j) qf[j] = ld16(a.q + b * a.q_sb + h * a.q_sh + int64_t(qrow) * a.q_st + 32 * j + 8 * c);
-  float m = kNegInf, l = 0.f;
-  f32x4 acc[kD / 16];
+  for (int t = 0; t < kQTiles; ++t) {
+    const int qi = q0w + 16 * t + n;
+    const int64_t qrow = pos_of(qi < kk ? qi : kk - 1);
 #pragma unroll
-  for (int nb = 0; nb < kD / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // keys of step kt: compact 64 kt + x; thread pieces tid + 256 i (row x = piece / 16)
-  uint4 rk[4], rv[4];
-  auto issue = [&](int kt) {
+    for (int j = 0; j < kD / 32; ++j) qf[t][j] = ld16(a.q + b * a.q_sb + h * a.q_sh + qrow * a.q_st + 32 * j + 8 * c);
+  }
+  float m[kQTiles], l[kQTiles];
+  f32x4 acc[kQTiles][kD / 16];
+#pragma unroll
+  for (int t = 0; t < kQTiles; ++t) {
+    m[t] = kNegInf;
+    l[t] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < kD / 16; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // keys of step kt: compact kKeyTile kt + x; thread pieces tid + 256 i (row x = piece / 16).
+  // LDS holds steps kt (being computed) and kt + 1 (written at the start of step kt); two register
+  // stages hold the loads of steps kt + 2 and kt + 3 in flight. One barrier per step.
+  uint4 rk[2][4], rv[2][4];
+  auto stage = [&](int sbuf, const uint4* dk, const uint4* dv) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pcs = tid + 256 * i, x = pcs >> 4, pc = pcs & 15;
-      const int kc = kt * kPfQueryBlock + x;
-      const int64_t row = pos_of(kc < kk ? kc : kk - 1);
-      rk[i] = ld16_stream(kbase + row * a.kv_st + pc * 8);
-      rv[i] = ld16_stream(vbase + row * a.kv_st + pc * 8);
+      kstb[sbuf][x * kPPR + (pc ^ pf_kswz(x))] = dk[i];
+      *reinterpret_cast<uint4*>(vstb[sbuf] + x * kVPitchW + pc * 4) = dv[i];
     }
   };
-  issue(0);
-  for (int kt = 0; kt <= qb; ++kt) {
-    __syncthreads();  // every wave is done with the previous step's tiles
+  const int nkt = (min(kk, (qb + 1) * kPfQueryBlock) + kKeyTile - 1) / kKeyTile;  // causal key tiles
+  auto issue = [&](uint4* dk, uint4* dv, int kt) {
+    kt = kt < nkt ? kt : nkt - 1;  // past the end: the last step again (still cached)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pcs = tid + 256 * i, x = pcs >> 4, pc = pcs & 15;
-      kst[x * kPPR + (pc ^ pf_kswz(x))] = rk[i];
-      *reinterpret_cast<uint4*>(vst + x * kVRowW + pc * 4) = rv[i];
+      const int kc = kt * kKeyTile + x;
+      const int64_t row = pos_of(kc < kk ? kc : kk - 1);
+      dk[i] = ld16_stream(kbase + row * a.kv_st + pc * 8);
+      dv[i] = ld16_stream(vbase + row * a.kv_st + pc * 8);
     }
+  };
+  issue(rk[0], rv[0], 0);
+  issue(rk[1], rv[1], 1);
+  stage(0, rk[0], rv[0]);
+  issue(rk[0], rv[0], 2);
+  for (int kt0 = 0; kt0 < nkt; kt0 += 2) {
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const int kt = kt0 + sb;
+    if (kt >= nkt) break;
+    // step kt's tiles (buffer sb) are complete, and every wave is done with step kt - 1, whose
+    // buffer now takes step kt + 1 (registers rk[sb ^ 1]); those registers then load step kt + 3
     __syncthreads();
-    if (kt < qb) issue(kt + 1);
-#pragma unroll 1
-    for (int st = 0; st < kPfQueryBlock / 16; ++st) {
-      const int kc0 = kt * kPfQueryBlock + 16 * st;  // first compact key of the sub-tile
-      if (kc0 > qb * kPfQueryBlock + 16 * wave + 15) break;  // past every query of this wave
-      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    stage(sb ^ 1, rk[sb ^ 1], rv[sb ^ 1]);
+    issue(rk[sb ^ 1], rv[sb ^ 1], kt + 3);
+    const uint4* kst = kstb[sb];
+    const uint32_t* vst = vstb[sb];
+    const int kc0 = kt * kKeyTile;
+    if (kc0 > q0w + 31) continue;  // every key of the step is after every query of this wave
+    // ---- logits: S^T[key 16 st + 4 c + i][query 16 t + n]
+    f32x4 sacc[kQTiles][kKeyTile / 16];
+#pragma unroll
+    for (int st = 0; st < kKeyTile / 16; ++st) {
       const int x = 16 * st + n;
+      uint4 kf[kD / 32];
 #pragma unroll
-      for (int j = 0; j < kD / 32; ++j)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kst[x * kPPR + ((4 * j + c) ^ pf_kswz(x))]),
-                                                        __builtin_bit_cast(bf16x8, qf[j]), sacc, 0, 0, 0);
-      // logits S^T[key 4c + i][query n]; causal in compact order and inside the budget
-      float lg[4];
+      for (int j = 0; j < kD / 32; ++j) kf[j] = kst[x * kPPR + ((4 * j + c) ^ pf_kswz(x))];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kc = kc0 + 4 * c + i;
-        lg[i] = (kc <= qi && kc < kk) ? sacc[i] * a.scale_log2 : kNegInf;
+      for (int t = 0; t < kQTiles; ++t) {
+        f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kD / 32; ++j)
+          s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[j]),
+                                                        __builtin_bit_cast(bf16x8, qf[t][j]), s4, 0, 0, 0);
+        sacc[t][st] = s4;
       }
-      float mt = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+    }
+    // the causal / budget mask is needed only where the step reaches this wave's queries or the
+    // end of the compact sequence
+    const bool edge = kc0 + kKeyTile - 1 > q0w || kc0 + kKeyTile > kk;
+    uint32_t ph[kQTiles][kKeyTile / 16][2], pl[kQTiles][kKeyTile / 16][2];
+#pragma unroll
+    for (int t = 0; t < kQTiles; ++t) {
+      const int qi = q0w + 16 * t + n;
+      float lg[kKeyTile / 16][4];
+      float mt = kNegInf;
+#pragma unroll
+      for (int st = 0; st < kKeyTile / 16; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = sacc[t][st][i] * a.scale_log2;
+          if (edge) {
+            const int kc = kc0 + 16 * st + 4 * c + i;
+            v = (kc <= qi && kc < kk) ? v : kNegInf;
+          }
+          lg[st][i] = v;
+          mt = fmaxf(mt, v);
+        }
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m, mt);
+      const float mn = fmaxf(m[t], mt);
       const bool none = mn == kNegInf;
-      if (__ballot(mn > m)) {
-        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m - mn);
-        l *= alpha;
+      if (__ballot(mn > m[t])) {
+        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m[t] - mn);
+        l[t] *= alpha;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float ai = __shfl(alpha, 4 * c + i);
 #pragma unroll
-          for (int nb = 0; nb < kD / 16; ++nb) acc[nb][i] *= ai;
+          for (int nb = 0; nb < kD / 16; ++nb) acc[t][nb][i] *= ai;
         }
-        m = mn;
+        m[t] = mn;
       }
-      u16x4 ph, pl;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pr = none ? 0.f : __builtin_amdgcn_exp2f(lg[i] - mn);
-        l += pr;
-        const uint16_t hi = f2bf(pr);
-        ph[i] = hi;
-        pl[i] = f2bf(pr - bf2f(hi));
+      for (int st = 0; st < kKeyTile / 16; ++st) {
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[i] = none ? 0.f : __builtin_amdgcn_exp2f(lg[st][i] - mn);
+          l[t] += pr[i];
+        }
+        // P = hi + lo, both bf16 (round to nearest even): fp32 accuracy through two MFMAs
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+          bf2 hv;
+          hv[0] = (__bf16)pr[2 * u];
+          hv[1] = (__bf16)pr[2 * u + 1];
+          bf2 lv;
+          lv[0] = (__bf16)(pr[2 * u] - float(hv[0]));
+          lv[1] = (__bf16)(pr[2 * u + 1] - float(hv[1]));
+          ph[t][st][u] = __builtin_bit_cast(uint32_t, hv);
+          pl[t][st][u] = __builtin_bit_cast(uint32_t, lv);
+        }
       }
-      const uint16_t* v16 = reinterpret_cast<const uint16_t*>(vst);
+    }
+    // ---- P.V: A = P (query rows, keys 4 c .. 4 c + 3 of sub-tile st), B = V via transpose reads
+#pragma unroll
+    for (int st = 0; st < kKeyTile / 16; ++st) {
+      const uint32_t* vrow = vst + (16 * st + 4 * c + (n >> 2)) * kVPitchW + 2 * (n & 3);
 #pragma unroll
       for (int nb = 0; nb < kD / 16; ++nb) {
-        u16x4 vb;
+        const v4s vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vrow + 8 * nb));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vb[i] = v16[(16 * st + 4 * c + i) * (2 * kVRowW) + 16 * nb + n];
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, ph),
-                                                             __builtin_bit_cast(bf16x4, vb), acc[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, pl),
-                                                             __builtin_bit_cast(bf16x4, vb), acc[nb], 0, 0, 0);
+        for (int t = 0; t < kQTiles; ++t) {
+          const uint2 hp = make_uint2(ph[t][st][0], ph[t][st][1]);
+          const uint2 lp = make_uint2(pl[t][st][0], pl[t][st][1]);
+          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, hp),
+                                                                  __builtin_bit_cast(bf16x4, vb), acc[t][nb], 0, 0, 0);
+          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, lp),
+                                                                  __builtin_bit_cast(bf16x4, vb), acc[t][nb], 0, 0, 0);
+        }
       }
     }
   }
-  // normaliser of every query column (the 4 lane groups hold partial sums of the same column)
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  // acc[nb][i]: query 16 wave + 4c + i (of the block), dimension 16 nb + n
+  }
+  // normaliser of every query column (the 4 lane groups hold partial sums of the same column);
+  // acc[t][nb][i]: query 16 t + 4 c + i of the wave, dimension 16 nb + n
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float li = __shfl(l, 4 * c + i);
-    const int qo = qb * kPfQueryBlock + 16 * wave + 4 * c + i;
-    if (qo < kk) {
-      float* orow = a.out + ((int64_t(b) * a.Hq + h) * a.L + pos_of(qo)) * kD;
+  for (int t = 0; t < kQTiles; ++t) {
+    float lt = l[t];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
 #pragma unroll
-      for (int nb = 0; nb < kD / 16; ++nb) orow[16 * nb + n] = acc[nb][i] / li;
+    for (int i = 0; i < 4; ++i) {
+      const float li = __shfl(lt, 4 * c + i);
+      const int qo = q0w + 16 * t + 4 * c + i;
+      if (qo < kk) {
+        float* orow = a.out + ((int64_t(b) * a.Hq + h) * a.L + pos_of(qo)) * kD;
+#pragma unroll
+        for (int nb = 0; nb < kD / 16; ++nb) orow[16 * nb + n] = acc[t][nb][i] / li;
+      }
     }
   }
 }
@@ -454,7 +572,7 @@ int launch_prefill_select(const PrefillPlan& p, const sp_tensors& t, char* ws, v
   s.pmq = at<double>(ws, p.o_pmq);
   s.status = status;
   hipLaunchKernelGGL(k_pf_scores, dim3(p.nkb, Hq, B), dim3(256), 0, st, s);
-  hipLaunchKernelGGL(k_pf_rowmax, dim3(Hq, B), dim3(256), 0, st, at<double>(ws, p.o_pmq), p.nkb, W, at<double>(ws, p.o_M));
+  hipLaunchKernelGGL(k_pf_rowmax, dim3(Hq, B), dim3(1024), 0, st, at<double>(ws, p.o_pmq), p.nkb, W, at<double>(ws, p.o_M));
   PfImpArgs ia;
   ia.S = at<double>(ws, p.o_S);
   ia.M = at<double>(ws, p.o_M);
