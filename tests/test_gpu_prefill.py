@@ -95,3 +95,45 @@ def test_prefill_deterministic():
     assert torch.equal(o1, o2)
     for k in ("importance", "budget", "head_bits"):
         assert torch.equal(s1[k], s2[k]), k
+
+
+def test_prefill_128k_sampled():
+    """The 128K prompt (32 heads): importance of two sampled heads against the oracle; every head's
+    set equals its top-budget by the GPU's own importance (verified on the sampled heads); the
+    budget equals the coverage cut of the GPU importances summed over heads; sampled output rows."""
+    from oracle import ref
+    w = configs.get("p1_tsa_llama31_8b_128k")
+    print(f"[prefill-128k] generating inputs", flush=True)
+    inp = gen.make_prefill_inputs(w, device="cuda")
+    sel, out = run_gpu(w, inp)
+    assert int(sel["status"][0]) == 0
+    src = PrefillSource(inp)
+    L, W = w.seq_len, w.window
+    imp_gpu = sel["importance"][0].numpy()
+    for h in (3, 26):
+        print(f"[prefill-128k] oracle importance of head {h}", flush=True)
+        imp = pref.proxy_importance(src.q_rows(0, h, np.arange(L - W, L)), src.k_all(0, h // w.group),
+                                    w.softmax_scale, L - W)
+        assert np.max(np.abs(imp_gpu[h] - imp) / imp) <= 1e-12
+    total = np.zeros(L)
+    for h in range(w.n_q_heads):
+        total = total + imp_gpu[h]
+    k, margin = ref.coverage_budget(total, w.tau)
+    assert int(sel["budget"][0]) == k, (int(sel["budget"][0]), k, margin)
+    for h in range(w.n_q_heads):
+        S = ref.select_top_k(imp_gpu[h], k)
+        assert np.array_equal(sel["list"][0, h, :k].numpy(), S), h
+    rng = np.random.default_rng(5)
+    got = out.cpu().numpy()
+    worst = 0.0
+    for h in (3, 26):
+        S = sel["list"][0, h, :k].numpy().astype(np.int64)
+        rows = sorted(set(rng.choice(k, 24, replace=False).tolist()) | {0, k - 1})
+        o, _ = pref.tsa_attend_rows(w, src, 0, h, S, rows)
+        d = got[0, h, S[rows]] - o
+        worst = max(worst, float(np.max(np.abs(d))))
+        assert np.max(np.abs(d)) <= ATOL and np.linalg.norm(d) / np.linalg.norm(o) <= RTOL_L2, h
+        keep = np.zeros(L, dtype=bool)
+        keep[S] = True
+        assert np.all(got[0, h, ~keep] == 0.0)
+    print(f"[prefill-128k] budget {k} margin {margin:.2e} max_abs {worst:.2e}", flush=True)
