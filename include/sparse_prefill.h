@@ -76,7 +76,8 @@ typedef struct {
 } sp_view;
 
 /* Validate and copy `cfg`, create a handle, report the workspace size in bytes
- * (it holds the fp64 proxy scores, B Hq W L x 8 bytes, and the selection state).
+ * (it holds the fp64 proxy scores, B Hq W L x 8 bytes, whose region attend reuses for every
+ * head's gathered K and V rows, B Hq L d x 4 bytes, and the selection state).
  * Host only. Errors: SD_EINVAL (null pointer, inconsistent shape or parameter),
  * SD_EUNSUPPORTED (head_dim != 128, kv_dtype != SD_BF16, window > 64). */
 sd_status sparse_prefill_init(const sp_config* cfg, sp_handle** out, size_t* workspace_bytes);

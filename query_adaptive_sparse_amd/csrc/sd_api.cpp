@@ -347,7 +347,11 @@ sd_status sparse_prefill_init(const sp_config* cfg, sp_handle** out, size_t* wor
     return o;
   };
   p.o_status = take(64);
-  p.o_S = take(size_t(B * Hq * L * W) * 8);
+  p.Lpad = (L + sd::kPfKeyTile - 1) / sd::kPfKeyTile * sd::kPfKeyTile;
+  // the proxy scores are dead once the selection is made: attend gathers every head's K and V
+  // rows into the same region
+  p.o_S = take(std::max(size_t(B * Hq * L * W) * 8, size_t(B * Hq * p.Lpad) * size_t(c.head_dim) * 2 * 2));
+  p.o_kvc = p.o_S;
   p.o_pmq = take(size_t(B * Hq * p.nkb * W) * 8);
   p.o_M = take(size_t(B * Hq * W) * 8);
   p.o_zq = take(size_t(B * Hq * p.nslab * W) * 8);

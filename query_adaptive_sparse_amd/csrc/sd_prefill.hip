@@ -17,11 +17,14 @@
 //   long-row pass    every head's top-budget tokens by its own importance;
 //   k_pf_lists       each head's bitmap as an ascending position list.
 // Attention:
-//   k_pf_attend      64 compact queries per workgroup (16 per wave), heaviest blocks first; the
-//                    workgroup gathers 64 compact keys' K and V rows per step into LDS (K pieces
-//                    XOR-swizzled per row, V rows as they are), each wave runs q.K^T on the bf16 MFMA,
-//                    the causal mask in compact order, an online softmax and P.V (hi and lo
-//                    halves of P on two MFMAs), then writes its rows to their positions;
+//   k_pf_gather      compression: every head's K and V rows at its kept positions, in list order,
+//                    into contiguous per-head sequences (padded with zero rows to a whole step);
+//   k_pf_attend      128 compact queries per workgroup (32 per wave), heaviest blocks first; the
+//                    workgroup stages 64 gathered keys' K and V rows per step in LDS (K pieces
+//                    XOR-swizzled per row, V rows padded for transpose reads), each wave runs q.K^T
+//                    on the bf16 MFMA, the causal mask in compact order, an online softmax whose
+//                    reference moves only when a logit exceeds it by 2^8, and P.V (hi and lo halves
+//                    of P), then writes its rows to their positions;
 //   k_pf_zero        positions a head did not keep get zero rows.
 #include "sd_device.h"
 
@@ -316,15 +319,52 @@ struct PfAttnArgs {
   int64_t kv_sb, kv_sh, kv_st;
   const int32_t* list;    // [B][Hq][L]
   const int32_t* budget;  // [B]
+  uint16_t* kc;           // gathered K rows [B][Hq][Lpad][d]
+  uint16_t* vc;           // gathered V rows [B][Hq][Lpad][d]
   float* out;             // [B][Hq][L][d]
-  int64_t L;
+  int64_t L, Lpad;
   int Hq, G;
   float scale_log2;
 };
 
+// Compression: every head's K and V rows at its kept positions, in list order, into contiguous
+// per-head sequences; rows from the budget up to the next multiple of kKeyTile are zero (their
+// logits are masked, and zero values keep their products finite). One workgroup per 64 rows.
+__global__ __launch_bounds__(256) void k_pf_gather(PfAttnArgs a) {
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int Li = int(a.L);
+  const int kk = min(max(a.budget[b], 1), Li);
+  const int r0 = blockIdx.x * 64;
+  if (r0 >= kk) return;
+  const int g = h / a.G;
+  const int32_t* lst = a.list + (int64_t(b) * a.Hq + h) * a.L;
+  const int64_t head = (int64_t(b) * a.Hq + h) * a.Lpad;
+  const int pc = tid & 15;
+  uint4 kv[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + (tid >> 4) + 16 * i;
+    if (r < kk) {
+      const int64_t pos = min(max(lst[r], 0), Li - 1);
+      const int64_t src = b * a.kv_sb + g * a.kv_sh + pos * a.kv_st + pc * 8;
+      kv[0][i] = ld16_stream(a.k + src);
+      kv[1][i] = ld16_stream(a.v + src);
+    } else {
+      kv[0][i] = kv[1][i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t dst = (head + r0 + (tid >> 4) + 16 * i) * kD + pc * 8;
+    *reinterpret_cast<uint4*>(a.kc + dst) = kv[0][i];
+    *reinterpret_cast<uint4*>(a.vc + dst) = kv[1][i];
+  }
+}
+
 constexpr int kPPR = kD / 8;   // 16-byte pieces per row
-constexpr int kKeyTile = 64;   // compact keys staged per step
+constexpr int kKeyTile = kPfKeyTile;  // compact keys staged per step
 constexpr int kQTiles = 2;     // 16-query tiles per wave
+constexpr float kPfLazy = 8.f; // log2 headroom of the lazily moved softmax reference
 // V rows are staged as they are (key-major), pitch 72 words: the B operand of P.V (4 consecutive
 // keys of one dimension) is one LDS transpose read. ds_read_b64_tr_b16 works on groups of 16
 // lanes: lane i of a group receives element i % 4 of the 8 bytes addressed by the group's lanes
@@ -341,8 +381,10 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
   __shared__ uint4 kstb[2][kKeyTile * kPPR];
   __shared__ uint32_t vstb[2][kKeyTile * kVPitchW];
   const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, n = lane & 15, c = lane >> 4;
-  const int kk = min(max(a.budget[b], 1), int(a.L));
+  const int lane = tid & 63, n = lane & 15, c = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Li = int(a.L);
+  const int kk = min(max(a.budget[b], 1), Li);
   const int nqb = (kk + kPfQueryBlock - 1) / kPfQueryBlock;
   if (int(blockIdx.x) >= nqb) return;
   const int qb = nqb - 1 - int(blockIdx.x);  // heaviest (longest causal range) first
@@ -350,12 +392,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
   const int32_t* lst = a.list + (int64_t(b) * a.Hq + h) * a.L;
   // list entries are positions in [0, L); clamped so that an incomplete selection row (status
   // flag raised) can never address outside the tensors
-  auto pos_of = [&](int i) {
-    const int v = lst[i];
-    return int64_t(v < 0 ? 0 : (v < a.L ? v : a.L - 1));
-  };
-  const uint16_t* kbase = a.k + b * a.kv_sb + g * a.kv_sh;
-  const uint16_t* vbase = a.v + b * a.kv_sb + g * a.kv_sh;
+  auto pos_of = [&](int i) { return int64_t(min(max(lst[i], 0), Li - 1)); };
   const int q0w = qb * kPfQueryBlock + 32 * wave;  // first query of this wave
   // query fragments (B operand of q.K^T: query n, dimensions 32 j + 8 c .. + 7) per query tile
   uint4 qf[kQTiles][kD / 32];
@@ -366,6 +403,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
 #pragma unroll
     for (int j = 0; j < kD / 32; ++j) qf[t][j] = ld16(a.q + b * a.q_sb + h * a.q_sh + qrow * a.q_st + 32 * j + 8 * c);
   }
+  // running reference of every query column in log2 units (scale_log2 x raw logit); it is moved
+  // only when a logit exceeds it by more than kPfLazy, so the probabilities stay below 2^kPfLazy
   float m[kQTiles], l[kQTiles];
   f32x4 acc[kQTiles][kD / 16];
 #pragma unroll
@@ -375,14 +414,19 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
 #pragma unroll
     for (int nb = 0; nb < kD / 16; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // keys of step kt: compact kKeyTile kt + x; thread pieces tid + 256 i (row x = piece / 16).
-  // LDS holds steps kt (being computed) and kt + 1 (written at the start of step kt); two register
-  // stages hold the loads of steps kt + 2 and kt + 3 in flight. One barrier per step.
+  // keys of step kt: gathered rows kKeyTile kt + x; thread pieces tid + 256 i (row x = tid / 16 +
+  // 16 i, 16-byte piece pc = tid % 16 of it). LDS holds steps kt (being computed) and kt + 1
+  // (written at the start of step kt); two register stages hold the loads of steps kt + 2 and
+  // kt + 3 in flight. One barrier per step.
+  const int pc = tid & 15, x0 = tid >> 4;
+  const int64_t head = (int64_t(b) * a.Hq + h) * a.Lpad * kD;
+  const uint16_t* kthr = a.kc + head + x0 * kD + pc * 8;
+  const uint16_t* vthr = a.vc + head + x0 * kD + pc * 8;
   uint4 rk[2][4], rv[2][4];
   auto stage = [&](int sbuf, const uint4* dk, const uint4* dv) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int pcs = tid + 256 * i, x = pcs >> 4, pc = pcs & 15;
+      const int x = x0 + 16 * i;
       kstb[sbuf][x * kPPR + (pc ^ pf_kswz(x))] = dk[i];
       *reinterpret_cast<uint4*>(vstb[sbuf] + x * kVPitchW + pc * 4) = dv[i];
     }
@@ -390,24 +434,25 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
   const int nkt = (min(kk, (qb + 1) * kPfQueryBlock) + kKeyTile - 1) / kKeyTile;  // causal key tiles
   auto issue = [&](uint4* dk, uint4* dv, int kt) {
     kt = kt < nkt ? kt : nkt - 1;  // past the end: the last step again (still cached)
+    const int64_t o = int64_t(kt) * kKeyTile * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int pcs = tid + 256 * i, x = pcs >> 4, pc = pcs & 15;
-      const int kc = kt * kKeyTile + x;
-      const int64_t row = pos_of(kc < kk ? kc : kk - 1);
-      dk[i] = ld16_stream(kbase + row * a.kv_st + pc * 8);
-      dv[i] = ld16_stream(vbase + row * a.kv_st + pc * 8);
+      dk[i] = ld16(kthr + o + 16 * i * kD);
+      dv[i] = ld16(vthr + o + 16 * i * kD);
     }
   };
   issue(rk[0], rv[0], 0);
   issue(rk[1], rv[1], 1);
   stage(0, rk[0], rv[0]);
+  // keep the prologue's loads in the loop's order (the in-flight state entering the loop is then
+  // the state at its back edge, and the loop waits only for the stage it writes to LDS)
+  __builtin_amdgcn_sched_barrier(0);
   issue(rk[0], rv[0], 2);
-  for (int kt0 = 0; kt0 < nkt; kt0 += 2) {
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    const int kt = kt0 + sb;
-    if (kt >= nkt) break;
+  __builtin_amdgcn_sched_barrier(0);
+  const float cs = a.scale_log2;
+  // one step; sb = kt % 2 is a constant at each call site, so every register stage stays in
+  // registers
+  auto step = [&](const int sb, const int kt) {
     // step kt's tiles (buffer sb) are complete, and every wave is done with step kt - 1, whose
     // buffer now takes step kt + 1 (registers rk[sb ^ 1]); those registers then load step kt + 3
     __syncthreads();
@@ -416,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
     const uint4* kst = kstb[sb];
     const uint32_t* vst = vstb[sb];
     const int kc0 = kt * kKeyTile;
-    if (kc0 > q0w + 31) continue;  // every key of the step is after every query of this wave
+    if (kc0 > q0w + 31) return;  // every key of the step is after every query of this wave
     // ---- logits: S^T[key 16 st + 4 c + i][query 16 t + n]
     f32x4 sacc[kQTiles][kKeyTile / 16];
 #pragma unroll
@@ -436,32 +481,37 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
       }
     }
     // the causal / budget mask is needed only where the step reaches this wave's queries or the
-    // end of the compact sequence
-    const bool edge = kc0 + kKeyTile - 1 > q0w || kc0 + kKeyTile > kk;
+    // end of the compact sequence (a wave-uniform test)
+    if (kc0 + kKeyTile - 1 > q0w || kc0 + kKeyTile > kk) {
+#pragma unroll
+      for (int t = 0; t < kQTiles; ++t) {
+        const int qi = q0w + 16 * t + n;
+#pragma unroll
+        for (int st = 0; st < kKeyTile / 16; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kc = kc0 + 16 * st + 4 * c + i;
+            sacc[t][st][i] = (kc <= qi && kc < kk) ? sacc[t][st][i] : kNegInf;
+          }
+      }
+    }
+    // P = hi + lo, both bf16 (hi rounded to nearest even, lo the rounded remainder): fp32
+    // accuracy of P through two MFMAs. ph / pl [t][st][u]: keys 16 st + 4 c + 2 u, + 1 of query
+    // 16 t + n, packed
     uint32_t ph[kQTiles][kKeyTile / 16][2], pl[kQTiles][kKeyTile / 16][2];
 #pragma unroll
     for (int t = 0; t < kQTiles; ++t) {
-      const int qi = q0w + 16 * t + n;
-      float lg[kKeyTile / 16][4];
       float mt = kNegInf;
 #pragma unroll
       for (int st = 0; st < kKeyTile / 16; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[t][st][i] * a.scale_log2;
-          if (edge) {
-            const int kc = kc0 + 16 * st + 4 * c + i;
-            v = (kc <= qi && kc < kk) ? v : kNegInf;
-          }
-          lg[st][i] = v;
-          mt = fmaxf(mt, v);
-        }
+        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sacc[t][st][i]);
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m[t], mt);
-      const bool none = mn == kNegInf;
-      if (__ballot(mn > m[t])) {
-        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m[t] - mn);
+      mt *= cs;  // scale > 0: the scaled maximum is the maximum of the scaled logits
+      if (__ballot(mt > m[t] + kPfLazy)) {
+        const float mn = fmaxf(m[t], mt);
+        const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[t] - mn);
         l[t] *= alpha;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -471,48 +521,60 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
         }
         m[t] = mn;
       }
+      // a column whose reference is still -inf has seen masked logits only: exponent -inf
+      const float nm = m[t] == kNegInf ? 0.f : -m[t];
 #pragma unroll
       for (int st = 0; st < kKeyTile / 16; ++st) {
         float pr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pr[i] = none ? 0.f : __builtin_amdgcn_exp2f(lg[st][i] - mn);
+          pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][st][i], cs, nm));
           l[t] += pr[i];
         }
-        // P = hi + lo, both bf16 (round to nearest even): fp32 accuracy through two MFMAs
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
           bf2 hv;
           hv[0] = (__bf16)pr[2 * u];
           hv[1] = (__bf16)pr[2 * u + 1];
+          const uint32_t hw = __builtin_bit_cast(uint32_t, hv);
           bf2 lv;
-          lv[0] = (__bf16)(pr[2 * u] - float(hv[0]));
-          lv[1] = (__bf16)(pr[2 * u + 1] - float(hv[1]));
-          ph[t][st][u] = __builtin_bit_cast(uint32_t, hv);
+          lv[0] = (__bf16)(pr[2 * u] - __uint_as_float(hw << 16));
+          lv[1] = (__bf16)(pr[2 * u + 1] - __uint_as_float(hw & 0xffff0000u));
+          ph[t][st][u] = hw;
           pl[t][st][u] = __builtin_bit_cast(uint32_t, lv);
         }
       }
     }
-    // ---- P.V: A = P (query rows, keys 4 c .. 4 c + 3 of sub-tile st), B = V via transpose reads
+    // ---- P.V on K = 32 MFMAs over sub-tile pairs (2 sp, 2 sp + 1): k-slots 8 c .. 8 c + 3 are keys
+    // 4 c .. 4 c + 3 of the first sub-tile, 8 c + 4 .. 8 c + 7 the same keys of the second; A = P
+    // (hi, then lo) of query 16 t + n, B = V by transpose reads
 #pragma unroll
-    for (int st = 0; st < kKeyTile / 16; ++st) {
-      const uint32_t* vrow = vst + (16 * st + 4 * c + (n >> 2)) * kVPitchW + 2 * (n & 3);
+    for (int sp = 0; sp < kKeyTile / 32; ++sp) {
+      const uint32_t* vr0 = vst + (32 * sp + 4 * c + (n >> 2)) * kVPitchW + 2 * (n & 3);
+      const uint32_t* vr1 = vr0 + 16 * kVPitchW;
 #pragma unroll
       for (int nb = 0; nb < kD / 16; ++nb) {
-        const v4s vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vrow + 8 * nb));
+        const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                        (__attribute__((address_space(3))) v4s*)(vr0 + 8 * nb)));
+        const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                        (__attribute__((address_space(3))) v4s*)(vr1 + 8 * nb)));
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
 #pragma unroll
         for (int t = 0; t < kQTiles; ++t) {
-          const uint2 hp = make_uint2(ph[t][st][0], ph[t][st][1]);
-          const uint2 lp = make_uint2(pl[t][st][0], pl[t][st][1]);
-          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, hp),
-                                                                  __builtin_bit_cast(bf16x4, vb), acc[t][nb], 0, 0, 0);
-          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, lp),
-                                                                  __builtin_bit_cast(bf16x4, vb), acc[t][nb], 0, 0, 0);
+          const uint4 ah = make_uint4(ph[t][2 * sp][0], ph[t][2 * sp][1], ph[t][2 * sp + 1][0], ph[t][2 * sp + 1][1]);
+          const uint4 al = make_uint4(pl[t][2 * sp][0], pl[t][2 * sp][1], pl[t][2 * sp + 1][0], pl[t][2 * sp + 1][1]);
+          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), bop, acc[t][nb], 0, 0, 0);
+          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), bop, acc[t][nb], 0, 0, 0);
         }
       }
     }
-  }
+  };
+  for (int kt = 0;;) {
+    step(0, kt);
+    if (++kt >= nkt) break;
+    step(1, kt);
+    if (++kt >= nkt) break;
   }
   // normaliser of every query column (the 4 lane groups hold partial sums of the same column);
   // acc[t][nb][i]: query 16 t + 4 c + i of the wave, dimension 16 nb + n
@@ -647,14 +709,18 @@ int launch_prefill_attend(const PrefillPlan& p, const sp_tensors& t, char* ws, f
   a.kv_st = t.kv_st;
   a.list = at<int32_t>(ws, p.o_list);
   a.budget = at<int32_t>(ws, p.o_budget);
+  a.kc = at<uint16_t>(ws, p.o_kvc);
+  a.vc = a.kc + size_t(B) * Hq * p.Lpad * kD;
   a.out = out;
   a.L = p.L;
+  a.Lpad = p.Lpad;
   a.Hq = Hq;
   a.G = p.G;
   a.scale_log2 = float(c.softmax_scale * 1.4426950408889634);
   const int nqb = int((p.L + kPfQueryBlock - 1) / kPfQueryBlock);
   hipLaunchKernelGGL(k_pf_zero, dim3(int((p.L + 255) / 256), Hq, B), dim3(256), 0, st, at<uint32_t>(ws, p.o_bits),
                      p.words, p.L, out);
+  hipLaunchKernelGGL(k_pf_gather, dim3(int(p.Lpad / kKeyTile), Hq, B), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_pf_attend, dim3(nqb, Hq, B), dim3(256), 0, st, a);
   return int(hipGetLastError());
 }
