@@ -25,7 +25,8 @@
 //                    on the bf16 MFMA, the causal mask in compact order, an online softmax whose
 //                    reference moves only when a logit exceeds it by 2^8, and P.V (hi and lo halves
 //                    of P), then writes its rows to their positions;
-//   k_pf_zero        positions a head did not keep get zero rows.
+//                    the workgroups past a head's query blocks write the zero rows of the
+//                    positions it did not keep.
 #include "sd_device.h"
 
 namespace sd {
@@ -321,6 +322,8 @@ struct PfAttnArgs {
   const int32_t* budget;  // [B]
   uint16_t* kc;           // gathered K rows [B][Hq][Lpad][d]
   uint16_t* vc;           // gathered V rows [B][Hq][Lpad][d]
+  const uint32_t* bits;   // kept positions [B][Hq][words]
+  int64_t words;
   float* out;             // [B][Hq][L][d]
   int64_t L, Lpad;
   int Hq, G;
@@ -328,13 +331,13 @@ struct PfAttnArgs {
 };
 
 // Compression: every head's K and V rows at its kept positions, in list order, into contiguous
-// per-head sequences; rows from the budget up to the next multiple of kKeyTile are zero (their
+// per-head sequences; rows from the budget up to the next multiple of kPfKeyTile are zero (their
 // logits are masked, and zero values keep their products finite). One workgroup per 64 rows.
 __global__ __launch_bounds__(256) void k_pf_gather(PfAttnArgs a) {
   const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int Li = int(a.L);
   const int kk = min(max(a.budget[b], 1), Li);
-  const int r0 = blockIdx.x * 64;
+  const int r0 = blockIdx.x * kPfKeyTile;
   if (r0 >= kk) return;
   const int g = h / a.G;
   const int32_t* lst = a.list + (int64_t(b) * a.Hq + h) * a.L;
@@ -386,7 +389,32 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
   const int Li = int(a.L);
   const int kk = min(max(a.budget[b], 1), Li);
   const int nqb = (kk + kPfQueryBlock - 1) / kPfQueryBlock;
-  if (int(blockIdx.x) >= nqb) return;
+  if (int(blockIdx.x) >= nqb) {
+    // decompression: the workgroups past the head's query blocks (at least one per head, by the
+    // launch) write the zero rows of the positions the head did not keep, 8 rows of 32 x 16 bytes
+    // per pass, while the attention blocks run
+    const int nz = int(gridDim.x) - nqb, z = int(blockIdx.x) - nqb;
+    const int per = ((Li + nz - 1) / nz + 7) & ~7;
+    const int j1 = min(Li, (z + 1) * per);
+    const uint32_t* hb = a.bits + (int64_t(b) * a.Hq + h) * a.words;
+    float* ob = a.out + (int64_t(b) * a.Hq + h) * a.L * kD + (tid & 31) * 4;
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    for (int j0 = z * per + (tid >> 5); j0 < j1; j0 += 64) {
+      uint32_t w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + 8 * u;
+        const uint32_t wj = hb[min(j, j1 - 1) >> 5] >> (j & 31);  // j0 < j1: an in-range word
+        w[u] = j < j1 ? wj : 1u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (!(w[u] & 1u))
+          __builtin_nontemporal_store(f4v{0.f, 0.f, 0.f, 0.f},
+                                      reinterpret_cast<f4v*>(ob + int64_t(j0 + 8 * u) * kD));
+    }
+    return;
+  }
   const int qb = nqb - 1 - int(blockIdx.x);  // heaviest (longest causal range) first
   const int g = h / a.G;
   const int32_t* lst = a.list + (int64_t(b) * a.Hq + h) * a.L;
@@ -499,18 +527,23 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
     // accuracy of P through two MFMAs. ph / pl [t][st][u]: keys 16 st + 4 c + 2 u, + 1 of query
     // 16 t + n, packed
     uint32_t ph[kQTiles][kKeyTile / 16][2], pl[kQTiles][kKeyTile / 16][2];
+    // both tiles' column maxima, then one wave-uniform test for the rare move of a reference
+    float mt[kQTiles];
 #pragma unroll
     for (int t = 0; t < kQTiles; ++t) {
-      float mt = kNegInf;
+      mt[t] = kNegInf;
 #pragma unroll
       for (int st = 0; st < kKeyTile / 16; ++st)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sacc[t][st][i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      mt *= cs;  // scale > 0: the scaled maximum is the maximum of the scaled logits
-      if (__ballot(mt > m[t] + kPfLazy)) {
-        const float mn = fmaxf(m[t], mt);
+        for (int i = 0; i < 4; ++i) mt[t] = fmaxf(mt[t], sacc[t][st][i]);
+      mt[t] = fmaxf(mt[t], __shfl_xor(mt[t], 16));
+      mt[t] = fmaxf(mt[t], __shfl_xor(mt[t], 32));
+      mt[t] *= cs;  // scale > 0: the scaled maximum is the maximum of the scaled logits
+    }
+    if (__ballot(mt[0] > m[0] + kPfLazy || mt[1] > m[1] + kPfLazy)) {
+#pragma unroll
+      for (int t = 0; t < kQTiles; ++t) {
+        const float mn = fmaxf(m[t], mt[t]);
         const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[t] - mn);
         l[t] *= alpha;
 #pragma unroll
@@ -521,6 +554,9 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
         }
         m[t] = mn;
       }
+    }
+#pragma unroll
+    for (int t = 0; t < kQTiles; ++t) {
       // a column whose reference is still -inf has seen masked logits only: exponent -inf
       const float nm = m[t] == kNegInf ? 0.f : -m[t];
 #pragma unroll
@@ -594,19 +630,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
       }
     }
   }
-}
-
-// Zero rows at the positions a head did not keep (one thread per position).
-__global__ __launch_bounds__(256) void k_pf_zero(const uint32_t* __restrict__ bits, int64_t words, int64_t L,
-                                                 float* __restrict__ out) {
-  const int h = blockIdx.y, b = blockIdx.z, Hq = gridDim.y;
-  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (j >= L) return;
-  const int64_t row = int64_t(b) * Hq + h;
-  if ((bits[row * words + (j >> 5)] >> (j & 31)) & 1u) return;
-  float4* o = reinterpret_cast<float4*>(out + (row * L + j) * kD);
-#pragma unroll
-  for (int i = 0; i < kD / 4; ++i) o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 }  // namespace
@@ -709,6 +732,8 @@ int launch_prefill_attend(const PrefillPlan& p, const sp_tensors& t, char* ws, f
   a.kv_st = t.kv_st;
   a.list = at<int32_t>(ws, p.o_list);
   a.budget = at<int32_t>(ws, p.o_budget);
+  a.bits = at<uint32_t>(ws, p.o_bits);
+  a.words = p.words;
   a.kc = at<uint16_t>(ws, p.o_kvc);
   a.vc = a.kc + size_t(B) * Hq * p.Lpad * kD;
   a.out = out;
@@ -718,10 +743,9 @@ int launch_prefill_attend(const PrefillPlan& p, const sp_tensors& t, char* ws, f
   a.G = p.G;
   a.scale_log2 = float(c.softmax_scale * 1.4426950408889634);
   const int nqb = int((p.L + kPfQueryBlock - 1) / kPfQueryBlock);
-  hipLaunchKernelGGL(k_pf_zero, dim3(int((p.L + 255) / 256), Hq, B), dim3(256), 0, st, at<uint32_t>(ws, p.o_bits),
-                     p.words, p.L, out);
   hipLaunchKernelGGL(k_pf_gather, dim3(int(p.Lpad / kKeyTile), Hq, B), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_pf_attend, dim3(nqb, Hq, B), dim3(256), 0, st, a);
+  // query blocks for a budget up to L, and at least one zero-row block per head past them
+  hipLaunchKernelGGL(k_pf_attend, dim3(nqb + int((p.L + 1023) / 1024), Hq, B), dim3(256), 0, st, a);
   return int(hipGetLastError());
 }
 
