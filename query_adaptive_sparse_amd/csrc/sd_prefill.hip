@@ -444,54 +444,52 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
   }
   // keys of step kt: gathered rows kKeyTile kt + x; thread pieces tid + 256 i (row x = tid / 16 +
   // 16 i, 16-byte piece pc = tid % 16 of it). LDS holds steps kt (being computed) and kt + 1
-  // (written at the start of step kt); two register stages hold the loads of steps kt + 2 and
-  // kt + 3 in flight. One barrier per step.
+  // (written at the start of step kt); one register stage holds the loads of step kt + 2 in flight
+  // for a whole step. One barrier per step.
   const int pc = tid & 15, x0 = tid >> 4;
   const int64_t head = (int64_t(b) * a.Hq + h) * a.Lpad * kD;
   const uint16_t* kthr = a.kc + head + x0 * kD + pc * 8;
   const uint16_t* vthr = a.vc + head + x0 * kD + pc * 8;
-  uint4 rk[2][4], rv[2][4];
-  auto stage = [&](int sbuf, const uint4* dk, const uint4* dv) {
+  uint4 rk[4], rv[4];
+  auto stage = [&](int sbuf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int x = x0 + 16 * i;
-      kstb[sbuf][x * kPPR + (pc ^ pf_kswz(x))] = dk[i];
-      *reinterpret_cast<uint4*>(vstb[sbuf] + x * kVPitchW + pc * 4) = dv[i];
+      kstb[sbuf][x * kPPR + (pc ^ pf_kswz(x))] = rk[i];
+      *reinterpret_cast<uint4*>(vstb[sbuf] + x * kVPitchW + pc * 4) = rv[i];
     }
   };
   const int nkt = (min(kk, (qb + 1) * kPfQueryBlock) + kKeyTile - 1) / kKeyTile;  // causal key tiles
-  auto issue = [&](uint4* dk, uint4* dv, int kt) {
+  auto issue = [&](int kt) {
     kt = kt < nkt ? kt : nkt - 1;  // past the end: the last step again (still cached)
     const int64_t o = int64_t(kt) * kKeyTile * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      dk[i] = ld16(kthr + o + 16 * i * kD);
-      dv[i] = ld16(vthr + o + 16 * i * kD);
+      rk[i] = ld16(kthr + o + 16 * i * kD);
+      rv[i] = ld16(vthr + o + 16 * i * kD);
     }
   };
-  issue(rk[0], rv[0], 0);
-  issue(rk[1], rv[1], 1);
-  stage(0, rk[0], rv[0]);
-  // keep the prologue's loads in the loop's order (the in-flight state entering the loop is then
-  // the state at its back edge, and the loop waits only for the stage it writes to LDS)
-  __builtin_amdgcn_sched_barrier(0);
-  issue(rk[0], rv[0], 2);
-  __builtin_amdgcn_sched_barrier(0);
+  issue(0);
+  stage(0);
+  issue(1);
+  // let step 1's loads land before the loop: the loop head then sees only the loads in flight at
+  // its back edge, and waits for none of them before the barrier
+  __builtin_amdgcn_s_waitcnt(0);
   const float cs = a.scale_log2;
-  // one step; sb = kt % 2 is a constant at each call site, so every register stage stays in
-  // registers
+  // one step; sb = kt % 2 is a constant at each call site
   auto step = [&](const int sb, const int kt) {
     // step kt's tiles (buffer sb) are complete, and every wave is done with step kt - 1, whose
-    // buffer now takes step kt + 1 (registers rk[sb ^ 1]); those registers then load step kt + 3
+    // buffer now takes step kt + 1; the registers then load step kt + 2
     __syncthreads();
-    stage(sb ^ 1, rk[sb ^ 1], rv[sb ^ 1]);
-    issue(rk[sb ^ 1], rv[sb ^ 1], kt + 3);
+    stage(sb ^ 1);
+    issue(kt + 2);
     const uint4* kst = kstb[sb];
     const uint32_t* vst = vstb[sb];
     const int kc0 = kt * kKeyTile;
     if (kc0 > q0w + 31) return;  // every key of the step is after every query of this wave
     // ---- logits: S^T[key 16 st + 4 c + i][query 16 t + n]
     f32x4 sacc[kQTiles][kKeyTile / 16];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int st = 0; st < kKeyTile / 16; ++st) {
       const int x = 16 * st + n;
@@ -508,6 +506,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
         sacc[t][st] = s4;
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // the causal / budget mask is needed only where the step reaches this wave's queries or the
     // end of the compact sequence (a wave-uniform test)
     if (kc0 + kKeyTile - 1 > q0w || kc0 + kKeyTile > kk) {
@@ -585,6 +584,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
     // ---- P.V on K = 32 MFMAs over sub-tile pairs (2 sp, 2 sp + 1): k-slots 8 c .. 8 c + 3 are keys
     // 4 c .. 4 c + 3 of the first sub-tile, 8 c + 4 .. 8 c + 7 the same keys of the second; A = P
     // (hi, then lo) of query 16 t + n, B = V by transpose reads
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int sp = 0; sp < kKeyTile / 32; ++sp) {
       const uint32_t* vr0 = vst + (32 * sp + 4 * c + (n >> 2)) * kVPitchW + 2 * (n & 3);
@@ -605,6 +605,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   for (int kt = 0;;) {
     step(0, kt);
