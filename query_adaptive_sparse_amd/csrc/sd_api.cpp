@@ -9,6 +9,7 @@
 #include <new>
 
 #include "sd_internal.h"
+#include "sp_internal.h"
 
 namespace {
 

@@ -1,11 +1,10 @@
-// Internal plan shared by the host API (sd_api.cpp) and the kernels (sd_kernels.hip).
+// Internal decode plan shared by the host API (sd_api.cpp) and the decode kernels.
 #pragma once
 
 #include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/sparse_decode.h"
-#include "../../include/sparse_prefill.h"
 
 namespace sd {
 
@@ -106,33 +105,8 @@ struct LongRows {
 size_t long_rows_scratch(int64_t rows, int64_t len);
 int launch_long_rows(const LongRows& r, void* stream);
 
-// ---- Token-Sparse prefill
-constexpr int kPfSlab = kMinMaxBlock;  // keys per importance workgroup (and per partial max / min)
-constexpr int kPfKeyBlock = 64;        // keys per proxy-score workgroup
-constexpr int kPfMaxWindow = 64;
-constexpr int kPfQueryBlock = 128;     // compact queries per attention workgroup
-constexpr int kPfKeyTile = 64;         // compact keys per attention step (gathered rows are padded to it)
-
-struct PrefillPlan {
-  sp_config cfg;
-  int32_t G;
-  int64_t L, words;
-  int64_t Lpad;        // L rounded up to kPfKeyTile: rows per head of the gathered K / V
-  int32_t nslab, nkb;  // importance slabs, proxy-score key blocks
-  size_t o_status, o_S, o_pmq, o_M, o_zq, o_imp, o_pmax, o_pmin, o_gimp, o_gpmax, o_gpmin;
-  size_t o_long, o_bbits, o_budget, o_bits, o_list;
-  size_t o_kvc;  // gathered K then V rows [B][Hq][Lpad][d] bf16 each; shares the region of S
-  size_t ws_bytes;
-};
-int launch_prefill_select(const PrefillPlan& p, const sp_tensors& t, char* ws, void* stream);
-int launch_prefill_attend(const PrefillPlan& p, const sp_tensors& t, char* ws, float* out, void* stream);
-
 }  // namespace sd
 
 struct sd_handle {
   sd::Plan plan;
-};
-
-struct sp_handle {
-  sd::PrefillPlan plan;
 };

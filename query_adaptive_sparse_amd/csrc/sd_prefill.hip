@@ -28,6 +28,7 @@
 //                    the workgroups past a head's query blocks write the zero rows of the
 //                    positions it did not keep.
 #include "sd_device.h"
+#include "sp_internal.h"
 
 namespace sd {
 namespace {

@@ -1,0 +1,34 @@
+// Internal plan of the Token-Sparse prefill path, shared by the host API (sd_api.cpp) and the
+// prefill kernels (sd_prefill.hip).
+#pragma once
+
+#include "sd_internal.h"
+#include "../../include/sparse_prefill.h"
+
+namespace sd {
+
+constexpr int kPfSlab = kMinMaxBlock;  // keys per importance workgroup (and per partial max / min)
+constexpr int kPfKeyBlock = 64;        // keys per proxy-score workgroup
+constexpr int kPfMaxWindow = 64;
+constexpr int kPfQueryBlock = 128;     // compact queries per attention workgroup
+constexpr int kPfKeyTile = 64;         // compact keys per attention step (gathered rows are padded to it)
+
+struct PrefillPlan {
+  sp_config cfg;
+  int32_t G;
+  int64_t L, words;
+  int64_t Lpad;        // L rounded up to kPfKeyTile: rows per head of the gathered K / V
+  int32_t nslab, nkb;  // importance slabs, proxy-score key blocks
+  size_t o_status, o_S, o_pmq, o_M, o_zq, o_imp, o_pmax, o_pmin, o_gimp, o_gpmax, o_gpmin;
+  size_t o_long, o_bbits, o_budget, o_bits, o_list;
+  size_t o_kvc;  // gathered K then V rows [B][Hq][Lpad][d] bf16 each; shares the region of S
+  size_t ws_bytes;
+};
+int launch_prefill_select(const PrefillPlan& p, const sp_tensors& t, char* ws, void* stream);
+int launch_prefill_attend(const PrefillPlan& p, const sp_tensors& t, char* ws, float* out, void* stream);
+
+}  // namespace sd
+
+struct sp_handle {
+  sd::PrefillPlan plan;
+};
