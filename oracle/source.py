@@ -59,3 +59,26 @@ class PrefillSource:
 
     def kv_rows(self, b: int, g: int, rows):
         return self._rows(self._K, b, g, rows), self._rows(self._V, b, g, rows)
+
+
+class GistPrefillSource:
+    """Inputs of one gist-masked prefill step as the oracle reads them: raw Q [B][Hq][N][d],
+    K, V [B][Hkv][N][d] and gist Qg [B][Hq][M][d], Kg, Vg [B][Hkv][M][d] on any device; rows are
+    widened to fp64 on demand."""
+
+    def __init__(self, inputs: dict):
+        self._t = {k: inputs[k] for k in ("Q", "K", "V", "Qg", "Kg", "Vg")}
+
+    def _rows(self, name, b, h, rows):
+        t = self._t[name]
+        idx = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=t.device)
+        return _f64(t[b, h].index_select(0, idx))
+
+    def q_row(self, b: int, h: int, kind: str, i: int) -> np.ndarray:
+        return self._rows("Q" if kind == "raw" else "Qg", b, h, [i])[0]
+
+    def raw_kv_rows(self, b: int, g: int, rows):
+        return self._rows("K", b, g, rows), self._rows("V", b, g, rows)
+
+    def gist_kv_rows(self, b: int, g: int, rows):
+        return self._rows("Kg", b, g, rows), self._rows("Vg", b, g, rows)
