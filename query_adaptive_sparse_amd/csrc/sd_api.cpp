@@ -10,6 +10,7 @@
 
 #include "sd_internal.h"
 #include "sp_internal.h"
+#include "gp_internal.h"
 
 namespace {
 
@@ -427,6 +428,55 @@ sd_status sparse_prefill_view(const sp_handle* h, void* ws, sp_view* v) {
 }
 
 void sparse_prefill_destroy(sp_handle* h) { delete h; }
+
+// ---- gist-masked (SSA) prefill
+sd_status sparse_gist_prefill_init(const gp_config* cfg, gp_handle** out) {
+  if (!cfg || !out) return fail(SD_EINVAL, "gist prefill init: NULL argument");
+  *out = nullptr;
+  const gp_config& c = *cfg;
+  if (c.batch < 1) return fail(SD_EINVAL, "batch must be >= 1 (got %d)", c.batch);
+  if (c.n_q_heads < 1 || c.n_kv_heads < 1 || c.n_q_heads % c.n_kv_heads)
+    return fail(SD_EINVAL, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", c.n_q_heads, c.n_kv_heads);
+  if (c.head_dim != 128) return fail(SD_EUNSUPPORTED, "gist prefill: head_dim must be 128 (got %d)", c.head_dim);
+  if (c.kv_dtype != SD_BF16) return fail(SD_EUNSUPPORTED, "gist prefill: kv_dtype must be SD_BF16");
+  if (c.chunk_size < 1) return fail(SD_EINVAL, "chunk_size must be >= 1 (got %d)", c.chunk_size);
+  if (c.n_tokens < 1 || c.n_tokens >= (int64_t(1) << 31))
+    return fail(SD_EINVAL, "n_tokens must be in [1, 2^31) (got %lld)", (long long)c.n_tokens);
+  if (c.n_tokens % c.chunk_size)
+    return fail(SD_EINVAL, "n_tokens (%lld) must be a multiple of chunk_size (%d)", (long long)c.n_tokens, c.chunk_size);
+  if (!(c.softmax_scale > 0.0) || !std::isfinite(c.softmax_scale))
+    return fail(SD_EINVAL, "softmax_scale must be finite and > 0 (got %g)", c.softmax_scale);
+  gp_handle* h = new (std::nothrow) gp_handle();
+  if (!h) return fail(SD_EINVAL, "gist prefill init: out of host memory");
+  h->plan.cfg = c;
+  h->plan.G = c.n_q_heads / c.n_kv_heads;
+  h->plan.M = int32_t(c.n_tokens / c.chunk_size);
+  *out = h;
+  return ok();
+}
+
+sd_status sparse_gist_prefill_attend(const gp_handle* h, const gp_tensors* t, float* out, float* out_gist,
+                                     void* stream) {
+  if (!h) return fail(SD_EINVAL, "gist prefill attend: NULL handle");
+  if (!t) return fail(SD_EINVAL, "gist prefill attend: tensors is NULL");
+  const void* ptrs[6] = {t->q, t->k, t->v, t->qg, t->kg, t->vg};
+  for (const void* ptr : ptrs)
+    if (!ptr || !aligned16(ptr))
+      return fail(SD_EINVAL, "gist prefill: q, k, v, qg, kg and vg must be non-NULL 16-byte aligned pointers");
+  const int64_t d = h->plan.cfg.head_dim;
+  auto ok8 = [](int64_t x) { return x >= 0 && x % 8 == 0; };
+  auto rows_ok = [&](int64_t sb, int64_t sh, int64_t st) { return ok8(sb) && ok8(sh) && ok8(st) && st >= d; };
+  if (!rows_ok(t->q_sb, t->q_sh, t->q_st) || !rows_ok(t->kv_sb, t->kv_sh, t->kv_st) ||
+      !rows_ok(t->qg_sb, t->qg_sh, t->qg_st) || !rows_ok(t->kvg_sb, t->kvg_sh, t->kvg_st))
+    return fail(SD_EINVAL, "gist prefill: strides must be multiples of 8 elements with rows of at least head_dim");
+  if (!out || !out_gist || !aligned16(out) || !aligned16(out_gist))
+    return fail(SD_EINVAL, "gist prefill attend: out and out_gist must be non-NULL 16-byte aligned pointers");
+  int e = sd::launch_gist_prefill(h->plan, *t, out, out_gist, stream);
+  if (e) return fail(SD_EHIP, "gist prefill attend: HIP error %d (%s)", e, sd::hip_error_string(e));
+  return ok();
+}
+
+void sparse_gist_prefill_destroy(gp_handle* h) { delete h; }
 
 const char* sparse_decode_last_error(void) { return g_err; }
 

@@ -24,7 +24,8 @@ EXPORTS = ("sparse_decode_init", "sparse_decode_num_levels", "sparse_decode_atte
            "sparse_decode_attend", "sparse_decode_combine", "sparse_decode_selection_view",
            "sparse_decode_last_error", "sparse_decode_destroy",
            "sparse_prefill_init", "sparse_prefill_select", "sparse_prefill_attend", "sparse_prefill_view",
-           "sparse_prefill_destroy")
+           "sparse_prefill_destroy",
+           "sparse_gist_prefill_init", "sparse_gist_prefill_attend", "sparse_gist_prefill_destroy")
 
 
 class sd_config(ctypes.Structure):
@@ -92,6 +93,25 @@ class sp_view(ctypes.Structure):
     ]
 
 
+class gp_config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("n_tokens", ctypes.c_int64), ("chunk_size", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_double),
+    ]
+
+
+class gp_tensors(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64), ("q_st", ctypes.c_int64),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("kv_sb", ctypes.c_int64), ("kv_sh", ctypes.c_int64), ("kv_st", ctypes.c_int64),
+        ("qg", ctypes.c_void_p), ("qg_sb", ctypes.c_int64), ("qg_sh", ctypes.c_int64), ("qg_st", ctypes.c_int64),
+        ("kg", ctypes.c_void_p), ("vg", ctypes.c_void_p),
+        ("kvg_sb", ctypes.c_int64), ("kvg_sh", ctypes.c_int64), ("kvg_st", ctypes.c_int64),
+    ]
+
+
 class SparseDecodeError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
@@ -139,6 +159,12 @@ def lib() -> ctypes.CDLL:
         L.sparse_prefill_view.restype = st
         L.sparse_prefill_destroy.argtypes = [vp]
         L.sparse_prefill_destroy.restype = None
+        L.sparse_gist_prefill_init.argtypes = [ctypes.POINTER(gp_config), ctypes.POINTER(vp)]
+        L.sparse_gist_prefill_init.restype = st
+        L.sparse_gist_prefill_attend.argtypes = [vp, ctypes.POINTER(gp_tensors), vp, vp, vp]
+        L.sparse_gist_prefill_attend.restype = st
+        L.sparse_gist_prefill_destroy.argtypes = [vp]
+        L.sparse_gist_prefill_destroy.restype = None
         _lib = L
     return _lib
 
@@ -218,3 +244,18 @@ def sparse_prefill_view(handle, ws: int) -> sp_view:
 
 def sparse_prefill_destroy(handle):
     lib().sparse_prefill_destroy(handle)
+
+
+def sparse_gist_prefill_init(cfg: gp_config):
+    """Returns the handle (the path needs no workspace)."""
+    h = ctypes.c_void_p()
+    _check(lib().sparse_gist_prefill_init(ctypes.byref(cfg), ctypes.byref(h)))
+    return h
+
+
+def sparse_gist_prefill_attend(handle, tensors: gp_tensors, out: int, out_gist: int, stream: int):
+    _check(lib().sparse_gist_prefill_attend(handle, ctypes.byref(tensors), out, out_gist, stream))
+
+
+def sparse_gist_prefill_destroy(handle):
+    lib().sparse_gist_prefill_destroy(handle)

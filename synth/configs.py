@@ -173,8 +173,42 @@ P1T = replace(P1, name="p1t", batch=2, n_q_heads=8, n_kv_heads=2, seq_len=1024, 
 PREFILL = {w.name: w for w in (P1, P1S, P1T)}
 
 
+@dataclass(frozen=True)
+class GistWorkload:
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    n_tokens: int              # N raw tokens, M = N / chunk_size gists
+    chunk_size: int
+    softmax_scale: float
+    dtype: str = "bf16"
+    seed: int = 0
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def n_chunks(self) -> int:
+        return self.n_tokens // self.chunk_size
+
+
+# Gist-masked prefill of the Qwen2-7B shape with the SSA decode workload's chunking (16 raw tokens per
+# gist) over a 32K prompt; small cases for parity: a 2K prompt, and odd shapes (one-token chunks,
+# chunks that do not divide the 128-query block, a sequence that ends mid-block).
+G1 = GistWorkload(name="p2_ssa_qwen2_7b_32k", batch=1, n_q_heads=28, n_kv_heads=4, head_dim=128, n_tokens=32768,
+                  chunk_size=16, softmax_scale=_inv_sqrt(128), seed=41)
+G1S = replace(G1, name="p2s", n_tokens=2048, seed=42)
+G1T = replace(G1, name="p2t", batch=2, n_q_heads=4, n_kv_heads=2, n_tokens=1000, chunk_size=20, seed=43)
+GIST = {w.name: w for w in (G1, G1S, G1T)}
+
+
 def get(name: str):
-    return ALL[name] if name in ALL else PREFILL[name]
+    if name in ALL:
+        return ALL[name]
+    return PREFILL[name] if name in PREFILL else GIST[name]
 
 
 def library_params(w: Workload) -> dict:

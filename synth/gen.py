@@ -53,6 +53,7 @@ _M32 = 0xFFFFFFFF
 T_Q, T_K, T_V, T_KG, T_VG, T_KMG, T_P = 1, 2, 3, 4, 5, 6, 7
 T_PERM, T_OFF, T_Z = 8, 9, 10
 T_PQ, T_PK, T_PV, T_PU, T_PPERM = 11, 12, 13, 14, 15  # prefill
+T_GQ, T_GK, T_GV, T_GQG, T_GKG, T_GVG = 16, 17, 18, 19, 20, 21  # gist-masked prefill
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "f64": torch.float64}
 
@@ -266,3 +267,18 @@ def make_prefill_inputs(w: PrefillWorkload, device="cpu", seed: int | None = Non
             z = normal_at(seed, T_PK, flat, "f64").view(L, d)
             K[b, g] = (z + gamma[:, None] * u[None, :]).to(dt)
     return {"workload": w, "seed": seed, "Q": Q, "K": K, "V": V}
+
+
+def make_gist_inputs(w, device="cpu", seed: int | None = None) -> dict:
+    """Raw Q [B][Hq][N][d], K, V [B][Hkv][N][d] and gist Qg [B][Hq][M][d], Kg, Vg [B][Hkv][M][d] of one
+    gist-masked prefill step of workload ``w``: independent N(0, 1) entries rounded to the dtype (the
+    attention's cost does not depend on the values; the parity tests check every visible key)."""
+    seed = w.seed if seed is None else seed
+    B, Hq, Hk, d, N, C = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_tokens, w.chunk_size
+    M = N // C
+    out = {"workload": w, "seed": seed}
+    for name, tag, shape in (("Q", T_GQ, (B, Hq, N, d)), ("K", T_GK, (B, Hk, N, d)), ("V", T_GV, (B, Hk, N, d)),
+                             ("Qg", T_GQG, (B, Hq, M, d)), ("Kg", T_GKG, (B, Hk, M, d)),
+                             ("Vg", T_GVG, (B, Hk, M, d))):
+        out[name] = normal(shape, seed, tag, w.dtype, device)
+    return out

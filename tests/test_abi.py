@@ -15,7 +15,7 @@ INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 
 def test_header_symbols_exported():
     src = "".join(open(os.path.join(INCLUDE, f)).read() for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h"))
-    declared = sorted(set(re.findall(r"\b(sparse_(?:decode|prefill)_\w+)\s*\(", src)))
+    declared = sorted(set(re.findall(r"\b(sparse_(?:decode|prefill|gist_prefill)_\w+)\s*\(", src)))
     assert declared, "no declarations found"
     lib = ctypes.CDLL(N.LIB_PATH)
     for name in declared:
@@ -253,3 +253,51 @@ def test_prefill_calls_reject_before_enqueue():
     assert L.sparse_prefill_view(h, 256, ctypes.byref(v)) == N.SD_OK
     assert v.words == (configs.get("p1s").seq_len + 31) // 32
     N.sparse_prefill_destroy(h)
+
+
+def _gist_cfg(**kw):
+    w = configs.get("p2s")
+    c = N.gp_config()
+    c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    c.n_tokens, c.chunk_size, c.kv_dtype, c.softmax_scale = w.n_tokens, w.chunk_size, N.SD_BF16, w.softmax_scale
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+GIST_BAD = [
+    (dict(batch=0), N.SD_EINVAL, "batch"),
+    (dict(n_kv_heads=5), N.SD_EINVAL, "multiple"),
+    (dict(head_dim=64), N.SD_EUNSUPPORTED, "head_dim"),
+    (dict(kv_dtype=N.SD_F32), N.SD_EUNSUPPORTED, "kv_dtype"),
+    (dict(chunk_size=0), N.SD_EINVAL, "chunk_size"),
+    (dict(n_tokens=0), N.SD_EINVAL, "n_tokens"),
+    (dict(n_tokens=1 << 31), N.SD_EINVAL, "n_tokens"),
+    (dict(n_tokens=2050), N.SD_EINVAL, "multiple of chunk_size"),
+    (dict(softmax_scale=float("inf")), N.SD_EINVAL, "softmax_scale"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", GIST_BAD, ids=[b[2] + str(i) for i, b in enumerate(GIST_BAD)])
+def test_gist_init_rejects(kw, status, msg):
+    with pytest.raises(N.SparseDecodeError) as e:
+        N.sparse_gist_prefill_init(_gist_cfg(**kw))
+    assert e.value.status == status
+    assert msg in str(e.value)
+
+
+def test_gist_attend_rejects_before_enqueue():
+    h = N.sparse_gist_prefill_init(_gist_cfg())
+    L = N.lib()
+    t = N.gp_tensors()
+    assert L.sparse_gist_prefill_attend(None, ctypes.byref(t), 0x1000, 0x2000, None) == N.SD_EINVAL
+    assert L.sparse_gist_prefill_attend(h, None, 0x1000, 0x2000, None) == N.SD_EINVAL
+    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), 0x1000, 0x2000, None) == N.SD_EINVAL  # null tensors
+    t.q, t.k, t.v, t.qg, t.kg, t.vg = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000
+    t.q_st = t.kv_st = t.qg_st = t.kvg_st = 128
+    t.kvg_st = 100                                                      # gist rows not 16-byte aligned
+    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), 0x1000, 0x2000, None) == N.SD_EINVAL
+    t.kvg_st = 128
+    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), None, 0x2000, None) == N.SD_EINVAL  # null out
+    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), 0x1000, 0x2008, None) == N.SD_EINVAL  # misaligned
+    N.sparse_gist_prefill_destroy(h)
