@@ -250,6 +250,104 @@ def bench_prefill(args, w):
     print(json.dumps(line), flush=True)
 
 
+def gist_pairs(w) -> int:
+    """(query, visible key) pairs of one head of a gist-masked layer: raw token t sees t // C gists
+    and t % C + 1 raw tokens, gist m sees m + 1 gists and C raw tokens."""
+    C, M = w.chunk_size, w.n_chunks
+    return C * M * (M - 1) // 2 + M * C * (C + 1) // 2 + M * (M + 1) // 2 + M * C
+
+
+def gist_cpu_baseline(w, inp, target_s=15.0):
+    """The fp64 gist-prefill oracle (as it stands) on a bounded sample: query rows of one head drawn
+    uniformly over the raw tokens and the gists, scaled to a full layer (every head, every row)."""
+    from oracle import GistPrefillSource, gref
+    from threadpoolctl import threadpool_info
+
+    src = GistPrefillSource({k: inp[k].cpu() for k in ("Q", "K", "V", "Qg", "Kg", "Vg")})
+    rng = np.random.default_rng(0)
+    n_rows = w.n_tokens + w.n_chunks
+    done, t_rows = 0, 0.0
+    while t_rows < target_s and done < n_rows:
+        i = int(rng.integers(0, n_rows))
+        kind, row = ("raw", i) if i < w.n_tokens else ("gist", i - w.n_tokens)
+        t0 = time.perf_counter()
+        gref.gp_attend_rows(w, src, 0, 0, kind, [row])
+        t_rows += time.perf_counter() - t0
+        done += 1
+    step_s = w.batch * w.n_q_heads * n_rows * t_rows / done
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(w.batch * w.n_tokens / step_s, 4), "unit": "prompt tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{w.name}: {done} of {n_rows} query rows (raw and gist, uniform) of 1 of "
+                      f"{w.batch * w.n_q_heads} heads ({t_rows:.1f} s), scaled to a full layer ({step_s:.0f} s)",
+            "cpu": _cpu_model()}
+
+
+def bench_gist(args, w):
+    """Gist-masked (SSA) prefill layer: every raw and gist query over its visible keys (a gist prefix
+    and its chunk's raw run), over a seeded synthetic prompt resident in HBM."""
+    from synth import gen
+    from query_adaptive_sparse_amd import GistPrefill, make_gist_tensors
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    print(f"[bench] gist prefill workload {w.name}: generating inputs on {torch.cuda.get_device_name(0)}",
+          file=sys.stderr, flush=True)
+    inp = gen.make_gist_inputs(w, device=dev)
+    gp = GistPrefill(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
+                     n_tokens=w.n_tokens, chunk_size=w.chunk_size, softmax_scale=w.softmax_scale)
+    t = make_gist_tensors(inp["Q"], inp["K"], inp["V"], inp["Qg"], inp["Kg"], inp["Vg"])
+    out = torch.empty(w.batch, w.n_q_heads, w.n_tokens, w.head_dim, dtype=torch.float32, device=dev)
+    outg = torch.empty(w.batch, w.n_q_heads, w.n_chunks, w.head_dim, dtype=torch.float32, device=dev)
+    warm, K = max(1, args.warmup), max(1, min(args.steps, 200))
+    for _ in range(warm):
+        gp.attend(t, out, outg)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({warm} steps)", file=sys.stderr, flush=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        gp.attend(t, out, outg)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+    attend_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    print(f"[bench] timed {K} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    # useful flops: 2 (q.k) + 2 (p.v) per (query, visible key, dimension)
+    flops = float(w.batch * w.n_q_heads * gist_pairs(w) * w.head_dim * 4)
+    tflops = flops / (attend_ms * 1e-3) / 1e12
+    dense = float(w.batch * w.n_q_heads * (w.n_tokens + w.n_chunks) * (w.n_tokens + w.n_chunks + 1) // 2
+                  * w.head_dim * 4)
+    line = {
+        "metric": "gist-masked (SSA) prefill attention prompt tokens/s at 32K ctx",
+        "value": round(w.batch * w.n_tokens / (ms_per_step * 1e-3), 2),
+        "unit": "prompt tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": warm,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based N(0,1) raw and gist Q, K, V)",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "context": w.n_tokens, "chunk_size": w.chunk_size,
+                   "gists": w.n_chunks},
+        "useful_fraction_of_dense": round(flops / dense, 4),
+        "roofline": {"kernel": "k_gp_attend (gist-masked block-sparse attention)", "bound": "mfma",
+                     "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None, "flops_per_launch": flops,
+                     "avg_launch_ms": round(attend_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] gist prefill cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = gist_cpu_baseline(w, inp)
+    print(json.dumps(line), flush=True)
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -275,6 +373,8 @@ def main():
 
     if args.workload in configs.PREFILL:
         return bench_prefill(args, configs.get(args.workload))
+    if args.workload in configs.GIST:
+        return bench_gist(args, configs.get(args.workload))
     w = configs.get(args.workload) if args.workload else configs.BENCH
     params = configs.library_params(w)
     if args.attend_blocks is not None:
