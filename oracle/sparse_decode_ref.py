@@ -164,7 +164,7 @@ def coverage_budget(imp: np.ndarray, tau: float):
     removed = int(hit[0]) + 1 if hit.size else n
     above = abs(c[removed - 1] - thr)
     below = abs(c[removed - 2] - thr) if removed >= 2 else abs(thr)
-    return max(1, n - removed), min(above, below) / T
+    return max(1, n - removed), (min(above, below) / T if T > 0 else math.inf)
 
 
 def candidates(segments: np.ndarray, seg_size: int) -> np.ndarray:

@@ -32,6 +32,13 @@ Readings where the page is silent (fixed choices of this oracle):
   ``softmax_scale``; output rows scattered back to positions S_h, every other
   row of the head is zero. Keys and values come from the head's KV group
   (h // G).
+* Mixed heads ([EA] technical summary of "Elastic Attention" (gist.science,
+  paper 2601.17367), sections 2.1 and 2.3: a router assigns every attention head full attention (FA) or sparse
+  attention (SA), and one fused kernel runs all heads): ``head_mode[h] = 1``
+  marks a full-attention query head, 0 a sparse one (the router's decision is an
+  input; the page does not define SA's pattern, read here as the Token-Sparse
+  selection above). Full heads keep every position (plain causal attention);
+  the budget is the coverage cut of the sparse heads' importances only.
 
 Arithmetic: inputs arrive as fp64 (their bf16 values are exact in fp64).
 """
@@ -67,20 +74,31 @@ def proxy_importance(Qw: np.ndarray, K: np.ndarray, scale: float, pos0: int) -> 
     return imp
 
 
+def head_modes(w) -> list:
+    """[EA] head-wise routing: 1 = full-attention head, 0 = sparse head (all sparse by default)."""
+    m = getattr(w, "head_mode", None)
+    return [0] * w.n_q_heads if m is None else [int(x) for x in m]
+
+
 def tsa_select(w, src, b: int) -> dict:
     """Per-head importances, the global budget and every head's positions for sequence b."""
     L, W, Hq = w.seq_len, w.window, w.n_q_heads
     G = Hq // w.n_kv_heads
+    modes = head_modes(w)
     imps = []
     for h in range(Hq):
         Qw = src.q_rows(b, h, np.arange(L - W, L))
         imps.append(proxy_importance(Qw, src.k_all(b, h // G), w.softmax_scale, L - W))
     total = np.zeros(L, dtype=np.float64)
-    for imp in imps:
-        total = total + imp
+    for h in range(Hq):
+        if not modes[h]:
+            total = total + imps[h]
     k, margin = coverage_budget(total, w.tau)
     sets, gaps = {}, {}
     for h in range(Hq):
+        if modes[h]:
+            sets[h], gaps[h] = np.arange(L), math.inf
+            continue
         sets[h] = select_top_k(imps[h], k)
         o = order_desc(imps[h])
         gaps[h] = abs(imps[h][o[k - 1]] - imps[h][o[k]]) if k < L else math.inf

@@ -169,5 +169,42 @@ def pin_attention_dense_limit(pref, seed=24):
         assert np.allclose(o, ref.numpy(), rtol=1e-11, atol=1e-12), h
 
 
+def pin_mixed_heads(pref, seed=25):
+    """Head-wise full / sparse routing: the budget is the exact coverage cut of the sparse heads'
+    summed importance only, every sparse head keeps its brute-force top-budget subset, and a full
+    head keeps every position."""
+    rng = np.random.default_rng(seed)
+    for t, modes in enumerate([(1, 0, 0, 1), (0, 1, 1, 1), (1, 1, 0, 0)]):
+        w = _workload(seq_len=int(rng.integers(6, 12)), window=3, tau=float(rng.uniform(0.05, 0.7)),
+                      n_q_heads=4, n_kv_heads=2, head_dim=4, head_mode=modes)
+        src = _Src(w, rng, scale=1.5)
+        for b in range(w.batch):
+            r = pref.tsa_select(w, src, b)
+            total = sum(_torch_importance(src.Q[b, h, w.seq_len - w.window:], src.K[b, h // 2], w.softmax_scale,
+                                          w.seq_len - w.window) for h in range(w.n_q_heads) if not modes[h])
+            k = _brute_budget(total, w.tau)
+            assert r["budget"] == k, (t, b, r["budget"], k)
+            for h in range(w.n_q_heads):
+                want = list(range(w.seq_len)) if modes[h] else _brute_topk(r["importance"][h], k)
+                assert r["sets"][h].tolist() == want, (t, b, h)
+
+
+def pin_full_heads_textbook(pref, seed=26):
+    """Every head routed to full attention: the layer is textbook causal attention (torch SDPA,
+    fp64) for every head."""
+    rng = np.random.default_rng(seed)
+    w = _workload(seq_len=33, window=4, head_mode=(1, 1, 1, 1))
+    src = _Src(w, rng)
+    res = pref.tsa_prefill(w, src)
+    G = w.n_q_heads // w.n_kv_heads
+    for b in range(w.batch):
+        for h in range(w.n_q_heads):
+            q = torch.from_numpy(src.Q[b, h])[None, None]
+            k = torch.from_numpy(src.K[b, h // G])[None, None]
+            v = torch.from_numpy(src.V[b, h // G])[None, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=w.softmax_scale)
+            assert np.allclose(res["out"][b, h], ref[0, 0].numpy(), rtol=1e-11, atol=1e-12), (b, h)
+
+
 PREFILL_PINS = [pin_importance_library, pin_importance_invariants, pin_select_bruteforce,
-                pin_attention_masked_dense, pin_attention_dense_limit]
+                pin_attention_masked_dense, pin_attention_dense_limit, pin_mixed_heads, pin_full_heads_textbook]

@@ -22,6 +22,9 @@ MUTATIONS = {
     "attention_wrong_kv_group": ("    g = h // G\n    o =", "    g = h % w.n_kv_heads\n    o ="),
     "query_at_compact_index": ("src.q_rows(b, h, S[i:i + 1])", "src.q_rows(b, h, [i])"),
     "scatter_not_zeroed": ("            O[b, h] = 0.0\n", "            O[b, h] = 1.0\n"),
+    "full_heads_in_budget": ("        if not modes[h]:\n            total = total + imps[h]", "        total = total + imps[h]"),
+    "full_head_uses_budget": ("        if modes[h]:\n            sets[h], gaps[h] = np.arange(L), math.inf\n            continue\n", ""),
+    "modes_ignored": ("return [0] * w.n_q_heads if m is None else", "return [0] * w.n_q_heads if True else"),
 }
 
 
