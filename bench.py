@@ -147,34 +147,40 @@ def counter_traffic(workload: str, attend_blocks: int):
 
 def prefill_cpu_baseline(w, inp, sel, target_s=15.0):
     """The fp64 prefill oracle (as it stands) on a bounded sample: one head's proxy-map importance
-    and the compressed attention of sampled query rows of that head (the oracle's per-row cost
-    grows with the row's causal range, so rows are drawn uniformly over the compact sequence),
-    scaled to a full layer (every head's importance, every head's k rows)."""
+    and the compressed attention of sampled query rows of one sparse head (and of one full-attention
+    head, if the routing has any; the oracle's per-row cost grows with the row's causal range, so
+    rows are drawn uniformly over the head's sequence), scaled to a full layer (every head's
+    importance, every head's rows)."""
     from oracle import PrefillSource, pref
     from threadpoolctl import threadpool_info
 
     src = PrefillSource({k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inp.items() if k in ("Q", "K", "V")})
     L, W = w.seq_len, w.window
+    modes = pref.head_modes(w)
     t0 = time.perf_counter()
     pref.proxy_importance(src.q_rows(0, 0, np.arange(L - W, L)), src.k_all(0, 0), w.softmax_scale, L - W)
     t_imp = time.perf_counter() - t0
     k = int(sel["budget"][0])
-    S = sel["list"][0, 0, :k].cpu().numpy().astype(np.int64)
+    kinds = [m for m in (0, 1) if m in modes]
     rng = np.random.default_rng(0)
-    done, t_rows = 0, 0.0
-    while t_rows < target_s and done < k:
-        i = int(rng.integers(0, k))
-        t0 = time.perf_counter()
-        pref.tsa_attend_rows(w, src, 0, 0, S, [i])
-        t_rows += time.perf_counter() - t0
-        done += 1
-    per_row = t_rows / done
-    step_s = w.batch * w.n_q_heads * (t_imp + k * per_row)
+    step_s, notes = w.batch * w.n_q_heads * t_imp, []
+    for m in kinds:
+        h = modes.index(m)
+        n = L if m else k
+        S = sel["list"][0, h, :n].cpu().numpy().astype(np.int64)
+        done, t_rows = 0, 0.0
+        while t_rows < target_s / len(kinds) and done < n:
+            i = int(rng.integers(0, n))
+            t0 = time.perf_counter()
+            pref.tsa_attend_rows(w, src, 0, h, S, [i])
+            t_rows += time.perf_counter() - t0
+            done += 1
+        step_s += w.batch * modes.count(m) * n * t_rows / done
+        notes.append(f"{done} of {n} attention rows of {'full' if m else 'sparse'} head {h} ({t_rows:.1f} s)")
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(w.batch * L / step_s, 4), "unit": "prompt tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{w.name}: importance of 1 of {w.batch * w.n_q_heads} heads ({t_imp:.1f} s) and {done} of "
-                      f"{k} compact attention rows of that head ({t_rows:.1f} s), scaled to a full layer "
-                      f"({step_s:.0f} s)",
+            "sample": f"{w.name}: importance of 1 of {w.batch * w.n_q_heads} heads ({t_imp:.1f} s), "
+                      + ", ".join(notes) + f"; scaled to a full layer ({step_s:.0f} s)",
             "cpu": _cpu_model()}
 
 
@@ -192,7 +198,8 @@ def bench_prefill(args, w):
     sp = SparsePrefill(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
                        seq_len=w.seq_len, window=w.window, tau=w.tau, softmax_scale=w.softmax_scale, device=dev)
     sp.alloc_workspace()
-    t = make_prefill_tensors(inp["Q"], inp["K"], inp["V"])
+    hm = None if w.head_mode is None else torch.tensor(w.head_mode, dtype=torch.int8, device=dev)
+    t = make_prefill_tensors(inp["Q"], inp["K"], inp["V"], head_mode=hm)
     out = torch.empty(w.batch, w.n_q_heads, w.seq_len, w.head_dim, dtype=torch.float32, device=dev)
     warm, K = max(1, min(args.warmup, 3)), max(1, min(args.steps, 10))
     for _ in range(warm):
@@ -216,12 +223,15 @@ def bench_prefill(args, w):
     sel = sp.selection()
     budgets = sel["budget"].cpu().numpy().astype(np.int64)
     status = int(sel["status"].cpu().numpy()[0])
-    # useful attention flops: per head, causal compact attention over k tokens, 2 (q.k) + 2 (p.v)
-    # flops per (query, key, dimension)
-    flops = float(sum(w.n_q_heads * (kk * (kk + 1) // 2) * w.head_dim * 4 for kk in budgets))
+    # useful attention flops: per head, causal compact attention over k tokens (every token for a
+    # full-attention head), 2 (q.k) + 2 (p.v) flops per (query, key, dimension)
+    modes = list(w.head_mode) if w.head_mode is not None else [0] * w.n_q_heads
+    flops = float(sum((w.seq_len if m else kk) * ((w.seq_len if m else kk) + 1) // 2 * w.head_dim * 4
+                      for kk in budgets for m in modes))
     tflops = flops / (attend_ms * 1e-3) / 1e12
     line = {
-        "metric": "token-sparse prefill attention prompt tokens/s at 128K ctx",
+        "metric": ("token-sparse prefill attention prompt tokens/s at 128K ctx" if w.head_mode is None else
+                   "mixed full / token-sparse head prefill attention prompt tokens/s at 128K ctx"),
         "value": round(w.batch * w.seq_len / (ms_per_step * 1e-3), 2),
         "unit": "prompt tokens/s",
         "n_gpus": 1,
@@ -234,7 +244,8 @@ def bench_prefill(args, w):
         "dtype": "bf16",
         "data": "synthetic (seeded counter-based N(0,1) Q, K, V with a planted Zipf key-importance profile per KV group)",
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
-                   "head_dim": w.head_dim, "context": w.seq_len, "window": w.window, "tau": w.tau},
+                   "head_dim": w.head_dim, "context": w.seq_len, "window": w.window, "tau": w.tau,
+                   "full_attention_heads": sum(modes)},
         "budget_tokens": budgets.tolist(),
         "stages_ms": {"select": round(select_ms, 4), "attend": round(attend_ms, 4),
                       "note": "attend = zero rows for unkept positions + compressed attention"},

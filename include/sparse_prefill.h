@@ -13,6 +13,7 @@
  *               left give the budget k (at least 1). Every head then keeps its own k
  *               tokens of highest importance (equal importance: lower position
  *               first), as an ascending position list.
+ *               A head routed to full attention (head_mode) keeps every position instead.
  *   2. attend   compression: the head's Q, K and V rows at its k positions form a
  *               compact sequence; causal softmax attention runs on it (compact row i
  *               attends compact rows 0..i); decompression: row i of the result is
@@ -54,16 +55,23 @@ typedef struct {
 } sp_config;
 
 /* Device tensors, last dimension contiguous, element strides, 16-byte aligned rows.
- *   q    [B][Hq][L][d]     bf16   strides q_sb, q_sh, q_st
- *   k, v [B][Hkv][L][d]    bf16   strides kv_sb, kv_sh, kv_st (k and v share them) */
+ *   q         [B][Hq][L][d]   bf16   strides q_sb, q_sh, q_st
+ *   k, v      [B][Hkv][L][d]  bf16   strides kv_sb, kv_sh, kv_st (k and v share them)
+ *   head_mode [Hq]            int8   or NULL (every head sparse). Head-wise routing of the technical
+ *             summary of "Elastic Attention" (gist.science, paper 2601.17367), sections 2.1 and 2.3:
+ *             1 = full-attention head (keeps every position: plain causal attention), 0 = sparse head
+ *             (the selection above). The budget is cut from the sparse heads' importances only; all
+ *             heads run in the same launches. Values other than 0 count as 1. select and attend
+ *             must be given the same routing. */
 typedef struct {
   const void* q;  int64_t q_sb, q_sh, q_st;
   const void* k;  const void* v;  int64_t kv_sb, kv_sh, kv_st;
+  const int8_t* head_mode;
 } sp_tensors;
 
 /* Device pointers into a workspace after select.
  *   importance fp64 [B][Hq][L]    head h's proxy-map column sums
- *   budget     int32 [B]          tokens kept per head
+ *   budget     int32 [B]          tokens kept per sparse head (unused when every head is full)
  *   head_bits  u32 [B][Hq][words] head h's positions, bit j of word j/32
  *   list       int32 [B][Hq][L]   head h's positions ascending; the first budget[b] valid
  *   status     u32 [4]            [0] != 0: a selection row overflowed its candidate buffer */

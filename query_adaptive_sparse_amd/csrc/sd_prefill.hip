@@ -10,12 +10,13 @@
 //   k_pf_zpart       per 2048-key slab and query, the sum of exp(scale (s - max)) over the slab;
 //   k_pf_importance  per key, the sum over the window queries (in order) of the query's softmax
 //                    probability of that key, and the slab's max / min of it;
-//   k_pf_global      per key, the heads' importances summed in head order;
+//   k_pf_global      per key, the sparse heads' importances summed in head order;
 //   long-row pass    top-p of the global importance with the values as masses, p = 1 - tau;
 //   k_pf_budget      budget = (that count) - 1, at least 1: the tokens left after cutting the
 //                    ascending tail whose mass exceeds tau of the total;
 //   long-row pass    every head's top-budget tokens by its own importance;
-//   k_pf_lists       each head's bitmap as an ascending position list.
+//   k_pf_lists       each head's bitmap as an ascending position list (a full-attention head:
+//                    every position).
 // Attention:
 //   k_pf_gather      compression: every head's K and V rows at its kept positions, in list order,
 //                    into contiguous per-head sequences (padded with zero rows to a whole step);
@@ -235,16 +236,17 @@ __global__ __launch_bounds__(256) void k_pf_importance(PfImpArgs a) {
 }
 
 // Per key: the heads' importances summed in head order; and the slab's max / min.
-__global__ __launch_bounds__(256) void k_pf_global(const double* __restrict__ imp, int Hq, int64_t L, int nslab,
-                                                   double* __restrict__ gimp, double* __restrict__ gpmax,
-                                                   double* __restrict__ gpmin) {
+__global__ __launch_bounds__(256) void k_pf_global(const double* __restrict__ imp, const int8_t* __restrict__ mode,
+                                                   int Hq, int64_t L, int nslab, double* __restrict__ gimp,
+                                                   double* __restrict__ gpmax, double* __restrict__ gpmin) {
   const int sl = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ double rmax[4], rmin[4];
   const int64_t j0 = int64_t(sl) * kPfSlab, j1 = j0 + kPfSlab < L ? j0 + kPfSlab : L;
   double mx = kNegInfD, mn = kPosInfD;
   for (int64_t j = j0 + tid; j < j1; j += 256) {
     double v = 0.0;
-    for (int h = 0; h < Hq; ++h) v += imp[(int64_t(b) * Hq + h) * L + j];
+    for (int h = 0; h < Hq; ++h)
+      if (!mode || !mode[h]) v += imp[(int64_t(b) * Hq + h) * L + j];  // sparse heads only
     gimp[int64_t(b) * L + j] = v;
     mx = fmax(mx, v);
     mn = fmin(mn, v);
@@ -280,13 +282,22 @@ __global__ __launch_bounds__(1024) void k_pf_budget(const uint32_t* __restrict__
 }
 
 // Each head's bitmap as an ascending position list (one workgroup per head).
-__global__ __launch_bounds__(1024) void k_pf_lists(const uint32_t* __restrict__ bits, int64_t words,
-                                                   int64_t L, int32_t* __restrict__ list) {
+__global__ __launch_bounds__(1024) void k_pf_lists(uint32_t* __restrict__ bits, const int8_t* __restrict__ mode,
+                                                   int64_t words, int64_t L, int32_t* __restrict__ list) {
   const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int wtot[16];
   const int64_t row = int64_t(b) * Hq + h;
-  const uint32_t* bw = bits + row * words;
+  uint32_t* bw = bits + row * words;
   int32_t* out = list + row * L;
+  if (mode && mode[h]) {
+    // a full-attention head keeps every position
+    for (int64_t w = tid; w < words; w += 1024) {
+      const int64_t left = L - w * 32;
+      bw[w] = left >= 32 ? 0xffffffffu : (1u << left) - 1u;
+    }
+    for (int64_t j = tid; j < L; j += 1024) out[j] = int32_t(j);
+    return;
+  }
   const int64_t per = (words + 1023) / 1024;
   const int64_t w0 = tid * per, w1 = w0 + per < words ? w0 + per : words;
   int pc = 0;
@@ -321,6 +332,7 @@ struct PfAttnArgs {
   int64_t kv_sb, kv_sh, kv_st;
   const int32_t* list;    // [B][Hq][L]
   const int32_t* budget;  // [B]
+  const int8_t* mode;     // [Hq] 1 = full-attention head (keeps every position), or null
   uint16_t* kc;           // gathered K rows [B][Hq][Lpad][d]
   uint16_t* vc;           // gathered V rows [B][Hq][Lpad][d]
   const uint32_t* bits;   // kept positions [B][Hq][words]
@@ -337,7 +349,7 @@ struct PfAttnArgs {
 __global__ __launch_bounds__(256) void k_pf_gather(PfAttnArgs a) {
   const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int Li = int(a.L);
-  const int kk = min(max(a.budget[b], 1), Li);
+  const int kk = a.mode && a.mode[h] ? Li : min(max(a.budget[b], 1), Li);
   const int r0 = blockIdx.x * kPfKeyTile;
   if (r0 >= kk) return;
   const int g = h / a.G;
@@ -388,7 +400,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
   const int lane = tid & 63, n = lane & 15, c = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Li = int(a.L);
-  const int kk = min(max(a.budget[b], 1), Li);
+  const int kk = a.mode && a.mode[h] ? Li : min(max(a.budget[b], 1), Li);
   const int nqb = (kk + kPfQueryBlock - 1) / kPfQueryBlock;
   if (int(blockIdx.x) >= nqb) {
     // decompression: the workgroups past the head's query blocks (at least one per head, by the
@@ -674,7 +686,8 @@ int launch_prefill_select(const PrefillPlan& p, const sp_tensors& t, char* ws, v
   ia.scale = c.softmax_scale;
   hipLaunchKernelGGL(k_pf_zpart, dim3(p.nslab, Hq, B), dim3(256), 0, st, ia);
   hipLaunchKernelGGL(k_pf_importance, dim3(p.nslab, Hq, B), dim3(256), 0, st, ia);
-  hipLaunchKernelGGL(k_pf_global, dim3(p.nslab, B), dim3(256), 0, st, at<double>(ws, p.o_imp), Hq, p.L, p.nslab,
+  hipLaunchKernelGGL(k_pf_global, dim3(p.nslab, B), dim3(256), 0, st, at<double>(ws, p.o_imp), t.head_mode, Hq, p.L,
+                     p.nslab,
                      at<double>(ws, p.o_gimp), at<double>(ws, p.o_gpmax), at<double>(ws, p.o_gpmin));
   int e = int(hipGetLastError());
   if (e) return e;
@@ -713,8 +726,8 @@ int launch_prefill_select(const PrefillPlan& p, const sp_tensors& t, char* ws, v
   r.bits = at<uint32_t>(ws, p.o_bits);
   e = launch_long_rows(r, stream);
   if (e) return e;
-  hipLaunchKernelGGL(k_pf_lists, dim3(Hq, B), dim3(1024), 0, st, at<uint32_t>(ws, p.o_bits), p.words, p.L,
-                     at<int32_t>(ws, p.o_list));
+  hipLaunchKernelGGL(k_pf_lists, dim3(Hq, B), dim3(1024), 0, st, at<uint32_t>(ws, p.o_bits), t.head_mode, p.words,
+                     p.L, at<int32_t>(ws, p.o_list));
   return int(hipGetLastError());
 }
 
@@ -734,6 +747,7 @@ int launch_prefill_attend(const PrefillPlan& p, const sp_tensors& t, char* ws, f
   a.kv_st = t.kv_st;
   a.list = at<int32_t>(ws, p.o_list);
   a.budget = at<int32_t>(ws, p.o_budget);
+  a.mode = t.head_mode;
   a.bits = at<uint32_t>(ws, p.o_bits);
   a.words = p.words;
   a.kc = at<uint16_t>(ws, p.o_kvc);

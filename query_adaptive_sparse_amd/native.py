@@ -82,6 +82,7 @@ class sp_tensors(ctypes.Structure):
         ("q", ctypes.c_void_p), ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64), ("q_st", ctypes.c_int64),
         ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("kv_sb", ctypes.c_int64), ("kv_sh", ctypes.c_int64), ("kv_st", ctypes.c_int64),
+        ("head_mode", ctypes.c_void_p),
     ]
 
 

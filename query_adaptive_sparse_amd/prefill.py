@@ -9,13 +9,17 @@ import torch
 from . import native as N
 
 
-def make_prefill_tensors(Q, K, V) -> N.sp_tensors:
-    """sp_tensors from Q [B][Hq][L][d] and K, V [B][Hkv][L][d] (bf16, shared K / V strides)."""
+def make_prefill_tensors(Q, K, V, head_mode=None) -> N.sp_tensors:
+    """sp_tensors from Q [B][Hq][L][d] and K, V [B][Hkv][L][d] (bf16, shared K / V strides), and an
+    optional device int8 head_mode [Hq] (1 = full-attention head, 0 = sparse head)."""
     assert K.stride() == V.stride(), "K and V must share a layout"
     t = N.sp_tensors()
     t.q, t.q_sb, t.q_sh, t.q_st = Q.data_ptr(), Q.stride(0), Q.stride(1), Q.stride(2)
     t.k, t.v = K.data_ptr(), V.data_ptr()
     t.kv_sb, t.kv_sh, t.kv_st = K.stride(0), K.stride(1), K.stride(2)
+    if head_mode is not None:
+        assert head_mode.dtype == torch.int8 and head_mode.numel() == Q.shape[1] and head_mode.is_contiguous()
+        t.head_mode = head_mode.data_ptr()
     return t
 
 

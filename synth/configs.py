@@ -158,6 +158,7 @@ class PrefillWorkload:
     beta: float = 4.0          # plant: every query of a KV group gets beta * u_g ...
     zipf_s: float = 1.1        # ... and key j gets gamma_j * u_g, a Zipf(s) logit profile
     seed: int = 0
+    head_mode: tuple | None = None  # per query head: 1 = full attention, 0 = sparse (None: all sparse)
 
     @property
     def group(self) -> int:
@@ -170,7 +171,10 @@ P1 = PrefillWorkload(name="p1_tsa_llama31_8b_128k", batch=1, n_q_heads=32, n_kv_
                      seq_len=131072, window=64, tau=0.2, softmax_scale=_inv_sqrt(128), seed=31)
 P1S = replace(P1, name="p1s", seq_len=4096, window=64, seed=32)
 P1T = replace(P1, name="p1t", batch=2, n_q_heads=8, n_kv_heads=2, seq_len=1024, window=32, tau=0.3, seed=33)
-PREFILL = {w.name: w for w in (P1, P1S, P1T)}
+# Head-wise routing over the same prompt: the first query head of every KV group runs full attention
+# (8 of 32 heads), the others the Token-Sparse selection, all in the same launches.
+P1M = replace(P1, name="p1m_elastic_llama31_8b_128k", head_mode=tuple(int(h % 4 == 0) for h in range(32)))
+PREFILL = {w.name: w for w in (P1, P1S, P1T, P1M)}
 
 
 @dataclass(frozen=True)
