@@ -82,28 +82,6 @@ int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream);
 int launch_combine(const Plan& p, char* ws, float* out, float* lse, void* stream);
 const char* hip_error_string(int code);
 
-// Long-row selection (histogram passes) over caller-given fp64 rows s [B][H][len]: top-k (k, or
-// kbudget[b] for every row of sequence b when non-null) with unit weights, or top-p of the
-// weights exp(scale (s - smax)), or (ident) of the values themselves as masses (s >= 0).
-// pmax / pmin hold each row's max / min per kMinMaxBlock entries. Writes the selection bitmaps
-// bits [B][H][words] (whole words) and raises status[0] for an incomplete row.
-struct LongRows {
-  const double* s;
-  int64_t len;
-  int B, H;
-  int topp, ident, k;
-  const int32_t* kbudget;
-  double p, scale;
-  const double* pmax;
-  const double* pmin;
-  int nblk;
-  char* scratch;  // long_rows_scratch(B * H, len) bytes, 256-byte aligned
-  uint32_t* bits;
-  int64_t words;
-  uint32_t* status;
-};
-size_t long_rows_scratch(int64_t rows, int64_t len);
-int launch_long_rows(const LongRows& r, void* stream);
 
 }  // namespace sd
 

@@ -699,6 +699,7 @@ int launch_prefill_select(const PrefillPlan& p, const sp_tensors& t, char* ws, v
   r.H = 1;
   r.topp = 1;
   r.ident = 1;
+  r.bitbins = 1;  // importances are >= 0 and span many binades
   r.k = 0;
   r.kbudget = nullptr;
   r.p = 1.0 - c.tau;

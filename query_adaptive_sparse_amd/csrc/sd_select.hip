@@ -3,6 +3,7 @@
 // Compiled with -ffp-contract=off: every fused multiply-add is an explicit fma(), so fp64 score
 // arithmetic can be matched bit for bit by a sequential CPU evaluation.
 #include "sd_device.h"
+#include "long_rows.h"
 
 namespace sd {
 namespace {
@@ -510,6 +511,7 @@ struct LongArgs {
   uint64_t local_mask;
   int topp, k;
   int ident;               // top-p of the values themselves (masses), not of exp weights
+  int bitbins;             // values >= 0, binned by their bit patterns (see coarse_pos_of)
   const int32_t* kbudget;  // top-k per sequence (row / Hq), or NULL: k
   double p, scale;
   RowInfo* info;
@@ -531,6 +533,19 @@ struct LongArgs {
 __device__ __forceinline__ double coarse_pos(double s, double smax, double binscale) {
   const double d = (smax - s) * binscale;
   return d >= 0.0 ? (d < double(kBins1) ? d : double(kBins1)) : 0.0;  // NaN -> 0
+}
+// Bin axis of a long row. Default: linear in the score from the row max (kBins1 bins over the
+// row's range), the right axis for exp weights. With bitbins (nonnegative values: importances,
+// masses) the axis is the distance in IEEE bit patterns from the row max, 2^48 patterns per coarse
+// bin: 16 bins per binade over 64 binades, everything smaller (zero included) in the last bin.
+// Both are monotone non-increasing in the value, and every long-row kernel bins through here.
+__device__ __forceinline__ double coarse_pos_of(const LongArgs& a, double s, double smax, double binscale) {
+  if (a.bitbins) {
+    const int64_t dv = __double_as_longlong(smax) - __double_as_longlong(s + 0.0);
+    const double d = double(dv) * 0x1p-48;
+    return d >= 0.0 ? (d < double(kBins1) ? d : double(kBins1)) : 0.0;
+  }
+  return coarse_pos(s, smax, binscale);
 }
 __device__ __forceinline__ int coarse_bin(double d) {
   const int c = int(d);
@@ -629,7 +644,7 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
       const int64_t t = t0 + int64_t(it) * (NT * 8) + tid + NT * k;
       if (t < t1) {
         const double v = sv[it & 1][k];
-        const int c = coarse_bin(coarse_pos(v, smax, binscale));
+        const int c = coarse_bin(coarse_pos_of(a, v, smax, binscale));
         br[t] = uint16_t(c);
         unsafeAtomicAdd(&hm[c], long_weight(a, smax, v));
         atomicAdd(&hc[c], 1u);
@@ -859,7 +874,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
     for (int64_t t = tid; t < a.len; t += NT) {
       if (br[t] == ri.bin1) {
         const double s = sr[t];
-        const int f = fine_bin(coarse_pos(s, ri.smax, ri.binscale), ri.bin1);
+        const int f = fine_bin(coarse_pos_of(a, s, ri.smax, ri.binscale), ri.bin1);
         unsafeAtomicAdd(&fm[f], long_weight(a, ri.smax, s));
         atomicAdd(&fc[f], 1u);
       }
@@ -908,7 +923,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
       for (int64_t t = r0; t < r1; ++t) {
         if (br[t] == ri.bin1) {
           const double sc = sr[t];
-          const int f = fine_bin(coarse_pos(sc, ri.smax, ri.binscale), ri.bin1);
+          const int f = fine_bin(coarse_pos_of(a, sc, ri.smax, ri.binscale), ri.bin1);
           if (f < bin2) {
             atomicOr(&bw[t >> 5], 1u << (t & 31));
           } else if (f == bin2) {
@@ -941,7 +956,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
       const int rank0 = int(block_scan<NT>(double(mine), wtot, &tot)) - mine;
       int rank = rank0;
       for (int64_t t = r0; t < r1 && rank < take; ++t) {
-        if (br[t] == ri.bin1 && fine_bin(coarse_pos(sr[t], ri.smax, ri.binscale), ri.bin1) == bin2) {
+        if (br[t] == ri.bin1 && fine_bin(coarse_pos_of(a, sr[t], ri.smax, ri.binscale), ri.bin1) == bin2) {
           atomicOr(&bw[t >> 5], 1u << (t & 31));
           ++rank;
         }
@@ -952,7 +967,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
     for (int64_t t = tid; t < a.len; t += NT) {
       if (br[t] == ri.bin1) {
         const double s = sr[t];
-        const int f = fine_bin(coarse_pos(s, ri.smax, ri.binscale), ri.bin1);
+        const int f = fine_bin(coarse_pos_of(a, s, ri.smax, ri.binscale), ri.bin1);
         if (f < bin2) {
           atomicOr(&bw[t >> 5], 1u << (t & 31));
         } else if (f == bin2) {
@@ -985,7 +1000,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   __syncthreads();
   for (int i = tid; i < n; i += NT) {
     const double s = dkey_inv(keys[i]);
-    const double x = (coarse_pos(s, ri.smax, ri.binscale) - dlo) * sscale;
+    const double x = (coarse_pos_of(a, s, ri.smax, ri.binscale) - dlo) * sscale;
     int sb = x >= 0.0 ? (x < double(kSub) ? int(x) : kSub - 1) : 0;
     sb = sb < kSub - 1 ? sb : kSub - 1;
     sub[i] = uint16_t(sb);
@@ -1356,6 +1371,7 @@ __global__ __launch_bounds__(256) void k_union_write(UnionArgs a) {
 LongArgs long_args(const Plan& p, char* ws) {
   const sd_config& c = p.cfg;
   LongArgs a;
+  a.bitbins = 0;
   a.s0 = at<double>(ws, p.o_s0);
   a.len = p.len0;
   a.Hq = c.n_q_heads;
@@ -1522,6 +1538,7 @@ int launch_long_rows(const LongRows& r, void* stream) {
   a.topp = r.topp;
   a.k = r.k;
   a.ident = r.ident;
+  a.bitbins = r.bitbins;
   a.kbudget = r.kbudget;
   a.p = r.p;
   a.scale = r.scale;

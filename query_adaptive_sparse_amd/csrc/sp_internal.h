@@ -2,7 +2,7 @@
 // prefill kernels (sd_prefill.hip).
 #pragma once
 
-#include "sd_internal.h"
+#include "long_rows.h"
 #include "../../include/sparse_prefill.h"
 
 namespace sd {
