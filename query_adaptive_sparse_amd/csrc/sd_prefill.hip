@@ -2,10 +2,11 @@
 // each head's kept tokens, scattered back into the sequence-length output.
 //
 // Selection (fp64, matching a sequential CPU evaluation up to the order of the softmax sums):
-//   k_pf_scores      proxy scores s[key][q] = q . k of the W window queries against 64 keys per
-//                    workgroup, on the fp64 MFMA (16 keys x 16 queries x 4 dimensions per
-//                    instruction; chained over the dimensions in index order, each output is the
-//                    sequential fma chain of the dot product), and each query's max per key block;
+//   k_pf_scores      proxy scores s[key][q] = q . k of the W window queries against 4 blocks of 64
+//                    keys per workgroup (the next block's keys load during a block's MFMAs), on
+//                    the fp64 MFMA (16 keys x 16 queries x 4 dimensions per instruction; chained
+//                    over the dimensions in index order, each output is the sequential fma chain
+//                    of the dot product), and each query's max per key block;
 //   k_pf_rowmax      every window query's max over its visible keys;
 //   k_pf_zpart       per 2048-key slab and query, the sum of exp(scale (s - max)) over the slab;
 //   k_pf_importance  per key, the sum over the window queries (in order) of the query's softmax
@@ -56,65 +57,88 @@ struct PfScoreArgs {
 constexpr int kD = 128;
 constexpr int kKRow = kD + 8;  // padded bf16 row in LDS (elements)
 
+constexpr int kPfScoreBlocks = 4;  // key blocks per proxy-score workgroup (the window queries load once)
+
 __global__ __launch_bounds__(256) void k_pf_scores(PfScoreArgs a) {
   __shared__ uint16_t qs[kPfMaxWindow * kKRow];
   __shared__ uint16_t ks[kPfKeyBlock * kKRow];
   __shared__ double wmax[4][kPfMaxWindow];
-  const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, n = lane & 15, c = lane >> 4;
-  if (a.status && kb == 0 && h == 0 && b == 0 && tid < 16) a.status[tid] = 0;
+  if (a.status && blockIdx.x == 0 && h == 0 && b == 0 && tid < 16) a.status[tid] = 0;
   const int g = h / a.G;
-  const int64_t key0 = int64_t(kb) * kPfKeyBlock;
   const int64_t qpos0 = a.L - a.W;
-  // window queries (rows past W are zero) and the block's keys (past L: the last key) -> LDS
+  const int kbA = blockIdx.x * kPfScoreBlocks;
+  const int kbB = kbA + kPfScoreBlocks < a.nkb ? kbA + kPfScoreBlocks : a.nkb;
+  // window queries (rows past W are zero) -> LDS, once
   for (int i = tid; i < kPfMaxWindow * (kD / 8); i += 256) {
     const int r = i / (kD / 8), pc = i - r * (kD / 8);
     uint4 v = make_uint4(0, 0, 0, 0);
     if (r < a.W) v = ld16(a.q + b * a.q_sb + h * a.q_sh + (qpos0 + r) * a.q_st + pc * 8);
     *reinterpret_cast<uint4*>(qs + r * kKRow + pc * 8) = v;
   }
-  for (int i = tid; i < kPfKeyBlock * (kD / 8); i += 256) {
-    const int r = i / (kD / 8), pc = i - r * (kD / 8);
-    const int64_t key = key0 + r < a.L ? key0 + r : a.L - 1;
-    *reinterpret_cast<uint4*>(ks + r * kKRow + pc * 8) =
-        ld16(a.k + b * a.kv_sb + g * a.kv_sh + key * a.kv_st + pc * 8);
-  }
-  __syncthreads();
-  // wave: keys 16 wave .. + 15 of the block against the 4 query tiles
-  f64x4 acc[4];
+  // a key block's rows (past L: the last key), 4 pieces per thread: registers, then LDS
+  constexpr int kKPer = kPfKeyBlock * (kD / 8) / 256;
+  uint4 rk[kKPer];
+  auto load = [&](int kb) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f64x4{0.0, 0.0, 0.0, 0.0};
-  const uint16_t* kr = ks + (16 * wave + n) * kKRow + c;
-#pragma unroll 4
-  for (int s = 0; s < kD / 4; ++s) {
-    const double av = double(bf2f(kr[4 * s]));
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const double bv = double(bf2f(qs[(16 * t + n) * kKRow + 4 * s + c]));
-      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[t], 0, 0, 0);
+    for (int u = 0; u < kKPer; ++u) {
+      const int i = tid + 256 * u, r = i / (kD / 8), pc = i - r * (kD / 8);
+      const int64_t key0 = int64_t(kb) * kPfKeyBlock;
+      const int64_t key = key0 + r < a.L ? key0 + r : a.L - 1;
+      rk[u] = ld16(a.k + b * a.kv_sb + g * a.kv_sh + key * a.kv_st + pc * 8);
     }
-  }
-  // scores out (key-major, W per key) and each query's max over the visible keys of the wave
+  };
+  auto store = [&]() {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int qi = 16 * t + n;
-    double m = kNegInfD;
+    for (int u = 0; u < kKPer; ++u) {
+      const int i = tid + 256 * u, r = i / (kD / 8), pc = i - r * (kD / 8);
+      *reinterpret_cast<uint4*>(ks + r * kKRow + pc * 8) = rk[u];
+    }
+  };
+  load(kbA);
+  store();
+  for (int kb = kbA; kb < kbB; ++kb) {
+    __syncthreads();  // the block's keys (and the queries) are in LDS
+    if (kb + 1 < kbB) load(kb + 1);  // in flight during the block's MFMAs
+    const int64_t key0 = int64_t(kb) * kPfKeyBlock;
+    // wave: keys 16 wave .. + 15 of the block against the 4 query tiles
+    f64x4 acc[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t key = key0 + 16 * wave + c + 4 * v;
-      if (key < a.L && qi < a.W) {
-        a.S[((int64_t(b) * a.Hq + h) * a.L + key) * a.W + qi] = acc[t][v];
-        if (key <= qpos0 + qi) m = fmax(m, acc[t][v]);
+    for (int t = 0; t < 4; ++t) acc[t] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const uint16_t* kr = ks + (16 * wave + n) * kKRow + c;
+#pragma unroll 4
+    for (int s = 0; s < kD / 4; ++s) {
+      const double av = double(bf2f(kr[4 * s]));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const double bv = double(bf2f(qs[(16 * t + n) * kKRow + 4 * s + c]));
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[t], 0, 0, 0);
       }
     }
-    m = fmax(m, __shfl_xor(m, 16));
-    m = fmax(m, __shfl_xor(m, 32));
-    if (c == 0) wmax[wave][qi] = m;
+    // scores out (key-major, W per key) and each query's max over the visible keys of the wave
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int qi = 16 * t + n;
+      double m = kNegInfD;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t key = key0 + 16 * wave + c + 4 * v;
+        if (key < a.L && qi < a.W) {
+          a.S[((int64_t(b) * a.Hq + h) * a.L + key) * a.W + qi] = acc[t][v];
+          if (key <= qpos0 + qi) m = fmax(m, acc[t][v]);
+        }
+      }
+      m = fmax(m, __shfl_xor(m, 16));
+      m = fmax(m, __shfl_xor(m, 32));
+      if (c == 0) wmax[wave][qi] = m;
+    }
+    __syncthreads();  // every wave is done with ks and has its maxima in wmax
+    if (tid < a.W)
+      a.pmq[((int64_t(b) * a.Hq + h) * a.nkb + kb) * a.W + tid] =
+          fmax(fmax(wmax[0][tid], wmax[1][tid]), fmax(wmax[2][tid], wmax[3][tid]));
+    if (kb + 1 < kbB) store();
   }
-  __syncthreads();
-  if (tid < a.W)
-    a.pmq[((int64_t(b) * a.Hq + h) * a.nkb + kb) * a.W + tid] =
-        fmax(fmax(wmax[0][tid], wmax[1][tid]), fmax(wmax[2][tid], wmax[3][tid]));
 }
 
 // Every window query's max over its visible keys: the block maxima, 16 parts of the blocks per
@@ -180,18 +204,18 @@ __global__ __launch_bounds__(256) void k_pf_zpart(PfImpArgs a) {
 }
 
 // Per key of the slab: importance = sum over the window queries, in order, of
-// exp(scale s - scale max_q) / Z_q (Z_q: the slab partials summed in slab order); and the slab's
-// max / min of the importance.
+// exp(scale s - scale max_q) x (1 / Z_q) (Z_q: the slab partials summed in slab order; the product
+// with the reciprocal is within an ulp of the quotient); and the slab's max / min of the importance.
 __global__ __launch_bounds__(256) void k_pf_importance(PfImpArgs a) {
   const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  __shared__ double zs[kPfMaxWindow], ms[kPfMaxWindow];
+  __shared__ double zs[kPfMaxWindow], ms[kPfMaxWindow];  // 1 / Z_q, scale x max_q
   __shared__ double rmax[4], rmin[4];
   const int64_t row = int64_t(b) * a.Hq + h;
   if (tid < a.W) {
     double z = 0.0;
     for (int s = 0; s < a.nslab; ++s) z += a.zq[(row * a.nslab + s) * a.W + tid];
-    zs[tid] = z;
+    zs[tid] = 1.0 / z;
     ms[tid] = a.scale * a.M[row * a.W + tid];
   }
   __syncthreads();
@@ -213,10 +237,10 @@ __global__ __launch_bounds__(256) void k_pf_importance(PfImpArgs a) {
           sv[u + 1] = d2.y;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v += exp(a.scale * sv[u] - ms[q8 + u]) / zs[q8 + u];
+        for (int u = 0; u < 8; ++u) v += exp(a.scale * sv[u] - ms[q8 + u]) * zs[q8 + u];
       }
     } else {
-      for (int qi = qa; qi < a.W; ++qi) v += exp(a.scale * sp[qi] - ms[qi]) / zs[qi];
+      for (int qi = qa; qi < a.W; ++qi) v += exp(a.scale * sp[qi] - ms[qi]) * zs[qi];
     }
     a.imp[row * a.L + j] = v;
     mx = fmax(mx, v);
@@ -670,7 +694,7 @@ int launch_prefill_select(const PrefillPlan& p, const sp_tensors& t, char* ws, v
   s.S = at<double>(ws, p.o_S);
   s.pmq = at<double>(ws, p.o_pmq);
   s.status = status;
-  hipLaunchKernelGGL(k_pf_scores, dim3(p.nkb, Hq, B), dim3(256), 0, st, s);
+  hipLaunchKernelGGL(k_pf_scores, dim3((p.nkb + kPfScoreBlocks - 1) / kPfScoreBlocks, Hq, B), dim3(256), 0, st, s);
   hipLaunchKernelGGL(k_pf_rowmax, dim3(Hq, B), dim3(1024), 0, st, at<double>(ws, p.o_pmq), p.nkb, W, at<double>(ws, p.o_M));
   PfImpArgs ia;
   ia.S = at<double>(ws, p.o_S);
