@@ -89,3 +89,15 @@ def test_gist_32k_sampled():
     out, outg = run_gpu(w, inp)
     rep = compare(w, inp, out, outg, raw_k=12, gist_k=6, seed=2)
     print(f"[gist] {w.name}: {rep}", flush=True)
+
+
+def test_gist_token_major_layout():
+    """Token-major storage ([B][N][H][d] viewed as [B][H][N][d]): the kernels take the strides."""
+    w = replace(configs.get("p2t"), chunk_size=8, n_tokens=264)
+    inp = gen.make_gist_inputs(w, device="cuda")
+    tm = {k: (v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) if torch.is_tensor(v) else v)
+          for k, v in inp.items()}
+    assert tm["Q"].stride(2) == w.n_q_heads * w.head_dim
+    out, outg = run_gpu(w, tm)
+    rep = compare(w, inp, out, outg)
+    print(f"[gist] token-major {w.name}: {rep}", flush=True)

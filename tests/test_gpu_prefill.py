@@ -176,3 +176,15 @@ def test_prefill_mixed_128k_sampled():
         worst = max(worst, float(np.max(np.abs(d))))
         assert np.max(np.abs(d)) <= ATOL and np.linalg.norm(d) / np.linalg.norm(o) <= RTOL_L2, h
     print(f"[prefill-mixed] budget {k} margin {margin:.2e} max_abs {worst:.2e}", flush=True)
+
+
+def test_prefill_token_major_layout():
+    """Token-major storage ([B][L][H][d] viewed as [B][H][L][d]): the kernels take the strides."""
+    w = replace(configs.get("p1t"), seq_len=300, window=16)
+    inp = gen.make_prefill_inputs(w, device="cuda")
+    tm = {k: (v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) if torch.is_tensor(v) else v)
+          for k, v in inp.items()}
+    assert tm["K"].stride(2) == w.n_kv_heads * w.head_dim
+    sel, out = run_gpu(w, tm)
+    rep = compare(w, inp, sel, out)
+    print(f"[prefill] token-major {w.name}: {rep}", flush=True)
