@@ -368,6 +368,8 @@ sd_status sparse_prefill_init(const sp_config* cfg, sp_handle** out, size_t* wor
   p.o_budget = take(size_t(B) * 4);
   p.o_bits = take(size_t(B * Hq * p.words) * 4);
   p.o_list = take(size_t(B * Hq * L) * 4);
+  p.o_vmaxp = take(size_t(B * c.n_kv_heads * p.nslab) * 4);
+  p.o_vexp = take(size_t(B * Hq) * 4);
   p.ws_bytes = off;
   *out = h;
   *workspace_bytes = p.ws_bytes;

@@ -1,4 +1,6 @@
-// Gist-masked (SSA) block-sparse prefill attention.
+// Gist-masked (SSA) block-sparse prefill attention: the review of "Simplified Sparse Attention"
+// (aitrends.kr, article 69798), sections on the method and technical details (a gist token after
+// every chunk; the gist causal mask) and contributions (key-column permutation, block skipping).
 //
 // Queries come in blocks of 128 of one kind: raw tokens t0 .. t0 + 127, or gists m0 .. m0 + 127.
 // After the key-column permutation [gists | raw tokens], a block's visible keys are

@@ -19,14 +19,16 @@
 //   k_pf_lists       each head's bitmap as an ascending position list (a full-attention head:
 //                    every position).
 // Attention:
+//   k_pf_vmax        each KV head's max |v| (per slab);
 //   k_pf_gather      compression: every head's K and V rows at its kept positions, in list order,
-//                    into contiguous per-head sequences (padded with zero rows to a whole step);
+//                    into contiguous per-head sequences (padded with zero rows to a whole step), V
+//                    converted to fp16 under the head's power-of-two scale;
 //   k_pf_attend      128 compact queries per workgroup (32 per wave), heaviest blocks first; the
 //                    workgroup stages 64 gathered keys' K and V rows per step in LDS (K pieces
 //                    XOR-swizzled per row, V rows padded for transpose reads), each wave runs q.K^T
 //                    on the bf16 MFMA, the causal mask in compact order, an online softmax whose
-//                    reference moves only when a logit exceeds it by 2^8, and P.V (hi and lo halves
-//                    of P), then writes its rows to their positions;
+//                    reference moves only when a logit exceeds it by 2^8, and P.V on the fp16
+//                    MFMA (P rounded to fp16, V converted at the gather), then writes its rows;
 //                    the workgroups past a head's query blocks write the zero rows of the
 //                    positions it did not keep.
 #include "sd_device.h"
@@ -357,8 +359,11 @@ struct PfAttnArgs {
   const int32_t* list;    // [B][Hq][L]
   const int32_t* budget;  // [B]
   const int8_t* mode;     // [Hq] 1 = full-attention head (keeps every position), or null
-  uint16_t* kc;           // gathered K rows [B][Hq][Lpad][d]
-  uint16_t* vc;           // gathered V rows [B][Hq][Lpad][d]
+  uint16_t* kc;           // gathered K rows [B][Hq][Lpad][d], bf16
+  uint16_t* vc;           // gathered V rows [B][Hq][Lpad][d], fp16 scaled by 2^-vexp[b][h]
+  float* vmaxp;           // [B][Hkv][nslab] max |v| per slab
+  int32_t* vexp;          // [B][Hq]
+  int nslab, Hkv;
   const uint32_t* bits;   // kept positions [B][Hq][words]
   int64_t words;
   float* out;             // [B][Hq][L][d]
@@ -367,9 +372,45 @@ struct PfAttnArgs {
   float scale_log2;
 };
 
+// max |v| over a slab of kPfSlab rows of one KV head (one workgroup per slab).
+__global__ __launch_bounds__(256) void k_pf_vmax(PfAttnArgs a) {
+  const int sl = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  __shared__ float red[4];
+  const int64_t j0 = int64_t(sl) * kPfSlab, j1 = j0 + kPfSlab < a.L ? j0 + kPfSlab : a.L;
+  const uint16_t* vb = a.v + b * a.kv_sb + g * a.kv_sh;
+  uint32_t mx = 0;  // |v| as bits: monotone for nonnegative floats
+  for (int64_t i = j0 * (kD / 8) + tid; i < j1 * (kD / 8); i += 256) {
+    const int64_t r = i / (kD / 8), pc = i - r * (kD / 8);
+    const uint4 w = ld16_stream(vb + r * a.kv_st + pc * 8);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mx = max(mx, max((u[k] << 16) & 0x7fff0000u, u[k] & 0x7fff0000u));
+  }
+#pragma unroll
+  for (int o = 32; o; o >>= 1) mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
+  if ((tid & 63) == 0) red[tid >> 6] = __uint_as_float(mx);
+  __syncthreads();
+  if (tid == 0) a.vmaxp[(int64_t(b) * a.Hkv + g) * a.nslab + sl] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
 // Compression: every head's K and V rows at its kept positions, in list order, into contiguous
 // per-head sequences; rows from the budget up to the next multiple of kPfKeyTile are zero (their
-// logits are masked, and zero values keep their products finite). One workgroup per 64 rows.
+// logits are masked, and zero values keep their products finite). K stays bf16; V becomes fp16
+// scaled by 2^-e with e = (exponent of the KV head's max |v|) - 15, so the largest value lands in
+// [2^14, 2^15): every bf16 value of magnitude down to 2^-29 of the max converts exactly, smaller ones
+// round to the fp16 grid (absolute error below 2^-39 of the max). One workgroup per 64 rows.
+__device__ __forceinline__ int pf_vexp(const PfAttnArgs& a, int b, int g) {
+  const float* vm = a.vmaxp + (int64_t(b) * a.Hkv + g) * a.nslab;
+  float m = 0.f;
+  for (int s = 0; s < a.nslab; ++s) m = fmaxf(m, vm[s]);
+  int e = 0;
+  if (m > 0.f && m <= 3.0e38f) {
+    frexpf(m, &e);  // m = f 2^e, f in [0.5, 1)
+    e -= 15;
+  }
+  return e;
+}
+
 __global__ __launch_bounds__(256) void k_pf_gather(PfAttnArgs a) {
   const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int Li = int(a.L);
@@ -393,11 +434,24 @@ __global__ __launch_bounds__(256) void k_pf_gather(PfAttnArgs a) {
       kv[0][i] = kv[1][i] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
+  const int e = pf_vexp(a, b, g);
+  if (blockIdx.x == 0 && tid == 0) a.vexp[int64_t(b) * a.Hq + h] = e;
+  const float sc = ldexpf(1.f, -e);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t dst = (head + r0 + (tid >> 4) + 16 * i) * kD + pc * 8;
     *reinterpret_cast<uint4*>(a.kc + dst) = kv[0][i];
-    *reinterpret_cast<uint4*>(a.vc + dst) = kv[1][i];
+    const uint32_t u[4] = {kv[1][i].x, kv[1][i].y, kv[1][i].z, kv[1][i].w};
+    uint32_t hw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      h2 hv;
+      hv[0] = (_Float16)(__uint_as_float(u[k] << 16) * sc);
+      hv[1] = (_Float16)(__uint_as_float(u[k] & 0xffff0000u) * sc);
+      hw[k] = __builtin_bit_cast(uint32_t, hv);
+    }
+    *reinterpret_cast<uint4*>(a.vc + dst) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
   }
 }
 
@@ -418,6 +472,7 @@ __device__ __forceinline__ int pf_kswz(int x) { return x & 15; }
 
 __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
   typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   __shared__ uint4 kstb[2][kKeyTile * kPPR];
   __shared__ uint32_t vstb[2][kKeyTile * kVPitchW];
   const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -559,10 +614,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
           }
       }
     }
-    // P = hi + lo, both bf16 (hi rounded to nearest even, lo the rounded remainder): fp32
-    // accuracy of P through two MFMAs. ph / pl [t][st][u]: keys 16 st + 4 c + 2 u, + 1 of query
-    // 16 t + n, packed
-    uint32_t ph[kQTiles][kKeyTile / 16][2], pl[kQTiles][kKeyTile / 16][2];
     // both tiles' column maxima, then one wave-uniform test for the rare move of a reference
     float mt[kQTiles];
 #pragma unroll
@@ -591,6 +642,9 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
         m[t] = mn;
       }
     }
+    // P in fp16 (rounded to nearest even; the probabilities are below 2^8 by the lazy reference):
+    // ph[t][st][u]: keys 16 st + 4 c + 2 u, + 1 of query 16 t + n, packed
+    uint32_t ph[kQTiles][kKeyTile / 16][2];
 #pragma unroll
     for (int t = 0; t < kQTiles; ++t) {
       // a column whose reference is still -inf has seen masked logits only: exponent -inf
@@ -605,22 +659,17 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-          bf2 hv;
-          hv[0] = (__bf16)pr[2 * u];
-          hv[1] = (__bf16)pr[2 * u + 1];
-          const uint32_t hw = __builtin_bit_cast(uint32_t, hv);
-          bf2 lv;
-          lv[0] = (__bf16)(pr[2 * u] - __uint_as_float(hw << 16));
-          lv[1] = (__bf16)(pr[2 * u + 1] - __uint_as_float(hw & 0xffff0000u));
-          ph[t][st][u] = hw;
-          pl[t][st][u] = __builtin_bit_cast(uint32_t, lv);
+          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+          h2 hv;
+          hv[0] = (_Float16)pr[2 * u];
+          hv[1] = (_Float16)pr[2 * u + 1];
+          ph[t][st][u] = __builtin_bit_cast(uint32_t, hv);
         }
       }
     }
-    // ---- P.V on K = 32 MFMAs over sub-tile pairs (2 sp, 2 sp + 1): k-slots 8 c .. 8 c + 3 are keys
-    // 4 c .. 4 c + 3 of the first sub-tile, 8 c + 4 .. 8 c + 7 the same keys of the second; A = P
-    // (hi, then lo) of query 16 t + n, B = V by transpose reads
+    // ---- P.V on fp16 K = 32 MFMAs over sub-tile pairs (2 sp, 2 sp + 1): k-slots 8 c .. 8 c + 3 are
+    // keys 4 c .. 4 c + 3 of the first sub-tile, 8 c + 4 .. 8 c + 7 the same keys of the second; A = P
+    // of query 16 t + n, B = the scaled fp16 V by transpose reads
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int sp = 0; sp < kKeyTile / 32; ++sp) {
@@ -632,13 +681,11 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
                                                         (__attribute__((address_space(3))) v4s*)(vr0 + 8 * nb)));
         const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                         (__attribute__((address_space(3))) v4s*)(vr1 + 8 * nb)));
-        const bf16x8 bop = __builtin_bit_cast(bf16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
+        const f16x8 bop = __builtin_bit_cast(f16x8, make_uint4(w0.x, w0.y, w1.x, w1.y));
 #pragma unroll
         for (int t = 0; t < kQTiles; ++t) {
           const uint4 ah = make_uint4(ph[t][2 * sp][0], ph[t][2 * sp][1], ph[t][2 * sp + 1][0], ph[t][2 * sp + 1][1]);
-          const uint4 al = make_uint4(pl[t][2 * sp][0], pl[t][2 * sp][1], pl[t][2 * sp + 1][0], pl[t][2 * sp + 1][1]);
-          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), bop, acc[t][nb], 0, 0, 0);
-          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), bop, acc[t][nb], 0, 0, 0);
+          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ah), bop, acc[t][nb], 0, 0, 0);
         }
       }
     }
@@ -650,6 +697,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
     step(1, kt);
     if (++kt >= nkt) break;
   }
+  const float vscale = ldexpf(1.f, a.vexp[int64_t(b) * a.Hq + h]);  // undo the V scaling
   // normaliser of every query column (the 4 lane groups hold partial sums of the same column);
   // acc[t][nb][i]: query 16 t + 4 c + i of the wave, dimension 16 nb + n
 #pragma unroll
@@ -664,7 +712,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
       if (qo < kk) {
         float* orow = a.out + ((int64_t(b) * a.Hq + h) * a.L + pos_of(qo)) * kD;
 #pragma unroll
-        for (int nb = 0; nb < kD / 16; ++nb) orow[16 * nb + n] = acc[t][nb][i] / li;
+        for (int nb = 0; nb < kD / 16; ++nb) orow[16 * nb + n] = acc[t][nb][i] / li * vscale;
       }
     }
   }
@@ -775,6 +823,10 @@ int launch_prefill_attend(const PrefillPlan& p, const sp_tensors& t, char* ws, f
   a.mode = t.head_mode;
   a.bits = at<uint32_t>(ws, p.o_bits);
   a.words = p.words;
+  a.vmaxp = at<float>(ws, p.o_vmaxp);
+  a.vexp = at<int32_t>(ws, p.o_vexp);
+  a.nslab = p.nslab;
+  a.Hkv = c.n_kv_heads;
   a.kc = at<uint16_t>(ws, p.o_kvc);
   a.vc = a.kc + size_t(B) * Hq * p.Lpad * kD;
   a.out = out;
@@ -784,6 +836,7 @@ int launch_prefill_attend(const PrefillPlan& p, const sp_tensors& t, char* ws, f
   a.G = p.G;
   a.scale_log2 = float(c.softmax_scale * 1.4426950408889634);
   const int nqb = int((p.L + kPfQueryBlock - 1) / kPfQueryBlock);
+  hipLaunchKernelGGL(k_pf_vmax, dim3(p.nslab, c.n_kv_heads, B), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_pf_gather, dim3(int(p.Lpad / kKeyTile), Hq, B), dim3(256), 0, st, a);
   // query blocks for a budget up to L, and at least one zero-row block per head past them
   hipLaunchKernelGGL(k_pf_attend, dim3(nqb + int((p.L + 1023) / 1024), Hq, B), dim3(256), 0, st, a);

@@ -21,7 +21,9 @@ struct PrefillPlan {
   int32_t nslab, nkb;  // importance slabs, proxy-score key blocks
   size_t o_status, o_S, o_pmq, o_M, o_zq, o_imp, o_pmax, o_pmin, o_gimp, o_gpmax, o_gpmin;
   size_t o_long, o_bbits, o_budget, o_bits, o_list;
-  size_t o_kvc;  // gathered K then V rows [B][Hq][Lpad][d] bf16 each; shares the region of S
+  size_t o_kvc;    // gathered K (bf16) then V (fp16, scaled) rows [B][Hq][Lpad][d]; shares the region of S
+  size_t o_vmaxp;  // float [B][Hkv][nslab]: max |v| per slab of each KV head's rows
+  size_t o_vexp;   // int32 [B][Hq]: the power of two the head's gathered V rows are scaled by
   size_t ws_bytes;
 };
 int launch_prefill_select(const PrefillPlan& p, const sp_tensors& t, char* ws, void* stream);
