@@ -97,7 +97,7 @@ sd_status sparse_prefill_select(const sp_handle* h, const sp_tensors* t, void* w
  * out fp32 [B][Hq][L][d] (contiguous); positions a head did not keep are written as 0.
  * Arithmetic: q.k on bf16 inputs with fp32 accumulation; P.V in fp16 with fp32 accumulation (V
  * converted exactly under a power-of-two scale per KV head, P rounded to fp16), so an output
- * differs from exact attention by at most about 2^-12 times the head's max |v|. */
+ * differs from exact attention by at most about 2^-11 times the head's max |v|. */
 sd_status sparse_prefill_attend(const sp_handle* h, const sp_tensors* t, void* ws, float* out, void* stream);
 
 /* Fill `view` with device pointers into `ws` (no device access). */
