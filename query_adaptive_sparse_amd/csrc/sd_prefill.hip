@@ -470,7 +470,11 @@ constexpr int kVPitchW = kD / 2 + 8;  // 32-bit words per staged V row
 
 __device__ __forceinline__ int pf_kswz(int x) { return x & 15; }
 
-__global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfPieces = kKeyTile * kPPR / kPfThreads;  // 16-byte K (and V) pieces per thread per step
+static_assert(kPfPieces * kPfThreads == kKeyTile * kPPR, "the threads cover a step's pieces");
+
+__global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
   typedef short v4s __attribute__((ext_vector_type(4)));
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   __shared__ uint4 kstb[2][kKeyTile * kPPR];
@@ -483,19 +487,20 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
   const int nqb = (kk + kPfQueryBlock - 1) / kPfQueryBlock;
   if (int(blockIdx.x) >= nqb) {
     // decompression: the workgroups past the head's query blocks (at least one per head, by the
-    // launch) write the zero rows of the positions the head did not keep, 8 rows of 32 x 16 bytes
-    // per pass, while the attention blocks run
+    // launch) write the zero rows of the positions the head did not keep, kZr rows of 32 x 16
+    // bytes at a time, 8 times per pass, while the attention blocks run
+    constexpr int kZr = kPfThreads / 32;
     const int nz = int(gridDim.x) - nqb, z = int(blockIdx.x) - nqb;
     const int per = ((Li + nz - 1) / nz + 7) & ~7;
     const int j1 = min(Li, (z + 1) * per);
     const uint32_t* hb = a.bits + (int64_t(b) * a.Hq + h) * a.words;
     float* ob = a.out + (int64_t(b) * a.Hq + h) * a.L * kD + (tid & 31) * 4;
     typedef float f4v __attribute__((ext_vector_type(4)));
-    for (int j0 = z * per + (tid >> 5); j0 < j1; j0 += 64) {
+    for (int j0 = z * per + (tid >> 5); j0 < j1; j0 += 8 * kZr) {
       uint32_t w[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int j = j0 + 8 * u;
+        const int j = j0 + kZr * u;
         const uint32_t wj = hb[min(j, j1 - 1) >> 5] >> (j & 31);  // j0 < j1: an in-range word
         w[u] = j < j1 ? wj : 1u;
       }
@@ -503,12 +508,11 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
       for (int u = 0; u < 8; ++u)
         if (!(w[u] & 1u))
           __builtin_nontemporal_store(f4v{0.f, 0.f, 0.f, 0.f},
-                                      reinterpret_cast<f4v*>(ob + int64_t(j0 + 8 * u) * kD));
+                                      reinterpret_cast<f4v*>(ob + int64_t(j0 + kZr * u) * kD));
     }
     return;
   }
   const int qb = nqb - 1 - int(blockIdx.x);  // heaviest (longest causal range) first
-  const int g = h / a.G;
   const int32_t* lst = a.list + (int64_t(b) * a.Hq + h) * a.L;
   // list entries are positions in [0, L); clamped so that an incomplete selection row (status
   // flag raised) can never address outside the tensors
@@ -534,19 +538,20 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
 #pragma unroll
     for (int nb = 0; nb < kD / 16; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // keys of step kt: gathered rows kKeyTile kt + x; thread pieces tid + 256 i (row x = tid / 16 +
-  // 16 i, 16-byte piece pc = tid % 16 of it). LDS holds steps kt (being computed) and kt + 1
+  // keys of step kt: gathered rows kKeyTile kt + x; thread pieces tid + kPfThreads i (row x =
+  // tid / 16 + (kPfThreads / 16) i, 16-byte piece pc = tid % 16 of it). LDS holds steps kt (being computed) and kt + 1
   // (written at the start of step kt); one register stage holds the loads of step kt + 2 in flight
   // for a whole step. One barrier per step.
   const int pc = tid & 15, x0 = tid >> 4;
   const int64_t head = (int64_t(b) * a.Hq + h) * a.Lpad * kD;
   const uint16_t* kthr = a.kc + head + x0 * kD + pc * 8;
   const uint16_t* vthr = a.vc + head + x0 * kD + pc * 8;
-  uint4 rk[4], rv[4];
+  constexpr int kRowStep = kPfThreads / 16;
+  uint4 rk[kPfPieces], rv[kPfPieces];
   auto stage = [&](int sbuf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int x = x0 + 16 * i;
+    for (int i = 0; i < kPfPieces; ++i) {
+      const int x = x0 + kRowStep * i;
       kstb[sbuf][x * kPPR + (pc ^ pf_kswz(x))] = rk[i];
       *reinterpret_cast<uint4*>(vstb[sbuf] + x * kVPitchW + pc * 4) = rv[i];
     }
@@ -556,9 +561,9 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfAttnArgs a) {
     kt = kt < nkt ? kt : nkt - 1;  // past the end: the last step again (still cached)
     const int64_t o = int64_t(kt) * kKeyTile * kD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rk[i] = ld16(kthr + o + 16 * i * kD);
-      rv[i] = ld16(vthr + o + 16 * i * kD);
+    for (int i = 0; i < kPfPieces; ++i) {
+      rk[i] = ld16(kthr + o + kRowStep * i * kD);
+      rv[i] = ld16(vthr + o + kRowStep * i * kD);
     }
   };
   issue(0);
@@ -839,7 +844,7 @@ int launch_prefill_attend(const PrefillPlan& p, const sp_tensors& t, char* ws, f
   hipLaunchKernelGGL(k_pf_vmax, dim3(p.nslab, c.n_kv_heads, B), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_pf_gather, dim3(int(p.Lpad / kKeyTile), Hq, B), dim3(256), 0, st, a);
   // query blocks for a budget up to L, and at least one zero-row block per head past them
-  hipLaunchKernelGGL(k_pf_attend, dim3(nqb + int((p.L + 1023) / 1024), Hq, B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_pf_attend, dim3(nqb + int((p.L + 1023) / 1024), Hq, B), dim3(kPfThreads), 0, st, a);
   return int(hipGetLastError());
 }
 

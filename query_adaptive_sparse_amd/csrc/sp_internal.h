@@ -10,7 +10,8 @@ namespace sd {
 constexpr int kPfSlab = kMinMaxBlock;  // keys per importance workgroup (and per partial max / min)
 constexpr int kPfKeyBlock = 64;        // keys per proxy-score workgroup
 constexpr int kPfMaxWindow = 64;
-constexpr int kPfQueryBlock = 128;     // compact queries per attention workgroup
+constexpr int kPfWaves = 8;            // waves per attention workgroup, 32 compact queries each
+constexpr int kPfQueryBlock = 32 * kPfWaves;  // compact queries per attention workgroup
 constexpr int kPfKeyTile = 64;         // compact keys per attention step (gathered rows are padded to it)
 
 struct PrefillPlan {
