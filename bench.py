@@ -89,11 +89,34 @@ def algorithmic_bytes(w, counts: np.ndarray) -> dict:
     return {"step": step, "attend": attend, "routing": routing, "raw_kv": raw_kv, "entries": U}
 
 
+class _OracleClock:
+    """Wall and process CPU time of the timed oracle calls. Their ratio is the number of host threads
+    the oracle actually kept busy: numpy's elementwise loops run on one, its BLAS calls on the pool."""
+
+    def __init__(self):
+        self.wall = self.cpu = 0.0
+
+    def __enter__(self):
+        self._w, self._c = time.perf_counter(), time.process_time()
+        return self
+
+    def __exit__(self, *exc):
+        self.wall += time.perf_counter() - self._w
+        self.cpu += time.process_time() - self._c
+
+    def cores(self) -> float:
+        return round(self.cpu / self.wall, 1) if self.wall > 0 else 1.0
+
+
+def _blas_pool() -> int:
+    from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+
+
 def cpu_baseline(w, inp, target_s=15.0, max_groups=0):
     """The fp64 oracle (as it stands) on whole (sequence, KV group) units of the same workload:
     units in a fixed random order, cycling over the step until about target_s of CPU time."""
     from oracle import HostSource, ref
-    from threadpoolctl import threadpool_info
 
     groups = [(b, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
     rng = np.random.default_rng(0)
@@ -101,22 +124,22 @@ def cpu_baseline(w, inp, target_s=15.0, max_groups=0):
     # host copies of the inputs (PCIe time is not oracle time)
     host = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inp.items()}
     src = HostSource(host)
-    done, t_total = 0, 0.0
+    done, clk = 0, _OracleClock()
     while True:
         b, g = order[done % len(order)]
-        t0 = time.perf_counter()
-        r = ref.select_group(w, src, b, g)
-        ref.attend_group(w, src, b, g, r["union"], r["heads"])
-        t_total += time.perf_counter() - t0
+        with clk:
+            r = ref.select_group(w, src, b, g)
+            ref.attend_group(w, src, b, g, r["union"], r["heads"])
+        t_total = clk.wall
         done += 1
         if (max_groups and done >= max_groups) or (not max_groups and t_total >= target_s):
             break
     per_group = t_total / done
     step_s = per_group * len(groups)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(w.batch * w.n_queries / step_s, 4), "unit": "queries/s", "cores": threads, "kind": "oracle",
+    return {"value": round(w.batch * w.n_queries / step_s, 4), "unit": "queries/s", "cores": clk.cores(), "kind": "oracle",
             "sample": f"{done} (sequence, KV group) units of {w.name} ({len(groups)} per step, cycled): "
-                      f"selection + attention, {t_total:.1f} s, scaled to a full step ({step_s:.2f} s)",
+                      f"selection + attention, {t_total:.1f} s, scaled to a full step ({step_s:.2f} s); "
+                      f"cores = process CPU time / wall time (BLAS pool {_blas_pool()} threads)",
             "cpu": _cpu_model()}
 
 
@@ -152,14 +175,14 @@ def prefill_cpu_baseline(w, inp, sel, target_s=15.0):
     rows are drawn uniformly over the head's sequence), scaled to a full layer (every head's
     importance, every head's rows)."""
     from oracle import PrefillSource, pref
-    from threadpoolctl import threadpool_info
 
     src = PrefillSource({k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inp.items() if k in ("Q", "K", "V")})
     L, W = w.seq_len, w.window
     modes = pref.head_modes(w)
-    t0 = time.perf_counter()
-    pref.proxy_importance(src.q_rows(0, 0, np.arange(L - W, L)), src.k_all(0, 0), w.softmax_scale, L - W)
-    t_imp = time.perf_counter() - t0
+    clk = _OracleClock()
+    with clk:
+        pref.proxy_importance(src.q_rows(0, 0, np.arange(L - W, L)), src.k_all(0, 0), w.softmax_scale, L - W)
+    t_imp = clk.wall
     k = int(sel["budget"][0])
     kinds = [m for m in (0, 1) if m in modes]
     rng = np.random.default_rng(0)
@@ -171,16 +194,17 @@ def prefill_cpu_baseline(w, inp, sel, target_s=15.0):
         done, t_rows = 0, 0.0
         while t_rows < target_s / len(kinds) and done < n:
             i = int(rng.integers(0, n))
-            t0 = time.perf_counter()
-            pref.tsa_attend_rows(w, src, 0, h, S, [i])
-            t_rows += time.perf_counter() - t0
+            w0 = clk.wall
+            with clk:
+                pref.tsa_attend_rows(w, src, 0, h, S, [i])
+            t_rows += clk.wall - w0
             done += 1
         step_s += w.batch * modes.count(m) * n * t_rows / done
         notes.append(f"{done} of {n} attention rows of {'full' if m else 'sparse'} head {h} ({t_rows:.1f} s)")
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(w.batch * L / step_s, 4), "unit": "prompt tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(w.batch * L / step_s, 4), "unit": "prompt tokens/s", "cores": clk.cores(), "kind": "oracle",
             "sample": f"{w.name}: importance of 1 of {w.batch * w.n_q_heads} heads ({t_imp:.1f} s), "
-                      + ", ".join(notes) + f"; scaled to a full layer ({step_s:.0f} s)",
+                      + ", ".join(notes) + f"; scaled to a full layer ({step_s:.0f} s); cores = process CPU "
+                      f"time / wall time (BLAS pool {_blas_pool()} threads)",
             "cpu": _cpu_model()}
 
 
@@ -272,25 +296,24 @@ def gist_cpu_baseline(w, inp, target_s=15.0):
     """The fp64 gist-prefill oracle (as it stands) on a bounded sample: query rows of one head drawn
     uniformly over the raw tokens and the gists, scaled to a full layer (every head, every row)."""
     from oracle import GistPrefillSource, gref
-    from threadpoolctl import threadpool_info
 
     src = GistPrefillSource({k: inp[k].cpu() for k in ("Q", "K", "V", "Qg", "Kg", "Vg")})
     rng = np.random.default_rng(0)
     n_rows = w.n_tokens + w.n_chunks
-    done, t_rows = 0, 0.0
-    while t_rows < target_s and done < n_rows:
+    done, clk = 0, _OracleClock()
+    while clk.wall < target_s and done < n_rows:
         i = int(rng.integers(0, n_rows))
         kind, row = ("raw", i) if i < w.n_tokens else ("gist", i - w.n_tokens)
-        t0 = time.perf_counter()
-        gref.gp_attend_rows(w, src, 0, 0, kind, [row])
-        t_rows += time.perf_counter() - t0
+        with clk:
+            gref.gp_attend_rows(w, src, 0, 0, kind, [row])
         done += 1
+    t_rows = clk.wall
     step_s = w.batch * w.n_q_heads * n_rows * t_rows / done
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(w.batch * w.n_tokens / step_s, 4), "unit": "prompt tokens/s", "cores": threads,
+    return {"value": round(w.batch * w.n_tokens / step_s, 4), "unit": "prompt tokens/s", "cores": clk.cores(),
             "kind": "oracle",
             "sample": f"{w.name}: {done} of {n_rows} query rows (raw and gist, uniform) of 1 of "
-                      f"{w.batch * w.n_q_heads} heads ({t_rows:.1f} s), scaled to a full layer ({step_s:.0f} s)",
+                      f"{w.batch * w.n_q_heads} heads ({t_rows:.1f} s), scaled to a full layer ({step_s:.0f} s); "
+                      f"cores = process CPU time / wall time (BLAS pool {_blas_pool()} threads)",
             "cpu": _cpu_model()}
 
 
