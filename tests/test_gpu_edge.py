@@ -155,3 +155,20 @@ def test_two_handles_on_two_streams():
         l_ = lse.cpu().numpy().reshape(alone["lse"].shape)
         assert np.array_equal(o, alone["out"]) and np.array_equal(l_, alone["lse"]), w.name
         print(f"[edge] {w.name}: concurrent run equals the run alone", flush=True)
+
+
+DTYPE_DIM = [("c2s", dict(head_dim=64, softmax_scale=0.125)),
+             ("c3s", dict(head_dim=64, softmax_scale=0.125, select_scale=0.125)),
+             ("c2s", dict(head_dim=64, softmax_scale=0.125, n_queries=2)),  # 14 rows: two P.V MFMAs
+             ("c2s", dict(dtype="f32", softmax_scale=128 ** -0.5)),
+             ("c1s", dict(head_dim=128, softmax_scale=128 ** -0.5))]
+
+
+@pytest.mark.parametrize("name,kw", DTYPE_DIM, ids=[f"{n}-{kw.get('dtype', 'bf16' if n != 'c1s' else 'f32')}"
+                                                    f"-d{kw.get('head_dim', 128)}-T{kw.get('n_queries', 1)}"
+                                                    for n, kw in DTYPE_DIM])
+def test_dtype_and_head_dim(name, kw):
+    """Every element type and head size the library is built for (bf16 / fp32 x d 64 / 128),
+    against the oracle on reduced shapes."""
+    w = replace(configs.get(name), name=f"{name}_dd", **kw)
+    _run(w, gen.make_inputs(w, device="cuda"))
