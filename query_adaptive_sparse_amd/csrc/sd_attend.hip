@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   __shared__ int32_t lst[kListLds];
   __shared__ uint16_t lmask[kListLds];
   __shared__ uint32_t wlds[kWaves * CF::kWaveWords];
-  __shared__ int32_t sbuf[256];
+  __shared__ int32_t sbuf[kWaves];
   const int tid = threadIdx.x;
   const int NG = a.n_groups;
   const int cs = a.chunk_shift;
@@ -356,20 +356,18 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
     for (int gg = g0; gg < min(NG, g0 + per); ++gg) {
       sum += group_extent(a.cnt[gg], cs, a.attend_summary, a.n_list);
     }
-    sbuf[tid] = sum;
+    // inclusive scan over the 256 threads in thread order: DPP within each wave, then the
+    // earlier waves' totals (one barrier)
+    const int incl = wave_scan_i32_dpp(sum, tid & 63);
+    if ((tid & 63) == 63) sbuf[tid >> 6] = incl;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int add = tid >= off ? sbuf[tid - off] : 0;
-      __syncthreads();
-      sbuf[tid] += add;
-      __syncthreads();
-    }
-    int run = sbuf[tid] - sum;
+    int run = incl - sum;
+    for (int w = 0; w < (tid >> 6); ++w) run += sbuf[w];
     for (int gg = g0; gg < min(NG, g0 + per); ++gg) {
       gpre[gg] = run;
       run += group_extent(a.cnt[gg], cs, a.attend_summary, a.n_list);
     }
-    if (tid == 255) gpre[NG] = sbuf[255];
+    if (tid == 255) gpre[NG] = run;  // the last thread's running sum is the total
     __syncthreads();
   }
   const int total = gpre[NG];
