@@ -389,6 +389,28 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   uint32_t* vt = wlds + wave * CF::kWaveWords;
   Attender<T, D, SPLIT> at(a, lst, lmask, vt);
   const int lane = tid & 63, n = lane & 15, c = lane >> 4;
+  // a piece of the list (ne <= kListLds entries) into LDS, in rounds of 8 entries per thread
+  // whose loads (from clamped indices) are all issued before the first is stored: a piece costs
+  // at most kListLds / 2048 memory round trips, not one per 256 entries
+  auto load_list = [&](const int32_t* src, int ne, int gid) {
+    constexpr int kPer = 8;
+    for (int r0 = 0; r0 < ne; r0 += 256 * kPer) {
+      int32_t ev[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = r0 + tid + 256 * k;
+        ev[k] = src[i < ne ? i : ne - 1];
+      }
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = r0 + tid + 256 * k;
+        if (i < ne) {
+          lst[i] = ev[k];
+          if (a.head_masks) lmask[i] = uint16_t(head_mask_of(a, gid, ev[k]));
+        }
+      }
+    }
+  };
 
   for (int gi = lo; gi < NG && gpre[gi] < b1; ++gi) {
     const int s0 = max(b0, gpre[gi]) - gpre[gi];
@@ -418,11 +440,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
         const int e0 = (u0 * kTile) >> cs;
         const int e1 = min(cnt, ((u1 * kTile - 1) >> cs) + 1);
         __syncthreads();
-        for (int i = tid; i < e1 - e0; i += 256) {
-          const int e = glist[e0 + i];
-          lst[i] = e;
-          if (a.head_masks) lmask[i] = uint16_t(head_mask_of(a, gi, e));
-        }
+        load_list(glist + e0, e1 - e0, gi);
         __syncthreads();
         at.run(false, u0, u1, ntok, e0, st);
       }
@@ -442,11 +460,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
         if (a.attend_summary == 1) {
           const int e1 = min(cnt, u1 * kTile);
           __syncthreads();
-          for (int i = tid; i < e1 - e0; i += 256) {
-            const int e = glist[e0 + i];
-            lst[i] = e;
-            if (a.head_masks) lmask[i] = uint16_t(head_mask_of(a, gi, e));
-          }
+          load_list(glist + e0, e1 - e0, gi);
           __syncthreads();
         }
         at.run(true, u0, u1, nsum, e0, st);
