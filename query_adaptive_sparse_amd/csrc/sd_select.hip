@@ -675,7 +675,7 @@ __global__ __launch_bounds__(kFindThreads) void k_long_find1(LongArgs a) {
   double m = 0.0;
   uint32_t cn = 0;
   const int64_t o = row * a.nb1 * kBins1 + tid;
-#pragma unroll 8
+#pragma unroll 16
   for (int sl = 0; sl < a.nb1; ++sl) {
     m += a.h1m[o + int64_t(sl) * kBins1];
     cn += a.h1c[o + int64_t(sl) * kBins1];
@@ -1286,13 +1286,24 @@ __global__ __launch_bounds__(256) void k_union_count(UnionArgs a) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) u[i] = 0u;
   if (!local) {
-    for (int j = 0; j < a.G; ++j) {
-      const uint32_t* src = a.bits + (int64_t(b) * a.Hq + g * a.G + j) * a.words;
+    // the group's heads four at a time, every load of a block issued before the first is used
+    // (heads past the group repeat its last head: the OR is unchanged)
+    for (int j0 = 0; j0 < a.G; j0 += 4) {
+      uint32_t v[4][PER];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int64_t w = w0 + tid + 256 * i;
-        u[i] |= src[w < a.words ? w : a.words - 1];
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = j0 + jj < a.G ? j0 + jj : a.G - 1;
+        const uint32_t* src = a.bits + (int64_t(b) * a.Hq + g * a.G + j) * a.words;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int64_t w = w0 + tid + 256 * i;
+          v[jj][i] = src[w < a.words ? w : a.words - 1];
+        }
       }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) u[i] |= v[jj][i];
     }
   }
   int c = 0;
