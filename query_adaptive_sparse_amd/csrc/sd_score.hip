@@ -125,10 +125,10 @@ __global__ __launch_bounds__(256) void k_proxy_query(const T* __restrict__ q, QR
 
 // Proxy scores s_t = q_p . k_p[t] over the 16 proxy dims, separate multiply and add in index
 // order (q_p has 53 significant bits, so the products round). One 512-thread workgroup per
-// kMinMaxBlock tokens of one scored KV group; each thread takes 4 tokens 512 apart with all their
-// loads issued first, and the group's G heads share each token's proxy key. The workgroup projects
-// the group's queries itself (q_p = q P, fp64 in index order, the same arithmetic as
-// k_proxy_query) while the key loads are in flight, and writes its max and min per head.
+// kMinMaxBlock tokens of one scored KV group; each thread takes 4 tokens 512 apart, and the group's
+// G heads share each token's proxy key. The workgroup projects the group's queries itself (q_p =
+// q P, fp64 in index order, the same arithmetic as k_proxy_query) while the key loads are in
+// flight, and writes its max and min per head.
 // Workgroup (0, 0, 0) clears the status words and the per-group arrival counters.
 struct ProxyArgs {
   const uint16_t* kp;
@@ -158,6 +158,26 @@ __global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
     if (tid < 16) a.status[tid] = 0;
     for (int i = tid; i < a.n_groups; i += 512) a.arrivals[i] = 0;
   }
+  // The group's projection and queries are loaded first (one unrolled round into registers, from
+  // clamped rows, so every load is issued before any is used), then the tokens' proxy keys; the
+  // projection is staged in LDS and q_p = q P computed (one thread per (head, proxy dim), the
+  // index-order fma chain) while the key loads are still in flight.
+  __shared__ float Ps[D * 16];
+  __shared__ float Qs[kMaxProxyGroup][D];
+  constexpr int PPT = D * 16 / 512;              // projection entries per thread
+  constexpr int QPT = kMaxProxyGroup * D / 512;  // query slots per thread
+  static_assert(PPT * 512 == D * 16 && QPT * 512 == kMaxProxyGroup * D, "512 threads cover P and q");
+  const float* P = a.proj + int64_t(g) * D * 16;
+  float pv[PPT];
+  T qv[QPT];
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) pv[k] = P[tid + 512 * k];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + 512 * k, hh = i / D, e = i - hh * D;
+    qv[k] = static_cast<const T*>(a.q)[q_offset(a.qm, b, g * G + (hh < G ? hh : G - 1)) + e];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the key loads
   const int64_t t0 = int64_t(blockIdx.x) * kMinMaxBlock;
   const uint16_t* kb = a.kp + b * a.kp_sb + int64_t(g) * a.kp_sh;
   constexpr int TPT = kMinMaxBlock / 512;  // tokens per thread (512 threads)
@@ -169,25 +189,21 @@ __global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
     raw[k][0] = ld16(kb + t * a.kp_st);
     raw[k][1] = ld16(kb + t * a.kp_st + 8);
   }
-  {
-    // stage the group's projection and queries in LDS (one parallel round of loads), then one
-    // thread per (head, proxy dim) runs the index-order fma chain
-    __shared__ float Ps[D * 16];
-    __shared__ float Qs[kMaxProxyGroup][D];
-    const float* P = a.proj + int64_t(g) * D * 16;
-    for (int i = tid; i < D * 16; i += 512) Ps[i] = P[i];
-    for (int i = tid; i < G * D; i += 512) {
-      const int hh = i / D, e = i - hh * D;
-      Qs[hh][e] = elem_f32<T>(static_cast<const T*>(a.q) + q_offset(a.qm, b, g * G + hh) + e);
-    }
-    __syncthreads();
-    if (tid < G * 16) {
-      const int hh = tid >> 4, j = tid & 15;
-      double acc = 0.0;
+  __builtin_amdgcn_sched_barrier(0);  // every key load is issued before P and q are staged
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) Ps[tid + 512 * k] = pv[k];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + 512 * k, hh = i / D, e = i - hh * D;
+    if (hh < G) Qs[hh][e] = elem_f32<T>(&qv[k]);
+  }
+  __syncthreads();
+  if (tid < G * 16) {
+    const int hh = tid >> 4, j = tid & 15;
+    double acc = 0.0;
 #pragma unroll 16
-      for (int i = 0; i < D; ++i) acc = fma(double(Qs[hh][i]), double(Ps[i * 16 + j]), acc);
-      qs[hh][j] = acc;
-    }
+    for (int i = 0; i < D; ++i) acc = fma(double(Qs[hh][i]), double(Ps[i * 16 + j]), acc);
+    qs[hh][j] = acc;
   }
   __syncthreads();
   double mx[kMaxProxyGroup], mn[kMaxProxyGroup];
