@@ -42,21 +42,44 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRo
   const int h0 = cand ? y : y * G;
   const int nh = cand ? 1 : G;
   const int64_t r0 = int64_t(blockIdx.x) * kScoreRows;
-  // key rows of this workgroup, 16 bytes per thread per step (rows past the end repeat the last),
-  // loaded first; the queries are staged while they are in flight
+  // the slots' query elements (4 HPT slots at most: one unrolled round of loads from clamped rows),
+  // then the key rows of this workgroup, 16 bytes per thread per step (rows past the end repeat
+  // the last); the queries are staged in LDS while the key loads are in flight
+  constexpr int QPT = 4 * HPT * D / 256;
+  T qv[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + 256 * k, j = i / D, dd = i - j * D;
+    qv[k] = q[q_offset(qm, b, h0 + (j < nh ? j : nh - 1)) + dd];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the key loads
   constexpr int KPT = kScoreRows * PPR / 256;
   uint4 kreg[KPT];
+  const T* kbase = keys + b * k_sb + int64_t(g) * k_sh;
+  auto piece_row = [&](int k) {
+    const int r = (tid + 256 * k) / PPR;
+    return int32_t(r0 + r < n_rows ? r0 + r : n_rows - 1);
+  };
+  if (cand) {
+    // candidate rows: every chunk id is looked up first, then every key piece loaded
+    const int32_t* cr = cand + (int64_t(b) * Hq + h0) * out_len;
+    int32_t src[KPT];
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int i = tid + 256 * k, r = i / PPR, pc = i - r * PPR;
-    int64_t row = r0 + r < n_rows ? r0 + r : n_rows - 1;
-    int64_t src = cand ? int64_t(cand[(int64_t(b) * Hq + h0) * out_len + row]) : row;
-    src = src < 0 ? 0 : (src < n_keys ? src : n_keys - 1);
-    kreg[k] = ld16(keys + b * k_sb + int64_t(g) * k_sh + src * k_st + pc * EPV);
+    for (int k = 0; k < KPT; ++k) src[k] = cr[piece_row(k)];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int64_t sk = src[k] < 0 ? 0 : (src[k] < n_keys ? src[k] : n_keys - 1);
+      kreg[k] = ld16(kbase + sk * k_st + ((tid + 256 * k) % PPR) * EPV);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) kreg[k] = ld16(kbase + int64_t(piece_row(k)) * k_st + ((tid + 256 * k) % PPR) * EPV);
   }
-  for (int i = tid; i < nh * D; i += 256) {
-    const int j = i / D, dd = i - j * D;
-    qs[j * QW + dd] = double(elem_f32<T>(q + q_offset(qm, b, h0 + j) + dd));
+  __builtin_amdgcn_sched_barrier(0);  // every key load is issued before the queries are staged
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + 256 * k, j = i / D, dd = i - j * D;
+    if (j < nh) qs[j * QW + dd] = double(elem_f32<T>(&qv[k]));
   }
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
