@@ -457,8 +457,18 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
     for (int w = tid; w < uwords; w += kSelT) {
       uint32_t u = edge_bits(w, a.n_entries, first, last);
       if (!local)
-        for (int j = 0; j < G; ++j)
-          u |= __builtin_nontemporal_load(&a.bits[(int64_t(b) * a.Hq + g * G + j) * a.words + w]);
+        // the heads' words 8 at a time, every load of a block issued before the first is used
+        // (heads past the group repeat its last head: the OR is unchanged)
+        for (int j0 = 0; j0 < G; j0 += 8) {
+          uint32_t v[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const int j = j0 + jj < G ? j0 + jj : G - 1;
+            v[jj] = __builtin_nontemporal_load(&a.bits[(int64_t(b) * a.Hq + g * G + j) * a.words + w]);
+          }
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) u |= v[jj];
+        }
       ubits[w] = u;
     }
   }
