@@ -847,7 +847,9 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
         if (soff[mid] <= j) lo = mid; else hi = mid;
       }
       int s = lo * per, off = j - soff[lo];
-      while (s + 1 < a.nb1 && off >= a.ccnt[row * a.nb1 + s]) {  // at most `per` steps
+      // with one slab per thread, soff[lo + 1] - soff[lo] is that slab's count, so j lies in slab
+      // lo and no count needs reading
+      while (per > 1 && s + 1 < a.nb1 && off >= a.ccnt[row * a.nb1 + s]) {  // at most `per` steps
         off -= a.ccnt[row * a.nb1 + s];
         ++s;
       }
