@@ -80,7 +80,7 @@ typedef struct {
   int32_t n_q_heads;      /* Hq */
   int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0 and G = Hq / Hkv, T x G <= 16 */
   int32_t head_dim;       /* d: 64 or 128 */
-  int64_t n_ctx;          /* N tokens in the cache, 1 <= N < 2^31 */
+  int64_t n_ctx;          /* N tokens in the cache, 1 <= N < 2^31, N / C <= 2^24 */
   int32_t chunk_size;     /* C tokens per chunk, N % C == 0; 1 = token-level */
   int32_t seg_size;       /* SD_HIER_TOPK: chunks per segment, M % seg == 0 */
   int32_t route;          /* SD_ROUTE_SUMMARY or SD_ROUTE_PROXY (needs C == 1) */
@@ -146,9 +146,12 @@ typedef struct {
  *                                 (forced and local entries are not included)
  *   list      int32 [B][Hkv][n_entries] group union, ascending; first cnt valid
  *   count     int32 [B][Hkv]      union size
- *   status    u32 [4]             device flags: [0] != 0 when a top-p row
- *                                 overflowed its candidate buffer (that row's
- *                                 selection is then incomplete) */
+ *   status    u32 [4]             internal-invariant flags, cleared by every
+ *                                 step's first call: every row is resolved
+ *                                 exactly for any input (near-equal and tied
+ *                                 scores included), so a nonzero word after a
+ *                                 step is a library defect, never an input
+ *                                 condition */
 typedef struct {
   const double* scores0;   int64_t len0;
   const double* scores1;   int64_t len1;

@@ -46,7 +46,7 @@ typedef struct {
   int32_t n_q_heads;      /* Hq */
   int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0 */
   int32_t head_dim;       /* d: 128 */
-  int64_t seq_len;        /* L prompt tokens, window <= L < 2^31 */
+  int64_t seq_len;        /* L prompt tokens, window <= L <= 2^24 */
   int32_t window;         /* W most recent queries of the proxy map, 1 .. 64 */
   int32_t kv_dtype;       /* SD_BF16 */
   double tau;             /* coverage threshold, in [0, 1) */
@@ -74,7 +74,8 @@ typedef struct {
  *   budget     int32 [B]          tokens kept per sparse head (unused when every head is full)
  *   head_bits  u32 [B][Hq][words] head h's positions, bit j of word j/32
  *   list       int32 [B][Hq][L]   head h's positions ascending; the first budget[b] valid
- *   status     u32 [4]            [0] != 0: a selection row overflowed its candidate buffer */
+ *   status     u32 [4]            internal-invariant flags (zero after every call on any
+ *                                 input; a nonzero word is a library defect) */
 typedef struct {
   const double* importance;
   const int32_t* budget;

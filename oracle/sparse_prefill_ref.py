@@ -80,15 +80,25 @@ def head_modes(w) -> list:
     return [0] * w.n_q_heads if m is None else [int(x) for x in m]
 
 
-def tsa_select(w, src, b: int) -> dict:
-    """Per-head importances, the global budget and every head's positions for sequence b."""
+def head_importances(w, src, b: int, pool_map=map) -> list:
+    """[TSA] dynamic token coverage, scoring: every query head's proxy-map importance for
+    sequence b, head by head (``pool_map`` may evaluate the heads concurrently; each head's
+    arithmetic is ``proxy_importance`` alone)."""
     L, W, Hq = w.seq_len, w.window, w.n_q_heads
     G = Hq // w.n_kv_heads
-    modes = head_modes(w)
-    imps = []
-    for h in range(Hq):
+
+    def one(h):
         Qw = src.q_rows(b, h, np.arange(L - W, L))
-        imps.append(proxy_importance(Qw, src.k_all(b, h // G), w.softmax_scale, L - W))
+        return proxy_importance(Qw, src.k_all(b, h // G), w.softmax_scale, L - W)
+
+    return list(pool_map(one, range(Hq)))
+
+
+def select_from_importances(w, imps: list) -> dict:
+    """The global budget and every head's positions from the heads' importances ([TSA] dynamic
+    token coverage: budget from the summed importance of the sparse heads, then top-k per head)."""
+    L, Hq = w.seq_len, w.n_q_heads
+    modes = head_modes(w)
     total = np.zeros(L, dtype=np.float64)
     for h in range(Hq):
         if not modes[h]:
@@ -103,6 +113,11 @@ def tsa_select(w, src, b: int) -> dict:
         o = order_desc(imps[h])
         gaps[h] = abs(imps[h][o[k - 1]] - imps[h][o[k]]) if k < L else math.inf
     return {"importance": imps, "budget": k, "margin": margin, "sets": sets, "gaps": gaps}
+
+
+def tsa_select(w, src, b: int, pool_map=map) -> dict:
+    """Per-head importances, the global budget and every head's positions for sequence b."""
+    return select_from_importances(w, head_importances(w, src, b, pool_map=pool_map))
 
 
 def tsa_attend_rows(w, src, b: int, h: int, S: np.ndarray, rows) -> tuple:

@@ -58,6 +58,9 @@ sd_status check_cfg(const sd_config& c) {
   if (c.n_ctx < 1 || c.n_ctx >= (int64_t(1) << 31)) return fail(SD_EINVAL, "n_ctx out of range (%lld)", (long long)c.n_ctx);
   if (c.chunk_size < 1 || c.n_ctx % c.chunk_size)
     return fail(SD_EINVAL, "chunk_size %d must be >= 1 and divide n_ctx %lld", c.chunk_size, (long long)c.n_ctx);
+  if (c.n_ctx / c.chunk_size > sd::kMaxRowEntries)
+    return fail(SD_EUNSUPPORTED, "more than %lld selection entries (n_ctx / chunk_size) per row",
+                (long long)sd::kMaxRowEntries);
   if (c.route != SD_ROUTE_SUMMARY && c.route != SD_ROUTE_PROXY) return fail(SD_EINVAL, "route %d unknown", c.route);
   if (c.mode != SD_TOPK && c.mode != SD_TOPP && c.mode != SD_HIER_TOPK && c.mode != SD_COVERAGE)
     return fail(SD_EINVAL, "mode %d unknown", c.mode);
@@ -156,7 +159,8 @@ void plan_workspace(sd::Plan& p) {
   p.o_pmax = take(mm_rows * p.score_blocks0 * 8);
   p.o_pmin = take(mm_rows * p.score_blocks0 * 8);
   p.o_info = take(rows * sizeof(sd::RowInfo));
-  p.o_h1m = take(rows * p.long_blocks * sd::kBins1 * 8);
+  p.o_h1h = take(rows * p.long_blocks * sd::kBins1 * 8);
+  p.o_h1l = take(rows * p.long_blocks * sd::kBins1 * 8);
   p.o_h1c = take(rows * p.long_blocks * sd::kBins1 * 4);
   p.o_cbin = take(rows * ((p.len0 + 7) & ~int64_t(7)) * 2);
   p.o_cidx = take(rows * p.long_blocks * sd::kResolveCap * 4);
@@ -327,6 +331,8 @@ sd_status sparse_prefill_init(const sp_config* cfg, sp_handle** out, size_t* wor
   if (c.window > sd::kPfMaxWindow) return fail(SD_EUNSUPPORTED, "window must be <= %d (got %d)", sd::kPfMaxWindow, c.window);
   if (c.seq_len < c.window || c.seq_len >= (int64_t(1) << 31))
     return fail(SD_EINVAL, "seq_len must be in [window, 2^31) (got %lld)", (long long)c.seq_len);
+  if (c.seq_len > sd::kMaxRowEntries)
+    return fail(SD_EUNSUPPORTED, "seq_len above %lld (selection rows)", (long long)sd::kMaxRowEntries);
   if (!(c.tau >= 0.0) || !(c.tau < 1.0)) return fail(SD_EINVAL, "tau must be in [0, 1) (got %g)", c.tau);
   if (!(c.softmax_scale > 0.0) || !std::isfinite(c.softmax_scale))
     return fail(SD_EINVAL, "softmax_scale must be finite and > 0 (got %g)", c.softmax_scale);

@@ -19,6 +19,9 @@ constexpr int64_t small_row_limit(int) { return kSmallRowMax; }
 constexpr int kBins1 = 1024;
 constexpr int kBins2 = 4096;
 constexpr int kResolveCap = 4096;
+// Most entries in one selection row: the exact fixed-point mass sums of the selection kernels
+// (2^39 and 2^40 units per weight in two 64-bit words) hold up to 2^24 weights.
+constexpr int64_t kMaxRowEntries = int64_t(1) << 24;
 // Entries per workgroup ("slab") in the long-row histogram and marking passes.
 constexpr int kLongBlock = 32768;
 // Entries per partial max / min written by the score passes of long rows.
@@ -58,7 +61,7 @@ struct Plan {
   int8_t scored[kMaxKvHeads];  // their indices, ascending
   // workspace byte offsets
   size_t o_status, o_arrive, o_qp, o_s0, o_s1, o_cand, o_bits, o_ubits, o_rcnt, o_list, o_cnt;
-  size_t o_gpre, o_po, o_pl, o_pmax, o_pmin, o_info, o_h1m, o_h1c, o_cbin, o_cidx, o_ccnt, o_budget, o_cmass, o_cimp, o_csort;
+  size_t o_gpre, o_po, o_pl, o_pmax, o_pmin, o_info, o_h1h, o_h1l, o_h1c, o_cbin, o_cidx, o_ccnt, o_budget, o_cmass, o_cimp, o_csort;
   int64_t n_arrive;  // arrival counters: one per (sequence, KV group)
   size_t ws_bytes;
 };
@@ -70,7 +73,7 @@ struct RowInfo {
   double before1;               // weight of everything ahead of the crossing coarse bin
   int32_t bin1;                 // crossing coarse bin
   int32_t all;                  // 1: the whole row is selected
-  int32_t gather;               // 1: the crossing coarse bin holds <= kResolveCap entries
+  int32_t wexp;                 // masses of an `ident` row are held as value * 2^-wexp (< 1)
   int32_t pad;
 };
 

@@ -28,7 +28,8 @@
 //                    XOR-swizzled per row, V rows padded for transpose reads), each wave runs q.K^T
 //                    on the bf16 MFMA, the causal mask in compact order, an online softmax whose
 //                    reference moves only when a logit exceeds it by 2^8, and P.V on the fp16
-//                    MFMA (P rounded to fp16, V converted at the gather), then writes its rows;
+//                    MFMA (P split into fp16 high and low parts, V converted at the gather),
+//                    then writes its rows;
 //                    the workgroups past a head's query blocks write the zero rows of the
 //                    positions it did not keep.
 #include "sd_device.h"
@@ -404,9 +405,13 @@ __device__ __forceinline__ int pf_vexp(const PfAttnArgs& a, int b, int g) {
   float m = 0.f;
   for (int s = 0; s < a.nslab; ++s) m = fmaxf(m, vm[s]);
   int e = 0;
-  if (m > 0.f && m <= 3.0e38f) {
+  if (m > 0.f && m <= 3.4028235e38f) {  // every finite max (inputs are finite)
     frexpf(m, &e);  // m = f 2^e, f in [0.5, 1)
     e -= 15;
+    // 2^-e and 2^e stay finite fp32 values: a head whose max |v| is below 2^-111 is scaled by
+    // 2^126 only (its values then fill less of the fp16 range; each keeps an absolute error of
+    // at most 2^-151)
+    e = e > -126 ? e : -126;
   }
   return e;
 }
@@ -514,8 +519,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
   }
   const int qb = nqb - 1 - int(blockIdx.x);  // heaviest (longest causal range) first
   const int32_t* lst = a.list + (int64_t(b) * a.Hq + h) * a.L;
-  // list entries are positions in [0, L); clamped so that an incomplete selection row (status
-  // flag raised) can never address outside the tensors
+  // list entries are positions in [0, L); clamped so that no list entry can ever address outside
+  // the tensors
   auto pos_of = [&](int i) { return int64_t(min(max(lst[i], 0), Li - 1)); };
   const int q0w = qb * kPfQueryBlock + 32 * wave;  // first query of this wave
   // query fragments (B operand of q.K^T: query n, dimensions 32 j + 8 c .. + 7) per query tile
@@ -647,9 +652,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
         m[t] = mn;
       }
     }
-    // P in fp16 (rounded to nearest even; the probabilities are below 2^8 by the lazy reference):
-    // ph[t][st][u]: keys 16 st + 4 c + 2 u, + 1 of query 16 t + n, packed
-    uint32_t ph[kQTiles][kKeyTile / 16][2];
+    // P as two fp16 parts, hi = fp16(p) and lo = fp16(p - hi) (rounded to nearest even; the
+    // probabilities are below 2^8 by the lazy reference): hi + lo carries p to about 2^-22, so the
+    // weights that multiply V agree with the fp32 normaliser l. ph / pl[t][st][u]: keys
+    // 16 st + 4 c + 2 u, + 1 of query 16 t + n, packed
+    uint32_t ph[kQTiles][kKeyTile / 16][2], pl[kQTiles][kKeyTile / 16][2];
 #pragma unroll
     for (int t = 0; t < kQTiles; ++t) {
       // a column whose reference is still -inf has seen masked logits only: exponent -inf
@@ -665,10 +672,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-          h2 hv;
+          h2 hv, lv;
           hv[0] = (_Float16)pr[2 * u];
           hv[1] = (_Float16)pr[2 * u + 1];
+          lv[0] = (_Float16)(pr[2 * u] - (float)hv[0]);  // the difference is exact in fp32
+          lv[1] = (_Float16)(pr[2 * u + 1] - (float)hv[1]);
           ph[t][st][u] = __builtin_bit_cast(uint32_t, hv);
+          pl[t][st][u] = __builtin_bit_cast(uint32_t, lv);
         }
       }
     }
@@ -690,7 +700,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
 #pragma unroll
         for (int t = 0; t < kQTiles; ++t) {
           const uint4 ah = make_uint4(ph[t][2 * sp][0], ph[t][2 * sp][1], ph[t][2 * sp + 1][0], ph[t][2 * sp + 1][1]);
+          const uint4 al = make_uint4(pl[t][2 * sp][0], pl[t][2 * sp][1], pl[t][2 * sp + 1][0], pl[t][2 * sp + 1][1]);
           acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ah), bop, acc[t][nb], 0, 0, 0);
+          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, al), bop, acc[t][nb], 0, 0, 0);
         }
       }
     }

@@ -55,6 +55,38 @@ __device__ double block_excl_scan(double v, double* buf, double* total) {
   return incl - v;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Exact, order-independent histogram masses. A weight w in [0, 1] is held as two integers,
+// hi = floor(w 2^39) and lo = floor((w 2^39 - hi) 2^40): w to a resolution of 2^-79 (exactly when
+// w >= 2^-26; a smaller weight loses less than 2^-79). Integer addition is associative, so the
+// bin sums that workgroups build with LDS atomics, and the slab partials summed afterwards, hold
+// the same bits whatever order the entries arrive in. Up to 2^24 weights sum without overflow, so
+// rows are limited to kMaxRowEntries
+// (hi sums stay below 2^63, lo sums below 2^64); a sum's value is hi 2^-39 + lo 2^-79, rounded
+// once per word when converted to fp64.
+// ---------------------------------------------------------------------------------------------
+constexpr int kFixLoBits = 40;
+constexpr uint64_t kFixLoMask = (uint64_t(1) << kFixLoBits) - 1;
+static_assert(kMaxRowEntries <= (int64_t(1) << 24), "fixed-point sums of a row must not overflow");
+struct FixW {
+  uint64_t hi, lo;
+};
+__device__ __forceinline__ FixW fix_of(double w) {
+  const double x = w * 0x1p39;  // exact: a power-of-two scaling
+  const double h = floor(x);
+  return FixW{uint64_t(h), uint64_t((x - h) * 0x1p40)};  // x - h and the scaling are exact
+}
+__device__ __forceinline__ double fix_value(uint64_t hi, uint64_t lo) {
+  hi += lo >> kFixLoBits;  // whole 2^-39 units of the low word
+  lo &= kFixLoMask;
+  return double(hi) * 0x1p-39 + double(lo) * 0x1p-79;
+}
+__device__ __forceinline__ void fix_add(unsigned long long* hi, unsigned long long* lo, double w) {
+  const FixW f = fix_of(w);
+  atomicAdd(hi, (unsigned long long)f.hi);
+  atomicAdd(lo, (unsigned long long)f.lo);
+}
+
 // First sorted position (< n) at which the running weight base + w_0 + ... + w_i reaches
 // `target`, or -1. Positions are split into contiguous per-thread segments; weights come from
 // weight(i). Returns the same value to every thread.
@@ -110,6 +142,11 @@ constexpr int kCandCap = 256;
 // (ranking by counting costs n^2 LDS reads).
 constexpr int kRankDirect = 16;
 constexpr int kSelT = 256;                          // threads per head
+// entry count of a short-row bin, kept in the high bits of its low mass word (a row of at most
+// kSmallRowMax = 2^11 entries: low parts sum below 2^51, counts times 2^52 stay below 2^64)
+constexpr int kCountShift = 52;
+constexpr uint64_t kCountOne = uint64_t(1) << kCountShift;
+static_assert(kSmallRowMax <= 2048, "short-row bin counts share the low mass word");
 constexpr int kSelW = kSelT / 64;                   // waves per head
 constexpr int kLaneEntries = kSmallRowMax / kSelT;  // 8
 constexpr int kUnionWordsMax = 4096;
@@ -148,8 +185,10 @@ __device__ __forceinline__ void bins_of(double s, double smax, double binscale, 
 }
 
 __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
-  __shared__ double hm[kNBin];
-  __shared__ uint32_t hc[kNBin];
+  // bin masses (exact fixed point, see fix_of): high words, and low words with the bin's entry
+  // count in bits kCountShift and up (a row's low parts sum below 2^51)
+  __shared__ unsigned long long hhi[kNBin];
+  __shared__ unsigned long long hlo[kNBin];
   __shared__ uint64_t ckey[kCandCap];
   __shared__ double cw[kCandCap];
   __shared__ double rw[kCandCap];
@@ -174,8 +213,8 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
 
   for (int w = tid; w < words_row; w += kSelT) selb[w] = 0;
   for (int i = tid; i < kNBin; i += kSelT) {
-    hm[i] = 0.0;
-    hc[i] = 0;
+    hhi[i] = 0;
+    hlo[i] = 0;
   }
   if (tid == 0) ncand = 0;
 
@@ -242,20 +281,30 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
         bins_of(sv[k], smax, binscale, &c1, &c2);
         if (lv == 2 && c1 != b1) continue;
         const int bin = lv == 1 ? c1 : c2;
-        unsafeAtomicAdd(&hm[bin], wt[k]);
-        atomicAdd(&hc[bin], 1u);
+        if (a.topp) {
+          const FixW f = fix_of(wt[k]);
+          atomicAdd(&hhi[bin], (unsigned long long)f.hi);
+          atomicAdd(&hlo[bin], (unsigned long long)(f.lo + kCountOne));
+        } else {
+          atomicAdd(&hlo[bin], (unsigned long long)kCountOne);  // unit weights: the mass is the count
+        }
       }
     }
     __syncthreads();
     if (wv == 0) {
+      double hm[4];
+      for (int j = 0; j < 4; ++j) {
+        const int bn = 4 * lane + j;
+        hm[j] = a.topp ? fix_value(hhi[bn], hlo[bn] & (kCountOne - 1)) : double(hlo[bn] >> kCountShift);
+      }
       double wl = 0.0;
-      for (int j = 0; j < 4; ++j) wl += hm[4 * lane + j];
+      for (int j = 0; j < 4; ++j) wl += hm[j];
       const double incl = wave_scan_dpp(wl, lane);
       double c = before + (incl - wl);
       int hit = -1;
       double before_hit = 0.0;
       for (int j = 0; j < 4 && hit < 0; ++j) {
-        const double cn = c + hm[4 * lane + j];
+        const double cn = c + hm[j];
         if (cn >= target) {
           hit = 4 * lane + j;
           before_hit = c;
@@ -274,7 +323,8 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
         } else {
           res_i = hb;
           res_d = bb;
-          res_state = hc[hb] <= uint32_t(lv == 1 ? kRankDirect : kCandCap) ? lv : (lv == 2 ? 3 : 0);
+          const uint32_t n_hb = uint32_t(hlo[hb] >> kCountShift);
+          res_state = n_hb <= uint32_t(lv == 1 ? kRankDirect : kCandCap) ? lv : (lv == 2 ? 3 : 0);
         }
       }
     }
@@ -286,8 +336,8 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
     }
     if (state == 0) {
       for (int i = tid; i < kNBin; i += kSelT) {
-        hm[i] = 0.0;
-        hc[i] = 0;
+        hhi[i] = 0;
+        hlo[i] = 0;
       }
       __syncthreads();
     }
@@ -501,18 +551,20 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
 // over the bins of (smax - s) on the row's score range, then the entries of the coarse bin where
 // the running weight crosses the target. Weight = softmax mass exp(scale*s - scale*smax) for
 // top-p, 1 for top-k. Bins are monotone in the score, so every entry of an earlier bin precedes
-// every entry of a later one in the order. Passes:
+// every entry of a later one in the order. Histogram masses are exact fixed-point sums (fix_of),
+// so they do not depend on the order of the atomic adds. Passes:
 //   hist     per slab of kLongBlock entries: coarse bin of every entry (kept, 2 bytes), partial
 //            coarse histogram (no atomics across workgroups);
-//   find1    per row: bin totals (slab partials in slab order), Z and the target, the crossing
-//            coarse bin and the weight ahead of it;
-//   mark     per slab: bitmap words of the entries of earlier coarse bins, and the indices of the
-//            crossing bin's entries in the slab's own region of the resolution buffer;
-//   resolve  per row: the crossing bin's entries split by a sub-bin histogram of their interval;
-//            earlier sub-bins are selected, the crossing sub-bin's entries are ranked and walked to
-//            the first crossing.
-// A crossing coarse bin of more than kResolveCap entries (heavily tied scores) is split inside the
-// resolve workgroup by a fine histogram over one more pass of the row (slow, and only then).
+//   find1    per row: bin totals (slab partials summed as integers), Z and the target, the
+//            crossing coarse bin and the weight ahead of it;
+//   mark     per slab: bitmap words of the entries of earlier coarse bins, the number of the
+//            crossing bin's entries in the slab and (up to kResolveCap of them) their indices in
+//            the slab's own region of the resolution buffer;
+//   resolve  per row: when the crossing bin holds at most kResolveCap entries, they are split by a
+//            sub-bin histogram of their interval; earlier sub-bins are selected, the crossing
+//            sub-bin's entries are ranked and walked to the first crossing. A fuller crossing bin
+//            (near-equal or tied scores) is narrowed by radix levels over the order keys, each
+//            one more pass of the row, until its crossing part fits the buffer or is one key.
 // ---------------------------------------------------------------------------------------------
 struct LongArgs {
   const double* s0;
@@ -529,12 +581,13 @@ struct LongArgs {
   const double* pmin;
   int nblk;
   int nb1;             // slabs per row
-  double* h1m;         // [row][slab][kBins1] partial coarse histograms
-  uint32_t* h1c;
+  unsigned long long* h1h;  // [row][slab][kBins1] partial coarse histograms: fixed-point masses
+  unsigned long long* h1l;  //   (top-p) ...
+  uint32_t* h1c;            //   ... or entry counts (top-k)
   uint16_t* cbin;      // [row][cstride] coarse bin of every entry
   int64_t cstride;     // len rounded up to a multiple of 8 (16-byte aligned rows)
   int32_t* cidx;       // [row][slab][kResolveCap] indices of the crossing bin's entries
-  int32_t* ccnt;       // [row][slab] their counts
+  int32_t* ccnt;       // [row][slab] their counts (not capped)
   uint32_t* bits;
   int64_t words;
   uint32_t* status;
@@ -561,12 +614,17 @@ __device__ __forceinline__ int coarse_bin(double d) {
   const int c = int(d);
   return c < kBins1 - 1 ? c : kBins1 - 1;
 }
-__device__ __forceinline__ int fine_bin(double d, int c1) {
-  const int c2 = int((d - double(c1)) * double(kBins2));
-  return c2 < 0 ? 0 : (c2 < kBins2 - 1 ? c2 : kBins2 - 1);
+// Exponent e with every value of a row whose maximum is smax below 2^e (0 when smax <= 0): the
+// masses of an `ident` row are held as value 2^-e, weights in [0, 1) as the fixed-point sums need.
+// A power-of-two scaling is exact and keeps every comparison of sums with the target.
+__device__ __forceinline__ int ident_exp(double smax) {
+  if (!(smax > 0.0)) return 0;
+  int e;
+  frexp(smax, &e);  // smax = f 2^e, f in [0.5, 1)
+  return e;
 }
-__device__ __forceinline__ double long_weight(const LongArgs& a, double smax, double s) {
-  return a.topp ? (a.ident ? s : exp(a.scale * s - a.scale * smax)) : 1.0;
+__device__ __forceinline__ double long_weight(const LongArgs& a, double smax, int wexp, double s) {
+  return a.topp ? (a.ident ? ldexp(s, -wexp) : exp(a.scale * s - a.scale * smax)) : 1.0;
 }
 __device__ __forceinline__ int long_k(const LongArgs& a, int b) { return a.kbudget ? a.kbudget[b] : a.k; }
 
@@ -593,11 +651,12 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
   const int b = blockIdx.z, h = blockIdx.y, slab = blockIdx.x, tid = threadIdx.x;
   if ((a.local_mask >> (h / a.G)) & 1) return;
   const int64_t row = int64_t(b) * a.Hq + h;
-  __shared__ double hm[kBins1];
+  __shared__ unsigned long long hh[kBins1], hl[kBins1];
   __shared__ uint32_t hc[kBins1];
   __shared__ double rmax[NT / 64], rmin[NT / 64];
   for (int i = tid; i < kBins1; i += NT) {
-    hm[i] = 0.0;
+    hh[i] = 0;
+    hl[i] = 0;
     hc[i] = 0;
   }
   // the row's score range from the score pass's partials (every workgroup gets the same bits)
@@ -620,6 +679,7 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
   }
   const double range = smax - smin;
   const double binscale = range > 0.0 ? double(kBins1) / range : 0.0;
+  const int wexp = a.ident ? ident_exp(smax) : 0;
   const bool all = a.topp ? (a.p >= 1.0) : (int64_t(long_k(a, b)) >= a.len);
   if (slab == 0 && tid == 0) {
     RowInfo ri = {};
@@ -627,6 +687,7 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
     ri.smin = smin;
     ri.binscale = binscale;
     ri.all = all;
+    ri.wexp = wexp;
     a.info[row] = ri;
   }
   if (all) return;
@@ -656,21 +717,27 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
         const double v = sv[it & 1][k];
         const int c = coarse_bin(coarse_pos_of(a, v, smax, binscale));
         br[t] = uint16_t(c);
-        unsafeAtomicAdd(&hm[c], long_weight(a, smax, v));
-        atomicAdd(&hc[c], 1u);
+        if (a.topp)
+          fix_add(&hh[c], &hl[c], long_weight(a, smax, wexp, v));
+        else
+          atomicAdd(&hc[c], 1u);
       }
     }
   }
   __syncthreads();
   const int64_t o = (row * a.nb1 + slab) * kBins1;
   for (int i = tid; i < kBins1; i += NT) {
-    a.h1m[o + i] = hm[i];
-    a.h1c[o + i] = hc[i];
+    if (a.topp) {
+      a.h1h[o + i] = hh[i];
+      a.h1l[o + i] = hl[i];
+    } else {
+      a.h1c[o + i] = hc[i];
+    }
   }
 }
 
-// Per row: coarse bin totals (slab partials summed in slab order), Z and the target, the crossing
-// coarse bin, the weight ahead of it, and whether its entries fit the resolution buffer.
+// Per row: coarse bin totals (slab partials summed as integers), Z and the target, the crossing
+// coarse bin and the weight ahead of it.
 constexpr int kFindThreads = kBins1;
 __global__ __launch_bounds__(kFindThreads) void k_long_find1(LongArgs a) {
   const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
@@ -679,16 +746,23 @@ __global__ __launch_bounds__(kFindThreads) void k_long_find1(LongArgs a) {
   __shared__ double wtot[kFindThreads / 64];
   __shared__ int hit_bin;
   __shared__ double hit_before;
-  __shared__ uint32_t hit_count;
   RowInfo ri = a.info[row];
   if (ri.all) return;
-  double m = 0.0;
-  uint32_t cn = 0;
+  double m;
   const int64_t o = row * a.nb1 * kBins1 + tid;
+  if (a.topp) {
+    unsigned long long sh = 0, sl = 0;
 #pragma unroll 16
-  for (int sl = 0; sl < a.nb1; ++sl) {
-    m += a.h1m[o + int64_t(sl) * kBins1];
-    cn += a.h1c[o + int64_t(sl) * kBins1];
+    for (int sl_ = 0; sl_ < a.nb1; ++sl_) {
+      sh += a.h1h[o + int64_t(sl_) * kBins1];
+      sl += a.h1l[o + int64_t(sl_) * kBins1];
+    }
+    m = fix_value(sh, sl);
+  } else {
+    uint32_t cn = 0;
+#pragma unroll 16
+    for (int sl_ = 0; sl_ < a.nb1; ++sl_) cn += a.h1c[o + int64_t(sl_) * kBins1];
+    m = double(cn);
   }
   double Z;
   const double incl = block_scan<kFindThreads>(m, wtot, &Z);
@@ -699,10 +773,7 @@ __global__ __launch_bounds__(kFindThreads) void k_long_find1(LongArgs a) {
   if (excl + m >= target) atomicMin(&hit_bin, tid);
   __syncthreads();
   const int bin1 = hit_bin;
-  if (bin1 == tid) {
-    hit_before = excl;
-    hit_count = cn;
-  }
+  if (bin1 == tid) hit_before = excl;
   __syncthreads();
   if (tid == 0) {
     if (bin1 == 0x7FFFFFFF) {
@@ -711,17 +782,16 @@ __global__ __launch_bounds__(kFindThreads) void k_long_find1(LongArgs a) {
       ri.bin1 = bin1;
       ri.before1 = hit_before;
       ri.target = target;
-      ri.gather = hit_count <= uint32_t(kResolveCap);
     }
     a.info[row] = ri;
   }
 }
 
 // Per slab: the row's bitmap (entries of coarse bins ahead of the crossing bin, or every entry
-// when the whole row is kept; zero for local heads) and, in gather mode, the indices of the
-// crossing bin's entries in the slab's region of the resolution buffer. Each lane takes 8
-// consecutive entries (one 16-byte load of their bins, all of a slab's loads issued at once) and
-// writes their 8 bits as one byte of the bitmap.
+// when the whole row is kept; zero for local heads), the number of the crossing bin's entries in
+// the slab and, up to kResolveCap of them, their indices in the slab's region of the resolution
+// buffer. Each lane takes 8 consecutive entries (one 16-byte load of their bins, all of a slab's
+// loads issued at once) and writes their 8 bits as one byte of the bitmap.
 __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
   constexpr int NT = kLongThreads;
   const int b = blockIdx.z, h = blockIdx.y, slab = blockIdx.x, tid = threadIdx.x;
@@ -738,7 +808,7 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
   if (tid == 0) scnt = 0;
   __syncthreads();
   const RowInfo ri = a.info[row];
-  const bool gather = !ri.all && ri.gather;
+  const bool gather = !ri.all;
   const uint16_t* br = a.cbin + row * a.cstride;
   uint8_t* bb = reinterpret_cast<uint8_t*>(bw);
   int32_t* out = a.cidx + (row * a.nb1 + slab) * kResolveCap;
@@ -782,18 +852,210 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
     }
   }
   __syncthreads();
-  if (tid == 0) a.ccnt[row * a.nb1 + slab] = scnt < kResolveCap ? scnt : kResolveCap;
+  if (tid == 0) a.ccnt[row * a.nb1 + slab] = scnt;
 }
 
-// Exact resolution of the crossing bin's entries. They span one interval of the bin axis; a
-// kSub-bin histogram of that interval (monotone in the score) finds the sub-bin where the running
-// weight, started at the weight ahead of the interval, crosses the target. Entries of earlier
-// sub-bins are selected; the crossing sub-bin's entries are ranked by counting in (score desc,
-// index asc) order and walked to the first crossing. A crossing sub-bin of more than kSubCap
-// entries is resolved by sorting every gathered entry instead.
+// Exact resolution of the crossing coarse bin. When its entries fit the resolution buffer they
+// span one interval of the bin axis; a kSub-bin histogram of that interval (monotone in the score)
+// finds the sub-bin where the running weight, started at the weight ahead of the interval, crosses
+// the target. Entries of earlier sub-bins are selected; the crossing sub-bin's entries are ranked
+// by counting in (score desc, index asc) order and walked to the first crossing. A crossing
+// sub-bin of more than kSubCap entries is resolved by sorting every gathered entry instead.
+// A crossing coarse bin with more entries than the buffer goes to resolve_radix.
 constexpr int kSub = 1024;
 constexpr int kSubCap = 256;
 constexpr int kResolveThreads = 512;
+// radix levels of an overfull crossing bin: kRadixBits bits of the order key per level (the
+// level histograms use the sub-bin arrays)
+constexpr int kRadixBits = 10;
+constexpr int kRadixBins = 1 << kRadixBits;
+static_assert(kRadixBins <= kSub, "radix levels reuse the sub-bin histogram");
+
+struct ResolveLds {
+  uint64_t* keys;  // [kResolveCap] gather buffer (order keys) ...
+  int32_t* idx;    // ... and entry indices
+  unsigned long long* hh;  // [kSub] histogram: fixed-point masses (top-p) ...
+  unsigned long long* hl;
+  uint32_t* hc;            // ... and entry counts
+  double* wtot;    // [kResolveThreads / 64]
+  double* buf;     // [kSelThreads] (block_first_crossing)
+  int* ibuf;
+  int* nx;
+  int* hit;
+  double* hit_before;
+  uint64_t* kred;  // [2 * kResolveThreads / 64] key min / max per wave
+};
+
+__device__ __forceinline__ void set_bit(uint32_t* bw, int64_t t) { atomicOr(&bw[t >> 5], 1u << (t & 31)); }
+
+// Narrows a crossing coarse bin of `cnt` (> kResolveCap) entries. Its entries occupy one interval
+// [klo, khi] of order keys (dkey: a larger key comes earlier in the order). A level histograms the
+// interval's entries by (khi - key) >> shift over kRadixBins bins (exact fixed-point masses and
+// counts, one pass of the row), finds the bin where the running weight -- started at the weight
+// of everything ahead of the interval -- reaches the target, and narrows the interval to that bin.
+// Every level resolves kRadixBits bits of the key, so a few levels reach an interval of one key.
+// The loop ends when the interval holds at most kResolveCap entries (gathered, sorted in (score
+// desc, index asc) order and walked to the first crossing) or a single key (exact ties, equal
+// weights: the lowest indices up to the crossing). Entries of the coarse bin ahead of the final
+// interval are selected in the last pass. Exact for every input.
+template <int NT>
+__device__ void resolve_radix(const LongArgs& a, const RowInfo& ri, int64_t row, int64_t cnt, const ResolveLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const double* sr = a.s0 + row * a.len;
+  const uint16_t* br = a.cbin + row * a.cstride;
+  uint32_t* bw = a.bits + row * a.words;
+  const int wexp = ri.wexp;
+  auto weight = [&](uint64_t k) { return long_weight(a, ri.smax, wexp, dkey_inv(k)); };
+  // key interval of the bin's entries
+  uint64_t kmn = ~0ull, kmx = 0ull;
+  for (int64_t t = tid; t < a.len; t += NT)
+    if (br[t] == ri.bin1) {
+      const uint64_t k = dkey(sr[t]);
+      kmn = k < kmn ? k : kmn;
+      kmx = k > kmx ? k : kmx;
+    }
+  for (int o = 32; o; o >>= 1) {
+    const uint64_t x = __shfl_xor(kmn, o), y = __shfl_xor(kmx, o);
+    kmn = x < kmn ? x : kmn;
+    kmx = y > kmx ? y : kmx;
+  }
+  if (lane == 0) {
+    L.kred[wv] = kmn;
+    L.kred[NT / 64 + wv] = kmx;
+  }
+  __syncthreads();
+  uint64_t klo = L.kred[0], khi = L.kred[NT / 64];
+  for (int w = 1; w < NT / 64; ++w) {
+    klo = L.kred[w] < klo ? L.kred[w] : klo;
+    khi = L.kred[NT / 64 + w] > khi ? L.kred[NT / 64 + w] : khi;
+  }
+  double before = ri.before1;
+  for (;;) {
+    const uint64_t span = khi - klo;
+    if (span == 0 || cnt <= kResolveCap) break;
+    const int nbits = 64 - __clzll((long long)span);
+    const int shift = nbits > kRadixBits ? nbits - kRadixBits : 0;  // (span >> shift) < kRadixBins
+    __syncthreads();
+    for (int i = tid; i < kRadixBins; i += NT) {
+      L.hh[i] = 0;
+      L.hl[i] = 0;
+      L.hc[i] = 0;
+    }
+    if (tid == 0) *L.hit = 0x7FFFFFFF;
+    __syncthreads();
+    for (int64_t t = tid; t < a.len; t += NT)
+      if (br[t] == ri.bin1) {
+        const uint64_t k = dkey(sr[t]);
+        if (k >= klo && k <= khi) {
+          const int j = int((khi - k) >> shift);
+          atomicAdd(&L.hc[j], 1u);
+          if (a.topp) fix_add(&L.hh[j], &L.hl[j], weight(k));
+        }
+      }
+    __syncthreads();
+    constexpr int PER = kRadixBins / NT;
+    double m[PER];
+    double local = 0.0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = PER * tid + u;
+      m[u] = a.topp ? fix_value(L.hh[j], L.hl[j]) : double(L.hc[j]);
+      local += m[u];
+    }
+    double tot;
+    const double incl = block_scan<NT>(local, L.wtot, &tot);
+    double c = before + (incl - local);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const double cn = c + m[u];
+      if (cn >= ri.target) {
+        atomicMin(L.hit, PER * tid + u);
+        break;
+      }
+      c = cn;
+    }
+    __syncthreads();
+    const int jc = *L.hit;
+    if (jc == 0x7FFFFFFF) {
+      // rounding left the target beyond the interval's weight: every entry of the interval is kept
+      for (int64_t t = tid; t < a.len; t += NT)
+        if (br[t] == ri.bin1 && dkey(sr[t]) >= klo) set_bit(bw, t);
+      return;
+    }
+    if (jc / PER == tid) {
+      double cb = before + (incl - local);
+      for (int u = 0; u < jc - PER * tid; ++u) cb += m[u];
+      *L.hit_before = cb;
+    }
+    __syncthreads();
+    before = *L.hit_before;
+    cnt = L.hc[jc];
+    const uint64_t nhi = khi - (uint64_t(jc) << shift);
+    const uint64_t wdt = (uint64_t(1) << shift) - 1;
+    klo = nhi - klo >= wdt ? nhi - wdt : klo;
+    khi = nhi;
+  }
+  __syncthreads();
+  if (cnt <= kResolveCap) {
+    // gather the interval's entries, select the ones ahead of it, sort and walk
+    if (tid == 0) *L.nx = 0;
+    __syncthreads();
+    for (int64_t t = tid; t < a.len; t += NT)
+      if (br[t] == ri.bin1) {
+        const uint64_t k = dkey(sr[t]);
+        if (k > khi) {
+          set_bit(bw, t);
+        } else if (k >= klo) {
+          const int q = atomicAdd(L.nx, 1);
+          if (q < kResolveCap) {
+            L.keys[q] = k;
+            L.idx[q] = int32_t(t);
+          }
+        }
+      }
+    __syncthreads();
+    // the gathered entries are exactly the level's crossing bin (cnt of them)
+    if (tid == 0 && *L.nx != int(cnt)) atomicOr(&a.status[0], 2u);
+    const int n = *L.nx < kResolveCap ? *L.nx : kResolveCap;
+    if (n == 0) return;
+    int Lp = 2;
+    while (Lp < n) Lp <<= 1;
+    for (int i = n + tid; i < Lp; i += NT) {
+      L.keys[i] = 0ull;
+      L.idx[i] = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    bitonic_desc<int32_t, NT>(L.keys, L.idx, Lp);
+    auto wsorted = [&](int i) { return weight(L.keys[i]); };
+    const int pos = block_first_crossing(n, before, ri.target, wsorted, L.buf, L.ibuf);
+    const int n_sel = pos < 0 ? n : pos + 1;
+    for (int i = tid; i < n_sel; i += NT) set_bit(bw, L.idx[i]);
+    return;
+  }
+  // one key: equal weights, the lowest indices up to the crossing. Entries are taken in contiguous
+  // per-thread index ranges, so a thread-order scan of their counts ranks them by index.
+  const double wt = weight(khi);
+  auto same = [&](int) { return wt; };
+  const int pos = block_first_crossing(int(cnt), before, ri.target, same, L.buf, L.ibuf);
+  const int take = pos < 0 ? int(cnt) : pos + 1;
+  const int64_t per = (a.len + NT - 1) / NT;
+  const int64_t r0 = int64_t(tid) * per, r1 = r0 + per < a.len ? r0 + per : a.len;
+  int mine = 0;
+  for (int64_t t = r0; t < r1; ++t)
+    if (br[t] == ri.bin1 && dkey(sr[t]) == khi) ++mine;
+  double tot;
+  int rank = int(block_scan<NT>(double(mine), L.wtot, &tot)) - mine;
+  for (int64_t t = r0; t < r1; ++t)
+    if (br[t] == ri.bin1) {
+      const uint64_t k = dkey(sr[t]);
+      if (k > khi) {
+        set_bit(bw, t);
+      } else if (k == khi) {
+        if (rank < take) set_bit(bw, t);
+        ++rank;
+      }
+    }
+}
 
 __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   constexpr int NT = kResolveThreads;
@@ -805,7 +1067,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   __shared__ uint64_t keys[kResolveCap];
   __shared__ int32_t idx[kResolveCap];
   __shared__ uint16_t sub[kResolveCap];
-  __shared__ double hm[kSub];
+  __shared__ unsigned long long hh[kSub], hl[kSub];
   __shared__ uint32_t hc[kSub];
   __shared__ uint64_t xkey[kSubCap];
   __shared__ int32_t xidx[kSubCap];
@@ -813,27 +1075,33 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   __shared__ int32_t ridx[kSubCap];
   __shared__ double wtot[NT / 64];
   __shared__ double buf[kSelThreads];
+  __shared__ uint64_t kred[2 * NT / 64];
   __shared__ int soff[NT + 1];
   __shared__ int hit_bin, nx, ibuf;
   __shared__ double hit_before;
   const double* sr = a.s0 + row * a.len;
   uint32_t* bw = a.bits + row * a.words;
-  int n;
-  double before, dlo, sscale;
-  if (ri.gather) {
-    // ---- the crossing bin's entries, slab after slab (slab s owns soff[s] .. soff[s+1])
-    const int per = (a.nb1 + NT - 1) / NT;  // slabs per thread
-    double local = 0.0;
-    for (int s = tid * per; s < min(a.nb1, tid * per + per); ++s) local += double(a.ccnt[row * a.nb1 + s]);
-    double tot;
-    const double incl = block_scan<NT>(local, wtot, &tot);
-    // soff holds the first position of every thread's first slab; slabs inside a thread's range
-    // are walked in order below
-    soff[tid] = int(incl - local);
-    if (tid == NT - 1) soff[NT] = int(tot);
-    __syncthreads();
-    n = int(tot) < kResolveCap ? int(tot) : kResolveCap;
-    if (n == 0) return;
+  const int wexp = ri.wexp;
+  // ---- the crossing bin's entry count over the slabs (slab s owns soff[s] .. soff[s+1] of the
+  // gathered entries when they fit the buffer)
+  const int per = (a.nb1 + NT - 1) / NT;  // slabs per thread
+  double local = 0.0;
+  for (int s = tid * per; s < min(a.nb1, tid * per + per); ++s) local += double(a.ccnt[row * a.nb1 + s]);
+  double tot;
+  const double incl = block_scan<NT>(local, wtot, &tot);
+  if (tot > double(kResolveCap)) {
+    const ResolveLds L{keys, idx, hh, hl, hc, wtot, buf, &ibuf, &nx, &hit_bin, &hit_before, kred};
+    resolve_radix<NT>(a, ri, row, int64_t(tot), L);
+    return;
+  }
+  // soff holds the first position of every thread's first slab; slabs inside a thread's range
+  // are walked in order below
+  soff[tid] = int(incl - local);
+  if (tid == NT - 1) soff[NT] = int(tot);
+  __syncthreads();
+  const int n = int(tot);
+  if (n == 0) return;
+  {
     constexpr int PER = kResolveCap / NT;
     int32_t tv[PER];
 #pragma unroll
@@ -866,143 +1134,14 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
         idx[i] = tv[k];
       }
     }
-    before = ri.before1;
-    dlo = double(ri.bin1);
-    sscale = double(kSub);
-  } else {
-    // ---- crossing coarse bin too full: fine histogram of its entries over one pass of the row
-    double* fm = reinterpret_cast<double*>(keys);    // kBins2 doubles
-    uint32_t* fc = reinterpret_cast<uint32_t*>(idx);  // kBins2 counts
-    for (int i = tid; i < kBins2; i += NT) {
-      fm[i] = 0.0;
-      fc[i] = 0;
-    }
-    if (tid == 0) {
-      nx = 0;
-      hit_bin = 0x7FFFFFFF;
-    }
-    __syncthreads();
-    const uint16_t* br = a.cbin + row * a.cstride;
-    for (int64_t t = tid; t < a.len; t += NT) {
-      if (br[t] == ri.bin1) {
-        const double s = sr[t];
-        const int f = fine_bin(coarse_pos_of(a, s, ri.smax, ri.binscale), ri.bin1);
-        unsafeAtomicAdd(&fm[f], long_weight(a, ri.smax, s));
-        atomicAdd(&fc[f], 1u);
-      }
-    }
-    __syncthreads();
-    constexpr int FPER = kBins2 / NT;
-    double m[FPER];
-    double local = 0.0;
-#pragma unroll
-    for (int j = 0; j < FPER; ++j) {
-      m[j] = fm[FPER * tid + j];
-      local += m[j];
-    }
-    double tot;
-    const double incl = block_scan<NT>(local, wtot, &tot);
-    double c = ri.before1 + (incl - local);
-    const double c0 = c;
-#pragma unroll
-    for (int j = 0; j < FPER; ++j) {
-      const double cn = c + m[j];
-      if (cn >= ri.target) {
-        atomicMin(&hit_bin, FPER * tid + j);
-        break;
-      }
-      c = cn;
-    }
-    __syncthreads();
-    const int bin2 = hit_bin == 0x7FFFFFFF ? kBins2 : hit_bin;  // none: keep the whole coarse bin
-    if (bin2 < kBins2 && bin2 / FPER == tid) {
-      double cb = c0;
-      for (int j = 0; j < bin2 - FPER * tid; ++j) cb += m[j];
-      hit_before = cb;
-    }
-    __syncthreads();
-    const uint32_t cnt2 = bin2 < kBins2 ? fc[bin2] : 0u;
-    if (cnt2 > uint32_t(kResolveCap)) {
-      // The crossing fine bin holds more entries than the buffer. Resolvable here when they all
-      // carry one score (exact ties): their order is then the index order and their weights are
-      // equal. Entries are taken in contiguous per-thread index ranges, so a thread-order scan of
-      // their counts ranks them by index.
-      __shared__ double tmin[NT / 64], tmax[NT / 64];
-      const int64_t per = (a.len + NT - 1) / NT;
-      const int64_t r0 = int64_t(tid) * per, r1 = r0 + per < a.len ? r0 + per : a.len;
-      double lo = kPosInfD, hi = kNegInfD;
-      int mine = 0;
-      for (int64_t t = r0; t < r1; ++t) {
-        if (br[t] == ri.bin1) {
-          const double sc = sr[t];
-          const int f = fine_bin(coarse_pos_of(a, sc, ri.smax, ri.binscale), ri.bin1);
-          if (f < bin2) {
-            atomicOr(&bw[t >> 5], 1u << (t & 31));
-          } else if (f == bin2) {
-            lo = fmin(lo, sc);
-            hi = fmax(hi, sc);
-            ++mine;
-          }
-        }
-      }
-      lo = wave_min_dpp(lo);
-      hi = wave_max_dpp(hi);
-      if ((tid & 63) == 0) {
-        tmin[tid >> 6] = lo;
-        tmax[tid >> 6] = hi;
-      }
-      __syncthreads();
-      for (int w = 0; w < NT / 64; ++w) {
-        lo = fmin(lo, tmin[w]);
-        hi = fmax(hi, tmax[w]);
-      }
-      if (lo != hi) {  // near-equal but distinct scores beyond the buffer: not resolved
-        if (tid == 0) atomicOr(&a.status[0], 1u);
-        return;
-      }
-      const double wt = long_weight(a, ri.smax, lo);
-      auto same = [&](int) { return wt; };
-      const int pos = block_first_crossing(int(cnt2), hit_before, ri.target, same, buf, &ibuf);
-      const int take = pos < 0 ? int(cnt2) : pos + 1;
-      double tot;
-      const int rank0 = int(block_scan<NT>(double(mine), wtot, &tot)) - mine;
-      int rank = rank0;
-      for (int64_t t = r0; t < r1 && rank < take; ++t) {
-        if (br[t] == ri.bin1 && fine_bin(coarse_pos_of(a, sr[t], ri.smax, ri.binscale), ri.bin1) == bin2) {
-          atomicOr(&bw[t >> 5], 1u << (t & 31));
-          ++rank;
-        }
-      }
-      return;
-    }
-    // the fine histogram is dead from here: keys / idx take the candidates
-    for (int64_t t = tid; t < a.len; t += NT) {
-      if (br[t] == ri.bin1) {
-        const double s = sr[t];
-        const int f = fine_bin(coarse_pos_of(a, s, ri.smax, ri.binscale), ri.bin1);
-        if (f < bin2) {
-          atomicOr(&bw[t >> 5], 1u << (t & 31));
-        } else if (f == bin2) {
-          const int q = atomicAdd(&nx, 1);
-          if (q < kResolveCap) {
-            keys[q] = dkey(s);
-            idx[q] = int32_t(t);
-          } else {
-            atomicOr(&a.status[0], 1u);
-          }
-        }
-      }
-    }
-    __syncthreads();
-    n = nx < kResolveCap ? nx : kResolveCap;
-    if (n == 0) return;
-    before = hit_before;
-    dlo = double(ri.bin1) + double(bin2) / double(kBins2);
-    sscale = double(kSub) * double(kBins2);
   }
+  const double before = ri.before1;
+  const double dlo = double(ri.bin1);
+  const double sscale = double(kSub);
   // ---- sub-bin histogram of the gathered entries
   for (int i = tid; i < kSub; i += NT) {
-    hm[i] = 0.0;
+    hh[i] = 0;
+    hl[i] = 0;
     hc[i] = 0;
   }
   if (tid == 0) {
@@ -1016,21 +1155,22 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
     int sb = x >= 0.0 ? (x < double(kSub) ? int(x) : kSub - 1) : 0;
     sb = sb < kSub - 1 ? sb : kSub - 1;
     sub[i] = uint16_t(sb);
-    unsafeAtomicAdd(&hm[sb], long_weight(a, ri.smax, s));
     atomicAdd(&hc[sb], 1u);
+    if (a.topp) fix_add(&hh[sb], &hl[sb], long_weight(a, ri.smax, wexp, s));
   }
   __syncthreads();
   constexpr int SPER = kSub / NT;
   double m[SPER];
-  double local = 0.0;
+  double lsum = 0.0;
 #pragma unroll
   for (int j = 0; j < SPER; ++j) {
-    m[j] = hm[SPER * tid + j];
-    local += m[j];
+    const int bj = SPER * tid + j;
+    m[j] = a.topp ? fix_value(hh[bj], hl[bj]) : double(hc[bj]);
+    lsum += m[j];
   }
-  double tot;
-  const double incl = block_scan<NT>(local, wtot, &tot);
-  double c = before + (incl - local);
+  double stot;
+  const double sincl = block_scan<NT>(lsum, wtot, &stot);
+  double c = before + (sincl - lsum);
   const double c0 = c;
 #pragma unroll
   for (int j = 0; j < SPER; ++j) {
@@ -1051,14 +1191,14 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   __syncthreads();
   if (hb == 0x7FFFFFFF) {
     // rounding: the target lies beyond the gathered entries; keep all of them
-    for (int i = tid; i < n; i += NT) atomicOr(&bw[idx[i] >> 5], 1u << (idx[i] & 31));
+    for (int i = tid; i < n; i += NT) set_bit(bw, idx[i]);
     return;
   }
   if (hc[hb] <= uint32_t(kSubCap)) {
     for (int i = tid; i < n; i += NT) {
       const int sb = sub[i];
       if (sb < hb) {
-        atomicOr(&bw[idx[i] >> 5], 1u << (idx[i] & 31));
+        set_bit(bw, idx[i]);
       } else if (sb == hb) {
         const int q = atomicAdd(&nx, 1);
         xkey[q] = keys[i];
@@ -1075,7 +1215,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
         const uint64_t ku = xkey[u];
         r += (ku > kq || (ku == kq && xidx[u] < iq)) ? 1 : 0;
       }
-      xw[r] = long_weight(a, ri.smax, dkey_inv(kq));
+      xw[r] = long_weight(a, ri.smax, wexp, dkey_inv(kq));
       ridx[r] = iq;
     }
     __syncthreads();
@@ -1092,7 +1232,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
       ibuf = ns;
     }
     __syncthreads();
-    for (int r = tid; r < ibuf; r += NT) atomicOr(&bw[ridx[r] >> 5], 1u << (ridx[r] & 31));
+    for (int r = tid; r < ibuf; r += NT) set_bit(bw, ridx[r]);
     return;
   }
   // near-equal scores fill the crossing sub-bin: sort every gathered entry and walk them all
@@ -1104,10 +1244,10 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   }
   __syncthreads();
   bitonic_desc<int32_t, NT>(keys, idx, Lp);
-  auto weight = [&](int i) { return long_weight(a, ri.smax, dkey_inv(keys[i])); };
+  auto weight = [&](int i) { return long_weight(a, ri.smax, wexp, dkey_inv(keys[i])); };
   const int pos = block_first_crossing(n, before, ri.target, weight, buf, &ibuf);
   const int n_sel = pos < 0 ? n : pos + 1;
-  for (int i = tid; i < n_sel; i += NT) atomicOr(&bw[idx[i] >> 5], 1u << (idx[i] & 31));
+  for (int i = tid; i < n_sel; i += NT) set_bit(bw, idx[i]);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1411,7 +1551,8 @@ LongArgs long_args(const Plan& p, char* ws) {
   a.pmin = at<double>(ws, p.o_pmin);
   a.nblk = p.score_blocks0;
   a.nb1 = p.long_blocks;
-  a.h1m = at<double>(ws, p.o_h1m);
+  a.h1h = at<unsigned long long>(ws, p.o_h1h);
+  a.h1l = at<unsigned long long>(ws, p.o_h1l);
   a.h1c = at<uint32_t>(ws, p.o_h1c);
   a.cbin = at<uint16_t>(ws, p.o_cbin);
   a.cstride = (p.len0 + 7) & ~int64_t(7);
@@ -1525,7 +1666,7 @@ int launch_select(const Plan& p, int level, char* ws, void* stream) {
 // ---- long-row selection over caller-given rows (the prefill path's budget and per-head top-k)
 namespace {
 struct LongScratch {
-  size_t info, h1m, h1c, cbin, cidx, ccnt, total;
+  size_t info, h1h, h1l, h1c, cbin, cidx, ccnt, total;
 };
 LongScratch long_scratch_layout(int64_t rows, int64_t len) {
   const int64_t nb1 = (len + kLongBlock - 1) / kLongBlock;
@@ -1537,7 +1678,8 @@ LongScratch long_scratch_layout(int64_t rows, int64_t len) {
     return o;
   };
   l.info = take(size_t(rows) * sizeof(RowInfo));
-  l.h1m = take(size_t(rows * nb1 * kBins1) * 8);
+  l.h1h = take(size_t(rows * nb1 * kBins1) * 8);
+  l.h1l = take(size_t(rows * nb1 * kBins1) * 8);
   l.h1c = take(size_t(rows * nb1 * kBins1) * 4);
   l.cbin = take(size_t(rows * ((len + 7) & ~int64_t(7))) * 2);
   l.cidx = take(size_t(rows * nb1 * kResolveCap) * 4);
@@ -1570,7 +1712,8 @@ int launch_long_rows(const LongRows& r, void* stream) {
   a.pmin = r.pmin;
   a.nblk = r.nblk;
   a.nb1 = int((r.len + kLongBlock - 1) / kLongBlock);
-  a.h1m = reinterpret_cast<double*>(r.scratch + l.h1m);
+  a.h1h = reinterpret_cast<unsigned long long*>(r.scratch + l.h1h);
+  a.h1l = reinterpret_cast<unsigned long long*>(r.scratch + l.h1l);
   a.h1c = reinterpret_cast<uint32_t*>(r.scratch + l.h1c);
   a.cbin = reinterpret_cast<uint16_t*>(r.scratch + l.cbin);
   a.cstride = (r.len + 7) & ~int64_t(7);

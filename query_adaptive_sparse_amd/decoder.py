@@ -128,6 +128,12 @@ class SparseDecoder:
         self.attend(t)
         self.combine(out, lse)
 
+    def status(self) -> int:
+        """The device status word after the enqueued work (synchronises the current stream). It is
+        an internal-invariant flag: 0 after every step on any input; nonzero means a library defect."""
+        torch.cuda.current_stream().synchronize()
+        return int(self.selection()["status"][0].item())
+
     # ---- inspection (device views into the workspace)
     def selection(self) -> dict:
         ws = self.alloc_workspace()

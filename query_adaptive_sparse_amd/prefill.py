@@ -67,6 +67,12 @@ class SparsePrefill:
         self.select(t)
         self.attend(t, out)
 
+    def status(self) -> int:
+        """The device status word after the enqueued work (synchronises the current stream): an
+        internal-invariant flag, 0 on any input; nonzero means a library defect."""
+        torch.cuda.current_stream().synchronize()
+        return int(self.selection()["status"][0].item())
+
     def selection(self) -> dict:
         ws = self.alloc_workspace()
         v = N.sparse_prefill_view(self.handle, ws.data_ptr())

@@ -172,3 +172,78 @@ def test_dtype_and_head_dim(name, kw):
     against the oracle on reduced shapes."""
     w = replace(configs.get(name), name=f"{name}_dd", **kw)
     _run(w, gen.make_inputs(w, device="cuda"))
+
+
+def _near_equal_proxy_inputs(w, kind):
+    """c5s-shaped proxy inputs whose retrieval rows put the top-p crossing inside a crowd of
+    near-equal scores. Every query is e_0 and every projection maps it to q_p = (1, 2^-11, 0, ...),
+    so a token's proxy score is exactly kp[0] + 2^-11 kp[1]. A quarter of the tokens score about
+    -60000 (they widen the row's range until one coarse bin spans every other token, and weigh
+    nothing); the rest form the crowd:
+      dense: kp[0] in 1 + {0..15} 2^-10 and kp[1] in 0.5 + {0..1023} 2^-11 by a seeded hash, up to
+             16384 distinct scores within 0.016 of each other, about 49000 tokens;
+      tied:  one score shared by about 49000 tokens, with 300 tokens just above it and 300 just
+             below, so the crossing falls among exact ties far beyond the gather buffer."""
+    inp = gen.make_inputs(w, device="cuda")
+    Hq, Hk, d, N, r = w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.route_dim
+    q = torch.zeros_like(inp["q"])
+    q[..., 0] = 1.0
+    P = torch.zeros(Hk, d, r, dtype=torch.float32, device="cuda")
+    P[:, 0, 0] = 1.0
+    P[:, 0, 1] = 2.0 ** -11
+    t = torch.arange(N, dtype=torch.int64, device="cuda")
+    h = gen.hash32(w.seed, 99, t)
+    low = (h & 3) == 0
+    kp = torch.zeros(1, Hk, N, r, dtype=torch.float64, device="cuda")
+    if kind == "dense":
+        kp[0, :, :, 0] = 1.0 + ((h >> 2) & 15).double() * 2.0 ** -10
+        kp[0, :, :, 1] = 0.5 + ((h >> 6) & 1023).double() * 2.0 ** -11
+    else:
+        sel = (h >> 8) % 1000
+        kp[0, :, :, 0] = 1.0 + 2.0 ** -10
+        kp[0, :, :, 0] = torch.where(sel < 6, 1.0 + 2.0 ** -9, kp[0, :, :, 0])
+        kp[0, :, :, 0] = torch.where((sel >= 6) & (sel < 12), torch.ones_like(kp[0, :, :, 0]), kp[0, :, :, 0])
+    kp[0, :, low, 0] = -60000.0
+    kp[0, :, low, 1] = 0.0
+    inp["q"], inp["P"], inp["Kp"] = q.contiguous(), P.contiguous(), kp.to(torch.float16).contiguous()
+    return inp
+
+
+@pytest.mark.parametrize("kind", ["dense", "tied"])
+def test_long_rows_near_equal(kind):
+    """Top-p over 64K-token proxy rows whose crossing coarse bin holds far more entries than the
+    gather buffer: tens of thousands of distinct near-equal scores (dense), or a crossing among
+    exact ties (tied). The selection is exact: bit-identical to the oracle, no status flag."""
+    w = replace(configs.get("c5s"), name=f"near_equal_{kind}")
+    inp = _near_equal_proxy_inputs(w, kind)
+    s = inp["Kp"][0, 0, :, 0].double() + inp["Kp"][0, 0, :, 1].double() * 2.0 ** -11
+    crowd = s > 0
+    print(f"[edge] {w.name}: {int(crowd.sum())} crowd tokens, {int(torch.unique(s[crowd]).numel())} distinct "
+          f"crowd scores", flush=True)
+    g, o = _run(w, inp)
+    assert int(g["sel"]["status"][0]) == 0
+    for (b, gg), r in o["sel"].items():
+        for hh, S in r["heads"].items():
+            assert 1000 < len(S) < int(crowd.sum()), (hh, len(S))  # the crossing is inside the crowd
+
+
+def test_selection_repeatable():
+    """Twenty steps of the 16K top-p workload and of the near-equal proxy rows, each on its own
+    fresh workspace: every selection bit and every output bit is the same every time (the bin
+    masses are exact integer sums, so no atomic order reaches the result)."""
+    cases = [(configs.get("c3s"), gen.make_inputs(configs.get("c3s"), device="cuda"))]
+    w5 = replace(configs.get("c5s"), name="near_equal_dense")
+    cases.append((w5, _near_equal_proxy_inputs(w5, "dense")))
+    for w, inp in cases:
+        first = parity.run_gpu(w, inp)
+        for rep in range(19):
+            again = parity.run_gpu(w, inp)
+            for k in ("head_bits", "count"):
+                assert torch.equal(first["sel"][k], again["sel"][k]), (w.name, rep, k)
+            cnt = first["sel"]["count"]
+            for bb in range(w.batch):
+                for g in range(w.n_kv_heads):  # list entries past the count are unused workspace
+                    n = int(cnt[bb, g])
+                    assert torch.equal(first["sel"]["list"][bb, g, :n], again["sel"]["list"][bb, g, :n])
+            assert np.array_equal(first["out"], again["out"]) and np.array_equal(first["lse"], again["lse"])
+        print(f"[edge] {w.name}: 20 runs bit-identical", flush=True)
