@@ -192,6 +192,25 @@ sd_status sparse_decode_attend(const sd_handle* h, const sd_tensors* t, void* ws
 sd_status sparse_decode_combine(const sd_handle* h, void* ws, float* out, float* lse_out,
                                 void* stream);
 
+/* One whole step -- score and select at every level, attend, combine -- with the library's own
+ * static device scratch as the workspace. For callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the call
+ * allocates nothing, on the host or the device. Outputs as sparse_decode_combine: out fp32
+ * [B][T][Hq][d], lse_out fp32 [B][T][Hq], contiguous device buffers.
+ *   - The scratch is a 16 MiB device array per GPU (held until the process ends); a handle whose
+ *     workspace (sparse_decode_init's workspace_bytes) is larger is rejected with SD_EUNSUPPORTED
+ *     before anything is enqueued (the 128K, 32K and 512K workloads fit; the 1M-token proxy
+ *     workload does not).
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last call's contents; each
+ *     step clears what it needs zeroed (status words, arrival counters) itself. Calls that overlap
+ *     on one GPU (concurrent streams, or threads) race on it: order them on one stream.
+ *   - The scratch of the device current at the call is used; `stream` must belong to that device.
+ *   - The per-stage inspection view is not available for this scratch.
+ * Errors as the other calls: SD_EINVAL / SD_EUNSUPPORTED from host checks (nothing enqueued),
+ * SD_EHIP for a failed address lookup or launch. */
+sd_status sparse_decode_step_static(const sd_handle* h, const sd_tensors* t, float* out, float* lse_out,
+                                    void* stream);
+
 /* Fill `view` with device pointers into `ws` (no device access). */
 sd_status sparse_decode_selection_view(const sd_handle* h, void* ws, sd_selection_view* view);
 

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libsparse_decode.so")
-SOURCES = ["sd_api.cpp", "sd_score.hip", "sd_select.hip", "sd_attend.hip", "sd_prefill.hip", "sd_gist.hip"]
+SOURCES = ["sd_api.cpp", "sd_score.hip", "sd_select.hip", "sd_attend.hip", "sd_prefill.hip", "sd_gist.hip",
+           "sd_static.hip"]
 ARCH = os.environ.get("SD_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

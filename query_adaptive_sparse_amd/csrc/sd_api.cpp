@@ -297,6 +297,33 @@ sd_status sparse_decode_combine(const sd_handle* h, void* ws, float* out, float*
   return ok();
 }
 
+sd_status sparse_decode_step_static(const sd_handle* h, const sd_tensors* t, float* out, float* lse_out,
+                                    void* stream) {
+  if (!h) return fail(SD_EINVAL, "step_static: NULL handle");
+  const sd::Plan& p = h->plan;
+  if (p.ws_bytes > sd::kStaticScratchBytes)
+    return fail(SD_EUNSUPPORTED, "step_static: the step needs a %zu-byte workspace, above the %zu-byte static scratch",
+                p.ws_bytes, sd::kStaticScratchBytes);
+  sd_status st;
+  for (int level = 0; level < p.levels; ++level)
+    if ((st = check_tensors(p, t, true, level)) != SD_OK) return st;
+  if ((st = check_tensors(p, t, false, 0)) != SD_OK) return st;
+  if (!out || !lse_out || !aligned16(out))
+    return fail(SD_EINVAL, "step_static: out (16-byte aligned) and lse_out must be non-NULL");
+  void* ws = nullptr;
+  int e = sd::static_scratch(&ws);
+  if (e) return fail(SD_EHIP, "step_static: static scratch address: HIP error %d (%s)", e, sd::hip_error_string(e));
+  char* w = static_cast<char*>(ws);
+  for (int level = 0; level < p.levels && !e; ++level) {
+    e = sd::launch_score(p, *t, level, w, stream);
+    if (!e) e = sd::launch_select(p, level, w, stream);
+  }
+  if (!e) e = sd::launch_attend(p, *t, w, stream);
+  if (!e) e = sd::launch_combine(p, w, out, lse_out, stream);
+  if (e) return fail(SD_EHIP, "step_static: HIP error %d (%s)", e, sd::hip_error_string(e));
+  return ok();
+}
+
 sd_status sparse_decode_selection_view(const sd_handle* h, void* ws, sd_selection_view* v) {
   if (!h || !v) return fail(SD_EINVAL, "selection_view: NULL argument");
   const sd::Plan& p = h->plan;

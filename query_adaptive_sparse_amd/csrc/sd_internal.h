@@ -77,6 +77,11 @@ struct RowInfo {
   int32_t pad;
 };
 
+// The static device scratch of sparse_decode_step_static (sd_static.hip): its size, and its device
+// address on the current device (looked up once per device); returns hipSuccess or the error.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+int static_scratch(void** out);
+
 // Kernel launchers (sd_score.hip, sd_select.hip, sd_attend.hip). Each returns hipSuccess or the
 // launch error.
 int launch_score(const Plan& p, const sd_tensors& t, int level, char* ws, void* stream);

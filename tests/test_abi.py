@@ -175,6 +175,32 @@ def test_calls_reject_before_enqueue():
     N.sparse_decode_destroy(h)
 
 
+def test_step_static_rejects_before_enqueue():
+    """The no-allocation step checks everything on the host first: a handle whose workspace is
+    larger than the static scratch, a NULL handle, tensors or outputs are rejected without touching
+    a GPU."""
+    L = N.lib()
+    t = N.sd_tensors()
+    h, nbytes = _init(**_params("c5_rtpurbo_1m"))
+    assert nbytes > 16 << 20
+    assert L.sparse_decode_step_static(h, ctypes.byref(t), 0x2000, 0x3000, None) == N.SD_EUNSUPPORTED
+    assert b"static scratch" in L.sparse_decode_last_error()
+    N.sparse_decode_destroy(h)
+    h, nbytes = _init(**_params("c3s"))
+    assert nbytes <= 16 << 20
+    assert L.sparse_decode_step_static(None, ctypes.byref(t), 0x2000, 0x3000, None) == N.SD_EINVAL
+    assert L.sparse_decode_step_static(h, None, 0x2000, 0x3000, None) == N.SD_EINVAL
+    assert L.sparse_decode_step_static(h, ctypes.byref(t), 0x2000, 0x3000, None) == N.SD_EINVAL
+    assert b"q must be" in L.sparse_decode_last_error()
+    t.q, t.q_sb, t.q_sh = 0x10000, 32 * 128, 128
+    t.kg, t.vg, t.g_st = 0x20000, 0x30000, 128
+    t.k, t.v, t.kv_st = 0x40000, 0x50000, 128
+    assert L.sparse_decode_step_static(h, ctypes.byref(t), None, 0x3000, None) == N.SD_EINVAL
+    assert L.sparse_decode_step_static(h, ctypes.byref(t), 0x2004, 0x3000, None) == N.SD_EINVAL
+    assert b"out" in L.sparse_decode_last_error()
+    N.sparse_decode_destroy(h)
+
+
 def test_workspace_grows_with_batch():
     _, a = _init(**_params("c3s", batch=1, kv_batch=1))
     _, b = _init(**_params("c3s", batch=2, kv_batch=2))
