@@ -125,8 +125,24 @@ typedef struct {
  *   kmg  [Bkv][Hkv][S][d]      kv_dtype   meta-summary key per segment; mg_sb, mg_sh, mg_st
  *   kp   [Bkv][Hkv][N][r]      fp16       proxy key per token; kp_sb, kp_sh, kp_st
  *   proj [Hkv][d][r]           fp32       contiguous projection per KV head
+ *   ctx_len [B]                int32      growing cache: tokens sequence b holds this step
+ *                                         (NULL: every sequence holds n_ctx)
  * Row strides (kv_st, g_st, mg_st) must keep every row 16-byte aligned, and
- * every base pointer must be 16-byte aligned. */
+ * every base pointer must be 16-byte aligned.
+ *
+ * Growing cache (review of "Hierarchical Sparse Attention Done Right", section 3 and its kernel
+ * figure: decode steps of T adjacent tokens; AI Trends summary of SSA, "주요 결과" and "관련
+ * Figure": the cost per step is followed as the context grows). n_ctx is then the capacity: the
+ * handle and workspace are sized for it and the tensors are allocated for it, while ctx_len[b]
+ * (device memory, read by the step, values clamped to [0, n_ctx]) is the number of valid tokens
+ * of sequence b at this step. Between steps the caller appends T tokens' K / V (and proxy keys)
+ * and, when a chunk becomes complete, its summary K / V row, and raises ctx_len. Per sequence:
+ * the complete chunks M_b = ctx_len[b] / C are scored and selected (rows past them are never
+ * used); keep_first / keep_last count from 0 and from M_b; the raw tokens of the incomplete last
+ * chunk [M_b C, ctx_len[b]) have no summary yet and join the group's context unselected (every
+ * head attends them); local heads take [0, sink) and [ctx_len[b] - window, ctx_len[b]). The
+ * lengths are read once, by the step's score call, which copies them into the workspace for the
+ * later calls. Not available with SD_HIER_TOPK (SD_EUNSUPPORTED). */
 typedef struct {
   const void* q;   int64_t q_sb, q_sh, q_st;
   const void* k;   const void* v;   int64_t kv_sb, kv_sh, kv_st;
@@ -134,6 +150,7 @@ typedef struct {
   const void* kmg; int64_t mg_sb, mg_sh, mg_st;
   const void* kp;  int64_t kp_sb, kp_sh, kp_st;
   const float* proj;
+  const int32_t* ctx_len;
 } sd_tensors;
 
 /* Device pointers into a workspace, for inspection after a step. Per-query

@@ -59,6 +59,16 @@ Readings where the pages are silent (each is a fixed choice of this oracle):
 * Variant "per-head masks": the group still loads the union once, but head h
   attends only to the raw (and selected-summary) rows of its own selection plus
   the forced sink / recent chunks; local groups are unmasked.
+* Growing cache ([HiLS] section 3: decode advances by steps of adjacent tokens
+  whose keys join the cache; [SSA] "주요 결과" / "관련 Figure": the per-step cost
+  is followed as the context grows): at a step sequence b's cache holds n_b
+  tokens (``ctx_len[b]``) of a larger capacity. Its complete chunks,
+  ``n_b // chunk_size`` of them, are the ones with a summary key, so they are
+  what is scored and selected; forced chunks count from 0 and from the last
+  complete chunk; the raw tokens of the incomplete last chunk have no summary
+  yet and are attended by every head of the group without being selected
+  (within a chunk tokens see their own chunk's earlier tokens directly); local
+  heads take the sink and the window of the n_b tokens.
 
 Arithmetic: inputs arrive as fp64 (their bf16 / fp16 / fp32 values are exact in
 fp64). Scores are summed in index order, one rounding per multiply and per
@@ -244,19 +254,30 @@ def group_queries(w, g: int) -> list:
     return [t * w.n_q_heads + g * G + j for t in range(T) for j in range(G)]
 
 
-def sequence_budget(w, src, b: int):
-    """Coverage budget of sequence b from all its scored query rows' chunk scores."""
+def cache_tokens(w, b: int, ctx_len=None) -> int:
+    """Tokens sequence b's cache holds at this step: ctx_len[b] for a growing cache, else the
+    whole cache."""
+    return w.n_ctx if ctx_len is None else int(ctx_len[b])
+
+
+def sequence_budget(w, src, b: int, n_ent=None):
+    """Coverage budget of sequence b from all its scored query rows' chunk scores (over its first
+    ``n_ent`` chunks, default all)."""
     bk = b if w.kv_batch > 1 else 0
-    rows = [chunk_scores(src.q[b, qi], src.Kg[bk, g])
+    n_ent = w.n_ctx // w.chunk_size if n_ent is None else n_ent
+    rows = [chunk_scores(src.q[b, qi], src.Kg[bk, g][:n_ent])
             for g in range(w.n_kv_heads) if g not in tuple(w.local_kv_heads) for qi in group_queries(w, g)]
     return coverage_budget(coverage_importance(rows, w.select_scale), w.tau)
 
 
-def select_group(w, src, b: int, g: int) -> dict:
+def select_group(w, src, b: int, g: int, n_tok=None) -> dict:
     """Per-query-row selections (keyed by row ``t * Hq + h``) and the group union
-    for sequence b, KV group g."""
+    for sequence b, KV group g, over a cache of ``n_tok`` tokens (default: all of it)."""
     bk = b if w.kv_batch > 1 else 0
-    n_ent = w.n_ctx // w.chunk_size
+    n_tok = w.n_ctx if n_tok is None else n_tok
+    n_ent = n_tok // w.chunk_size  # complete chunks: the ones with a summary key
+    if n_tok != w.n_ctx and w.mode == HIER:
+        raise ValueError("two-level selection reads whole caches")
     res = {"heads": {}, "scores": {}, "margin": math.inf, "segments": {}, "cand": {}}
     if g in tuple(w.local_kv_heads):
         res["union"] = edge_entries(n_ent, w.sink, w.window)
@@ -264,11 +285,13 @@ def select_group(w, src, b: int, g: int) -> dict:
     per_head = []
     for h in group_queries(w, g):
         q = src.q[b, h]
-        if w.mode == TOPK:
-            s = chunk_scores(q, src.Kg[bk, g])
+        if n_ent == 0:  # nothing complete to score
+            s, sel = np.zeros(0), np.zeros(0, dtype=np.int64)
+        elif w.mode == TOPK:
+            s = chunk_scores(q, src.Kg[bk, g][:n_ent])
             sel = select_top_k(s, w.top_k)
         elif w.mode == TOPP:
-            s = chunk_scores(q, src.Kg[bk, g])
+            s = chunk_scores(q, src.Kg[bk, g][:n_ent])
             sel, mg = select_top_p(s, w.top_p, w.select_scale)
             res["margin"] = min(res["margin"], mg)
         elif w.mode == HIER:
@@ -278,14 +301,14 @@ def select_group(w, src, b: int, g: int) -> dict:
             res["segments"][h] = segs
             res["cand"][h] = (cand, s2)
         elif w.mode == COVERAGE:
-            s = chunk_scores(q, src.Kg[bk, g])
-            k_b, mg = sequence_budget(w, src, b)
+            s = chunk_scores(q, src.Kg[bk, g][:n_ent])
+            k_b, mg = sequence_budget(w, src, b, n_ent)
             sel = select_top_k(s, k_b)
             res["margin"] = min(res["margin"], mg)
             res["budget"] = k_b
         elif w.mode == PROXY_TOPP:
             qp = proxy_query(q, src.P[g])
-            s = proxy_scores(qp, src.Kp[bk, g])
+            s = proxy_scores(qp, src.Kp[bk, g][:n_tok])
             sel, mg = select_top_p(s, w.top_p, w.select_scale)
             res["margin"] = min(res["margin"], mg)
         else:
@@ -300,22 +323,26 @@ def select_group(w, src, b: int, g: int) -> dict:
     return res
 
 
-def attend_group(w, src, b: int, g: int, U: np.ndarray, heads=None):
+def attend_group(w, src, b: int, g: int, U: np.ndarray, heads=None, n_tok=None):
     """The query heads of group g attend to the hybrid context of union U: raw
-    rows of U's chunks, then (``attend_summary``) the summary rows of U, or of
-    every chunk with ``all_summaries``. With ``head_masks`` and a scored group,
-    head h attends only to its own selection ``heads[h]`` plus the forced
-    chunks (summary rows of every chunk stay visible to all heads)."""
+    rows of U's chunks and of the incomplete last chunk, then (``attend_summary``)
+    the summary rows of U, or of every complete chunk with ``all_summaries``. With
+    ``head_masks`` and a scored group, head h attends only to its own selection
+    ``heads[h]`` plus the forced chunks and the incomplete chunk (summary rows of
+    every chunk stay visible to all heads). ``n_tok``: tokens in the cache
+    (default all); an empty context gives o = 0 and lse = -inf."""
     rows_q = group_queries(w, g)
     bk = b if w.kv_batch > 1 else 0
-    n_ent = w.n_ctx // w.chunk_size
+    n_tok = w.n_ctx if n_tok is None else n_tok
+    n_ent = n_tok // w.chunk_size
+    tail = np.arange(n_ent * w.chunk_size, n_tok)  # the incomplete last chunk's raw tokens
     summaries = w.attend_summary and w.mode != PROXY_TOPP
     all_sum = summaries and getattr(w, "all_summaries", False)
     masked = getattr(w, "head_masks", False) and g not in tuple(w.local_kv_heads)
     qh = src.q[b, rows_q]
 
     def context(S):
-        rows = hybrid_rows(S, w.chunk_size)
+        rows = np.concatenate([hybrid_rows(S, w.chunk_size), tail]).astype(np.int64)
         Kc, Vc = src.kv_rows(bk, g, rows)
         if summaries:
             srows = np.arange(n_ent) if all_sum else np.asarray(S, dtype=np.int64)
@@ -323,24 +350,30 @@ def attend_group(w, src, b: int, g: int, U: np.ndarray, heads=None):
             Vc = np.concatenate([Vc, src.Vg[bk, g][srows]], axis=0)
         return Kc, Vc
 
+    def attend_or_empty(q, Kc, Vc):
+        if Kc.shape[0] == 0:
+            return np.zeros((q.shape[0], w.head_dim)), np.full(q.shape[0], -np.inf)
+        return attend(q, Kc, Vc, w.softmax_scale)
+
     if not masked:
         Kc, Vc = context(U)
-        return attend(qh, Kc, Vc, w.softmax_scale)
+        return attend_or_empty(qh, Kc, Vc)
     forced = edge_entries(n_ent, w.keep_first, w.keep_last)
     o = np.zeros((len(rows_q), w.head_dim))
     lse = np.zeros(len(rows_q))
     for j, qi in enumerate(rows_q):
         S = group_union([heads[qi], forced])
         Kc, Vc = context(S)
-        oj, lj = attend(qh[j:j + 1], Kc, Vc, w.softmax_scale)
+        oj, lj = attend_or_empty(qh[j:j + 1], Kc, Vc)
         o[j], lse[j] = oj[0], lj[0]
     return o, lse
 
 
-def decode_step(w, src, groups=None, attend_groups=None) -> dict:
+def decode_step(w, src, groups=None, attend_groups=None, ctx_len=None) -> dict:
     """One decode step: selections for ``groups`` (default all (b, g)), attention
-    for ``attend_groups`` (default the same). Returns per-(b, g) results and
-    output / lse arrays [B][T * Hq] (NaN where not computed)."""
+    for ``attend_groups`` (default the same), over caches of ``ctx_len[b]`` tokens
+    (default whole). Returns per-(b, g) results and output / lse arrays [B][T * Hq]
+    (NaN where not computed)."""
     B, Hq, Hk, d = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
     T = getattr(w, "n_queries", 1)
     if groups is None:
@@ -351,11 +384,12 @@ def decode_step(w, src, groups=None, attend_groups=None) -> dict:
     lse = np.full((B, T * Hq), np.nan)
     sel = {}
     for b, g in groups:
-        sel[(b, g)] = select_group(w, src, b, g)
+        sel[(b, g)] = select_group(w, src, b, g, cache_tokens(w, b, ctx_len))
     for b, g in attend_groups:
+        n_tok = cache_tokens(w, b, ctx_len)
         if (b, g) not in sel:
-            sel[(b, g)] = select_group(w, src, b, g)
-        o, l = attend_group(w, src, b, g, sel[(b, g)]["union"], sel[(b, g)]["heads"])
+            sel[(b, g)] = select_group(w, src, b, g, n_tok)
+        o, l = attend_group(w, src, b, g, sel[(b, g)]["union"], sel[(b, g)]["heads"], n_tok)
         out[b, group_queries(w, g)] = o
         lse[b, group_queries(w, g)] = l
     return {"sel": sel, "out": out, "lse": lse}

@@ -134,6 +134,7 @@ void plan_workspace(sd::Plan& p) {
     return o;
   };
   p.o_status = take(64);
+  p.o_ctx = take(size_t(B) * 4);     // cache length per sequence, this step
   p.o_budget = take(size_t(B) * 4);  // coverage budget per sequence
   p.o_cmass = take(c.mode == SD_COVERAGE ? size_t(B * Hq * p.len0) * 8 : 0);  // per-head softmax masses
   p.o_cimp = take(c.mode == SD_COVERAGE ? size_t(B * p.len0) * 8 : 0);        // importance per entry
@@ -177,6 +178,11 @@ sd_status check_ws(const sd::Plan&, const void* ws) {
 sd_status check_tensors(const sd::Plan& p, const sd_tensors* t, bool for_score, int level) {
   const sd_config& c = p.cfg;
   if (!t) return fail(SD_EINVAL, "tensors is NULL");
+  if (t->ctx_len) {
+    if (reinterpret_cast<uintptr_t>(t->ctx_len) & 3u) return fail(SD_EINVAL, "ctx_len must be 4-byte aligned");
+    if (c.mode == SD_HIER_TOPK)
+      return fail(SD_EUNSUPPORTED, "per-sequence cache lengths (ctx_len) with two-level selection");
+  }
   if (!t->q || !aligned16(t->q)) return fail(SD_EINVAL, "q must be a non-NULL 16-byte aligned pointer");
   const int es = c.kv_dtype == SD_F32 ? 4 : 2;
   auto row_ok = [&](int64_t st) { return st >= c.head_dim && (st * es) % 16 == 0; };
@@ -240,6 +246,8 @@ sd_status sparse_decode_init(const sd_config* cfg, sd_handle** out, size_t* work
   for (int g = 0; g < c.n_kv_heads; ++g)
     if (!p.head_mode[g]) p.scored[p.n_scored++] = int8_t(g);
   p.long_blocks = int32_t((p.len0 + sd::kLongBlock - 1) / sd::kLongBlock);
+  p.chunk_shift = 0;
+  while ((int64_t(1) << p.chunk_shift) < c.chunk_size) ++p.chunk_shift;
   plan_workspace(p);
   *out = h;
   *workspace_bytes = p.ws_bytes;

@@ -51,6 +51,9 @@ struct AttendArgs {
   int64_t words;
   int keep_first, keep_last;
   uint64_t local_mask;
+  // growing cache: the step's tokens per sequence (workspace copy [B]) and the capacity
+  const int32_t* ctx_len;
+  int64_t n_ctx;
 };
 
 template <typename T, int D>
@@ -93,23 +96,43 @@ constexpr int kListLds = 4096;
 // slower at 128K context without it).
 constexpr int kSegmentCost = 16;
 
-// Extent of a group in the sliced sequence: [kSegmentCost virtual tiles, raw tiles,
-// kSegmentCost virtual tiles, summary tiles]; an empty group has none.
+// A group's cache at this step: its complete chunks (the selection entries, each with a summary
+// row) and the raw tokens of its incomplete last chunk, which every head attends unselected.
+struct GroupCache {
+  int64_t M;   // complete chunks (entries)
+  int tail;    // tokens of the incomplete last chunk (0 for token rows)
+};
+__device__ __forceinline__ GroupCache group_cache(const AttendArgs& a, int gid) {
+  const int64_t n = seq_tokens(a.ctx_len, gid / a.Hk, a.n_ctx);
+  const int64_t M = n >> a.chunk_shift;
+  return GroupCache{M, int(n - (M << a.chunk_shift))};
+}
+
+// Extent of a group in the sliced sequence: [kSegmentCost virtual tiles, raw tiles (the listed
+// chunks' tokens), tail tiles (the incomplete chunk's tokens), kSegmentCost virtual tiles, summary
+// tiles]; an empty group has none.
 __device__ __forceinline__ int summary_tiles(int cnt, int attend_summary, int64_t M) {
   return attend_summary == 2 ? int((M + kTile - 1) / kTile) : (attend_summary ? (cnt + kTile - 1) / kTile : 0);
 }
-__device__ __forceinline__ int group_extent(int cnt, int cs, int attend_summary, int64_t M) {
-  if (cnt <= 0) return 0;
+__device__ __forceinline__ int group_extent(int cnt, int cs, int attend_summary, const GroupCache& gc) {
+  cnt = cnt > 0 ? cnt : 0;
+  if (cnt == 0 && gc.tail == 0) return 0;
   const int traw = ((cnt << cs) + kTile - 1) / kTile;
-  const int tsum = summary_tiles(cnt, attend_summary, M);
-  return kSegmentCost + traw + (tsum ? kSegmentCost + tsum : 0);
+  const int ttail = (gc.tail + kTile - 1) / kTile;
+  const int tsum = summary_tiles(cnt, attend_summary, gc.M);
+  return kSegmentCost + traw + ttail + (tsum ? kSegmentCost + tsum : 0);
 }
+
+// How the rows of a run of tiles are found: the listed chunks' tokens (list entry, token in the
+// chunk), the listed chunks' summary rows (list entry), or consecutive rows from a base (every
+// chunk's summary, or the incomplete chunk's tokens).
+enum RowKind { kRawRows = 0, kListedRows = 1, kDirectRows = 2 };
 
 // Heads of group `gid` whose own selection holds entry e (bit j = head j of the group): every head
 // for a forced entry or a local group.
-__device__ __forceinline__ uint32_t head_mask_of(const AttendArgs& a, int gid, int e) {
+__device__ __forceinline__ uint32_t head_mask_of(const AttendArgs& a, int gid, int e, int64_t M) {
   const int b = gid / a.Hk, g = gid - b * a.Hk;
-  if (((a.local_mask >> g) & 1) || e < a.keep_first || int64_t(e) >= a.n_list - a.keep_last) return 0xFFFFu;
+  if (((a.local_mask >> g) & 1) || e < a.keep_first || int64_t(e) >= M - a.keep_last) return 0xFFFFu;
   uint32_t m = 0;
   for (int j = 0; j < a.G; ++j) {
     const uint32_t w = a.bits[(int64_t(b) * a.Hq + g * a.G + j) * a.words + (e >> 5)];
@@ -162,43 +185,46 @@ struct Attender {
     }
   }
 
-  // Base pointers of the raw (summary = false) or summary (true) rows of the current group.
-  __device__ void set_kind(bool summary) {
+  // Base pointers of the raw (summary = false) or summary (true) rows of the current group,
+  // starting at row `row0`.
+  __device__ void set_kind(bool summary, int64_t row0 = 0) {
     const int b = gid / a.Hk, g = gid - b * a.Hk;
     if (summary) {
-      kb = reinterpret_cast<const T*>(a.kg) + b * a.g_sb + int64_t(g) * a.g_sh;
-      vb = reinterpret_cast<const T*>(a.vg) + b * a.g_sb + int64_t(g) * a.g_sh;
+      kb = reinterpret_cast<const T*>(a.kg) + b * a.g_sb + int64_t(g) * a.g_sh + row0 * a.g_st;
+      vb = reinterpret_cast<const T*>(a.vg) + b * a.g_sb + int64_t(g) * a.g_sh + row0 * a.g_st;
       st = a.g_st;
     } else {
-      kb = reinterpret_cast<const T*>(a.k) + b * a.kv_sb + int64_t(g) * a.kv_sh;
-      vb = reinterpret_cast<const T*>(a.v) + b * a.kv_sb + int64_t(g) * a.kv_sh;
+      kb = reinterpret_cast<const T*>(a.k) + b * a.kv_sb + int64_t(g) * a.kv_sh + row0 * a.kv_st;
+      vb = reinterpret_cast<const T*>(a.v) + b * a.kv_sb + int64_t(g) * a.kv_sh + row0 * a.kv_st;
       st = a.kv_st;
     }
   }
 
-  // Cache row of token x of a tile. Raw tiles: token v = first + x of the list's token sequence;
-  // summary tiles: list entry first + x. `e0` is the first list entry held in the LDS slice.
-  __device__ __forceinline__ int64_t row_of(bool summary, int first, int x, int nv, int e0) const {
+  // Row of token x of a tile: raw tiles, token v = first + x of the listed chunks' token sequence;
+  // listed summary tiles, list entry first + x; direct tiles, row first + x from the base. `e0` is
+  // the first list entry held in the LDS slice.
+  __device__ __forceinline__ int64_t row_of(int kind, int first, int x, int nv, int e0) const {
     x = x < nv ? x : 0;  // padded positions read a valid row; their logits are masked
-    if (summary) return a.attend_summary == 2 ? first + x : lst[first + x - e0];
+    if (kind == kDirectRows) return first + x;
+    if (kind == kListedRows) return lst[first + x - e0];
     const int cs = a.chunk_shift;
     const int v = first + x;
     return (int64_t(lst[(v >> cs) - e0]) << cs) | (v & ((1 << cs) - 1));
   }
 
-  __device__ __forceinline__ void issue(TileRegs<T, D>& r, bool summary, int first, int nv, int e0) const {
-    const T* kr = kb + row_of(summary, first, n, nv, e0) * st;
+  __device__ __forceinline__ void issue(TileRegs<T, D>& r, int kind, int first, int nv, int e0) const {
+    const T* kr = kb + row_of(kind, first, n, nv, e0) * st;
 #pragma unroll
     for (int q = 0; q < CF::KQ; ++q) r.k[q] = ld16_stream(kr + (CF::BF ? 32 * q + 8 * c : (D / 4) * c + 4 * q));
 #pragma unroll
     for (int kq = 0; kq < CF::VPL; ++kq) {
       const int pidx = kq * 64 + lane;
       const int x = pidx / CF::PPR, cp = pidx - x * CF::PPR;
-      r.v[kq] = ld16_stream(vb + row_of(summary, first, x, nv, e0) * st + cp * CF::EPV);
+      r.v[kq] = ld16_stream(vb + row_of(kind, first, x, nv, e0) * st + cp * CF::EPV);
     }
   }
 
-  __device__ __forceinline__ void compute(const TileRegs<T, D>& r, int nv, SoftmaxState<D>& s, bool summary,
+  __device__ __forceinline__ void compute(const TileRegs<T, D>& r, int nv, SoftmaxState<D>& s, int kind,
                                           int first, int e0) {
     // ---- logits: S^T[token][slot]; lane (n, c) gets tokens 4c + i of head slot n
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -226,12 +252,13 @@ struct Attender {
     float lg[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) lg[i] = 4 * c + i < nv ? sacc[i] * a.scale_log2 : kNegInf;
-    if (a.head_masks && !(summary && a.attend_summary == 2) && hs >= 0) {
-      // per-head masks: a token whose entry is outside this head's own set is not attended
+    if (a.head_masks && kind != kDirectRows && hs >= 0) {
+      // per-head masks: a token whose entry is outside this head's own set is not attended (direct
+      // rows -- every chunk's summary, the incomplete chunk's tokens -- are seen by every head)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int x = 4 * c + i < nv ? 4 * c + i : 0;
-        const int ei = summary ? first + x - e0 : ((first + x) >> a.chunk_shift) - e0;
+        const int ei = kind == kListedRows ? first + x - e0 : ((first + x) >> a.chunk_shift) - e0;
         if (!((lmask[ei] >> hs) & 1)) lg[i] = kNegInf;
       }
     }
@@ -307,10 +334,9 @@ struct Attender {
   }
 
   // This wave's tiles of [u0, u1) (alternating with the other waves) through an NS-stage register
-  // ring: the loads of the next NS - 1 tiles are in flight while a tile is computed. Raw tiles:
-  // tile u starts at token kTile*u of the group's token sequence; summary tiles: at list entry
-  // kTile*u. `limit` = tokens (raw) or entries (summary) in the group.
-  __device__ void run(bool summary, int u0, int u1, int limit, int e0, SoftmaxState<D>& s) {
+  // ring: the loads of the next NS - 1 tiles are in flight while a tile is computed. Tile u starts
+  // at position kTile*u of the run's rows (see row_of); `limit` = rows in the run.
+  __device__ void run(int kind, int u0, int u1, int limit, int e0, SoftmaxState<D>& s) {
     constexpr int NS = CF::NS;
     const int first = u0 + wave;
     if (first >= u1) return;
@@ -323,14 +349,14 @@ struct Attender {
     // stage being computed.
     auto clamp = [&](int k) { return tile(k < nt ? k : nt - 1); };
 #pragma unroll
-    for (int k = 0; k < NS - 1; ++k) issue(R[k], summary, clamp(k) * kTile, nv_of(clamp(k)), e0);
+    for (int k = 0; k < NS - 1; ++k) issue(R[k], kind, clamp(k) * kTile, nv_of(clamp(k)), e0);
     for (int k0 = 0; k0 < nt; k0 += NS) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const int k = k0 + j;
         const int kn = k + NS - 1;
-        issue(R[(j + NS - 1) % NS], summary, clamp(kn) * kTile, nv_of(clamp(kn)), e0);
-        if (k < nt) compute(R[j], nv_of(tile(k)), s, summary, tile(k) * kTile, e0);
+        issue(R[(j + NS - 1) % NS], kind, clamp(kn) * kTile, nv_of(clamp(kn)), e0);
+        if (k < nt) compute(R[j], nv_of(tile(k)), s, kind, tile(k) * kTile, e0);
       }
     }
   }
@@ -354,7 +380,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
     const int g0 = tid * per;
     int sum = 0;
     for (int gg = g0; gg < min(NG, g0 + per); ++gg) {
-      sum += group_extent(a.cnt[gg], cs, a.attend_summary, a.n_list);
+      sum += group_extent(a.cnt[gg], cs, a.attend_summary, group_cache(a, gg));
     }
     // inclusive scan over the 256 threads in thread order: DPP within each wave, then the
     // earlier waves' totals (one barrier)
@@ -365,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
     for (int w = 0; w < (tid >> 6); ++w) run += sbuf[w];
     for (int gg = g0; gg < min(NG, g0 + per); ++gg) {
       gpre[gg] = run;
-      run += group_extent(a.cnt[gg], cs, a.attend_summary, a.n_list);
+      run += group_extent(a.cnt[gg], cs, a.attend_summary, group_cache(a, gg));
     }
     if (tid == 255) gpre[NG] = run;  // the last thread's running sum is the total
     __syncthreads();
@@ -392,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   // a piece of the list (ne <= kListLds entries) into LDS, in rounds of 8 entries per thread
   // whose loads (from clamped indices) are all issued before the first is stored: a piece costs
   // at most kListLds / 2048 memory round trips, not one per 256 entries
-  auto load_list = [&](const int32_t* src, int ne, int gid) {
+  auto load_list = [&](const int32_t* src, int ne, int gid, int64_t M) {
     constexpr int kPer = 8;
     for (int r0 = 0; r0 < ne; r0 += 256 * kPer) {
       int32_t ev[kPer];
@@ -406,7 +432,7 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
         const int i = r0 + tid + 256 * k;
         if (i < ne) {
           lst[i] = ev[k];
-          if (a.head_masks) lmask[i] = uint16_t(head_mask_of(a, gid, ev[k]));
+          if (a.head_masks) lmask[i] = uint16_t(head_mask_of(a, gid, ev[k], M));
         }
       }
     }
@@ -417,8 +443,10 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
     const int s1 = min(b1, gpre[gi + 1]) - gpre[gi];
     if (s0 >= s1) continue;
     const int cnt = a.cnt[gi];
-    const int ntok = cnt << cs;
+    const GroupCache gc = group_cache(a, gi);
+    const int ntok = cnt << cs;  // the listed chunks' tokens
     const int traw = (ntok + kTile - 1) / kTile;
+    const int ttail = (gc.tail + kTile - 1) / kTile;
     at.load_query(gi);
     SoftmaxState<D> st;
     st.m = kNegInf;
@@ -440,17 +468,27 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
         const int e0 = (u0 * kTile) >> cs;
         const int e1 = min(cnt, ((u1 * kTile - 1) >> cs) + 1);
         __syncthreads();
-        load_list(glist + e0, e1 - e0, gi);
+        load_list(glist + e0, e1 - e0, gi, gc.M);
         __syncthreads();
-        at.run(false, u0, u1, ntok, e0, st);
+        at.run(kRawRows, u0, u1, ntok, e0, st);
       }
     }
-    // summary tiles [q0, q1) (at [2 kSegmentCost + traw, extent) of the group's extent): the listed
-    // chunks' summary rows, or (attend_summary 2) every chunk's, addressed directly
+    // tail tiles [t0, t1) (at [kSegmentCost + traw, kSegmentCost + traw + ttail)): the incomplete
+    // chunk's tokens, consecutive rows from its first token
+    if (gc.tail) {
+      const int base = kSegmentCost + traw;
+      const int t0 = max(s0, base) - base, t1 = min(s1 - base, ttail);
+      if (t0 < t1) {
+        at.set_kind(false, gc.M << cs);
+        at.run(kDirectRows, t0, t1, gc.tail, 0, st);
+      }
+    }
+    // summary tiles [q0, q1) (at [2 kSegmentCost + traw + ttail, extent) of the group's extent): the
+    // listed chunks' summary rows, or (attend_summary 2) every chunk's, addressed directly
     if (a.attend_summary) {
-      const int tsum = summary_tiles(cnt, a.attend_summary, a.n_list);
-      const int nsum = a.attend_summary == 2 ? int(a.n_list) : cnt;
-      const int base = 2 * kSegmentCost + traw;
+      const int tsum = summary_tiles(cnt, a.attend_summary, gc.M);
+      const int nsum = a.attend_summary == 2 ? int(gc.M) : cnt;
+      const int base = 2 * kSegmentCost + traw + ttail;
       const int q0 = max(s0, base) - base, q1 = min(s1 - base, tsum);
       at.set_kind(true);
       const int tiles_per_slice = a.attend_summary == 2 ? (1 << 30) : kListLds / kTile;
@@ -460,10 +498,10 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
         if (a.attend_summary == 1) {
           const int e1 = min(cnt, u1 * kTile);
           __syncthreads();
-          load_list(glist + e0, e1 - e0, gi);
+          load_list(glist + e0, e1 - e0, gi, gc.M);
           __syncthreads();
         }
-        at.run(true, u0, u1, nsum, e0, st);
+        at.run(a.attend_summary == 2 ? kDirectRows : kListedRows, u0, u1, nsum, e0, st);
       }
     }
 
@@ -634,6 +672,8 @@ int launch_attend(const Plan& p, const sd_tensors& t, char* ws, void* stream) {
   a.keep_first = c.keep_first;
   a.keep_last = c.keep_last;
   a.local_mask = p.local_mask;
+  a.ctx_len = at<int32_t>(ws, p.o_ctx);
+  a.n_ctx = c.n_ctx;
   const dim3 grid(p.attend_blocks);
   if (c.kv_dtype == SD_BF16) {
     if (c.head_dim == 128) {

@@ -63,6 +63,34 @@ __device__ __forceinline__ double wave_min(double v) {
   return v;
 }
 
+// Tokens sequence b's cache holds: ctx_len[b] clamped to [0, cap], or cap when no lengths are given
+// (a growing cache: workspace rows and tensor strides keep the capacity, the lengths vary per call).
+__device__ __forceinline__ int64_t seq_tokens(const int32_t* ctx_len, int b, int64_t cap) {
+  if (!ctx_len) return cap;
+  const int64_t n = ctx_len[b];
+  return n < 0 ? 0 : (n < cap ? n : cap);
+}
+
+// Per-sequence cache lengths of one step. The step's first kernel publishes them (from the caller's
+// array, or the capacity where it gives none) into the workspace copy `out`; every later kernel of
+// the step reads that copy, so all stages see the lengths the scores were computed for.
+struct StepLens {
+  const int32_t* in;  // caller's device array [B] of tokens, or NULL (every sequence: cap)
+  int32_t* out;       // workspace copy [B], or NULL where nothing is published
+  int B;
+  int64_t cap;        // capacity (tokens)
+  int shift;          // entries = tokens >> shift (chunks; 0 for token rows)
+  __device__ __forceinline__ void publish(int tid, int nt) const {
+    if (out)
+      for (int b = tid; b < B; b += nt) out[b] = int32_t(seq_tokens(in, b, cap));
+  }
+  // entries of sequence b's rows, at most `limit` (the row length a kernel was launched for)
+  __device__ __forceinline__ int64_t entries(int b, int64_t limit) const {
+    const int64_t e = seq_tokens(in, b, cap) >> shift;
+    return e < limit ? e : limit;
+  }
+};
+
 // Bits of word w (entries 32w .. 32w+31) that fall in [0, first) or [n - last, n).
 __device__ __forceinline__ uint32_t edge_bits(int64_t w, int64_t n, int64_t first, int64_t last) {
   uint32_t m = 0;

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRo
                                                     int64_t n_rows, int64_t n_keys, int G, int Hq,
                                                     uint64_t local_mask, double* __restrict__ out, int64_t out_len,
                                                     uint32_t* __restrict__ status, int32_t* __restrict__ arrivals,
-                                                    int n_groups) {
+                                                    int n_groups, StepLens lens) {
   constexpr int EPV = 16 / int(sizeof(T));
   constexpr int PPR = D / EPV;                          // 16-byte pieces per row
   constexpr int QW = D + 2;                             // padded fp64 query row
@@ -36,12 +36,16 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRo
   if (status && blockIdx.x == 0 && y == 0 && b == 0) {
     if (tid < 16) status[tid] = 0;
     for (int i = tid; i < n_groups; i += 256) arrivals[i] = 0;
+    lens.publish(tid, 256);
   }
   const int g = cand ? y / G : y;
   if ((local_mask >> g) & 1) return;
   const int h0 = cand ? y : y * G;
   const int nh = cand ? 1 : G;
   const int64_t r0 = int64_t(blockIdx.x) * kScoreRows;
+  // rows of this sequence: its complete chunks when the cache grows (candidate rows: all)
+  const int64_t rows_b = cand ? n_rows : lens.entries(b, n_rows);
+  if (r0 >= rows_b) return;
   // the slots' query elements (4 HPT slots at most: one unrolled round of loads from clamped rows),
   // then the key rows of this workgroup, 16 bytes per thread per step (rows past the end repeat
   // the last); the queries are staged in LDS while the key loads are in flight
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRo
   __syncthreads();
   const int r = tid >> 2, j0 = (tid & 3) * HPT;
   const int64_t row = r0 + r;
-  if (row >= n_rows || j0 >= nh) return;
+  if (row >= rows_b || j0 >= nh) return;
   const uint4* kr = ks + r * KW;
   double acc[HPT];
   const double* qrow[HPT];
@@ -127,12 +131,13 @@ __global__ __launch_bounds__(256) void k_proxy_query(const T* __restrict__ q, QR
                                                      const float* __restrict__ proj, int G, int Hq,
                                                      uint64_t local_mask, double* __restrict__ qp,
                                                      uint32_t* __restrict__ status, int32_t* __restrict__ arrivals,
-                                                     int n_groups) {
+                                                     int n_groups, StepLens lens) {
   const int b = blockIdx.y;
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (blockIdx.x == 0 && b == 0) {
     if (threadIdx.x < 16) status[threadIdx.x] = 0;
     for (int i = threadIdx.x; i < n_groups; i += 256) arrivals[i] = 0;
+    lens.publish(threadIdx.x, 256);
   }
   const int h = t >> 4, j = t & 15;
   if (h >= Hq) return;
@@ -168,6 +173,7 @@ struct ProxyArgs {
   uint32_t* status;
   int32_t* arrivals;
   int n_groups;
+  StepLens lens;
   int8_t scored[kMaxKvHeads];  // blockIdx.y -> KV group
 };
 
@@ -180,7 +186,9 @@ __global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
   if (blockIdx.x == 0 && blockIdx.y == 0 && b == 0) {
     if (tid < 16) a.status[tid] = 0;
     for (int i = tid; i < a.n_groups; i += 512) a.arrivals[i] = 0;
+    a.lens.publish(tid, 512);
   }
+  const int64_t n_b = a.lens.entries(b, a.N);  // this sequence's tokens
   // The group's projection and queries are loaded first (one unrolled round into registers, from
   // clamped rows, so every load is issued before any is used), then the tokens' proxy keys; the
   // projection is staged in LDS and q_p = q P computed (one thread per (head, proxy dim), the
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
 #pragma unroll
   for (int k = 0; k < TPT; ++k) {
     const int64_t t = t0 + tid + 512 * k;
-    const bool valid = t < a.N;
+    const bool valid = t < n_b;
     double kd[16];
     const _Float16* h0 = reinterpret_cast<const _Float16*>(&raw[k][0]);
     const _Float16* h1 = reinterpret_cast<const _Float16*>(&raw[k][1]);
@@ -289,9 +297,10 @@ __global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
 // routing (8 entries per thread, loads issued first).
 __global__ __launch_bounds__(256) void k_row_minmax(const double* __restrict__ s0, int64_t len, int G, int Hq,
                                                     uint64_t local_mask, double* __restrict__ pmax,
-                                                    double* __restrict__ pmin, int nblk) {
+                                                    double* __restrict__ pmin, int nblk, StepLens lens) {
   const int b = blockIdx.z, h = blockIdx.y, tid = threadIdx.x;
   if ((local_mask >> (h / G)) & 1) return;
+  const int64_t len_b = lens.entries(b, len);  // entries of this sequence's rows (stride: len)
   __shared__ double rmax[4], rmin[4];
   const int64_t row = int64_t(b) * Hq + h;
   const int64_t t0 = int64_t(blockIdx.x) * kMinMaxBlock;
@@ -301,10 +310,10 @@ __global__ __launch_bounds__(256) void k_row_minmax(const double* __restrict__ s
     const int64_t t = t0 + tid + 256 * k;
     v[k] = s0[row * len + (t < len ? t : len - 1)];
   }
-  double mx = kNegInfD, mn = kPosInfD;
+  double mx = kNegInfD, mn = kPosInfD;  // a block past the entries keeps the identities
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    if (t0 + tid + 256 * k < len) {
+    if (t0 + tid + 256 * k < len_b) {
       mx = fmax(mx, v[k]);
       mn = fmin(mn, v[k]);
     }
@@ -328,12 +337,15 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
   const int B = c.batch, Hq = c.n_q_heads, Hk = c.n_kv_heads;
   uint32_t* status = at<uint32_t>(ws, p.o_status);
   const QRows qm{t.q_sb, t.q_st, t.q_sh, p.G, p.Gq};
+  // the step's cache lengths: read from the caller's array, published into the workspace by the
+  // first kernel of the step (level 0)
+  const StepLens lens{t.ctx_len, level == 0 ? at<int32_t>(ws, p.o_ctx) : nullptr, B, c.n_ctx, p.chunk_shift};
   if (c.route == SD_ROUTE_PROXY) {
     if (p.n_scored == 0) {  // every group is local: only the status words and counters need clearing
       const int nb = (Hq * 16 + 255) / 256;
       hipLaunchKernelGGL((k_proxy_query<T, D>), dim3(nb, B), dim3(256), 0, st, static_cast<const T*>(t.q), qm,
                          t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status,
-                         at<int32_t>(ws, p.o_arrive), p.n_arrive);
+                         at<int32_t>(ws, p.o_arrive), p.n_arrive, lens);
     } else {
       ProxyArgs pa;
       pa.kp = static_cast<const uint16_t*>(t.kp);
@@ -353,6 +365,7 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
       pa.status = status;
       pa.arrivals = at<int32_t>(ws, p.o_arrive);
       pa.n_groups = p.n_arrive;
+      pa.lens = lens;
       for (int i = 0; i < kMaxKvHeads; ++i) pa.scored[i] = i < p.n_scored ? p.scored[i] : 0;
       hipLaunchKernelGGL((k_score_proxy<T, D>), dim3(p.score_blocks0, p.n_scored, B), dim3(512), 0, st, pa);
     }
@@ -362,7 +375,7 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
     hipLaunchKernelGGL((k_score_rows<T, D, 1>), dim3((p.len1 + kScoreRows - 1) / kScoreRows, Hq, B), dim3(256), 0, st,
                        static_cast<const T*>(t.q), qm, static_cast<const T*>(t.kg), t.g_sb, t.g_sh,
                        t.g_st, at<int32_t>(ws, p.o_cand), p.len1, p.M, p.G, Hq, p.local_mask, at<double>(ws, p.o_s1),
-                       p.len1, static_cast<uint32_t*>(nullptr), static_cast<int32_t*>(nullptr), 0);
+                       p.len1, static_cast<uint32_t*>(nullptr), static_cast<int32_t*>(nullptr), 0, lens);
     return int(hipGetLastError());
   }
   const bool meta = c.mode == SD_HIER_TOPK;
@@ -374,7 +387,7 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
 #define SD_SCORE_ROWS(HPT)                                                                                       \
   hipLaunchKernelGGL((k_score_rows<T, D, HPT>), grid, dim3(256), 0, st, static_cast<const T*>(t.q), qm, keys, ksb, \
                      ksh, kst, static_cast<const int32_t*>(nullptr), p.len0, p.len0, p.G, Hq, p.local_mask,          \
-                     at<double>(ws, p.o_s0), p.len0, status, at<int32_t>(ws, p.o_arrive), p.n_arrive)
+                     at<double>(ws, p.o_s0), p.len0, status, at<int32_t>(ws, p.o_arrive), p.n_arrive, lens)
   if (hpt == 1)
     SD_SCORE_ROWS(1);
   else if (hpt == 2)
@@ -385,7 +398,7 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
   if (p.long0)
     hipLaunchKernelGGL(k_row_minmax, dim3(p.score_blocks0, Hq, B), dim3(256), 0, st, at<double>(ws, p.o_s0),
                        p.len0, p.G, Hq, p.local_mask, at<double>(ws, p.o_pmax), at<double>(ws, p.o_pmin),
-                       p.score_blocks0);
+                       p.score_blocks0, lens);
   return int(hipGetLastError());
 }
 

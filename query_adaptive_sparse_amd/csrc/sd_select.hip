@@ -171,6 +171,11 @@ struct GroupSelArgs {
   int32_t* arrivals;  // [B][Hk], cleared by the score pass
   int64_t n_entries;
   int keep_first, keep_last, sink, window;
+  // growing cache: tokens per sequence (device [B], or NULL: n_ctx); a flat row of sequence b holds
+  // its complete chunks, ctx_len[b] >> chunk_shift of them
+  const int32_t* ctx_len;
+  int64_t n_ctx;
+  int chunk_shift;
 };
 
 // Bin of a score: coarse bin of (smax - s) over the row's range, and its fine sub-bin.
@@ -206,25 +211,29 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
   const int G = a.G, g = h / G;
-  const int L = int(a.len);
+  // entries of this sequence's rows and of its union (the whole row without a growing cache)
+  const int64_t n_ent = a.ctx_len ? (seq_tokens(a.ctx_len, b, a.n_ctx) >> a.chunk_shift) : a.n_entries;
+  const int L = a.kind == 0 ? int(n_ent) : int(a.len);
   const bool local = (a.local_mask >> g) & 1;
   const int64_t row = int64_t(b) * a.Hq + h;
   const int words_row = (L + 31) / 32;
 
-  for (int w = tid; w < words_row; w += kSelT) selb[w] = 0;
+  for (int w = tid; w < kSmallRowMax / 32; w += kSelT) selb[w] = 0;
   for (int i = tid; i < kNBin; i += kSelT) {
     hhi[i] = 0;
     hlo[i] = 0;
   }
   if (tid == 0) ncand = 0;
 
-  // ---- 1. scores (unconditional, clamped loads), range, weights, target
+  // ---- 1. scores (unconditional loads clamped to the row's capacity, so they do not wait for the
+  // row's length; entries past it are never used), range, weights, target
   double sv[kLaneEntries], wt[kLaneEntries];
   const int EPL = (L + kSelT - 1) / kSelT;
+  const int cap = int(a.len);
 #pragma unroll
   for (int k = 0; k < kLaneEntries; ++k) {
     const int i = tid + kSelT * k;
-    sv[k] = local ? 0.0 : a.s[row * a.len + (i < L ? i : L - 1)];
+    sv[k] = local ? 0.0 : a.s[row * a.len + (i < cap ? i : cap - 1)];
   }
   double smax = kNegInfD, smin = kPosInfD;
 #pragma unroll
@@ -500,12 +509,12 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int uwords = int((a.n_entries + 31) / 32);
+  const int uwords = int((n_ent + 31) / 32);
   {
     const int64_t first = local ? a.sink : a.keep_first;
     const int64_t last = local ? a.window : a.keep_last;
     for (int w = tid; w < uwords; w += kSelT) {
-      uint32_t u = edge_bits(w, a.n_entries, first, last);
+      uint32_t u = edge_bits(w, n_ent, first, last);
       if (!local)
         // the heads' words 8 at a time, every load of a block issued before the first is used
         // (heads past the group repeat its last head: the OR is unchanged)
@@ -591,7 +600,17 @@ struct LongArgs {
   uint32_t* bits;
   int64_t words;
   uint32_t* status;
+  // growing cache: tokens per sequence (device [B], or NULL: every row holds len entries); a row
+  // of sequence b holds ctx_len[b] >> chunk_shift entries (row strides keep len)
+  const int32_t* ctx_len;
+  int64_t n_ctx;
+  int chunk_shift;
 };
+
+// Entries of sequence b's rows.
+__device__ __forceinline__ int64_t long_len(const LongArgs& a, int b) {
+  return a.ctx_len ? (seq_tokens(a.ctx_len, b, a.n_ctx) >> a.chunk_shift) : a.len;
+}
 
 __device__ __forceinline__ double coarse_pos(double s, double smax, double binscale) {
   const double d = (smax - s) * binscale;
@@ -680,7 +699,8 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
   const double range = smax - smin;
   const double binscale = range > 0.0 ? double(kBins1) / range : 0.0;
   const int wexp = a.ident ? ident_exp(smax) : 0;
-  const bool all = a.topp ? (a.p >= 1.0) : (int64_t(long_k(a, b)) >= a.len);
+  const int64_t len = long_len(a, b);
+  const bool all = len == 0 || (a.topp ? (a.p >= 1.0) : (int64_t(long_k(a, b)) >= len));
   if (slab == 0 && tid == 0) {
     RowInfo ri = {};
     ri.smax = smax;
@@ -690,9 +710,9 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
     ri.wexp = wexp;
     a.info[row] = ri;
   }
-  if (all) return;
   const int64_t t0 = int64_t(slab) * kLongBlock;
-  const int64_t t1 = t0 + kLongBlock < a.len ? t0 + kLongBlock : a.len;
+  if (all || t0 >= len) return;  // slabs past the row's entries hold nothing (find1 skips them)
+  const int64_t t1 = t0 + kLongBlock < len ? t0 + kLongBlock : len;
   const double* sr = a.s0 + row * a.len;
   uint16_t* br = a.cbin + row * a.cstride;
   // kLongBlock / (8 NT) batches of 8 entries per thread; the next batch's loads are issued before
@@ -750,10 +770,11 @@ __global__ __launch_bounds__(kFindThreads) void k_long_find1(LongArgs a) {
   if (ri.all) return;
   double m;
   const int64_t o = row * a.nb1 * kBins1 + tid;
+  const int nb = int((long_len(a, b) + kLongBlock - 1) / kLongBlock);  // slabs holding entries
   if (a.topp) {
     unsigned long long sh = 0, sl = 0;
 #pragma unroll 16
-    for (int sl_ = 0; sl_ < a.nb1; ++sl_) {
+    for (int sl_ = 0; sl_ < nb; ++sl_) {
       sh += a.h1h[o + int64_t(sl_) * kBins1];
       sl += a.h1l[o + int64_t(sl_) * kBins1];
     }
@@ -761,7 +782,7 @@ __global__ __launch_bounds__(kFindThreads) void k_long_find1(LongArgs a) {
   } else {
     uint32_t cn = 0;
 #pragma unroll 16
-    for (int sl_ = 0; sl_ < a.nb1; ++sl_) cn += a.h1c[o + int64_t(sl_) * kBins1];
+    for (int sl_ = 0; sl_ < nb; ++sl_) cn += a.h1c[o + int64_t(sl_) * kBins1];
     m = double(cn);
   }
   double Z;
@@ -798,10 +819,13 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
   const int lane = tid & 63;
   const int64_t row = int64_t(b) * a.Hq + h;
   const int64_t t0 = int64_t(slab) * kLongBlock;
-  const int64_t t1 = t0 + kLongBlock < a.len ? t0 + kLongBlock : a.len;
+  const int64_t t1c = t0 + kLongBlock < a.len ? t0 + kLongBlock : a.len;  // the slab in the row
+  const int64_t len = long_len(a, b);
+  const int64_t t1 = t1c < len ? t1c : len;                              // its entries
   uint32_t* bw = a.bits + row * a.words;
-  if ((a.local_mask >> (h / a.G)) & 1) {
-    for (int64_t w = (t0 >> 5) + tid; w < ((t1 + 31) >> 5); w += NT) bw[w] = 0u;
+  if (((a.local_mask >> (h / a.G)) & 1) || t1 <= t0) {
+    for (int64_t w = (t0 >> 5) + tid; w < ((t1c + 31) >> 5); w += NT) bw[w] = 0u;
+    if (tid == 0 && t1 <= t0 && !((a.local_mask >> (h / a.G)) & 1)) a.ccnt[row * a.nb1 + slab] = 0;
     return;
   }
   __shared__ int scnt;
@@ -834,7 +858,7 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
       sel |= (valid && (ri.all || cb[u] < ri.bin1)) ? (1u << u) : 0u;
       cand |= (gather && valid && cb[u] == ri.bin1) ? (1u << u) : 0u;
     }
-    if (e0 < ((t1 + 31) & ~int64_t(31))) bb[e0 >> 3] = uint8_t(sel);  // whole words, zero past the row
+    if (e0 < ((t1c + 31) & ~int64_t(31))) bb[e0 >> 3] = uint8_t(sel);  // whole words, zero past the entries
     const int nc = __popc(cand);
     const int incl = wave_scan_i32_dpp(nc, lane);
     const int wtot = __builtin_amdgcn_readlane(incl, 63);
@@ -899,7 +923,8 @@ __device__ __forceinline__ void set_bit(uint32_t* bw, int64_t t) { atomicOr(&bw[
 // weights: the lowest indices up to the crossing). Entries of the coarse bin ahead of the final
 // interval are selected in the last pass. Exact for every input.
 template <int NT>
-__device__ void resolve_radix(const LongArgs& a, const RowInfo& ri, int64_t row, int64_t cnt, const ResolveLds& L) {
+__device__ void resolve_radix(const LongArgs& a, const RowInfo& ri, int64_t row, int64_t len, int64_t cnt,
+                              const ResolveLds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const double* sr = a.s0 + row * a.len;
   const uint16_t* br = a.cbin + row * a.cstride;
@@ -908,7 +933,7 @@ __device__ void resolve_radix(const LongArgs& a, const RowInfo& ri, int64_t row,
   auto weight = [&](uint64_t k) { return long_weight(a, ri.smax, wexp, dkey_inv(k)); };
   // key interval of the bin's entries
   uint64_t kmn = ~0ull, kmx = 0ull;
-  for (int64_t t = tid; t < a.len; t += NT)
+  for (int64_t t = tid; t < len; t += NT)
     if (br[t] == ri.bin1) {
       const uint64_t k = dkey(sr[t]);
       kmn = k < kmn ? k : kmn;
@@ -943,7 +968,7 @@ __device__ void resolve_radix(const LongArgs& a, const RowInfo& ri, int64_t row,
     }
     if (tid == 0) *L.hit = 0x7FFFFFFF;
     __syncthreads();
-    for (int64_t t = tid; t < a.len; t += NT)
+    for (int64_t t = tid; t < len; t += NT)
       if (br[t] == ri.bin1) {
         const uint64_t k = dkey(sr[t]);
         if (k >= klo && k <= khi) {
@@ -978,7 +1003,7 @@ __device__ void resolve_radix(const LongArgs& a, const RowInfo& ri, int64_t row,
     const int jc = *L.hit;
     if (jc == 0x7FFFFFFF) {
       // rounding left the target beyond the interval's weight: every entry of the interval is kept
-      for (int64_t t = tid; t < a.len; t += NT)
+      for (int64_t t = tid; t < len; t += NT)
         if (br[t] == ri.bin1 && dkey(sr[t]) >= klo) set_bit(bw, t);
       return;
     }
@@ -1000,7 +1025,7 @@ __device__ void resolve_radix(const LongArgs& a, const RowInfo& ri, int64_t row,
     // gather the interval's entries, select the ones ahead of it, sort and walk
     if (tid == 0) *L.nx = 0;
     __syncthreads();
-    for (int64_t t = tid; t < a.len; t += NT)
+    for (int64_t t = tid; t < len; t += NT)
       if (br[t] == ri.bin1) {
         const uint64_t k = dkey(sr[t]);
         if (k > khi) {
@@ -1038,8 +1063,8 @@ __device__ void resolve_radix(const LongArgs& a, const RowInfo& ri, int64_t row,
   auto same = [&](int) { return wt; };
   const int pos = block_first_crossing(int(cnt), before, ri.target, same, L.buf, L.ibuf);
   const int take = pos < 0 ? int(cnt) : pos + 1;
-  const int64_t per = (a.len + NT - 1) / NT;
-  const int64_t r0 = int64_t(tid) * per, r1 = r0 + per < a.len ? r0 + per : a.len;
+  const int64_t per = (len + NT - 1) / NT;
+  const int64_t r0 = int64_t(tid) * per, r1 = r0 + per < len ? r0 + per : len;
   int mine = 0;
   for (int64_t t = r0; t < r1; ++t)
     if (br[t] == ri.bin1 && dkey(sr[t]) == khi) ++mine;
@@ -1082,16 +1107,18 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   const double* sr = a.s0 + row * a.len;
   uint32_t* bw = a.bits + row * a.words;
   const int wexp = ri.wexp;
+  const int64_t len = long_len(a, b);
+  const int nb = int((len + kLongBlock - 1) / kLongBlock);  // slabs holding entries
   // ---- the crossing bin's entry count over the slabs (slab s owns soff[s] .. soff[s+1] of the
   // gathered entries when they fit the buffer)
-  const int per = (a.nb1 + NT - 1) / NT;  // slabs per thread
+  const int per = (nb + NT - 1) / NT;  // slabs per thread
   double local = 0.0;
-  for (int s = tid * per; s < min(a.nb1, tid * per + per); ++s) local += double(a.ccnt[row * a.nb1 + s]);
+  for (int s = tid * per; s < min(nb, tid * per + per); ++s) local += double(a.ccnt[row * a.nb1 + s]);
   double tot;
   const double incl = block_scan<NT>(local, wtot, &tot);
   if (tot > double(kResolveCap)) {
     const ResolveLds L{keys, idx, hh, hl, hc, wtot, buf, &ibuf, &nx, &hit_bin, &hit_before, kred};
-    resolve_radix<NT>(a, ri, row, int64_t(tot), L);
+    resolve_radix<NT>(a, ri, row, len, int64_t(tot), L);
     return;
   }
   // soff holds the first position of every thread's first slab; slabs inside a thread's range
@@ -1117,7 +1144,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
       int s = lo * per, off = j - soff[lo];
       // with one slab per thread, soff[lo + 1] - soff[lo] is that slab's count, so j lies in slab
       // lo and no count needs reading
-      while (per > 1 && s + 1 < a.nb1 && off >= a.ccnt[row * a.nb1 + s]) {  // at most `per` steps
+      while (per > 1 && s + 1 < nb && off >= a.ccnt[row * a.nb1 + s]) {  // at most `per` steps
         off -= a.ccnt[row * a.nb1 + s];
         ++s;
       }
@@ -1274,7 +1301,16 @@ struct CoverageArgs {
   double* imp;     // [B][len]
   double* sorted;  // [B][len] importance in ascending order
   int32_t* budget; // [B]
+  // growing cache: sequence b's rows hold ctx_len[b] >> chunk_shift entries (NULL: len)
+  const int32_t* ctx_len;
+  int64_t n_ctx;
+  int chunk_shift;
 };
+
+// Entries of sequence b's coverage rows.
+__device__ __forceinline__ int cov_len(const CoverageArgs& a, int b) {
+  return int(a.ctx_len ? (seq_tokens(a.ctx_len, b, a.n_ctx) >> a.chunk_shift) : a.len);
+}
 
 constexpr int kCovThreads = 256;
 constexpr int kCovRankEntries = 32;   // entries ranked per workgroup
@@ -1284,7 +1320,7 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_mass(CoverageArgs a) {
   constexpr int NT = kCovThreads, PT = kSmallRowMax / NT;
   __shared__ double wred[NT / 64];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int L = int(a.len);
+  const int L = cov_len(a, b);
   const int64_t row = int64_t(b) * a.Hq + h;
   double* mr = a.mass + row * a.len;
   if ((a.local_mask >> (h / a.G)) & 1) {
@@ -1323,7 +1359,7 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_mass(CoverageArgs a) {
 
 __global__ __launch_bounds__(kCovThreads) void k_cov_importance(CoverageArgs a) {
   const int b = blockIdx.y, m = blockIdx.x * kCovThreads + threadIdx.x;
-  if (m >= a.len) return;
+  if (m >= cov_len(a, b)) return;
   const double* mb = a.mass + int64_t(b) * a.Hq * a.len + m;
   double imp = 0.0;
 #pragma unroll 8
@@ -1337,7 +1373,7 @@ __global__ __launch_bounds__(kCovThreads) void k_cov_rank(CoverageArgs a) {
   __shared__ uint64_t keys[kSmallRowMax];
   __shared__ int part[S][E];
   const int b = blockIdx.y, tid = threadIdx.x;
-  const int L = int(a.len);
+  const int L = cov_len(a, b);
   const double* ib = a.imp + int64_t(b) * a.len;
   for (int j = tid; j < L; j += NT) keys[j] = dkey(ib[j]);
   __syncthreads();
@@ -1377,7 +1413,7 @@ __global__ __launch_bounds__(kCovBudgetThreads) void k_cov_budget(CoverageArgs a
   __shared__ double wtot[NT / 64];
   __shared__ int hit;
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int L = int(a.len);
+  const int L = cov_len(a, b);
   const double* sb = a.sorted + int64_t(b) * a.len;
   double w[PT];
   double local = 0.0;
@@ -1424,6 +1460,10 @@ struct UnionArgs {
   int Hq, Hk, G, ranges;
   uint64_t local_mask;
   int keep_first, keep_last, sink, window;
+  // growing cache: sequence b's union covers ctx_len[b] >> chunk_shift entries (NULL: n)
+  const int32_t* ctx_len;
+  int64_t n_ctx;
+  int chunk_shift;
 };
 
 // Per range of kUnionWordsPerBlock words: the union words (OR of the group's per-head words and
@@ -1459,12 +1499,15 @@ __global__ __launch_bounds__(256) void k_union_count(UnionArgs a) {
     }
   }
   int c = 0;
+  const int64_t n = a.ctx_len ? (seq_tokens(a.ctx_len, b, a.n_ctx) >> a.chunk_shift) : a.n;  // entries
+  const int64_t nw = (n + 31) >> 5;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t w = w0 + tid + 256 * i;
     if (w < a.words) {
-      uint32_t x = local ? edge_bits(w, a.n, a.sink, a.window) : (u[i] | edge_bits(w, a.n, a.keep_first, a.keep_last));
-      if (w == a.words - 1 && (a.n & 31)) x &= (1u << (a.n & 31)) - 1u;
+      uint32_t x = local ? edge_bits(w, n, a.sink, a.window) : (u[i] | edge_bits(w, n, a.keep_first, a.keep_last));
+      if (w >= nw) x = 0u;
+      if (w == nw - 1 && (n & 31)) x &= (1u << (n & 31)) - 1u;
       a.ubits[grp * a.words + w] = x;
       c += __popc(x);
     }
@@ -1561,6 +1604,9 @@ LongArgs long_args(const Plan& p, char* ws) {
   a.bits = at<uint32_t>(ws, p.o_bits);
   a.words = p.words;
   a.status = at<uint32_t>(ws, p.o_status);
+  a.ctx_len = at<int32_t>(ws, p.o_ctx);
+  a.n_ctx = c.n_ctx;
+  a.chunk_shift = p.chunk_shift;
   return a;
 }
 
@@ -1583,6 +1629,9 @@ int union_impl(const Plan& p, char* ws, hipStream_t st) {
   u.keep_last = c.keep_last;
   u.sink = c.sink;
   u.window = c.window;
+  u.ctx_len = at<int32_t>(ws, p.o_ctx);
+  u.n_ctx = c.n_ctx;
+  u.chunk_shift = p.chunk_shift;
   const dim3 grid(p.ranges, c.n_kv_heads, c.batch);
   hipLaunchKernelGGL(k_union_count, grid, dim3(256), 0, st, u);
   hipLaunchKernelGGL(k_union_write, grid, dim3(256), 0, st, u);
@@ -1619,6 +1668,9 @@ GroupSelArgs group_args(const Plan& p, char* ws, int level) {
   a.keep_last = c.keep_last;
   a.sink = c.sink;
   a.window = c.window;
+  a.ctx_len = at<int32_t>(ws, p.o_ctx);
+  a.n_ctx = c.n_ctx;
+  a.chunk_shift = p.chunk_shift;
   return a;
 }
 
@@ -1641,6 +1693,9 @@ int launch_select(const Plan& p, int level, char* ws, void* stream) {
     ca.imp = at<double>(ws, p.o_cimp);
     ca.sorted = at<double>(ws, p.o_csort);
     ca.budget = at<int32_t>(ws, p.o_budget);
+    ca.ctx_len = at<int32_t>(ws, p.o_ctx);
+    ca.n_ctx = c.n_ctx;
+    ca.chunk_shift = p.chunk_shift;
     const int L = int(p.len0);
     hipLaunchKernelGGL(k_cov_mass, dim3(Hq, B), dim3(kCovThreads), 0, st, ca);
     hipLaunchKernelGGL(k_cov_importance, dim3((L + kCovThreads - 1) / kCovThreads, B), dim3(kCovThreads), 0, st, ca);
@@ -1722,6 +1777,9 @@ int launch_long_rows(const LongRows& r, void* stream) {
   a.bits = r.bits;
   a.words = r.words;
   a.status = r.status;
+  a.ctx_len = nullptr;  // caller-given rows are whole
+  a.n_ctx = r.len;
+  a.chunk_shift = 0;
   const dim3 rows(r.H, r.B), blocks(a.nb1, r.H, r.B);
   hipLaunchKernelGGL(k_long_hist, blocks, dim3(kLongThreads), 0, st, a);
   hipLaunchKernelGGL(k_long_find1, rows, dim3(kFindThreads), 0, st, a);

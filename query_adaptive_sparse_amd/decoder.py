@@ -45,9 +45,13 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def make_tensors(q, K, V, Kg=None, Vg=None, Kmg=None, Kp=None, P=None) -> N.sd_tensors:
-    """sd_tensors from torch tensors (q [B][Hq][d] or [B][T][Hq][d]; K, V [Bkv][Hkv][N][d]; ...)."""
+def make_tensors(q, K, V, Kg=None, Vg=None, Kmg=None, Kp=None, P=None, ctx_len=None) -> N.sd_tensors:
+    """sd_tensors from torch tensors (q [B][Hq][d] or [B][T][Hq][d]; K, V [Bkv][Hkv][N][d]; ...);
+    ``ctx_len``: an optional device int32 [B] of the tokens each sequence's cache holds this step."""
     t = N.sd_tensors()
+    if ctx_len is not None:
+        assert ctx_len.dtype == torch.int32 and ctx_len.is_contiguous() and ctx_len.numel() == q.shape[0]
+        t.ctx_len = ctx_len.data_ptr()
     t.q = _ptr(q)
     if q.dim() == 4:
         t.q_sb, t.q_st, t.q_sh = q.stride(0), q.stride(1), q.stride(2)

@@ -53,7 +53,7 @@ class sd_tensors(ctypes.Structure):
         ("g_sb", ctypes.c_int64), ("g_sh", ctypes.c_int64), ("g_st", ctypes.c_int64),
         ("kmg", ctypes.c_void_p), ("mg_sb", ctypes.c_int64), ("mg_sh", ctypes.c_int64), ("mg_st", ctypes.c_int64),
         ("kp", ctypes.c_void_p), ("kp_sb", ctypes.c_int64), ("kp_sh", ctypes.c_int64), ("kp_st", ctypes.c_int64),
-        ("proj", ctypes.c_void_p),
+        ("proj", ctypes.c_void_p), ("ctx_len", ctypes.c_void_p),
     ]
 
 

@@ -508,7 +508,97 @@ def pin_multi_query(ref, seed=11):
             assert np.allclose(res["lse"][b, qi], l2, rtol=1e-11, atol=1e-11), w.mode
 
 
+class _CutSrc:
+    """The same caches cut to their first n tokens (n // chunk_size summary rows)."""
+
+    def __init__(self, src, n, chunk):
+        m = n // chunk
+        self.q, self.P = src.q, src.P
+        self.K, self.V, self.Kp = src.K[:, :, :n], src.V[:, :, :n], src.Kp[:, :, :n]
+        self.Kg, self.Vg = src.Kg[:, :, :m], src.Vg[:, :, :m]
+        self.Kmg = src.Kmg
+
+    def kv_rows(self, bk, g, rows):
+        return self.K[bk, g][rows], self.V[bk, g][rows]
+
+
+def pin_growing_cache(ref, seed=12):
+    """Caches holding n_b tokens of a larger capacity (a growing cache): (1) when n_b is whole
+    chunks, every selection and output equals the oracle on the caches cut to n_b tokens (forced
+    chunks and local windows follow n_b; nothing past it is read); (2) with everything selected
+    (k = all, p = 1) a step is dense attention (torch SDPA, fp64) over the n_b raw tokens plus the
+    complete chunks' summaries, the incomplete last chunk's tokens included without a summary; a
+    cache with no complete chunk attends its tokens alone, and an empty one gives o = 0, lse = -inf;
+    (3) a sparse step is dense attention masked to the union's chunk rows, the incomplete chunk's
+    tokens and the union's summaries (per-head masks: the head's own set, the forced chunks and the
+    incomplete chunk's tokens)."""
+    rng = np.random.default_rng(seed)
+    # (1) whole chunks: the oracle on the cut caches
+    for w in (_tiny_workload("topk", keep_first=1, keep_last=2), _tiny_workload("topp", top_p=0.7, keep_last=1),
+              _tiny_workload("coverage", tau=0.3),
+              _tiny_workload("proxy", chunk_size=1, top_p=0.6, attend_summary=False, local_kv_heads=(1,),
+                             sink=3, window=9)):
+        src = _Src(w, rng)
+        ctx = [64, 80] if w.chunk_size > 1 else [41, 77]
+        res = ref.decode_step(w, src, ctx_len=ctx)
+        for b in range(w.batch):
+            wc = SimpleNamespace(**{**vars(w), "n_ctx": ctx[b]})
+            cut = ref.decode_step(wc, _CutSrc(src, ctx[b], w.chunk_size), groups=[(b, g) for g in range(w.n_kv_heads)])
+            for g in range(w.n_kv_heads):
+                r, rc = res["sel"][(b, g)], cut["sel"][(b, g)]
+                assert r["union"].tolist() == rc["union"].tolist(), (w.mode, b, g)
+                for h in r["heads"]:
+                    assert r["heads"][h].tolist() == rc["heads"][h].tolist(), (w.mode, b, h)
+            assert np.array_equal(res["out"][b], cut["out"][b]) and np.array_equal(res["lse"][b], cut["lse"][b]), w.mode
+    # (2) everything selected: dense attention over the valid tokens and complete summaries
+    for w, ctx in ((_tiny_workload("topk", top_k=50), [83, 61]), (_tiny_workload("topp", top_p=1.0), [5, 8]),
+                   (_tiny_workload("topk", top_k=50), [0, 17]),
+                   (_tiny_workload("proxy", chunk_size=1, top_p=1.0, attend_summary=False, local_kv_heads=(1,),
+                                   sink=4, window=11), [50, 93])):
+        src = _Src(w, rng)
+        res = ref.decode_step(w, src, ctx_len=ctx)
+        G = w.n_q_heads // w.n_kv_heads
+        for b in range(w.batch):
+            n, m = ctx[b], ctx[b] // w.chunk_size
+            for g in range(w.n_kv_heads):
+                qs = slice(g * G, (g + 1) * G)
+                if n == 0:
+                    assert np.all(res["out"][b, qs] == 0.0) and np.all(res["lse"][b, qs] == -np.inf)
+                    continue
+                if g in w.local_kv_heads:
+                    rows = np.union1d(np.arange(min(w.sink, n)), np.arange(max(0, n - w.window), n))
+                    Kc, Vc = src.K[b, g][rows], src.V[b, g][rows]
+                elif w.attend_summary and w.mode != "proxy":
+                    Kc = np.concatenate([src.K[b, g][:n], src.Kg[b, g][:m]])
+                    Vc = np.concatenate([src.V[b, g][:n], src.Vg[b, g][:m]])
+                else:
+                    Kc, Vc = src.K[b, g][:n], src.V[b, g][:n]
+                o2, l2 = _sdpa(src.q[b, qs], Kc, Vc, w.softmax_scale)
+                assert np.allclose(res["out"][b, qs], o2, rtol=1e-11, atol=1e-11), (w.mode, b, g)
+                assert np.allclose(res["lse"][b, qs], l2, rtol=1e-11, atol=1e-11), (w.mode, b, g)
+    # (3) sparse steps with an incomplete last chunk: masked dense attention
+    for w, ctx in ((_tiny_workload("topp", top_p=0.7, keep_last=1), [83, 45]),
+                   (_tiny_workload("topk", top_k=2, keep_first=1, head_masks=True), [70, 91])):
+        src = _Src(w, rng)
+        res = ref.decode_step(w, src, ctx_len=ctx)
+        G = w.n_q_heads // w.n_kv_heads
+        for (b, g), r in res["sel"].items():
+            n, m = ctx[b], ctx[b] // w.chunk_size
+            assert all(int(e) < m for e in r["union"]), "selected past the complete chunks"
+            forced = [e for e in range(m) if e < w.keep_first or e >= m - w.keep_last]
+            Kc = np.concatenate([src.K[b, g], src.Kg[b, g]])
+            Vc = np.concatenate([src.V[b, g], src.Vg[b, g]])
+            for j in range(G):
+                h = g * G + j
+                chunks = sorted(set(r["heads"][h].tolist()) | set(forced)) if w.head_masks else r["union"].tolist()
+                mask = [c * w.chunk_size + t for c in chunks for t in range(w.chunk_size)]
+                mask += list(range(m * w.chunk_size, n)) + [w.n_ctx + c for c in chunks]
+                o2, l2 = _sdpa(src.q[b, h][None], Kc, Vc, w.softmax_scale, mask=np.array(mask))
+                assert np.allclose(res["out"][b, h], o2[0], rtol=1e-11, atol=1e-11), (w.mode, b, h)
+                assert np.allclose(res["lse"][b, h], l2[0], rtol=1e-11, atol=1e-11), (w.mode, b, h)
+
+
 ALL_PINS = [pin_golden_scores, pin_golden_proxy, pin_golden_topk, pin_golden_topp, pin_golden_two_level,
             pin_golden_union, pin_golden_attention, pin_scores_exact, pin_bruteforce, pin_topp_minimal,
             pin_reductions, pin_union, pin_masked_dense, pin_dense_limits, pin_step_masked,
-            pin_step_selection, pin_variants, pin_coverage, pin_multi_query]
+            pin_step_selection, pin_variants, pin_coverage, pin_multi_query, pin_growing_cache]

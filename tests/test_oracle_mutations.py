@@ -47,6 +47,14 @@ MUTATIONS = {
     "coverage_unnormalized": ("imp = imp + mass / math.fsum(mass.tolist())", "imp = imp + mass"),
     "coverage_descending": ("order = np.lexsort((-np.arange(n), imp))", "order = np.lexsort((-np.arange(n), -imp))"),
     "all_summaries_only_selected": ("srows = np.arange(n_ent) if all_sum else", "srows = np.asarray(S, dtype=np.int64) if all_sum else"),
+    "growing_tail_dropped": ("tail = np.arange(n_ent * w.chunk_size, n_tok)", "tail = np.arange(0)"),
+    "growing_scores_past_cache": ("s = chunk_scores(q, src.Kg[bk, g][:n_ent])\n            sel = select_top_k",
+                                  "s = chunk_scores(q, src.Kg[bk, g])\n            sel = select_top_k"),
+    "growing_forced_at_capacity": ("U = group_union([U, edge_entries(n_ent, w.keep_first, w.keep_last)])",
+                                   "U = group_union([U, edge_entries(w.n_ctx // w.chunk_size, w.keep_first, w.keep_last)])"),
+    "growing_proxy_past_cache": ("proxy_scores(qp, src.Kp[bk, g][:n_tok])", "proxy_scores(qp, src.Kp[bk, g])"),
+    "growing_window_at_capacity": ("res[\"union\"] = edge_entries(n_ent, w.sink, w.window)",
+                                   "res[\"union\"] = edge_entries(w.n_ctx // w.chunk_size, w.sink, w.window)"),
 }
 
 
