@@ -125,11 +125,13 @@ def cpu_baseline(w, inp, target_s=15.0, max_groups=0):
     host = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in inp.items()}
     src = HostSource(host)
     done, clk = 0, _OracleClock()
+    margin = float("inf")
     while True:
         b, g = order[done % len(order)]
         with clk:
             r = ref.select_group(w, src, b, g)
             ref.attend_group(w, src, b, g, r["union"], r["heads"])
+        margin = min(margin, r["margin"])
         t_total = clk.wall
         done += 1
         if (max_groups and done >= max_groups) or (not max_groups and t_total >= target_s):
@@ -140,7 +142,17 @@ def cpu_baseline(w, inp, target_s=15.0, max_groups=0):
             "sample": f"{done} (sequence, KV group) units of {w.name} ({len(groups)} per step, cycled): "
                       f"selection + attention, {t_total:.1f} s, scaled to a full step ({step_s:.2f} s); "
                       f"cores = process CPU time / wall time (BLAS pool {_blas_pool()} threads)",
-            "cpu": _cpu_model()}
+            "min_selection_margin": None if margin == float("inf") else float(f"{margin:.3g}"),
+            **_host_info()}
+
+
+def _host_info() -> dict:
+    """The host the oracle ran on: CPU model, logical CPUs and the ones this process may use."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu": _cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": affinity}
 
 
 COUNTER_PROFILE = os.path.join(ROOT, "profiles", "c3_128k_attend_counters.md")
@@ -205,7 +217,7 @@ def prefill_cpu_baseline(w, inp, sel, target_s=15.0):
             "sample": f"{w.name}: importance of 1 of {w.batch * w.n_q_heads} heads ({t_imp:.1f} s), "
                       + ", ".join(notes) + f"; scaled to a full layer ({step_s:.0f} s); cores = process CPU "
                       f"time / wall time (BLAS pool {_blas_pool()} threads)",
-            "cpu": _cpu_model()}
+            **_host_info()}
 
 
 def bench_prefill(args, w):
@@ -314,7 +326,7 @@ def gist_cpu_baseline(w, inp, target_s=15.0):
             "sample": f"{w.name}: {done} of {n_rows} query rows (raw and gist, uniform) of 1 of "
                       f"{w.batch * w.n_q_heads} heads ({t_rows:.1f} s), scaled to a full layer ({step_s:.0f} s); "
                       f"cores = process CPU time / wall time (BLAS pool {_blas_pool()} threads)",
-            "cpu": _cpu_model()}
+            **_host_info()}
 
 
 def bench_gist(args, w):
@@ -461,7 +473,7 @@ def main():
     attend_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     print(f"[bench] timed {K} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
 
-    # per-stage breakdown (not part of the timed region)
+    # per-stage breakdown and per-step latency distribution (not part of the timed region)
     KS = min(K, 20)
     sv = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(KS)]
     for i in range(KS):
@@ -475,9 +487,16 @@ def main():
         e[2].record()
         dec.combine(out, lse)
         e[3].record()
+    ps = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(K):
+        ps[i][0].record()
+        dec.step(t, out, lse)
+        ps[i][1].record()
     torch.cuda.synchronize()
     route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in sv]))
     combine_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in sv]))
+    step_ev = np.array([e[0].elapsed_time(e[1]) for e in ps])
+    pct = {f"p{q}": round(float(np.percentile(step_ev, q)), 5) for q in (10, 50, 90)}
 
     sel = dec.selection()
     counts = sel["count"].cpu().numpy()
@@ -513,6 +532,7 @@ def main():
         "stages_ms": {"score_select": round(route_ms, 4), "attend": round(attend_ms, 4),
                       "combine": round(combine_ms, 4), "note": "score_select and combine from a separate "
                       "event-bracketed loop; attend from the timed steps"},
+        "step_ms_events": {**pct, "steps": K, "note": "one event pair around each whole step, separate loop"},
         "roofline": {"kernel": "k_attend (gathered split-K attention)", "bound": "hbm",
                      "achieved": round(attend_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attend_gbps / HBM_PEAK_GBPS, 4),
