@@ -587,7 +587,10 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float* __rest
   const int64_t NB = nb_attend;
   const int k0 = int(((t0 + 1) * NB - 1) / T);
   const int nt = int((t1 * NB - 1) / T) - k0 + 1;
-  auto live = [&](int k) { return (int64_t(k) * T) / NB < (int64_t(k + 1) * T) / NB; };
+  // with at least one tile per workgroup every slice is non-empty (no 64-bit divisions, which are
+  // slow on the GPU)
+  const bool all_live = T >= NB;
+  auto live = [&](int k) { return all_live || (int64_t(k) * T) / NB < (int64_t(k + 1) * T) / NB; };
   // max over the partials' lse
   float M = kNegInf;
   for (int j = tid; j < nt; j += NT)

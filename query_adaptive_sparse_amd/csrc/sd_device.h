@@ -131,6 +131,34 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __hiloint2double(hi, lo);
 }
 
+// max / min of two doubles as one instruction each, for values that come from arithmetic (never
+// signalling NaNs): fmax / fmin would first quiet an operand that passed through a branch or a
+// lane exchange with an extra instruction. A quiet NaN operand yields the other operand.
+__device__ __forceinline__ double max_f64(double x, double y) {
+  double r;
+  asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
+__device__ __forceinline__ double min_f64(double x, double y) {
+  double r;
+  asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
+
+// x clamped into [0, 1] (NaN to 0) with two instructions and inline constants
+__device__ __forceinline__ double clamp01_f64(double x) {
+  double r;
+  asm("v_max_f64 %0, %1, 0\n\tv_min_f64 %0, %0, 1.0" : "=&v"(r) : "v"(x));
+  return r;
+}
+
+// x clamped into [0, hi] (NaN to 0); hi is uniform (a scalar register)
+__device__ __forceinline__ double clamp0_f64(double x, double hi) {
+  double r;
+  asm("v_max_f64 %0, %1, 0\n\tv_min_f64 %0, %0, %2" : "=&v"(r) : "v"(x), "s"(hi));
+  return r;
+}
+
 // Row-of-16 reduction: every lane of a row ends with the row's result.
 #define SD_ROW_REDUCE(v, OP)                      \
   v = OP(v, dpp_f64<kDppQuadXor1>(v));            \

@@ -124,155 +124,156 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRo
     if (j0 + u < nh) out[(int64_t(b) * Hq + h0 + j0 + u) * out_len + row] = acc[u];
 }
 
-// Projected query q_p = q P (d -> 16) per scored head, fp64, index order. A bf16 or fp32 query
-// times an fp32 projection entry is exact in fp64.
+// Projected query q_p = q P (d -> 16) per head, fp64, one fma chain in index order per output. A
+// bf16 or fp32 query element times an fp32 projection entry is exact in fp64, so every step rounds
+// only the sum, as the sequential CPU evaluation does. One workgroup per (KV group, sequence): the
+// group's projection and its heads' queries are staged in LDS with one round of coalesced loads,
+// then one lane per (head, proxy dim) runs the chain. Local groups get zeros. Workgroup (0, 0)
+// also clears the status words and the per-group arrival counters and publishes the step's cache
+// lengths.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_proxy_query(const T* __restrict__ q, QRows qm,
                                                      const float* __restrict__ proj, int G, int Hq,
                                                      uint64_t local_mask, double* __restrict__ qp,
                                                      uint32_t* __restrict__ status, int32_t* __restrict__ arrivals,
                                                      int n_groups, StepLens lens) {
-  const int b = blockIdx.y;
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (blockIdx.x == 0 && b == 0) {
-    if (threadIdx.x < 16) status[threadIdx.x] = 0;
-    for (int i = threadIdx.x; i < n_groups; i += 256) arrivals[i] = 0;
-    lens.publish(threadIdx.x, 256);
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  if (g == 0 && b == 0) {
+    if (tid < 16) status[tid] = 0;
+    for (int i = tid; i < n_groups; i += 256) arrivals[i] = 0;
+    lens.publish(tid, 256);
   }
-  const int h = t >> 4, j = t & 15;
-  if (h >= Hq) return;
-  const int g = h / G;
-  double acc = 0.0;
-  if (!((local_mask >> g) & 1)) {
-    const float* P = proj + int64_t(g) * D * 16;
-    const T* qh = q + q_offset(qm, b, h);
-    for (int i = 0; i < D; ++i) acc = fma(double(elem_f32<T>(qh + i)), double(P[i * 16 + j]), acc);
+  double* out = qp + (int64_t(b) * Hq + int64_t(g) * G) * 16;
+  if ((local_mask >> g) & 1) {
+    for (int o = tid; o < G * 16; o += 256) out[o] = 0.0;
+    return;
   }
-  qp[(int64_t(b) * Hq + h) * 16 + j] = acc;
+  __shared__ float Ps[D * 16];
+  __shared__ float Qs[kMaxProxyGroup * D];
+  constexpr int PPT = D * 16 / 256;  // projection entries per thread
+  static_assert(PPT * 256 == D * 16, "256 threads cover the projection");
+  const float* P = proj + int64_t(g) * D * 16;
+  float pv[PPT];
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) pv[k] = P[tid + 256 * k];
+  for (int i = tid; i < G * D; i += 256) {
+    const int hh = i / D;
+    Qs[i] = elem_f32<T>(q + q_offset(qm, b, g * G + hh) + (i - hh * D));
+  }
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) Ps[tid + 256 * k] = pv[k];
+  __syncthreads();
+  for (int o = tid; o < G * 16; o += 256) {
+    const int hh = o >> 4, j = o & 15;
+    double acc = 0.0;
+#pragma unroll 16
+    for (int i = 0; i < D; ++i) acc = fma(double(Qs[hh * D + i]), double(Ps[i * 16 + j]), acc);
+    out[o] = acc;
+  }
 }
 
 // Proxy scores s_t = q_p . k_p[t] over the 16 proxy dims, separate multiply and add in index
-// order (q_p has 53 significant bits, so the products round). One 512-thread workgroup per
-// kMinMaxBlock tokens of one scored KV group; each thread takes 4 tokens 512 apart, and the group's
-// G heads share each token's proxy key. The workgroup projects the group's queries itself (q_p =
-// q P, fp64 in index order, the same arithmetic as k_proxy_query) while the key loads are in
-// flight, and writes its max and min per head.
-// Workgroup (0, 0, 0) clears the status words and the per-group arrival counters.
+// order (q_p has 53 significant bits, so the products round). q_p comes from k_proxy_query, which
+// runs first in the step. One 256-thread workgroup per kMinMaxBlock tokens of one scored KV group;
+// each thread takes kProxyTok tokens 256 apart, two at a time: the next pair's keys are loaded
+// while the current pair is scored. A pair's keys are converted to fp64 once and scored against
+// every head of the group, two heads at a time: their q_p values are the same for every lane, so
+// they are read with uniform loads into scalar registers (q_p is read-only here and the outputs are
+// distinct restrict pointers, which lets the compiler use scalar loads). The workgroup writes its
+// max and min per head. GM bounds the group size (registers for the running max / min).
 struct ProxyArgs {
   const uint16_t* kp;
   int64_t kp_sb, kp_sh, kp_st;
-  const void* q;
-  QRows qm;
-  const float* proj;
   int G, Hq;
   int64_t N;
-  double* s0;
-  double* pmax;
-  double* pmin;
   int nblk;
-  uint32_t* status;
-  int32_t* arrivals;
-  int n_groups;
   StepLens lens;
   int8_t scored[kMaxKvHeads];  // blockIdx.y -> KV group
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
+constexpr int kProxyThreads = 256;
+constexpr int kProxyTok = kMinMaxBlock / kProxyThreads;  // tokens per thread
+static_assert(kProxyTok % 2 == 0, "tokens go in pairs");
+
+template <int GM>
+__global__ __launch_bounds__(kProxyThreads) void k_score_proxy(ProxyArgs a, const double* __restrict__ qp,
+                                                               double* __restrict__ s0, double* __restrict__ pmax,
+                                                               double* __restrict__ pmin) {
+  constexpr int NT = kProxyThreads, NW = NT / 64;
   const int b = blockIdx.z, g = a.scored[blockIdx.y], tid = threadIdx.x;
   const int G = a.G;
-  __shared__ double qs[kMaxProxyGroup][16];
-  __shared__ double rmax[kMaxProxyGroup][8], rmin[kMaxProxyGroup][8];
-  if (blockIdx.x == 0 && blockIdx.y == 0 && b == 0) {
-    if (tid < 16) a.status[tid] = 0;
-    for (int i = tid; i < a.n_groups; i += 512) a.arrivals[i] = 0;
-    a.lens.publish(tid, 512);
-  }
+  __shared__ double rmax[GM][NW], rmin[GM][NW];
   const int64_t n_b = a.lens.entries(b, a.N);  // this sequence's tokens
-  // The group's projection and queries are loaded first (one unrolled round into registers, from
-  // clamped rows, so every load is issued before any is used), then the tokens' proxy keys; the
-  // projection is staged in LDS and q_p = q P computed (one thread per (head, proxy dim), the
-  // index-order fma chain) while the key loads are still in flight.
-  __shared__ float Ps[D * 16];
-  __shared__ float Qs[kMaxProxyGroup][D];
-  constexpr int PPT = D * 16 / 512;              // projection entries per thread
-  constexpr int QPT = kMaxProxyGroup * D / 512;  // query slots per thread
-  static_assert(PPT * 512 == D * 16 && QPT * 512 == kMaxProxyGroup * D, "512 threads cover P and q");
-  const float* P = a.proj + int64_t(g) * D * 16;
-  float pv[PPT];
-  T qv[QPT];
-#pragma unroll
-  for (int k = 0; k < PPT; ++k) pv[k] = P[tid + 512 * k];
-#pragma unroll
-  for (int k = 0; k < QPT; ++k) {
-    const int i = tid + 512 * k, hh = i / D, e = i - hh * D;
-    qv[k] = static_cast<const T*>(a.q)[q_offset(a.qm, b, g * G + (hh < G ? hh : G - 1)) + e];
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the key loads
-  const int64_t t0 = int64_t(blockIdx.x) * kMinMaxBlock;
+  const int64_t t0 = int64_t(blockIdx.x) * kMinMaxBlock + tid;
   const uint16_t* kb = a.kp + b * a.kp_sb + int64_t(g) * a.kp_sh;
-  constexpr int TPT = kMinMaxBlock / 512;  // tokens per thread (512 threads)
-  uint4 raw[TPT][2];
+  const int64_t row0 = int64_t(b) * a.Hq + g * G;
+  auto load_pair = [&](uint4 (&dst)[2][2], int pr) {
 #pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    int64_t t = t0 + tid + 512 * k;
-    t = t < a.N ? t : a.N - 1;
-    raw[k][0] = ld16(kb + t * a.kp_st);
-    raw[k][1] = ld16(kb + t * a.kp_st + 8);
-  }
-  __builtin_amdgcn_sched_barrier(0);  // every key load is issued before P and q are staged
+    for (int k = 0; k < 2; ++k) {
+      int64_t t = t0 + int64_t(NT) * (2 * pr + k);
+      t = t < a.N ? t : a.N - 1;
+      dst[k][0] = ld16(kb + t * a.kp_st);
+      dst[k][1] = ld16(kb + t * a.kp_st + 8);
+    }
+  };
+  double mx[GM], mn[GM];
 #pragma unroll
-  for (int k = 0; k < PPT; ++k) Ps[tid + 512 * k] = pv[k];
-#pragma unroll
-  for (int k = 0; k < QPT; ++k) {
-    const int i = tid + 512 * k, hh = i / D, e = i - hh * D;
-    if (hh < G) Qs[hh][e] = elem_f32<T>(&qv[k]);
-  }
-  __syncthreads();
-  if (tid < G * 16) {
-    const int hh = tid >> 4, j = tid & 15;
-    double acc = 0.0;
-#pragma unroll 16
-    for (int i = 0; i < D; ++i) acc = fma(double(Qs[hh][i]), double(Ps[i * 16 + j]), acc);
-    qs[hh][j] = acc;
-  }
-  __syncthreads();
-  double mx[kMaxProxyGroup], mn[kMaxProxyGroup];
-#pragma unroll
-  for (int j = 0; j < kMaxProxyGroup; ++j) {
+  for (int j = 0; j < GM; ++j) {
     mx[j] = kNegInfD;
     mn[j] = kPosInfD;
   }
-  const int64_t row0 = int64_t(b) * a.Hq + g * G;
+  uint4 raw[2][2][2];
+  load_pair(raw[0], 0);
 #pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const int64_t t = t0 + tid + 512 * k;
-    const bool valid = t < n_b;
-    double kd[16];
-    const _Float16* h0 = reinterpret_cast<const _Float16*>(&raw[k][0]);
-    const _Float16* h1 = reinterpret_cast<const _Float16*>(&raw[k][1]);
+  for (int pr = 0; pr < kProxyTok / 2; ++pr) {
+    if (pr + 1 < kProxyTok / 2) load_pair(raw[(pr + 1) & 1], pr + 1);
+    double kd[2][16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      kd[u] = double(float(h0[u]));
-      kd[u + 8] = double(float(h1[u]));
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(&raw[pr & 1][k][0]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        kd[k][2 * u] = double(float(__builtin_bit_cast(_Float16, uint16_t(w[u] & 0xffffu))));
+        kd[k][2 * u + 1] = double(float(__builtin_bit_cast(_Float16, uint16_t(w[u] >> 16))));
+      }
     }
 #pragma unroll
-    for (int j = 0; j < kMaxProxyGroup; ++j) {
-      if (j < G) {
-        double acc = 0.0;
+    for (int h0 = 0; h0 < GM; h0 += 2) {
+      if (h0 < G) {
+        double q0[16], q1[16];
+        const double* qr0 = qp + (row0 + h0) * 16;
+        const double* qr1 = qp + (row0 + (h0 + 1 < G ? h0 + 1 : h0)) * 16;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) acc = acc + qs[j][u] * kd[u];
-        if (valid) {
-          a.s0[(row0 + j) * a.N + t] = acc;
-          mx[j] = fmax(mx[j], acc);
-          mn[j] = fmin(mn[j], acc);
+        for (int u = 0; u < 16; ++u) {
+          q0[u] = qr0[u];
+          q1[u] = qr1[u];
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int64_t t = t0 + int64_t(NT) * (2 * pr + k);
+          double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            acc0 = acc0 + q0[u] * kd[k][u];
+            acc1 = acc1 + q1[u] * kd[k][u];
+          }
+          if (t < n_b) {
+            s0[(row0 + h0) * a.N + t] = acc0;
+            mx[h0] = max_f64(mx[h0], acc0);
+            mn[h0] = min_f64(mn[h0], acc0);
+            if (h0 + 1 < G) {
+              s0[(row0 + h0 + 1) * a.N + t] = acc1;
+              mx[h0 + 1] = max_f64(mx[h0 + 1], acc1);
+              mn[h0 + 1] = min_f64(mn[h0 + 1], acc1);
+            }
+          }
         }
       }
     }
   }
   const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int j = 0; j < kMaxProxyGroup; ++j) {
+  for (int j = 0; j < GM; ++j) {
     if (j < G) {
       const double wx = wave_max_dpp(mx[j]), wn = wave_min_dpp(mn[j]);
       if (lane == 0) {
@@ -284,12 +285,13 @@ __global__ __launch_bounds__(512) void k_score_proxy(ProxyArgs a) {
   __syncthreads();
   if (tid < G) {
     double x = rmax[tid][0], y = rmin[tid][0];
-    for (int w = 1; w < 8; ++w) {
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
       x = fmax(x, rmax[tid][w]);
       y = fmin(y, rmin[tid][w]);
     }
-    a.pmax[(row0 + tid) * a.nblk + blockIdx.x] = x;
-    a.pmin[(row0 + tid) * a.nblk + blockIdx.x] = y;
+    pmax[(row0 + tid) * a.nblk + blockIdx.x] = x;
+    pmin[(row0 + tid) * a.nblk + blockIdx.x] = y;
   }
 }
 
@@ -341,33 +343,32 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
   // first kernel of the step (level 0)
   const StepLens lens{t.ctx_len, level == 0 ? at<int32_t>(ws, p.o_ctx) : nullptr, B, c.n_ctx, p.chunk_shift};
   if (c.route == SD_ROUTE_PROXY) {
-    if (p.n_scored == 0) {  // every group is local: only the status words and counters need clearing
-      const int nb = (Hq * 16 + 255) / 256;
-      hipLaunchKernelGGL((k_proxy_query<T, D>), dim3(nb, B), dim3(256), 0, st, static_cast<const T*>(t.q), qm,
-                         t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status,
-                         at<int32_t>(ws, p.o_arrive), p.n_arrive, lens);
-    } else {
+    // the projected queries (this launch also clears the status words and counters and publishes
+    // the step's lengths), then the proxy scores of the scored groups
+    hipLaunchKernelGGL((k_proxy_query<T, D>), dim3(Hk, B), dim3(256), 0, st, static_cast<const T*>(t.q), qm,
+                       t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status,
+                       at<int32_t>(ws, p.o_arrive), p.n_arrive, lens);
+    if (p.n_scored > 0) {
       ProxyArgs pa;
       pa.kp = static_cast<const uint16_t*>(t.kp);
       pa.kp_sb = t.kp_sb;
       pa.kp_sh = t.kp_sh;
       pa.kp_st = t.kp_st;
-      pa.q = t.q;
-      pa.qm = qm;
-      pa.proj = t.proj;
       pa.G = p.G;
       pa.Hq = Hq;
       pa.N = c.n_ctx;
-      pa.s0 = at<double>(ws, p.o_s0);
-      pa.pmax = at<double>(ws, p.o_pmax);
-      pa.pmin = at<double>(ws, p.o_pmin);
       pa.nblk = p.score_blocks0;
-      pa.status = status;
-      pa.arrivals = at<int32_t>(ws, p.o_arrive);
-      pa.n_groups = p.n_arrive;
-      pa.lens = lens;
+      pa.lens = StepLens{t.ctx_len, nullptr, B, c.n_ctx, p.chunk_shift};
       for (int i = 0; i < kMaxKvHeads; ++i) pa.scored[i] = i < p.n_scored ? p.scored[i] : 0;
-      hipLaunchKernelGGL((k_score_proxy<T, D>), dim3(p.score_blocks0, p.n_scored, B), dim3(512), 0, st, pa);
+      const double* qpw = at<double>(ws, p.o_qp);
+      double *s0 = at<double>(ws, p.o_s0), *pmx = at<double>(ws, p.o_pmax), *pmn = at<double>(ws, p.o_pmin);
+      const dim3 grid(p.score_blocks0, p.n_scored, B), blk(kProxyThreads);
+      if (p.G <= 2)
+        hipLaunchKernelGGL(k_score_proxy<2>, grid, blk, 0, st, pa, qpw, s0, pmx, pmn);
+      else if (p.G <= 4)
+        hipLaunchKernelGGL(k_score_proxy<4>, grid, blk, 0, st, pa, qpw, s0, pmx, pmn);
+      else
+        hipLaunchKernelGGL(k_score_proxy<kMaxProxyGroup>, grid, blk, 0, st, pa, qpw, s0, pmx, pmn);
     }
     return int(hipGetLastError());
   }

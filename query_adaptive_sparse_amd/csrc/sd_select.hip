@@ -74,7 +74,10 @@ struct FixW {
 __device__ __forceinline__ FixW fix_of(double w) {
   const double x = w * 0x1p39;  // exact: a power-of-two scaling
   const double h = floor(x);
-  return FixW{uint64_t(h), uint64_t((x - h) * 0x1p40)};  // x - h and the scaling are exact
+  const double f = floor((x - h) * 0x1p40);  // x - h and the scaling are exact
+  // h and f are integers below 2^52: added to 2^52 they sit in the low mantissa bits
+  constexpr uint64_t kMant = (uint64_t(1) << 52) - 1;
+  return FixW{uint64_t(__double_as_longlong(h + 0x1p52)) & kMant, uint64_t(__double_as_longlong(f + 0x1p52)) & kMant};
 }
 __device__ __forceinline__ double fix_value(uint64_t hi, uint64_t lo) {
   hi += lo >> kFixLoBits;  // whole 2^-39 units of the low word
@@ -546,6 +549,26 @@ __global__ __launch_bounds__(kSelT) void k_union_small(GroupSelArgs a) {
   for (int w = 0; w < wv; ++w) pos += wcnt[w];
   const int64_t grp = int64_t(b) * a.Hk + g;
   int32_t* out = a.list + grp * a.n_entries;
+  if (uwords <= kSmallRowMax / 32) {
+    // rows of at most kSmallRowMax entries: the list is expanded in LDS, then copied out with
+    // coalesced stores
+    __shared__ int32_t stage[kSmallRowMax];
+    __shared__ int total;
+    for (int w = w0; w < min(uwords, w0 + per); ++w) {
+      uint32_t m = ubits[w];
+      while (m) {
+        const int bit = __ffs(m) - 1;
+        m &= m - 1;
+        stage[pos++] = w * 32 + bit;
+      }
+    }
+    if (tid == kSelT - 1) total = pos;
+    __syncthreads();
+    const int n = total;
+    for (int i = tid; i < n; i += kSelT) out[i] = stage[i];
+    if (tid == 0) a.cnt[grp] = n;
+    return;
+  }
   for (int w = w0; w < min(uwords, w0 + per); ++w) {
     uint32_t m = ubits[w];
     while (m) {
@@ -567,9 +590,10 @@ __global__ __launch_bounds__(kSelT) void k_union_small(GroupSelArgs a) {
 // so they do not depend on the order of the atomic adds. Passes:
 //   hist     per slab of kLongBlock entries: coarse bin of every entry (kept, 2 bytes), partial
 //            coarse histogram (no atomics across workgroups);
-//   find1    per row: bin totals (slab partials summed as integers), Z and the target, the
-//            crossing coarse bin and the weight ahead of it;
-//   mark     per slab: bitmap words of the entries of earlier coarse bins, the number of the
+//   sum      per row: bin totals (slab partials summed as integers), spread over many workgroups;
+//   mark     per slab: Z, the target, the crossing coarse bin and the weight ahead of it (each
+//            workgroup of the row scans the totals itself), bitmap words of the entries of
+//            earlier coarse bins, the number of the
 //            crossing bin's entries in the slab and (up to kResolveCap of them) their indices in
 //            the slab's own region of the resolution buffer;
 //   resolve  per row: when the crossing bin holds at most kResolveCap entries, they are split by a
@@ -617,7 +641,7 @@ __device__ __forceinline__ int64_t long_len(const LongArgs& a, int b) {
 
 __device__ __forceinline__ double coarse_pos(double s, double smax, double binscale) {
   const double d = (smax - s) * binscale;
-  return d >= 0.0 ? (d < double(kBins1) ? d : double(kBins1)) : 0.0;  // NaN -> 0
+  return clamp0_f64(d, double(kBins1));  // NaN -> 0
 }
 // Bin axis of a long row. Default: linear in the score from the row max (kBins1 bins over the
 // row's range), the right axis for exp weights. With bitbins (nonnegative values: importances,
@@ -645,8 +669,57 @@ __device__ __forceinline__ int ident_exp(double smax) {
   frexp(smax, &e);  // smax = f 2^e, f in [0.5, 1)
   return e;
 }
-__device__ __forceinline__ double long_weight(const LongArgs& a, double smax, int wexp, double s) {
-  return a.topp ? (a.ident ? ldexp(s, -wexp) : exp(a.scale * s - a.scale * smax)) : 1.0;
+// Softmax weights of a long top-p row, exp(x) with x = scale s - scale smax <= 0. Let dx =
+// scale / binscale be the coarse bin width in logits. An entry of coarse bin c has r = x + c dx in
+// (-dx, 0] (up to rounding), so exp(x) = exp(-c dx) exp(r): exp at the bin's edge (one table entry
+// per bin) times a degree-9 Taylor polynomial of r, whose truncation error is below
+// dx^10 / 10! < 2^-61 when dx <= 1/16. Rows with wider bins take exp itself. Every kernel of the
+// row weighs an entry through here (the histogram through a table of the same edge values), so the
+// fixed-point sums of every pass agree bit for bit.
+constexpr double kTaylorMaxDx = 0.0625;
+__device__ __forceinline__ bool taylor_row(const LongArgs& a, double binscale) {
+  return a.topp && !a.ident && !a.bitbins && binscale > 0.0 && a.scale / binscale <= kTaylorMaxDx;
+}
+__device__ __forceinline__ double bin_edge_exp(const LongArgs& a, double binscale, int c) {
+  return exp(-double(c) * (a.scale / binscale));
+}
+// Taylor coefficients 1/9!, 1/8!, ..., 1/1!, 1/0! (Horner order). A kernel that evaluates many
+// weights first moves them into scalar registers (taylor_sgpr), so that the fma operands need no
+// per-entry copies.
+struct TaylorC {
+  double c[10];
+};
+__device__ __forceinline__ TaylorC taylor_consts() {
+  return TaylorC{{1.0 / 362880.0, 1.0 / 40320.0, 1.0 / 5040.0, 1.0 / 720.0, 1.0 / 120.0, 1.0 / 24.0, 1.0 / 6.0, 0.5,
+                  1.0, 1.0}};
+}
+__device__ __forceinline__ TaylorC taylor_sgpr() {
+  TaylorC t = taylor_consts();
+#pragma unroll
+  for (int i = 0; i < 10; ++i) asm volatile("" : "+s"(t.c[i]));  // opaque: kept in scalar registers
+  return t;
+}
+__device__ __forceinline__ double exp_in_bin(double x, int c, double dx, double edge, const TaylorC& tc) {
+  const double r = x + double(c) * dx;
+  double e = tc.c[0];
+#pragma unroll
+  for (int i = 1; i < 10; ++i) e = fma(e, r, tc.c[i]);
+  // into [0, 1]: r may round a hair above 0 in bin 0, and a NaN weight counts as 0
+  return clamp01_f64(edge * e);
+}
+// the weight of a top-p row without the bin tables: masses, or exp itself
+__device__ __forceinline__ double plain_weight(const LongArgs& a, double smax, int wexp, double s) {
+  return max_f64(a.ident ? ldexp(s, -wexp) : exp(a.scale * s - a.scale * smax), 0.0);  // NaN -> 0
+}
+__device__ __forceinline__ double long_weight(const LongArgs& a, double smax, double binscale, int wexp,
+                                              double s) {
+  if (!a.topp) return 1.0;
+  if (taylor_row(a, binscale)) {
+    const int c = coarse_bin(coarse_pos(s, smax, binscale));
+    return exp_in_bin(a.scale * s - a.scale * smax, c, a.scale / binscale, bin_edge_exp(a, binscale, c),
+                      taylor_consts());
+  }
+  return plain_weight(a, smax, wexp, s);
 }
 __device__ __forceinline__ int long_k(const LongArgs& a, int b) { return a.kbudget ? a.kbudget[b] : a.k; }
 
@@ -667,15 +740,22 @@ __device__ __forceinline__ double block_scan(double v, double* wtot, double* tot
   return before + incl;
 }
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 constexpr int kLongThreads = 1024;
-__global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
-  constexpr int NT = kLongThreads;
+constexpr int kHistThreads = 512;  // (1024 would cap the registers at 128 and spill)
+__global__ __launch_bounds__(kHistThreads) void k_long_hist(LongArgs a) {
+  constexpr int NT = kHistThreads;
   const int b = blockIdx.z, h = blockIdx.y, slab = blockIdx.x, tid = threadIdx.x;
   if ((a.local_mask >> (h / a.G)) & 1) return;
   const int64_t row = int64_t(b) * a.Hq + h;
   __shared__ unsigned long long hh[kBins1], hl[kBins1];
   __shared__ uint32_t hc[kBins1];
   __shared__ double rmax[NT / 64], rmin[NT / 64];
+  __shared__ double ebin[kBins1];
   for (int i = tid; i < kBins1; i += NT) {
     hh[i] = 0;
     hl[i] = 0;
@@ -704,6 +784,12 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
   const int wexp = a.ident ? ident_exp(smax) : 0;
   const int64_t len = long_len(a, b);
   const bool all = len == 0 || (a.topp ? (a.p >= 1.0) : (int64_t(long_k(a, b)) >= len));
+  // softmax weights by bin (long_weight): the bins' edge values in LDS
+  const bool taylor = taylor_row(a, binscale);
+  const double dx = taylor ? a.scale / binscale : 0.0;
+  if (taylor)
+    for (int i = tid; i < kBins1; i += NT) ebin[i] = bin_edge_exp(a, binscale, i);
+  __syncthreads();
   if (slab == 0 && tid == 0) {
     RowInfo ri = {};
     ri.smax = smax;
@@ -714,7 +800,7 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
     a.info[row] = ri;
   }
   const int64_t t0 = int64_t(slab) * kLongBlock;
-  if (all || t0 >= len) return;  // slabs past the row's entries hold nothing (find1 skips them)
+  if (all || t0 >= len) return;  // slabs past the row's entries hold nothing (the bin sums skip them)
   const int64_t t1 = t0 + kLongBlock < len ? t0 + kLongBlock : len;
   const double* sr = a.s0 + row * a.len;
   uint16_t* br = a.cbin + row * a.cstride;
@@ -729,24 +815,43 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
       dst[k] = sr[t < t1 ? t : t1 - 1];
     }
   };
-  load(sv[0], 0);
+  // one weight path per instantiation, chosen once per row (a branch inside the unrolled loop
+  // would put both paths' code in the loop body)
+  auto bin_all = [&](auto taylor_tag) {
+    constexpr bool kTaylor = decltype(taylor_tag)::value;
+    const TaylorC tc = taylor_sgpr();
+    auto bin8 = [&](const double* vals, int it) {
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    if (it + 1 < kIters) load(sv[(it + 1) & 1], it + 1);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int64_t t = t0 + int64_t(it) * (NT * 8) + tid + NT * k;
-      if (t < t1) {
-        const double v = sv[it & 1][k];
-        const int c = coarse_bin(coarse_pos_of(a, v, smax, binscale));
-        br[t] = uint16_t(c);
-        if (a.topp)
-          fix_add(&hh[c], &hl[c], long_weight(a, smax, wexp, v));
-        else
-          atomicAdd(&hc[c], 1u);
+      for (int k = 0; k < 8; ++k) {
+        const int64_t t = t0 + int64_t(it) * (NT * 8) + tid + NT * k;
+        if (t < t1) {
+          const double v = vals[k];
+          // (Taylor rows are never bitbins rows)
+          const int c = coarse_bin(kTaylor ? coarse_pos(v, smax, binscale) : coarse_pos_of(a, v, smax, binscale));
+          br[t] = uint16_t(c);
+          if (a.topp) {
+            const double w = kTaylor ? exp_in_bin(a.scale * v - a.scale * smax, c, dx, ebin[c], tc)
+                                     : plain_weight(a, smax, wexp, v);
+            fix_add(&hh[c], &hl[c], w);
+          } else {
+            atomicAdd(&hc[c], 1u);
+          }
+        }
       }
+    };
+    static_assert(kIters % 2 == 0, "batches go in pairs");
+    load(sv[0], 0);
+    for (int it = 0; it < kIters; it += 2) {
+      load(sv[1], it + 1);
+      bin8(sv[0], it);
+      if (it + 2 < kIters) load(sv[0], it + 2);
+      bin8(sv[1], it + 1);
     }
-  }
+  };
+  if (taylor)
+    bin_all(BoolTag<true>{});
+  else
+    bin_all(BoolTag<false>{});
   __syncthreads();
   const int64_t o = (row * a.nb1 + slab) * kBins1;
   for (int i = tid; i < kBins1; i += NT) {
@@ -759,60 +864,40 @@ __global__ __launch_bounds__(kLongThreads) void k_long_hist(LongArgs a) {
   }
 }
 
-// Per row: coarse bin totals (slab partials summed as integers), Z and the target, the crossing
-// coarse bin and the weight ahead of it.
-constexpr int kFindThreads = kBins1;
-__global__ __launch_bounds__(kFindThreads) void k_long_find1(LongArgs a) {
-  const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+// Per row: the coarse bin totals, the slabs' partial histograms summed as integers (exact in any
+// order) into slab 0's slot. One lane per bin, a few bins per workgroup, so that many workgroups
+// share the row's partials.
+constexpr int kSumThreads = 64;
+static_assert(kBins1 % kSumThreads == 0, "bins split evenly over the sum workgroups");
+__global__ __launch_bounds__(kSumThreads) void k_long_sum(LongArgs a) {
+  const int b = blockIdx.z, h = blockIdx.y;
   if ((a.local_mask >> (h / a.G)) & 1) return;
   const int64_t row = int64_t(b) * a.Hq + h;
-  __shared__ double wtot[kFindThreads / 64];
-  __shared__ int hit_bin;
-  __shared__ double hit_before;
-  RowInfo ri = a.info[row];
-  if (ri.all) return;
-  double m;
-  const int64_t o = row * a.nb1 * kBins1 + tid;
+  if (a.info[row].all) return;
+  const int64_t o = row * a.nb1 * kBins1 + int64_t(blockIdx.x) * kSumThreads + threadIdx.x;
   const int nb = int((long_len(a, b) + kLongBlock - 1) / kLongBlock);  // slabs holding entries
   if (a.topp) {
-    unsigned long long sh = 0, sl = 0;
+    unsigned long long sh = a.h1h[o], sl = a.h1l[o];
 #pragma unroll 16
-    for (int sl_ = 0; sl_ < nb; ++sl_) {
+    for (int sl_ = 1; sl_ < nb; ++sl_) {
       sh += a.h1h[o + int64_t(sl_) * kBins1];
       sl += a.h1l[o + int64_t(sl_) * kBins1];
     }
-    m = fix_value(sh, sl);
+    a.h1h[o] = sh;
+    a.h1l[o] = sl;
   } else {
-    uint32_t cn = 0;
+    uint32_t cn = a.h1c[o];
 #pragma unroll 16
-    for (int sl_ = 0; sl_ < nb; ++sl_) cn += a.h1c[o + int64_t(sl_) * kBins1];
-    m = double(cn);
-  }
-  double Z;
-  const double incl = block_scan<kFindThreads>(m, wtot, &Z);
-  const double target = a.topp ? a.p * Z : double(long_k(a, b));
-  if (tid == 0) hit_bin = 0x7FFFFFFF;
-  __syncthreads();
-  const double excl = incl - m;
-  if (excl + m >= target) atomicMin(&hit_bin, tid);
-  __syncthreads();
-  const int bin1 = hit_bin;
-  if (bin1 == tid) hit_before = excl;
-  __syncthreads();
-  if (tid == 0) {
-    if (bin1 == 0x7FFFFFFF) {
-      ri.all = 1;  // rounding left the target above the total weight: keep every entry
-    } else {
-      ri.bin1 = bin1;
-      ri.before1 = hit_before;
-      ri.target = target;
-    }
-    a.info[row] = ri;
+    for (int sl_ = 1; sl_ < nb; ++sl_) cn += a.h1c[o + int64_t(sl_) * kBins1];
+    a.h1c[o] = cn;
   }
 }
 
-// Per slab: the row's bitmap (entries of coarse bins ahead of the crossing bin, or every entry
-// when the whole row is kept; zero for local heads), the number of the crossing bin's entries in
+// Per slab: the crossing coarse bin of the row (a scan of the bin totals that every workgroup of
+// the row repeats bit for bit: Z, the target, the first bin where the running weight reaches it
+// and the weight ahead of it; slab 0's workgroup records them for the resolution), the row's
+// bitmap (entries of coarse bins ahead of the crossing bin, or every entry when the whole row is
+// kept; zero for local heads), the number of the crossing bin's entries in
 // the slab and, up to kResolveCap of them, their indices in the slab's region of the resolution
 // buffer. Each lane takes 8 consecutive entries (one 16-byte load of their bins, all of a slab's
 // loads issued at once) and writes their 8 bits as one byte of the bitmap.
@@ -831,11 +916,15 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
     if (tid == 0 && t1 <= t0 && !((a.local_mask >> (h / a.G)) & 1)) a.ccnt[row * a.nb1 + slab] = 0;
     return;
   }
-  __shared__ int scnt;
-  if (tid == 0) scnt = 0;
+  static_assert(NT == kBins1, "one lane per coarse bin in the crossing scan");
+  __shared__ int scnt, hit_bin;
+  __shared__ double btot[NT / 64], hit_before;
+  if (tid == 0) {
+    scnt = 0;
+    hit_bin = 0x7FFFFFFF;
+  }
   __syncthreads();
-  const RowInfo ri = a.info[row];
-  const bool gather = !ri.all;
+  const int all0 = a.info[row].all;
   const uint16_t* br = a.cbin + row * a.cstride;
   uint8_t* bb = reinterpret_cast<uint8_t*>(bw);
   int32_t* out = a.cidx + (row * a.nb1 + slab) * kResolveCap;
@@ -848,8 +937,36 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
     int64_t e = t0 + 8 * (int64_t(tid) + NT * v);
     const int64_t last = (t1 - 1) & ~int64_t(7);
     e = e < last ? e : last;
-    pc[v] = ri.all ? make_uint4(0, 0, 0, 0) : ld16(br + e);
+    pc[v] = all0 ? make_uint4(0, 0, 0, 0) : ld16(br + e);
   }
+  bool all = all0;
+  int bin1 = 0;
+  if (!all0) {
+    const int64_t o = row * a.nb1 * kBins1 + tid;
+    const double m = a.topp ? fix_value(a.h1h[o], a.h1l[o]) : double(a.h1c[o]);
+    double Z;
+    const double incl = block_scan<NT>(m, btot, &Z);
+    const double target = a.topp ? a.p * Z : double(long_k(a, b));
+    const double excl = incl - m;
+    const unsigned long long reach = __ballot(excl + m >= target);  // bins in lane order
+    if (reach && lane == __ffsll(reach) - 1) atomicMin(&hit_bin, tid);
+    __syncthreads();
+    bin1 = hit_bin;
+    if (bin1 == tid) hit_before = excl;
+    __syncthreads();
+    all = bin1 == 0x7FFFFFFF;  // rounding left the target above the total weight: keep every entry
+    if (slab == 0 && tid == 0) {
+      RowInfo* ri = a.info + row;
+      if (all) {
+        ri->all = 1;
+      } else {
+        ri->bin1 = bin1;
+        ri->before1 = hit_before;
+        ri->target = target;
+      }
+    }
+  }
+  const bool gather = !all;
 #pragma unroll
   for (int v = 0; v < kVec; ++v) {
     const int64_t e0 = t0 + 8 * (int64_t(tid) + NT * v);
@@ -858,8 +975,8 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const bool valid = e0 + u < t1;
-      sel |= (valid && (ri.all || cb[u] < ri.bin1)) ? (1u << u) : 0u;
-      cand |= (gather && valid && cb[u] == ri.bin1) ? (1u << u) : 0u;
+      sel |= (valid && (all || cb[u] < bin1)) ? (1u << u) : 0u;
+      cand |= (gather && valid && cb[u] == bin1) ? (1u << u) : 0u;
     }
     if (e0 < ((t1c + 31) & ~int64_t(31))) bb[e0 >> 3] = uint8_t(sel);  // whole words, zero past the entries
     const int nc = __popc(cand);
@@ -933,7 +1050,7 @@ __device__ void resolve_radix(const LongArgs& a, const RowInfo& ri, int64_t row,
   const uint16_t* br = a.cbin + row * a.cstride;
   uint32_t* bw = a.bits + row * a.words;
   const int wexp = ri.wexp;
-  auto weight = [&](uint64_t k) { return long_weight(a, ri.smax, wexp, dkey_inv(k)); };
+  auto weight = [&](uint64_t k) { return long_weight(a, ri.smax, ri.binscale, wexp, dkey_inv(k)); };
   // key interval of the bin's entries
   uint64_t kmn = ~0ull, kmx = 0ull;
   for (int64_t t = tid; t < len; t += NT)
@@ -1186,7 +1303,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
     sb = sb < kSub - 1 ? sb : kSub - 1;
     sub[i] = uint16_t(sb);
     atomicAdd(&hc[sb], 1u);
-    if (a.topp) fix_add(&hh[sb], &hl[sb], long_weight(a, ri.smax, wexp, s));
+    if (a.topp) fix_add(&hh[sb], &hl[sb], long_weight(a, ri.smax, ri.binscale, wexp, s));
   }
   __syncthreads();
   constexpr int SPER = kSub / NT;
@@ -1245,24 +1362,15 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
         const uint64_t ku = xkey[u];
         r += (ku > kq || (ku == kq && xidx[u] < iq)) ? 1 : 0;
       }
-      xw[r] = long_weight(a, ri.smax, wexp, dkey_inv(kq));
+      xw[r] = long_weight(a, ri.smax, ri.binscale, wexp, dkey_inv(kq));
       ridx[r] = iq;
     }
     __syncthreads();
-    if (tid == 0) {
-      double cw = hit_before;
-      int ns = nc;
-      for (int r = 0; r < nc; ++r) {
-        cw += xw[r];
-        if (cw >= ri.target) {
-          ns = r + 1;
-          break;
-        }
-      }
-      ibuf = ns;
-    }
-    __syncthreads();
-    for (int r = tid; r < ibuf; r += NT) set_bit(bw, ridx[r]);
+    // the first rank where the running weight reaches the target (a block scan, not a walk)
+    static_assert(NT == kSelThreads, "block_first_crossing spans the workgroup");
+    const int pos = block_first_crossing(nc, hit_before, ri.target, [&](int r) { return xw[r]; }, buf, &ibuf);
+    const int ns = pos < 0 ? nc : pos + 1;
+    for (int r = tid; r < ns; r += NT) set_bit(bw, ridx[r]);
     return;
   }
   // near-equal scores fill the crossing sub-bin: sort every gathered entry and walk them all
@@ -1274,7 +1382,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   }
   __syncthreads();
   bitonic_desc<int32_t, NT>(keys, idx, Lp);
-  auto weight = [&](int i) { return long_weight(a, ri.smax, wexp, dkey_inv(keys[i])); };
+  auto weight = [&](int i) { return long_weight(a, ri.smax, ri.binscale, wexp, dkey_inv(keys[i])); };
   const int pos = block_first_crossing(n, before, ri.target, weight, buf, &ibuf);
   const int n_sel = pos < 0 ? n : pos + 1;
   for (int i = tid; i < n_sel; i += NT) set_bit(bw, idx[i]);
@@ -1715,8 +1823,8 @@ int launch_select(const Plan& p, int level, char* ws, void* stream) {
   }
   const LongArgs a = long_args(p, ws);
   const dim3 rows(Hq, B), blocks(p.long_blocks, Hq, B);
-  hipLaunchKernelGGL(k_long_hist, blocks, dim3(kLongThreads), 0, st, a);
-  hipLaunchKernelGGL(k_long_find1, rows, dim3(kFindThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_hist, blocks, dim3(kHistThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_sum, dim3(kBins1 / kSumThreads, Hq, B), dim3(kSumThreads), 0, st, a);
   hipLaunchKernelGGL(k_long_mark, blocks, dim3(kLongThreads), 0, st, a);
   hipLaunchKernelGGL(k_long_resolve, rows, dim3(kResolveThreads), 0, st, a);
   int e = int(hipGetLastError());
@@ -1787,8 +1895,8 @@ int launch_long_rows(const LongRows& r, void* stream) {
   a.n_ctx = r.len;
   a.chunk_shift = 0;
   const dim3 rows(r.H, r.B), blocks(a.nb1, r.H, r.B);
-  hipLaunchKernelGGL(k_long_hist, blocks, dim3(kLongThreads), 0, st, a);
-  hipLaunchKernelGGL(k_long_find1, rows, dim3(kFindThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_hist, blocks, dim3(kHistThreads), 0, st, a);
+  hipLaunchKernelGGL(k_long_sum, dim3(kBins1 / kSumThreads, r.H, r.B), dim3(kSumThreads), 0, st, a);
   hipLaunchKernelGGL(k_long_mark, blocks, dim3(kLongThreads), 0, st, a);
   hipLaunchKernelGGL(k_long_resolve, rows, dim3(kResolveThreads), 0, st, a);
   return int(hipGetLastError());
