@@ -160,11 +160,12 @@ void plan_workspace(sd::Plan& p) {
   p.o_pmax = take(mm_rows * p.score_blocks0 * 8);
   p.o_pmin = take(mm_rows * p.score_blocks0 * 8);
   p.o_info = take(rows * sizeof(sd::RowInfo));
-  p.o_h1h = take(rows * p.long_blocks * sd::kBins1 * 8);
-  p.o_h1l = take(rows * p.long_blocks * sd::kBins1 * 8);
-  p.o_h1c = take(rows * p.long_blocks * sd::kBins1 * 4);
+  p.o_h1h = take(rows * sd::kBins1 * 8);
+  p.o_h1l = take(rows * sd::kBins1 * 8);
+  p.o_h1c = take(rows * sd::kBins1 * 4);
   p.o_cbin = take(rows * ((p.len0 + 7) & ~int64_t(7)) * 2);
   p.o_cidx = take(rows * p.long_blocks * sd::kResolveCap * 4);
+  p.o_ckey = take(rows * p.long_blocks * sd::kResolveCap * 8);
   p.o_ccnt = take(rows * p.long_blocks * 4);
   p.ws_bytes = off;
 }

@@ -145,6 +145,16 @@ __device__ __forceinline__ double min_f64(double x, double y) {
   return r;
 }
 
+// Clears one long row's coarse bin totals: kBins1 fixed-point mass words (high, low) and counts.
+__device__ __forceinline__ void zero_long_totals(unsigned long long* hh, unsigned long long* hl, uint32_t* hc,
+                                                 int64_t row, int tid, int nt) {
+  for (int i = tid; i < kBins1; i += nt) {
+    hh[row * kBins1 + i] = 0ull;
+    hl[row * kBins1 + i] = 0ull;
+    hc[row * kBins1 + i] = 0u;
+  }
+}
+
 // x clamped into [0, 1] (NaN to 0) with two instructions and inline constants
 __device__ __forceinline__ double clamp01_f64(double x) {
   double r;

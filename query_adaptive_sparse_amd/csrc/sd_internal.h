@@ -61,7 +61,7 @@ struct Plan {
   int8_t scored[kMaxKvHeads];  // their indices, ascending
   // workspace byte offsets
   size_t o_status, o_arrive, o_qp, o_s0, o_s1, o_cand, o_bits, o_ubits, o_rcnt, o_list, o_cnt;
-  size_t o_gpre, o_po, o_pl, o_pmax, o_pmin, o_info, o_h1h, o_h1l, o_h1c, o_cbin, o_cidx, o_ccnt, o_budget, o_cmass, o_cimp, o_csort;
+  size_t o_gpre, o_po, o_pl, o_pmax, o_pmin, o_info, o_h1h, o_h1l, o_h1c, o_cbin, o_cidx, o_ckey, o_ccnt, o_budget, o_cmass, o_cimp, o_csort;
   size_t o_ctx;        // int32 [B]: the step's cache length per sequence (published by the score pass)
   int32_t chunk_shift; // log2(chunk_size)
   int64_t n_arrive;  // arrival counters: one per (sequence, KV group)

@@ -130,19 +130,23 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRo
 // group's projection and its heads' queries are staged in LDS with one round of coalesced loads,
 // then one lane per (head, proxy dim) runs the chain. Local groups get zeros. Workgroup (0, 0)
 // also clears the status words and the per-group arrival counters and publishes the step's cache
-// lengths.
+// lengths; when the token rows take the long-row path (tot_h not NULL), each workgroup clears its
+// heads' coarse bin totals for the histogram pass.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_proxy_query(const T* __restrict__ q, QRows qm,
                                                      const float* __restrict__ proj, int G, int Hq,
                                                      uint64_t local_mask, double* __restrict__ qp,
                                                      uint32_t* __restrict__ status, int32_t* __restrict__ arrivals,
-                                                     int n_groups, StepLens lens) {
+                                                     int n_groups, StepLens lens, unsigned long long* __restrict__ tot_h,
+                                                     unsigned long long* __restrict__ tot_l, uint32_t* __restrict__ tot_c) {
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   if (g == 0 && b == 0) {
     if (tid < 16) status[tid] = 0;
     for (int i = tid; i < n_groups; i += 256) arrivals[i] = 0;
     lens.publish(tid, 256);
   }
+  if (tot_h)
+    for (int j = 0; j < G; ++j) zero_long_totals(tot_h, tot_l, tot_c, int64_t(b) * Hq + g * G + j, tid, 256);
   double* out = qp + (int64_t(b) * Hq + int64_t(g) * G) * 16;
   if ((local_mask >> g) & 1) {
     for (int o = tid; o < G * 16; o += 256) out[o] = 0.0;
@@ -347,7 +351,10 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
     // the step's lengths), then the proxy scores of the scored groups
     hipLaunchKernelGGL((k_proxy_query<T, D>), dim3(Hk, B), dim3(256), 0, st, static_cast<const T*>(t.q), qm,
                        t.proj, p.G, Hq, p.local_mask, at<double>(ws, p.o_qp), status,
-                       at<int32_t>(ws, p.o_arrive), p.n_arrive, lens);
+                       at<int32_t>(ws, p.o_arrive), p.n_arrive, lens,
+                       p.long0 ? at<unsigned long long>(ws, p.o_h1h) : nullptr,
+                       p.long0 ? at<unsigned long long>(ws, p.o_h1l) : nullptr,
+                       p.long0 ? at<uint32_t>(ws, p.o_h1c) : nullptr);
     if (p.n_scored > 0) {
       ProxyArgs pa;
       pa.kp = static_cast<const uint16_t*>(t.kp);

@@ -617,12 +617,13 @@ struct LongArgs {
   const double* pmin;
   int nblk;
   int nb1;             // slabs per row
-  unsigned long long* h1h;  // [row][slab][kBins1] partial coarse histograms: fixed-point masses
-  unsigned long long* h1l;  //   (top-p) ...
-  uint32_t* h1c;            //   ... or entry counts (top-k)
+  unsigned long long* h1h;  // [row][kBins1] coarse histograms, summed over the row's slabs with
+  unsigned long long* h1l;  //   integer atomics (zero before k_long_hist): fixed-point masses
+  uint32_t* h1c;            //   (top-p) or entry counts (top-k)
   uint16_t* cbin;      // [row][cstride] coarse bin of every entry
   int64_t cstride;     // len rounded up to a multiple of 8 (16-byte aligned rows)
-  int32_t* cidx;       // [row][slab][kResolveCap] indices of the crossing bin's entries
+  int32_t* cidx;       // [row][slab][kResolveCap] indices of the crossing bin's entries ...
+  uint64_t* ckey;      // ... and their order keys (dkey of the score)
   int32_t* ccnt;       // [row][slab] their counts (not capped)
   uint32_t* bits;
   int64_t words;
@@ -853,44 +854,23 @@ __global__ __launch_bounds__(kHistThreads) void k_long_hist(LongArgs a) {
   else
     bin_all(BoolTag<false>{});
   __syncthreads();
-  const int64_t o = (row * a.nb1 + slab) * kBins1;
+  // the slab's histogram into the row's totals (integer sums: the same bits in any order)
+  const int64_t o = row * kBins1;
   for (int i = tid; i < kBins1; i += NT) {
     if (a.topp) {
-      a.h1h[o + i] = hh[i];
-      a.h1l[o + i] = hl[i];
+      if (hh[i]) atomicAdd(&a.h1h[o + i], hh[i]);
+      if (hl[i]) atomicAdd(&a.h1l[o + i], hl[i]);
     } else {
-      a.h1c[o + i] = hc[i];
+      if (hc[i]) atomicAdd(&a.h1c[o + i], hc[i]);
     }
   }
 }
 
-// Per row: the coarse bin totals, the slabs' partial histograms summed as integers (exact in any
-// order) into slab 0's slot. One lane per bin, a few bins per workgroup, so that many workgroups
-// share the row's partials.
-constexpr int kSumThreads = 64;
-static_assert(kBins1 % kSumThreads == 0, "bins split evenly over the sum workgroups");
-__global__ __launch_bounds__(kSumThreads) void k_long_sum(LongArgs a) {
-  const int b = blockIdx.z, h = blockIdx.y;
-  if ((a.local_mask >> (h / a.G)) & 1) return;
-  const int64_t row = int64_t(b) * a.Hq + h;
-  if (a.info[row].all) return;
-  const int64_t o = row * a.nb1 * kBins1 + int64_t(blockIdx.x) * kSumThreads + threadIdx.x;
-  const int nb = int((long_len(a, b) + kLongBlock - 1) / kLongBlock);  // slabs holding entries
-  if (a.topp) {
-    unsigned long long sh = a.h1h[o], sl = a.h1l[o];
-#pragma unroll 16
-    for (int sl_ = 1; sl_ < nb; ++sl_) {
-      sh += a.h1h[o + int64_t(sl_) * kBins1];
-      sl += a.h1l[o + int64_t(sl_) * kBins1];
-    }
-    a.h1h[o] = sh;
-    a.h1l[o] = sl;
-  } else {
-    uint32_t cn = a.h1c[o];
-#pragma unroll 16
-    for (int sl_ = 1; sl_ < nb; ++sl_) cn += a.h1c[o + int64_t(sl_) * kBins1];
-    a.h1c[o] = cn;
-  }
+// Clears a row's coarse bin totals before k_long_hist adds into them (the kernel ahead of the
+// histogram does it: k_long_zero, or the proxy query kernel on the token-row path).
+__global__ __launch_bounds__(256) void k_long_zero(LongArgs a) {
+  const int64_t row = int64_t(blockIdx.y) * a.Hq + blockIdx.x;
+  zero_long_totals(a.h1h, a.h1l, a.h1c, row, threadIdx.x, 256);
 }
 
 // Per slab: the crossing coarse bin of the row (a scan of the bin totals that every workgroup of
@@ -928,6 +908,8 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
   const uint16_t* br = a.cbin + row * a.cstride;
   uint8_t* bb = reinterpret_cast<uint8_t*>(bw);
   int32_t* out = a.cidx + (row * a.nb1 + slab) * kResolveCap;
+  uint64_t* outk = a.ckey + (row * a.nb1 + slab) * kResolveCap;
+  __shared__ int32_t cst[kResolveCap];  // the crossing bin's entries, staged
   constexpr int kVec = kLongBlock / (NT * 8);  // 16-byte pieces per lane
   // piece v of lane tid covers entries t0 + 8 * (tid + NT v) .. + 7; pieces past the slab load
   // the slab's last piece again (rows are padded to a multiple of 8 entries) and are masked
@@ -942,7 +924,7 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
   bool all = all0;
   int bin1 = 0;
   if (!all0) {
-    const int64_t o = row * a.nb1 * kBins1 + tid;
+    const int64_t o = row * kBins1 + tid;
     const double m = a.topp ? fix_value(a.h1h[o], a.h1l[o]) : double(a.h1c[o]);
     double Z;
     const double incl = block_scan<NT>(m, btot, &Z);
@@ -990,12 +972,19 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
       while (cand) {
         const int u = __ffs(cand) - 1;
         cand &= cand - 1;
-        if (pos < kResolveCap) out[pos] = int32_t(e0 + u);
+        if (pos < kResolveCap) cst[pos] = int32_t(e0 + u);
         ++pos;
       }
     }
   }
   __syncthreads();
+  // the slab's crossing-bin entries with their order keys (one round of score loads)
+  const int nst = scnt < kResolveCap ? scnt : kResolveCap;
+  for (int i = tid; i < nst; i += NT) {
+    const int32_t t = cst[i];
+    out[i] = t;
+    outk[i] = dkey(a.s0[row * a.len + t]);
+  }
   if (tid == 0) a.ccnt[row * a.nb1 + slab] = scnt;
 }
 
@@ -1224,7 +1213,6 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   __shared__ int soff[NT + 1];
   __shared__ int hit_bin, nx, ibuf;
   __shared__ double hit_before;
-  const double* sr = a.s0 + row * a.len;
   uint32_t* bw = a.bits + row * a.words;
   const int wexp = ri.wexp;
   const int64_t len = long_len(a, b);
@@ -1251,6 +1239,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   {
     constexpr int PER = kResolveCap / NT;
     int32_t tv[PER];
+    uint64_t kv[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = tid + NT * k;
@@ -1269,21 +1258,29 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
         ++s;
       }
       tv[k] = a.cidx[(row * a.nb1 + s) * kResolveCap + off];
+      kv[k] = a.ckey[(row * a.nb1 + s) * kResolveCap + off];
     }
-    double sv[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) sv[k] = sr[tv[k]];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = tid + NT * k;
       if (i < n) {
-        keys[i] = dkey(sv[k]);
+        keys[i] = kv[k];
         idx[i] = tv[k];
       }
     }
   }
   const double before = ri.before1;
   const double dlo = double(ri.bin1);
+  // every gathered entry lies in the crossing coarse bin, so its weight (long_weight) takes that
+  // bin's edge value, computed once
+  const bool ty = taylor_row(a, ri.binscale);
+  const double dx1 = ty ? a.scale / ri.binscale : 0.0;
+  const double edge1 = ty ? bin_edge_exp(a, ri.binscale, ri.bin1) : 0.0;
+  const TaylorC tc = taylor_sgpr();
+  auto wt = [&](double s) {
+    if (!a.topp) return 1.0;
+    return ty ? exp_in_bin(a.scale * s - a.scale * ri.smax, ri.bin1, dx1, edge1, tc) : plain_weight(a, ri.smax, wexp, s);
+  };
   const double sscale = double(kSub);
   // ---- sub-bin histogram of the gathered entries
   for (int i = tid; i < kSub; i += NT) {
@@ -1303,7 +1300,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
     sb = sb < kSub - 1 ? sb : kSub - 1;
     sub[i] = uint16_t(sb);
     atomicAdd(&hc[sb], 1u);
-    if (a.topp) fix_add(&hh[sb], &hl[sb], long_weight(a, ri.smax, ri.binscale, wexp, s));
+    if (a.topp) fix_add(&hh[sb], &hl[sb], wt(s));
   }
   __syncthreads();
   constexpr int SPER = kSub / NT;
@@ -1362,7 +1359,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
         const uint64_t ku = xkey[u];
         r += (ku > kq || (ku == kq && xidx[u] < iq)) ? 1 : 0;
       }
-      xw[r] = long_weight(a, ri.smax, ri.binscale, wexp, dkey_inv(kq));
+      xw[r] = wt(dkey_inv(kq));
       ridx[r] = iq;
     }
     __syncthreads();
@@ -1382,7 +1379,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   }
   __syncthreads();
   bitonic_desc<int32_t, NT>(keys, idx, Lp);
-  auto weight = [&](int i) { return long_weight(a, ri.smax, ri.binscale, wexp, dkey_inv(keys[i])); };
+  auto weight = [&](int i) { return wt(dkey_inv(keys[i])); };
   const int pos = block_first_crossing(n, before, ri.target, weight, buf, &ibuf);
   const int n_sel = pos < 0 ? n : pos + 1;
   for (int i = tid; i < n_sel; i += NT) set_bit(bw, idx[i]);
@@ -1711,6 +1708,7 @@ LongArgs long_args(const Plan& p, char* ws) {
   a.cbin = at<uint16_t>(ws, p.o_cbin);
   a.cstride = (p.len0 + 7) & ~int64_t(7);
   a.cidx = at<int32_t>(ws, p.o_cidx);
+  a.ckey = at<uint64_t>(ws, p.o_ckey);
   a.ccnt = at<int32_t>(ws, p.o_ccnt);
   a.bits = at<uint32_t>(ws, p.o_bits);
   a.words = p.words;
@@ -1823,8 +1821,9 @@ int launch_select(const Plan& p, int level, char* ws, void* stream) {
   }
   const LongArgs a = long_args(p, ws);
   const dim3 rows(Hq, B), blocks(p.long_blocks, Hq, B);
+  // the proxy query kernel has cleared the bin totals on the token-row path
+  if (c.route != SD_ROUTE_PROXY) hipLaunchKernelGGL(k_long_zero, rows, dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_long_hist, blocks, dim3(kHistThreads), 0, st, a);
-  hipLaunchKernelGGL(k_long_sum, dim3(kBins1 / kSumThreads, Hq, B), dim3(kSumThreads), 0, st, a);
   hipLaunchKernelGGL(k_long_mark, blocks, dim3(kLongThreads), 0, st, a);
   hipLaunchKernelGGL(k_long_resolve, rows, dim3(kResolveThreads), 0, st, a);
   int e = int(hipGetLastError());
@@ -1835,7 +1834,7 @@ int launch_select(const Plan& p, int level, char* ws, void* stream) {
 // ---- long-row selection over caller-given rows (the prefill path's budget and per-head top-k)
 namespace {
 struct LongScratch {
-  size_t info, h1h, h1l, h1c, cbin, cidx, ccnt, total;
+  size_t info, h1h, h1l, h1c, cbin, cidx, ckey, ccnt, total;
 };
 LongScratch long_scratch_layout(int64_t rows, int64_t len) {
   const int64_t nb1 = (len + kLongBlock - 1) / kLongBlock;
@@ -1847,11 +1846,12 @@ LongScratch long_scratch_layout(int64_t rows, int64_t len) {
     return o;
   };
   l.info = take(size_t(rows) * sizeof(RowInfo));
-  l.h1h = take(size_t(rows * nb1 * kBins1) * 8);
-  l.h1l = take(size_t(rows * nb1 * kBins1) * 8);
-  l.h1c = take(size_t(rows * nb1 * kBins1) * 4);
+  l.h1h = take(size_t(rows * kBins1) * 8);
+  l.h1l = take(size_t(rows * kBins1) * 8);
+  l.h1c = take(size_t(rows * kBins1) * 4);
   l.cbin = take(size_t(rows * ((len + 7) & ~int64_t(7))) * 2);
   l.cidx = take(size_t(rows * nb1 * kResolveCap) * 4);
+  l.ckey = take(size_t(rows * nb1 * kResolveCap) * 8);
   l.ccnt = take(size_t(rows * nb1) * 4);
   l.total = off;
   return l;
@@ -1887,6 +1887,7 @@ int launch_long_rows(const LongRows& r, void* stream) {
   a.cbin = reinterpret_cast<uint16_t*>(r.scratch + l.cbin);
   a.cstride = (r.len + 7) & ~int64_t(7);
   a.cidx = reinterpret_cast<int32_t*>(r.scratch + l.cidx);
+  a.ckey = reinterpret_cast<uint64_t*>(r.scratch + l.ckey);
   a.ccnt = reinterpret_cast<int32_t*>(r.scratch + l.ccnt);
   a.bits = r.bits;
   a.words = r.words;
@@ -1895,8 +1896,8 @@ int launch_long_rows(const LongRows& r, void* stream) {
   a.n_ctx = r.len;
   a.chunk_shift = 0;
   const dim3 rows(r.H, r.B), blocks(a.nb1, r.H, r.B);
+  hipLaunchKernelGGL(k_long_zero, rows, dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_long_hist, blocks, dim3(kHistThreads), 0, st, a);
-  hipLaunchKernelGGL(k_long_sum, dim3(kBins1 / kSumThreads, r.H, r.B), dim3(kSumThreads), 0, st, a);
   hipLaunchKernelGGL(k_long_mark, blocks, dim3(kLongThreads), 0, st, a);
   hipLaunchKernelGGL(k_long_resolve, rows, dim3(kResolveThreads), 0, st, a);
   return int(hipGetLastError());
