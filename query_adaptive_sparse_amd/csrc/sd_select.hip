@@ -806,30 +806,51 @@ __global__ __launch_bounds__(kHistThreads) void k_long_hist(LongArgs a) {
   const double* sr = a.s0 + row * a.len;
   uint16_t* br = a.cbin + row * a.cstride;
   // kLongBlock / (8 NT) batches of 8 entries per thread; the next batch's loads are issued before
-  // the current batch is binned (clamped, so every load is unconditional)
+  // the current batch is binned (clamped, so every load is unconditional). Two layouts of a batch:
+  // strided (entry k of lane tid at tid + NT k: 8-byte loads, 2-byte bin stores), or, when the row
+  // length is a multiple of 8 (every 8-entry piece 64-byte aligned and inside the row), 8
+  // consecutive entries per lane (16-byte loads and one 16-byte store of the 8 bins).
   constexpr int kIters = kLongBlock / (NT * 8);
+  static_assert(kIters % 2 == 0, "batches go in pairs");
   double sv[2][8];
-  auto load = [&](double* dst, int it) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int64_t t = t0 + int64_t(it) * (NT * 8) + tid + NT * k;
-      dst[k] = sr[t < t1 ? t : t1 - 1];
-    }
-  };
-  // one weight path per instantiation, chosen once per row (a branch inside the unrolled loop
-  // would put both paths' code in the loop body)
-  auto bin_all = [&](auto taylor_tag) {
+  auto bin_all = [&](auto taylor_tag, auto vec_tag) {
     constexpr bool kTaylor = decltype(taylor_tag)::value;
+    constexpr bool kVec = decltype(vec_tag)::value;
     const TaylorC tc = taylor_sgpr();
+    auto entry = [&](int it, int k) -> int64_t {
+      return kVec ? t0 + 8 * (int64_t(tid) + int64_t(NT) * it) + k : t0 + int64_t(it) * (NT * 8) + tid + NT * k;
+    };
+    auto load = [&](double* dst, int it) {
+      if (kVec) {
+        int64_t e = entry(it, 0);
+        const int64_t last = (t1 - 1) & ~int64_t(7);
+        e = e < last ? e : last;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const double2 x = *reinterpret_cast<const double2*>(sr + e + 2 * k);
+          dst[2 * k] = x.x;
+          dst[2 * k + 1] = x.y;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int64_t t = entry(it, k);
+          dst[k] = sr[t < t1 ? t : t1 - 1];
+        }
+      }
+    };
     auto bin8 = [&](const double* vals, int it) {
+      if (kVec && entry(it, 0) >= t1) return;
+      uint16_t cb[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int64_t t = t0 + int64_t(it) * (NT * 8) + tid + NT * k;
+        const int64_t t = entry(it, k);
+        const double v = vals[k];
+        // (Taylor rows are never bitbins rows)
+        const int c = coarse_bin(kTaylor ? coarse_pos(v, smax, binscale) : coarse_pos_of(a, v, smax, binscale));
+        cb[k] = uint16_t(c);
         if (t < t1) {
-          const double v = vals[k];
-          // (Taylor rows are never bitbins rows)
-          const int c = coarse_bin(kTaylor ? coarse_pos(v, smax, binscale) : coarse_pos_of(a, v, smax, binscale));
-          br[t] = uint16_t(c);
+          if (!kVec) br[t] = uint16_t(c);
           if (a.topp) {
             const double w = kTaylor ? exp_in_bin(a.scale * v - a.scale * smax, c, dx, ebin[c], tc)
                                      : plain_weight(a, smax, wexp, v);
@@ -839,8 +860,15 @@ __global__ __launch_bounds__(kHistThreads) void k_long_hist(LongArgs a) {
           }
         }
       }
+      if (kVec) {  // bins past the row's entries are written too (inside the row; never read as entries)
+        uint4 pk;
+        pk.x = uint32_t(cb[0]) | (uint32_t(cb[1]) << 16);
+        pk.y = uint32_t(cb[2]) | (uint32_t(cb[3]) << 16);
+        pk.z = uint32_t(cb[4]) | (uint32_t(cb[5]) << 16);
+        pk.w = uint32_t(cb[6]) | (uint32_t(cb[7]) << 16);
+        *reinterpret_cast<uint4*>(br + entry(it, 0)) = pk;
+      }
     };
-    static_assert(kIters % 2 == 0, "batches go in pairs");
     load(sv[0], 0);
     for (int it = 0; it < kIters; it += 2) {
       load(sv[1], it + 1);
@@ -849,10 +877,18 @@ __global__ __launch_bounds__(kHistThreads) void k_long_hist(LongArgs a) {
       bin8(sv[1], it + 1);
     }
   };
-  if (taylor)
-    bin_all(BoolTag<true>{});
-  else
-    bin_all(BoolTag<false>{});
+  const bool vec = (a.len & 7) == 0 && (a.cstride & 7) == 0;
+  if (taylor) {
+    if (vec)
+      bin_all(BoolTag<true>{}, BoolTag<true>{});
+    else
+      bin_all(BoolTag<true>{}, BoolTag<false>{});
+  } else {
+    if (vec)
+      bin_all(BoolTag<false>{}, BoolTag<true>{});
+    else
+      bin_all(BoolTag<false>{}, BoolTag<false>{});
+  }
   __syncthreads();
   // the slab's histogram into the row's totals (integer sums: the same bits in any order)
   const int64_t o = row * kBins1;
