@@ -28,8 +28,8 @@
 //                    XOR-swizzled per row, V rows padded for transpose reads), each wave runs q.K^T
 //                    on the bf16 MFMA, the causal mask in compact order, an online softmax whose
 //                    reference moves only when a logit exceeds it by 2^8, and P.V on the fp16
-//                    MFMA (P split into fp16 high and low parts, V converted at the gather),
-//                    then writes its rows;
+//                    MFMA (P rounded to fp16 and the normaliser summed from the same rounded
+//                    values, V converted at the gather), then writes its rows;
 //                    the workgroups past a head's query blocks write the zero rows of the
 //                    positions it did not keep.
 #include "sd_device.h"
@@ -652,11 +652,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
         m[t] = mn;
       }
     }
-    // P as two fp16 parts, hi = fp16(p) and lo = fp16(p - hi) (rounded to nearest even; the
-    // probabilities are below 2^8 by the lazy reference): hi + lo carries p to about 2^-22, so the
-    // weights that multiply V agree with the fp32 normaliser l. ph / pl[t][st][u]: keys
-    // 16 st + 4 c + 2 u, + 1 of query 16 t + n, packed
-    uint32_t ph[kQTiles][kKeyTile / 16][2], pl[kQTiles][kKeyTile / 16][2];
+    // P in fp16 (rounded to nearest even; the probabilities are below 2^8 by the lazy reference),
+    // and the normaliser l summed from the same rounded values, so the output is the exact
+    // softmax average under logits moved by at most 2^-11 (the weights multiplying V and those
+    // dividing agree). ph[t][st][u]: keys 16 st + 4 c + 2 u, + 1 of query 16 t + n, packed
+    uint32_t ph[kQTiles][kKeyTile / 16][2];
 #pragma unroll
     for (int t = 0; t < kQTiles; ++t) {
       // a column whose reference is still -inf has seen masked logits only: exponent -inf
@@ -665,20 +665,16 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
       for (int st = 0; st < kKeyTile / 16; ++st) {
         float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][st][i], cs, nm));
-          l[t] += pr[i];
-        }
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][st][i], cs, nm));
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-          h2 hv, lv;
+          h2 hv;
           hv[0] = (_Float16)pr[2 * u];
           hv[1] = (_Float16)pr[2 * u + 1];
-          lv[0] = (_Float16)(pr[2 * u] - (float)hv[0]);  // the difference is exact in fp32
-          lv[1] = (_Float16)(pr[2 * u + 1] - (float)hv[1]);
+          l[t] += (float)hv[0];
+          l[t] += (float)hv[1];
           ph[t][st][u] = __builtin_bit_cast(uint32_t, hv);
-          pl[t][st][u] = __builtin_bit_cast(uint32_t, lv);
         }
       }
     }
@@ -700,9 +696,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
 #pragma unroll
         for (int t = 0; t < kQTiles; ++t) {
           const uint4 ah = make_uint4(ph[t][2 * sp][0], ph[t][2 * sp][1], ph[t][2 * sp + 1][0], ph[t][2 * sp + 1][1]);
-          const uint4 al = make_uint4(pl[t][2 * sp][0], pl[t][2 * sp][1], pl[t][2 * sp + 1][0], pl[t][2 * sp + 1][1]);
           acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ah), bop, acc[t][nb], 0, 0, 0);
-          acc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, al), bop, acc[t][nb], 0, 0, 0);
         }
       }
     }

@@ -2,8 +2,9 @@
 
 Selections bit-exact: the budget, every head's position bitmap and list. Importance within
 1e-12 relative (both sides fp64; the softmax normalisers are summed in different orders).
-Outputs (fp32; q.K on the bf16 MFMA, P.V on the fp16 MFMA with P split into fp16 high and low
-parts, fp32 accumulation) within max-abs 2e-3 and relative-L2 1e-3 of the oracle's fp64
+Outputs (fp32; q.K on the bf16 MFMA, P.V on the fp16 MFMA with P rounded to fp16 and the
+normaliser summed from the rounded values, fp32 accumulation) within max-abs 2e-3 (for values of
+the synthetic N(0,1) scale; the bound scales with |V|) and relative-L2 1e-3 of the oracle's fp64
 attention; positions a head did not keep are exactly zero.
 """
 from dataclasses import replace
@@ -32,7 +33,7 @@ def run_gpu(w, inp):
     return sel, out
 
 
-def compare(w, inp, sel, out, heads=None, rows_per_head=None):
+def compare(w, inp, sel, out, heads=None, rows_per_head=None, v_scale=1.0):
     src = PrefillSource(inp)
     o = pref.tsa_prefill(w, src, heads=heads, rows_per_head=rows_per_head)
     assert int(sel["status"][0]) == 0
@@ -62,7 +63,7 @@ def compare(w, inp, sel, out, heads=None, rows_per_head=None):
     rep["rel_l2"] = float(np.linalg.norm(d) / max(np.linalg.norm(ref[mask]), 1e-30))
     zero = ref == 0.0
     assert np.all(got[zero] == 0.0), "an unkept position is not zero"
-    assert rep["max_abs"] <= ATOL and rep["rel_l2"] <= RTOL_L2, rep
+    assert rep["max_abs"] <= ATOL * v_scale and rep["rel_l2"] <= RTOL_L2, rep
     return rep
 
 
@@ -191,13 +192,15 @@ def test_prefill_token_major_layout():
 
 
 def test_prefill_large_v():
-    """V eight times larger (|v| up to about 35): the P.V precision stays within the same absolute
-    tolerance (P carries about 22 bits through its fp16 high and low parts)."""
+    """V eight times larger (|v| up to about 35). Each output row is a softmax average of V rows;
+    rounding P to fp16 with the normaliser summed from the rounded values is the exact average under
+    logits moved by at most 2^-11, so the absolute error scales with |V|: the max-abs bound is the
+    N(0,1) one times 8, the relative-L2 bound unchanged."""
     w = configs.get("p1t")
     inp = gen.make_prefill_inputs(w, device="cuda")
     inp["V"] = (inp["V"].float() * 8.0).to(torch.bfloat16)
     sel, out = run_gpu(w, inp)
-    rep = compare(w, inp, sel, out)
+    rep = compare(w, inp, sel, out, v_scale=8.0)
     print(f"[prefill] V x8: {rep}", flush=True)
 
 
