@@ -79,6 +79,18 @@ def test_long_rows_topp_summary():
     _run(w, gen.make_inputs(w, device="cuda"))
 
 
+@pytest.mark.parametrize("kind", ["proxy", "summary"])
+def test_long_rows_odd_length(kind):
+    """Long rows whose length is not a multiple of 8: the histogram pass takes its strided layout
+    (8-byte loads, 2-byte bin stores) and the last slab and the last 8-entry piece are partial."""
+    if kind == "proxy":
+        w = replace(configs.get("c5s"), name="odd_proxy", n_ctx=40005, window=777, sink=5)
+    else:
+        w = replace(configs.get("c3s"), name="odd_summary", batch=1, kv_batch=1, chunk_size=2, n_ctx=16382,
+                    keep_first=2, keep_last=3)
+    _run(w, gen.make_inputs(w, device="cuda"))
+
+
 def test_token_topp_short_rows():
     """Token-level proxy top-p on rows short enough for the fused short-row kernel, mixed heads."""
     w = replace(configs.get("c5s"), name="tok_short", n_ctx=2048, window=100, sink=7)
