@@ -534,12 +534,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
   }
   // running reference of every query column in log2 units (scale_log2 x raw logit); it is moved
   // only when a logit exceeds it by more than kPfLazy, so the probabilities stay below 2^kPfLazy
-  float m[kQTiles], l[kQTiles];
+  // the normaliser of query row 4 c + i of tile t sits in accl[t][i] of every lane of group c: it
+  // is a P.V product against a block of ones, so it sums exactly the fp16 weights that multiply V
+  float m[kQTiles];
+  f32x4 accl[kQTiles];
   f32x4 acc[kQTiles][kD / 16];
 #pragma unroll
   for (int t = 0; t < kQTiles; ++t) {
     m[t] = kNegInf;
-    l[t] = 0.f;
+    accl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < kD / 16; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -642,18 +645,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
       for (int t = 0; t < kQTiles; ++t) {
         const float mn = fmaxf(m[t], mt[t]);
         const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m[t] - mn);
-        l[t] *= alpha;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float ai = __shfl(alpha, 4 * c + i);
+          accl[t][i] *= ai;
 #pragma unroll
           for (int nb = 0; nb < kD / 16; ++nb) acc[t][nb][i] *= ai;
         }
         m[t] = mn;
       }
     }
-    // P in fp16 (rounded to nearest even; the probabilities are below 2^8 by the lazy reference),
-    // and the normaliser l summed from the same rounded values, so the output is the exact
+    // P in fp16 (rounded to nearest even; the probabilities are below 2^8 by the lazy reference);
+    // the normaliser is summed from the same rounded values (accl), so the output is the exact
     // softmax average under logits moved by at most 2^-11 (the weights multiplying V and those
     // dividing agree). ph[t][st][u]: keys 16 st + 4 c + 2 u, + 1 of query 16 t + n, packed
     uint32_t ph[kQTiles][kKeyTile / 16][2];
@@ -672,8 +675,6 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
           h2 hv;
           hv[0] = (_Float16)pr[2 * u];
           hv[1] = (_Float16)pr[2 * u + 1];
-          l[t] += (float)hv[0];
-          l[t] += (float)hv[1];
           ph[t][st][u] = __builtin_bit_cast(uint32_t, hv);
         }
       }
@@ -686,6 +687,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
     for (int sp = 0; sp < kKeyTile / 32; ++sp) {
       const uint32_t* vr0 = vst + (32 * sp + 4 * c + (n >> 2)) * kVPitchW + 2 * (n & 3);
       const uint32_t* vr1 = vr0 + 16 * kVPitchW;
+      const f16x8 ones = f16x8{1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+      for (int t = 0; t < kQTiles; ++t) {
+        const uint4 ah = make_uint4(ph[t][2 * sp][0], ph[t][2 * sp][1], ph[t][2 * sp + 1][0], ph[t][2 * sp + 1][1]);
+        accl[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ah), ones, accl[t], 0, 0, 0);
+      }
 #pragma unroll
       for (int nb = 0; nb < kD / 16; ++nb) {
         const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -709,16 +716,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void k_pf_attend(PfAttnArgs a) {
     if (++kt >= nkt) break;
   }
   const float vscale = ldexpf(1.f, a.vexp[int64_t(b) * a.Hq + h]);  // undo the V scaling
-  // normaliser of every query column (the 4 lane groups hold partial sums of the same column);
-  // acc[t][nb][i]: query 16 t + 4 c + i of the wave, dimension 16 nb + n
+  // acc[t][nb][i]: query 16 t + 4 c + i of the wave, dimension 16 nb + n; accl[t][i]: its normaliser
 #pragma unroll
   for (int t = 0; t < kQTiles; ++t) {
-    float lt = l[t];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float li = __shfl(lt, 4 * c + i);
+      const float li = accl[t][i];
       const int qo = q0w + 16 * t + 4 * c + i;
       if (qo < kk) {
         float* orow = a.out + ((int64_t(b) * a.Hq + h) * a.L + pos_of(qo)) * kD;
