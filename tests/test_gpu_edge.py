@@ -91,6 +91,16 @@ def test_long_rows_odd_length(kind):
     _run(w, gen.make_inputs(w, device="cuda"))
 
 
+@pytest.mark.parametrize("factor", [0.25, 2.0, 8.0])
+def test_long_rows_bin_width(factor):
+    """Proxy top-p rows with the selection scale multiplied by `factor`: coarse bins from about
+    0.004 to 0.25 logit wide, so rows take the bin-edge Taylor weights (bins up to 1/16 logit),
+    exp itself (wider bins), or a mix of both across the heads."""
+    w0 = configs.get("c5s")
+    w = replace(w0, name=f"bin_width_{factor}", n_ctx=32768, select_scale=w0.select_scale * factor)
+    _run(w, gen.make_inputs(w, device="cuda"))
+
+
 def test_token_topp_short_rows():
     """Token-level proxy top-p on rows short enough for the fused short-row kernel, mixed heads."""
     w = replace(configs.get("c5s"), name="tok_short", n_ctx=2048, window=100, sink=7)
