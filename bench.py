@@ -412,7 +412,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the decode path "
-              "shards by sequence and KV group across GPUs, which this build does not run)", file=sys.stderr)
+              "shards by sequence and KV group across GPUs, which this benchmark does not run)", file=sys.stderr)
         sys.exit(2)
     from synth import configs, gen
     from query_adaptive_sparse_amd import SparseDecoder, make_tensors

@@ -57,7 +57,7 @@ typedef struct sd_handle sd_handle;
 typedef enum {
   SD_OK = 0,
   SD_EINVAL = 1,        /* a null, misaligned or out-of-range argument */
-  SD_EUNSUPPORTED = 2,  /* a valid request this build does not implement */
+  SD_EUNSUPPORTED = 2,  /* a valid request the library does not implement */
   SD_EWORKSPACE = 3,    /* workspace pointer null or not 256-byte aligned */
   SD_EHIP = 4           /* a HIP runtime call failed (message has the code) */
 } sd_status;

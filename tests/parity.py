@@ -54,7 +54,7 @@ def oracle_step(w, inp, groups=None, attend_groups=None):
 
 
 def compare(w, g_res, o_res, check_scores=True):
-    """Assert parity; returns a dict of the numbers behind the verdict."""
+    """Assert parity; returns a dict of the numbers behind the result."""
     sel = g_res["sel"]
     G = w.group
     report = {"heads": 0, "groups": 0, "min_margin": math.inf}
