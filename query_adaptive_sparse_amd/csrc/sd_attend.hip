@@ -548,22 +548,35 @@ __global__ __launch_bounds__(256, 2) void k_attend(AttendArgs a) {
   }
 }
 
-// LSE combine. One workgroup of kCombineThreads per (sequence, query row): the partials of the
-// head's group are the pool slots (k + group) of the persistent workgroups k whose tile slice
-// meets the group. Their lse values are read in one parallel round (max, then weights
-// exp(lse - max) in LDS, kCombineThreads partials at a time); each thread then accumulates one
-// output dimension over a fixed subset of the partials with independent loads. Summation order
-// is fixed: the result is deterministic.
-constexpr int kCombineThreads = 1024;
+// floor(a / b) for 0 <= a, 0 < b, both below 2^53: the fp64 quotient truncated is within one of
+// it, and one exact integer step corrects it (a 64-bit integer division is a long software
+// sequence on the GPU)
+__device__ __forceinline__ int64_t div_floor(int64_t a, int64_t b) {
+  int64_t q = int64_t(double(a) / double(b));
+  if (q * b > a)
+    --q;
+  else if ((q + 1) * b <= a)
+    ++q;
+  return q;
+}
 
-template <int D>
-__global__ __launch_bounds__(kCombineThreads) void k_combine(const float* __restrict__ po, const float* __restrict__ pl,
-                                                             const int32_t* __restrict__ gpre, int n_groups,
-                                                             int nb_attend, int G, int Hq, int Hk, int Gq,
-                                                             float* __restrict__ out, float* __restrict__ lse) {
-  constexpr int NT = kCombineThreads;
+// LSE combine. One workgroup of NT threads per (sequence, query row): the partials of the head's
+// group are the pool slots (k + group) of the persistent workgroups k whose tile slice meets the
+// group. Thread j holds partial j's lse; each thread accumulates one output dimension over a fixed
+// subset of the partials (j = grp, grp + NGRP, ...), kCombinePrefetch loads at a time, and the
+// first of those rounds is issued with the lse loads, before the max is known. Beyond NT partials
+// the rest is taken in further rounds. Summation order is fixed: the result is deterministic. NT
+// is 256 when groups have few partials (many groups share the persistent workgroups), else 1024.
+constexpr int kCombinePrefetch = 12;
+
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void k_combine(const float* __restrict__ po, const float* __restrict__ pl,
+                                                const int32_t* __restrict__ gpre, int n_groups, int nb_attend,
+                                                int G, int Hq, int Hk, int Gq, float* __restrict__ out,
+                                                float* __restrict__ lse) {
   constexpr int NW = NT / 64;
   constexpr int NGRP = NT / D;  // thread groups, each covering all D dims
+  constexpr int U = kCombinePrefetch;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int gid = b * Hk + h / G, hh = h % G;
@@ -575,9 +588,8 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float* __rest
   }
   const int64_t T = gpre[n_groups];
   const int64_t t0 = gpre[gid], t1 = gpre[gid + 1];
-  __shared__ float red[NW];
+  __shared__ float red[NW], red2[NW];
   __shared__ float wj[NT];
-  __shared__ int64_t sj[NT];
   __shared__ float part[NGRP][D];
   if (t0 == t1) {
     for (int d = tid; d < D; d += NT) out[hrow * D + d] = 0.f;
@@ -585,48 +597,62 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float* __rest
     return;
   }
   const int64_t NB = nb_attend;
-  const int k0 = int(((t0 + 1) * NB - 1) / T);
-  const int nt = int((t1 * NB - 1) / T) - k0 + 1;
-  // with at least one tile per workgroup every slice is non-empty (no 64-bit divisions, which are
-  // slow on the GPU)
+  const int k0 = int(div_floor((t0 + 1) * NB - 1, T));
+  const int nt = int(div_floor(t1 * NB - 1, T)) - k0 + 1;
+  // with at least one tile per workgroup every slice is non-empty
   const bool all_live = T >= NB;
-  auto live = [&](int k) { return all_live || (int64_t(k) * T) / NB < (int64_t(k + 1) * T) / NB; };
-  // max over the partials' lse
-  float M = kNegInf;
-  for (int j = tid; j < nt; j += NT)
-    if (live(k0 + j)) M = fmaxf(M, pl[(int64_t(k0 + j) + gid) * G + hh]);
+  auto live = [&](int k) { return all_live || div_floor(int64_t(k) * T, NB) < div_floor(int64_t(k + 1) * T, NB); };
+  auto lse_of = [&](int j) { return live(k0 + j) ? pl[(int64_t(k0 + j) + gid) * G + hh] : kNegInf; };
+  auto prow = [&](int j) { return po + ((int64_t(k0 + j) + gid) * G + hh) * D; };
+  const int grp = tid / D, d = tid - grp * D;
+  // an empty slice's slot is never written: it is read, but its weight is 0 and it is skipped
+  float v[U];
+  auto load_round = [&](int c0, int jb, int n) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + NGRP * u;
+      v[u] = j < n ? prow(c0 + j)[d] : 0.f;
+    }
+  };
+  const float lv = tid < nt ? lse_of(tid) : kNegInf;
+  load_round(0, grp, min(NT, nt));
+  float M = lv;
+  for (int j = tid + NT; j < nt; j += NT) M = fmaxf(M, lse_of(j));
   for (int o = 32; o; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   if (lane == 0) red[wave] = M;
   __syncthreads();
   M = red[0];
   for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
-  const int grp = tid / D, d = tid - grp * D;
   float acc = 0.f, wsum = 0.f;
   for (int c0 = 0; c0 < nt; c0 += NT) {
     const int n = min(NT, nt - c0);
-    __syncthreads();  // the previous chunk's weights (and red) are consumed
+    __syncthreads();  // the previous round's weights are consumed
+    float w = 0.f;
     if (tid < n) {
-      const int k = k0 + c0 + tid;
-      const int64_t slot = int64_t(k) + gid;
-      sj[tid] = slot;
-      wj[tid] = live(k) ? __expf(pl[slot * G + hh] - M) : 0.f;
+      const float l = c0 == 0 ? lv : lse_of(c0 + tid);
+      w = live(k0 + c0 + tid) ? __expf(l - M) : 0.f;
+      wj[tid] = w;
     }
+    wsum += w;
     __syncthreads();
-#pragma unroll 8
-    for (int j = grp; j < n; j += NGRP) {
-      // an empty slice's slot is never written: its weight is 0 and its contents are skipped
-      const float w = wj[j];
-      const float v = po[(sj[j] * G + hh) * D + d];
-      acc += w != 0.f ? w * v : 0.f;
+    for (int jb = grp; jb < n; jb += NGRP * U) {
+      if (c0 > 0 || jb > grp) load_round(c0, jb, n);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = jb + NGRP * u;
+        if (j < n) {
+          const float wu = wj[j];
+          acc += wu != 0.f ? wu * v[u] : 0.f;
+        }
+      }
     }
-    if (tid == 0)
-      for (int j = 0; j < n; ++j) wsum += wj[j];
   }
   part[grp][d] = acc;
+  for (int o = 32; o; o >>= 1) wsum += __shfl_xor(wsum, o);
+  if (lane == 0) red2[wave] = wsum;
   __syncthreads();
-  if (tid == 0) red[0] = wsum;
-  __syncthreads();
-  const float L = red[0];
+  float L = red2[0];
+  for (int w = 1; w < NW; ++w) L += red2[w];
   for (int e = tid; e < D; e += NT) {
     float o = 0.f;
     for (int g2 = 0; g2 < NGRP; ++g2) o += part[g2][e];
@@ -704,12 +730,17 @@ int launch_combine(const Plan& p, char* ws, float* out, float* lse, void* stream
   const sd_config& c = p.cfg;
   const dim3 grid(c.n_q_heads, c.batch);
   const int NG = c.batch * c.n_kv_heads;
-  if (c.head_dim == 128)
-    hipLaunchKernelGGL(k_combine<128>, grid, dim3(kCombineThreads), 0, st, at<float>(ws, p.o_po), at<float>(ws, p.o_pl),
-                       at<int32_t>(ws, p.o_gpre), NG, p.attend_blocks, p.G, c.n_q_heads, c.n_kv_heads, p.Gq, out, lse);
-  else
-    hipLaunchKernelGGL(k_combine<64>, grid, dim3(kCombineThreads), 0, st, at<float>(ws, p.o_po), at<float>(ws, p.o_pl),
-                       at<int32_t>(ws, p.o_gpre), NG, p.attend_blocks, p.G, c.n_q_heads, c.n_kv_heads, p.Gq, out, lse);
+  // partials per group: about attend_blocks / groups + 1
+  const bool few = int64_t(p.attend_blocks) <= int64_t(16) * NG;
+#define SD_COMBINE(D, NT)                                                                                   \
+  hipLaunchKernelGGL((k_combine<D, NT>), grid, dim3(NT), 0, st, at<float>(ws, p.o_po), at<float>(ws, p.o_pl), \
+                     at<int32_t>(ws, p.o_gpre), NG, p.attend_blocks, p.G, c.n_q_heads, c.n_kv_heads, p.Gq, out, lse)
+  if (c.head_dim == 128) {
+    if (few) SD_COMBINE(128, 256); else SD_COMBINE(128, 1024);
+  } else {
+    if (few) SD_COMBINE(64, 256); else SD_COMBINE(64, 1024);
+  }
+#undef SD_COMBINE
   return int(hipGetLastError());
 }
 
