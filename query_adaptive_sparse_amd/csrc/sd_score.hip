@@ -7,18 +7,20 @@
 namespace sd {
 namespace {
 // ---------------------------------------------------------------------------------------------
-// Scores. A workgroup scores kScoreRows summary rows (or candidate rows) for the query rows
-// ("slots") of one KV group: it stages the slots' queries in LDS as fp64 (exact) and the key rows
-// in LDS (one coalesced pass), then 4 lanes share a row and each runs HPT slots' dot products,
-// one fp64 fma per dimension in index order. A product of two bf16 or two fp32 values is exact in
-// fp64, so fma(q, k, acc) equals the CPU's acc + q*k step for step. A lane converts each key
-// element once for its HPT independent chains, which also hides the fma latency.
+// Scores. A workgroup scores 64 RPT summary rows (or candidate rows) for the query rows ("slots")
+// of one KV group: it stages the slots' queries in LDS as fp64 (exact) and the key rows in LDS
+// (each wave its own rows, one coalesced pass), then 4 lanes share RPT rows and each runs the dot
+// products of HPT slots with each of its RPT rows, one fp64 fma per dimension in index order. A
+// product of two bf16 or two fp32 values is exact in fp64, so fma(q, k, acc) equals the CPU's
+// acc + q*k step for step. A lane converts each key element once for its HPT chains, and each
+// query value it reads from LDS serves its RPT rows: the LDS reads of the queries, not HBM, bound
+// this kernel, so RPT = 2 halves them per row when there are rows enough for two workgroups per CU
+// at that size (else RPT = 1, for more workgroups). The HPT x RPT independent chains hide the fma
+// latency.
 // Block (0, 0, 0) also clears the device status words and the per-group arrival counters of the
 // selection.
 // ---------------------------------------------------------------------------------------------
-constexpr int kScoreRows = 64;
-
-template <typename T, int D, int HPT>
+template <typename T, int D, int HPT, int RPT>
 __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRows qm,
                                                     const T* __restrict__ keys, int64_t k_sb, int64_t k_sh,
                                                     int64_t k_st, const int32_t* __restrict__ cand,
@@ -26,6 +28,7 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRo
                                                     uint64_t local_mask, double* __restrict__ out, int64_t out_len,
                                                     uint32_t* __restrict__ status, int32_t* __restrict__ arrivals,
                                                     int n_groups, StepLens lens) {
+  constexpr int kScoreRows = 64 * RPT;
   constexpr int EPV = 16 / int(sizeof(T));
   constexpr int PPR = D / EPV;                          // 16-byte pieces per row
   constexpr int QW = D + 2;                             // padded fp64 query row
@@ -57,11 +60,21 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRo
     qv[k] = q[q_offset(qm, b, h0 + (j < nh ? j : nh - 1)) + dd];
   }
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the key loads
-  constexpr int KPT = kScoreRows * PPR / 256;
+  // lane l of wave w scores rows 16 w + l / 4 + 64 i (i < RPT); the wave loads exactly those rows,
+  // so that it can start on them as soon as its own loads arrive, with no workgroup barrier between
+  // the loads and the arithmetic
+  constexpr int WROWS = 16 * RPT;
+  constexpr int KPT = WROWS * PPR / 64;
   uint4 kreg[KPT];
   const T* kbase = keys + b * k_sb + int64_t(g) * k_sh;
+  const int wv = tid >> 6, ln = tid & 63;
+  auto piece_local = [&](int k) {  // row in the workgroup
+    const int e = (ln + 64 * k) / PPR;
+    return 16 * wv + 64 * (e >> 4) + (e & 15);
+  };
+  auto piece_col = [&](int k) { return (ln + 64 * k) % PPR; };
   auto piece_row = [&](int k) {
-    const int r = (tid + 256 * k) / PPR;
+    const int r = piece_local(k);
     return int32_t(r0 + r < n_rows ? r0 + r : n_rows - 1);
   };
   if (cand) {
@@ -73,11 +86,11 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRo
 #pragma unroll
     for (int k = 0; k < KPT; ++k) {
       const int64_t sk = src[k] < 0 ? 0 : (src[k] < n_keys ? src[k] : n_keys - 1);
-      kreg[k] = ld16(kbase + sk * k_st + ((tid + 256 * k) % PPR) * EPV);
+      kreg[k] = ld16(kbase + sk * k_st + piece_col(k) * EPV);
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < KPT; ++k) kreg[k] = ld16(kbase + int64_t(piece_row(k)) * k_st + ((tid + 256 * k) % PPR) * EPV);
+    for (int k = 0; k < KPT; ++k) kreg[k] = ld16(kbase + int64_t(piece_row(k)) * k_st + piece_col(k) * EPV);
   }
   __builtin_amdgcn_sched_barrier(0);  // every key load is issued before the queries are staged
 #pragma unroll
@@ -85,43 +98,54 @@ __global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ q, QRo
     const int i = tid + 256 * k, j = i / D, dd = i - j * D;
     if (j < nh) qs[j * QW + dd] = double(elem_f32<T>(&qv[k]));
   }
+  __syncthreads();  // the queries are staged (the key loads are still in flight)
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int i = tid + 256 * k, r = i / PPR, pc = i - r * PPR;
-    ks[r * KW + pc] = kreg[k];
-  }
-  __syncthreads();
+  for (int k = 0; k < KPT; ++k) ks[piece_local(k) * KW + piece_col(k)] = kreg[k];
+  // the wave reads only the rows it wrote: its LDS accesses are done in order
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int r = tid >> 2, j0 = (tid & 3) * HPT;
-  const int64_t row = r0 + r;
-  if (row >= rows_b || j0 >= nh) return;
-  const uint4* kr = ks + r * KW;
-  double acc[HPT];
+  if (r0 + r >= rows_b || j0 >= nh) return;  // row r + 64 i is then past the end as well
+  double acc[RPT][HPT];
   const double* qrow[HPT];
 #pragma unroll
   for (int u = 0; u < HPT; ++u) {
-    acc[u] = 0.0;
     qrow[u] = qs + min(j0 + u, nh - 1) * QW;  // slots past the group read a valid row; not stored
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) acc[i][u] = 0.0;
   }
 #pragma unroll 2
   for (int pc = 0; pc < PPR; ++pc) {
-    const uint4 piece = kr[pc];
-    const T* e = reinterpret_cast<const T*>(&piece);
-    double kd[EPV];
+    double kd[RPT][EPV];
 #pragma unroll
-    for (int x = 0; x < EPV; ++x) kd[x] = double(elem_f32<T>(e + x));
+    for (int i = 0; i < RPT; ++i) {
+      const uint4 piece = ks[(r + 64 * i) * KW + pc];
+      const T* e = reinterpret_cast<const T*>(&piece);
+#pragma unroll
+      for (int x = 0; x < EPV; ++x) kd[i][x] = double(elem_f32<T>(e + x));
+    }
 #pragma unroll
     for (int u = 0; u < HPT; ++u) {
 #pragma unroll
       for (int x = 0; x < EPV; x += 2) {
         const double2 q2 = *reinterpret_cast<const double2*>(qrow[u] + pc * EPV + x);
-        acc[u] = fma(q2.x, kd[x], acc[u]);
-        acc[u] = fma(q2.y, kd[x + 1], acc[u]);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          acc[i][u] = fma(q2.x, kd[i][x], acc[i][u]);
+          acc[i][u] = fma(q2.y, kd[i][x + 1], acc[i][u]);
+        }
       }
     }
   }
 #pragma unroll
-  for (int u = 0; u < HPT; ++u)
-    if (j0 + u < nh) out[(int64_t(b) * Hq + h0 + j0 + u) * out_len + row] = acc[u];
+  for (int i = 0; i < RPT; ++i) {
+    const int64_t row = r0 + r + 64 * i;
+    if (row < rows_b)
+#pragma unroll
+      for (int u = 0; u < HPT; ++u)
+        if (j0 + u < nh) out[(int64_t(b) * Hq + h0 + j0 + u) * out_len + row] = acc[i][u];
+  }
 }
 
 // Projected query q_p = q P (d -> 16) per head, fp64, one fma chain in index order per output. A
@@ -379,29 +403,50 @@ int score_impl(const Plan& p, const sd_tensors& t, int level, char* ws, hipStrea
     }
     return int(hipGetLastError());
   }
+  // rows per lane: 2 when that still gives two workgroups of 128 rows per CU of a 256-CU MI355X
+  auto rpt_of = [&](int64_t rows, int64_t wgs_per_row_set) {
+    return (rows + 127) / 128 * wgs_per_row_set >= 512 ? 2 : 1;
+  };
   if (c.mode == SD_HIER_TOPK && level == 1) {
-    hipLaunchKernelGGL((k_score_rows<T, D, 1>), dim3((p.len1 + kScoreRows - 1) / kScoreRows, Hq, B), dim3(256), 0, st,
-                       static_cast<const T*>(t.q), qm, static_cast<const T*>(t.kg), t.g_sb, t.g_sh,
-                       t.g_st, at<int32_t>(ws, p.o_cand), p.len1, p.M, p.G, Hq, p.local_mask, at<double>(ws, p.o_s1),
-                       p.len1, static_cast<uint32_t*>(nullptr), static_cast<int32_t*>(nullptr), 0, lens);
+    const int rpt = rpt_of(p.len1, int64_t(Hq) * B);
+#define SD_SCORE_CAND(RPT)                                                                                     \
+  hipLaunchKernelGGL((k_score_rows<T, D, 1, RPT>), dim3((p.len1 + 64 * RPT - 1) / (64 * RPT), Hq, B), dim3(256), 0, \
+                     st, static_cast<const T*>(t.q), qm, static_cast<const T*>(t.kg), t.g_sb, t.g_sh, t.g_st,       \
+                     at<int32_t>(ws, p.o_cand), p.len1, p.M, p.G, Hq, p.local_mask, at<double>(ws, p.o_s1), p.len1, \
+                     static_cast<uint32_t*>(nullptr), static_cast<int32_t*>(nullptr), 0, lens)
+    if (rpt == 2)
+      SD_SCORE_CAND(2);
+    else
+      SD_SCORE_CAND(1);
+#undef SD_SCORE_CAND
     return int(hipGetLastError());
   }
   const bool meta = c.mode == SD_HIER_TOPK;
   // query slots per lane (4 lanes per row): 1 up to 4 query rows per group, 2 up to 8, 4 up to 16
   const int hpt = p.G <= 4 ? 1 : (p.G <= 8 ? 2 : 4);
-  const dim3 grid((p.len0 + kScoreRows - 1) / kScoreRows, Hk, B);
+  const int rpt = rpt_of(p.len0, int64_t(Hk) * B);
   const T* keys = static_cast<const T*>(meta ? t.kmg : t.kg);
   const int64_t ksb = meta ? t.mg_sb : t.g_sb, ksh = meta ? t.mg_sh : t.g_sh, kst = meta ? t.mg_st : t.g_st;
-#define SD_SCORE_ROWS(HPT)                                                                                       \
-  hipLaunchKernelGGL((k_score_rows<T, D, HPT>), grid, dim3(256), 0, st, static_cast<const T*>(t.q), qm, keys, ksb, \
-                     ksh, kst, static_cast<const int32_t*>(nullptr), p.len0, p.len0, p.G, Hq, p.local_mask,          \
-                     at<double>(ws, p.o_s0), p.len0, status, at<int32_t>(ws, p.o_arrive), p.n_arrive, lens)
-  if (hpt == 1)
-    SD_SCORE_ROWS(1);
-  else if (hpt == 2)
-    SD_SCORE_ROWS(2);
-  else
-    SD_SCORE_ROWS(4);
+#define SD_SCORE_ROWS(HPT, RPT)                                                                                    \
+  hipLaunchKernelGGL((k_score_rows<T, D, HPT, RPT>), dim3((p.len0 + 64 * RPT - 1) / (64 * RPT), Hk, B), dim3(256), 0, \
+                     st, static_cast<const T*>(t.q), qm, keys, ksb, ksh, kst, static_cast<const int32_t*>(nullptr),   \
+                     p.len0, p.len0, p.G, Hq, p.local_mask, at<double>(ws, p.o_s0), p.len0, status,                   \
+                     at<int32_t>(ws, p.o_arrive), p.n_arrive, lens)
+  if (rpt == 2) {
+    if (hpt == 1)
+      SD_SCORE_ROWS(1, 2);
+    else if (hpt == 2)
+      SD_SCORE_ROWS(2, 2);
+    else
+      SD_SCORE_ROWS(4, 2);
+  } else {
+    if (hpt == 1)
+      SD_SCORE_ROWS(1, 1);
+    else if (hpt == 2)
+      SD_SCORE_ROWS(2, 1);
+    else
+      SD_SCORE_ROWS(4, 1);
+  }
 #undef SD_SCORE_ROWS
   if (p.long0)
     hipLaunchKernelGGL(k_row_minmax, dim3(p.score_blocks0, Hq, B), dim3(256), 0, st, at<double>(ws, p.o_s0),
