@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
   __shared__ double wred[kSelW], wred2[kSelW];
   __shared__ int wcnt[kSelW];
   __shared__ double res_d;
-  __shared__ int res_i, res_state, ncand;
+  __shared__ int res_i, res_state, ncand, nkept;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
@@ -234,6 +234,14 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
   for (int k = 0; k < kLaneEntries; ++k) {
     const int i = tid + kSelT * k;
     sv[k] = local ? 0.0 : a.s[row * a.len + (i < cap ? i : cap - 1)];
+  }
+  // candidate rows: the chunk id of each of the lane's entries, loaded with the scores (the bitmap
+  // of the chosen chunks is built from them at the end)
+  int32_t cid[kLaneEntries];
+#pragma unroll
+  for (int k = 0; k < kLaneEntries; ++k) {
+    const int i = tid + kSelT * k;
+    cid[k] = (a.kind == 2 && !local && k < EPL) ? a.cand_in[row * a.len + (i < cap ? i : cap - 1)] : 0;
   }
   double smax = kNegInfD, smin = kPosInfD;
 #pragma unroll
@@ -459,48 +467,59 @@ __global__ __launch_bounds__(kSelT) void k_select_head(GroupSelArgs a) {
 
   // ---- 5. per-head outputs
   if (a.kind == 1) {
-    // kept segments in ascending order -> candidate chunk lists (first wave)
-    if (!local && wv == 0) {
+    // kept segments in ascending order, as a list in LDS (the fallback sort's index array is free
+    // now), then their candidate chunk ids, written by every thread
+    uint16_t* segs = fidx;
+    if (wv == 0) {
       int base = 0;
       for (int w0 = 0; w0 < words_row; w0 += 64) {
         const int w = w0 + lane;
-        const int pc = w < words_row ? __popc(selb[w]) : 0;
+        uint32_t m = (!local && w < words_row) ? selb[w] : 0u;
+        const int pc = __popc(m);
         const int incl = wave_scan_i32_dpp(pc, lane);
         int rank = base + incl - pc;
-        if (w < words_row) {
-          uint32_t m = selb[w];
-          while (m) {
-            const int bit = __ffs(m) - 1;
-            m &= m - 1;
-            const int seg = w * 32 + bit;
-            for (int j = 0; j < a.seg_size; ++j)
-              a.cand_out[row * a.cand_len + int64_t(rank) * a.seg_size + j] = seg * a.seg_size + j;
-            ++rank;
-          }
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          m &= m - 1;
+          segs[rank++] = uint16_t(w * 32 + bit);
         }
         base += __builtin_amdgcn_readlane(incl, 63);
       }
+      if (lane == 0) nkept = base;
+    }
+    __syncthreads();
+    const int total = nkept * a.seg_size;
+    int32_t* co = a.cand_out + row * a.cand_len;
+    for (int e = tid; e < total; e += kSelT) {
+      const int r = e / a.seg_size;
+      co[e] = int(segs[r]) * a.seg_size + (e - r * a.seg_size);
     }
     return;
   }
   if (a.kind == 0) {
     for (int w = tid; w < a.words; w += kSelT) a.bits[row * a.words + w] = (!local && w < words_row) ? selb[w] : 0u;
   } else {
-    for (int w = tid; w < a.words; w += kSelT) a.bits[row * a.words + w] = 0u;
+    // the chosen candidates' chunk ids as a bitmap over the chunks: built in LDS (the fallback
+    // sort's key array is free now) and stored whole, or, past its size, cleared and set in place
+    const bool in_lds = a.words <= int64_t(2 * kSmallRowMax);
+    uint32_t* hb = in_lds ? reinterpret_cast<uint32_t*>(fkey) : a.bits + row * a.words;
+    for (int w = tid; w < a.words; w += kSelT) hb[w] = 0u;
     __syncthreads();  // the zeroing stores complete before the atomics below
     if (!local)
-      for (int w = tid; w < words_row; w += kSelT) {
-        uint32_t m = selb[w];
-        while (m) {
-          const int bit = __ffs(m) - 1;
-          m &= m - 1;
-          int e = a.cand_in[row * a.len + w * 32 + bit];
+#pragma unroll
+      for (int k = 0; k < kLaneEntries; ++k) {
+        const int i = tid + kSelT * k;
+        if (k < EPL && i < L && ((selb[i >> 5] >> (i & 31)) & 1u)) {
+          int e = cid[k];
           e = e < 0 ? 0 : (e < int(a.n_entries) ? e : int(a.n_entries) - 1);
-          atomicOr(&a.bits[row * a.words + (e >> 5)], 1u << (e & 31));
+          atomicOr(&hb[e >> 5], 1u << (e & 31));
         }
       }
+    if (in_lds) {
+      __syncthreads();
+      for (int w = tid; w < a.words; w += kSelT) a.bits[row * a.words + w] = hb[w];
+    }
   }
-
 }
 
 // GQA union and compaction of short rows, one workgroup per (sequence, KV group), launched after
