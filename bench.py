@@ -442,10 +442,11 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    # timed steps. The attention launch is bracketed by events (on the stream the library launches
-    # on) on every `stride`-th timed step: an event pair adds ~6 us of idle time to its step, so it
-    # is recorded on a sample of about five steps rather than on every step; the per-stage
-    # breakdown is taken in a separate, untimed loop below.
+    # timed steps, each one sparse_decode_step call. The attention launch is bracketed by events
+    # (on the stream the library launches on) on every `stride`-th timed step, which then runs the
+    # stages as separate calls: an event pair adds ~6 us of idle time to its step, so it is recorded
+    # on a sample of about five steps rather than on every step; the per-stage breakdown is taken
+    # in a separate, untimed loop below.
     K = args.steps
     stride = max(1, K // 5)
     sampled = [i for i in range(K) if i % stride == 0]
@@ -459,15 +460,16 @@ def main():
         if scratch is not None:
             scratch.fill_(i & 0xFF)
             fl[i][0].record()
-        for level in range(dec.levels):
-            dec.score_chunks(t, level)
-            dec.select(level)
-        if e is not None:
+        if e is None:
+            dec.step(t, out, lse)  # the whole step in one library call
+        else:
+            for level in range(dec.levels):
+                dec.score_chunks(t, level)
+                dec.select(level)
             e[0].record()
-        dec.attend(t)
-        if e is not None:
+            dec.attend(t)
             e[1].record()
-        dec.combine(out, lse)
+            dec.combine(out, lse)
         if scratch is not None:
             fl[i][1].record()
     torch.cuda.synchronize()

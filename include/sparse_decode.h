@@ -209,6 +209,17 @@ sd_status sparse_decode_attend(const sd_handle* h, const sd_tensors* t, void* ws
 sd_status sparse_decode_combine(const sd_handle* h, void* ws, float* out, float* lse_out,
                                 void* stream);
 
+/* One whole step -- score and select at every level, attend, combine -- on the caller's
+ * workspace, in one call: the stages the SSA summary's decode kernel chains (핵심 기여), with the
+ * host-side cost of one call instead of one per stage. Same arguments, layouts and results as
+ * calling sparse_decode_score_chunks / sparse_decode_select per level, then sparse_decode_attend
+ * and sparse_decode_combine, on `stream`; outputs out fp32 [B][T][Hq][d] and lse_out fp32
+ * [B][T][Hq], contiguous device buffers (out 16-byte aligned). Errors, all from host checks with
+ * nothing enqueued: SD_EINVAL (NULL handle, tensors or outputs), SD_EWORKSPACE (NULL or not
+ * 256-byte aligned workspace); SD_EHIP for a failed launch. */
+sd_status sparse_decode_step(const sd_handle* h, const sd_tensors* t, void* ws, float* out, float* lse_out,
+                             void* stream);
+
 /* One whole step -- score and select at every level, attend, combine -- with the library's own
  * static device scratch as the workspace. For callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the call

@@ -306,6 +306,38 @@ sd_status sparse_decode_combine(const sd_handle* h, void* ws, float* out, float*
   return ok();
 }
 
+namespace {
+// The whole step on `w`: score and select at every level, attend, combine. The tensors and outputs
+// are checked first, so a rejected call enqueues nothing.
+sd_status enqueue_step(const sd::Plan& p, const sd_tensors* t, char* w, float* out, float* lse_out, void* stream,
+                       const char* who) {
+  sd_status st;
+  for (int level = 0; level < p.levels; ++level)
+    if ((st = check_tensors(p, t, true, level)) != SD_OK) return st;
+  if ((st = check_tensors(p, t, false, 0)) != SD_OK) return st;
+  if (!out || !lse_out || !aligned16(out))
+    return fail(SD_EINVAL, "%s: out (16-byte aligned) and lse_out must be non-NULL", who);
+  int e = 0;
+  for (int level = 0; level < p.levels && !e; ++level) {
+    e = sd::launch_score(p, *t, level, w, stream);
+    if (!e) e = sd::launch_select(p, level, w, stream);
+  }
+  if (!e) e = sd::launch_attend(p, *t, w, stream);
+  if (!e) e = sd::launch_combine(p, w, out, lse_out, stream);
+  if (e) return fail(SD_EHIP, "%s: HIP error %d (%s)", who, e, sd::hip_error_string(e));
+  return ok();
+}
+}  // namespace
+
+sd_status sparse_decode_step(const sd_handle* h, const sd_tensors* t, void* ws, float* out, float* lse_out,
+                             void* stream) {
+  if (!h) return fail(SD_EINVAL, "step: NULL handle");
+  const sd::Plan& p = h->plan;
+  sd_status st = check_ws(p, ws);
+  if (st != SD_OK) return st;
+  return enqueue_step(p, t, static_cast<char*>(ws), out, lse_out, stream, "step");
+}
+
 sd_status sparse_decode_step_static(const sd_handle* h, const sd_tensors* t, float* out, float* lse_out,
                                     void* stream) {
   if (!h) return fail(SD_EINVAL, "step_static: NULL handle");
@@ -313,6 +345,8 @@ sd_status sparse_decode_step_static(const sd_handle* h, const sd_tensors* t, flo
   if (p.ws_bytes > sd::kStaticScratchBytes)
     return fail(SD_EUNSUPPORTED, "step_static: the step needs a %zu-byte workspace, above the %zu-byte static scratch",
                 p.ws_bytes, sd::kStaticScratchBytes);
+  // the tensors are checked before the scratch address is looked up (nothing touches the GPU on a
+  // rejected call)
   sd_status st;
   for (int level = 0; level < p.levels; ++level)
     if ((st = check_tensors(p, t, true, level)) != SD_OK) return st;
@@ -322,15 +356,7 @@ sd_status sparse_decode_step_static(const sd_handle* h, const sd_tensors* t, flo
   void* ws = nullptr;
   int e = sd::static_scratch(&ws);
   if (e) return fail(SD_EHIP, "step_static: static scratch address: HIP error %d (%s)", e, sd::hip_error_string(e));
-  char* w = static_cast<char*>(ws);
-  for (int level = 0; level < p.levels && !e; ++level) {
-    e = sd::launch_score(p, *t, level, w, stream);
-    if (!e) e = sd::launch_select(p, level, w, stream);
-  }
-  if (!e) e = sd::launch_attend(p, *t, w, stream);
-  if (!e) e = sd::launch_combine(p, w, out, lse_out, stream);
-  if (e) return fail(SD_EHIP, "step_static: HIP error %d (%s)", e, sd::hip_error_string(e));
-  return ok();
+  return enqueue_step(p, t, static_cast<char*>(ws), out, lse_out, stream, "step_static");
 }
 
 sd_status sparse_decode_selection_view(const sd_handle* h, void* ws, sd_selection_view* v) {

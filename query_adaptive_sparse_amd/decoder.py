@@ -125,12 +125,11 @@ class SparseDecoder:
                                 self._stream())
 
     def step(self, t: N.sd_tensors, out: torch.Tensor, lse: torch.Tensor):
-        """score -> select (per level) -> attend -> combine, enqueued on the current stream."""
-        for level in range(self.levels):
-            self.score_chunks(t, level)
-            self.select(level)
-        self.attend(t)
-        self.combine(out, lse)
+        """score -> select (per level) -> attend -> combine, enqueued on the current stream by one
+        library call (sparse_decode_step)."""
+        assert out.dtype == torch.float32 and lse.dtype == torch.float32 and out.is_contiguous() and lse.is_contiguous()
+        N.sparse_decode_step(self.handle, t, self.alloc_workspace().data_ptr(), out.data_ptr(), lse.data_ptr(),
+                             self._stream())
 
     def status(self) -> int:
         """The device status word after the enqueued work (synchronises the current stream). It is

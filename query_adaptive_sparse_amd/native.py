@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "SD_OK", 1: "SD_EINVAL", 2: "SD_EUNSUPPORTED", 3: "SD_EWORKSP
 
 EXPORTS = ("sparse_decode_init", "sparse_decode_num_levels", "sparse_decode_attend_blocks",
            "sparse_decode_score_chunks", "sparse_decode_select",
-           "sparse_decode_attend", "sparse_decode_combine", "sparse_decode_step_static", "sparse_decode_selection_view",
+           "sparse_decode_attend", "sparse_decode_combine", "sparse_decode_step", "sparse_decode_step_static",
+           "sparse_decode_selection_view",
            "sparse_decode_last_error", "sparse_decode_destroy",
            "sparse_prefill_init", "sparse_prefill_select", "sparse_prefill_attend", "sparse_prefill_view",
            "sparse_prefill_destroy",
@@ -144,6 +145,8 @@ def lib() -> ctypes.CDLL:
         L.sparse_decode_attend.restype = st
         L.sparse_decode_combine.argtypes = [vp, vp, vp, vp, vp]
         L.sparse_decode_combine.restype = st
+        L.sparse_decode_step.argtypes = [vp, ctypes.POINTER(sd_tensors), vp, vp, vp, vp]
+        L.sparse_decode_step.restype = st
         L.sparse_decode_step_static.argtypes = [vp, ctypes.POINTER(sd_tensors), vp, vp, vp]
         L.sparse_decode_step_static.restype = st
         L.sparse_decode_selection_view.argtypes = [vp, vp, ctypes.POINTER(sd_selection_view)]
@@ -207,6 +210,10 @@ def sparse_decode_attend(handle, tensors: sd_tensors, ws: int, stream: int):
 
 def sparse_decode_combine(handle, ws: int, out: int, lse_out: int, stream: int):
     _check(lib().sparse_decode_combine(handle, ws, out, lse_out, stream))
+
+
+def sparse_decode_step(handle, tensors: sd_tensors, ws: int, out: int, lse_out: int, stream: int):
+    _check(lib().sparse_decode_step(handle, ctypes.byref(tensors), ws, out, lse_out, stream))
 
 
 def sparse_decode_step_static(handle, tensors: sd_tensors, out: int, lse_out: int, stream: int):

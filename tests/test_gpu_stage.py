@@ -5,6 +5,7 @@
   max-abs 2e-3 and relative-L2 1e-3 of the oracle.
 * select fed the oracle's scores: the fp64 score rows are written into the workspace after the score
   call and select runs on them; per-head sets and group lists bit-exact.
+* the stage entry points called one by one against the whole-step entry point: equal bit for bit.
 """
 import numpy as np
 import pytest
@@ -86,3 +87,31 @@ def test_select_on_oracle_scores(name):
         n = int(got["count"][b, g])
         assert n == len(r["union"]) and np.array_equal(got["list"][b, g, :n].numpy(), r["union"]), (name, b, g)
     print(f"[stage] select on oracle scores {name}: every set and list equal", flush=True)
+
+
+@pytest.mark.parametrize("name", ["c1s", "c2s", "c3s", "c4s", "c5s", "c3s_mq4"])
+def test_stage_calls_equal_whole_step(name):
+    """The four stage entry points called one by one (score and select per level, attend, combine)
+    give the same outputs, lse and group lists as the whole-step entry point, bit for bit: the same
+    kernels in the same order."""
+    w = configs.get(name)
+    inp = gen.make_inputs(w, device="cuda")
+    ref = parity.run_gpu(w, inp)  # through sparse_decode_step
+    dec = _decoder(w)
+    t = parity.lib_tensors(inp)
+    T = w.n_queries
+    out = torch.full((w.batch, T, w.n_q_heads, w.head_dim), float("nan"), device="cuda")
+    lse = torch.full((w.batch, T, w.n_q_heads), float("nan"), device="cuda")
+    for level in range(dec.levels):
+        dec.score_chunks(t, level)
+        dec.select(level)
+    dec.attend(t)
+    dec.combine(out, lse)
+    torch.cuda.synchronize()
+    sel = dec.selection()
+    assert np.array_equal(out.cpu().numpy().reshape(ref["out"].shape), ref["out"]), name
+    assert np.array_equal(lse.cpu().numpy().reshape(ref["lse"].shape), ref["lse"]), name
+    assert torch.equal(sel["count"].cpu(), ref["sel"]["count"]), name
+    for (b, g) in np.ndindex(*sel["count"].shape):
+        n = int(sel["count"][b, g])
+        assert torch.equal(sel["list"][b, g, :n].cpu(), ref["sel"]["list"][b, g, :n]), (name, b, g)
