@@ -59,16 +59,24 @@ typedef struct {
   const void* kg; const void* vg; int64_t kvg_sb, kvg_sh, kvg_st;
 } gp_tensors;
 
-/* Validate and copy `cfg`, create a handle (host memory only).
- * Errors: SD_EINVAL (null pointer, inconsistent shape, n_tokens not a multiple of chunk_size,
- * bad scale), SD_EUNSUPPORTED (head_dim != 128, kv_dtype != SD_BF16). */
-sd_status sparse_gist_prefill_init(const gp_config* cfg, gp_handle** out);
+/* Validate and copy `cfg`, create a handle (host memory only) and report the bytes of device
+ * workspace the attention call needs: an fp16 copy of every KV head's values (gists, then raw
+ * tokens) scaled by a power of two, 2 (M + N) d bytes per (sequence, KV head), plus a few words
+ * per head. Errors: SD_EINVAL (null pointer, inconsistent shape, n_tokens not a multiple of
+ * chunk_size, bad scale), SD_EUNSUPPORTED (head_dim != 128, kv_dtype != SD_BF16). */
+sd_status sparse_gist_prefill_init(const gp_config* cfg, gp_handle** out, size_t* workspace_bytes);
 
 /* Attention of every raw and gist query over its visible keys. out fp32 [B][Hq][N][d] and
- * out_gist fp32 [B][Hq][M][d], both contiguous and 16-byte aligned, are written whole.
- * Errors: SD_EINVAL (null or misaligned pointer, bad stride), SD_EHIP (launch failure). */
-sd_status sparse_gist_prefill_attend(const gp_handle* h, const gp_tensors* t, float* out, float* out_gist,
-                                     void* stream);
+ * out_gist fp32 [B][Hq][M][d], both contiguous and 16-byte aligned, are written whole. `ws` is
+ * the caller's device workspace (256-byte aligned, the size init reported; its contents on entry
+ * do not matter). Arithmetic: q.k on bf16 inputs with fp32 accumulation; P.V in fp16 with fp32
+ * accumulation (V converted under a power-of-two scale per KV head, exactly for every value down
+ * to 2^-29 of the head's max |v|; P rounded to fp16 and the normaliser summed from the same
+ * rounded values), so an output differs from exact attention by at most about 2^-11 times the
+ * head's max |v|. Errors: SD_EINVAL (null or misaligned pointer, bad stride), SD_EWORKSPACE
+ * (null or misaligned workspace), SD_EHIP (launch failure). */
+sd_status sparse_gist_prefill_attend(const gp_handle* h, const gp_tensors* t, void* ws, float* out,
+                                     float* out_gist, void* stream);
 
 /* Release a handle (host memory only). NULL is ignored. */
 void sparse_gist_prefill_destroy(gp_handle* h);

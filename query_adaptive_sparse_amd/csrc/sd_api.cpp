@@ -500,9 +500,10 @@ sd_status sparse_prefill_view(const sp_handle* h, void* ws, sp_view* v) {
 void sparse_prefill_destroy(sp_handle* h) { delete h; }
 
 // ---- gist-masked (SSA) prefill
-sd_status sparse_gist_prefill_init(const gp_config* cfg, gp_handle** out) {
-  if (!cfg || !out) return fail(SD_EINVAL, "gist prefill init: NULL argument");
+sd_status sparse_gist_prefill_init(const gp_config* cfg, gp_handle** out, size_t* workspace_bytes) {
+  if (!cfg || !out || !workspace_bytes) return fail(SD_EINVAL, "gist prefill init: NULL argument");
   *out = nullptr;
+  *workspace_bytes = 0;
   const gp_config& c = *cfg;
   if (c.batch < 1) return fail(SD_EINVAL, "batch must be >= 1 (got %d)", c.batch);
   if (c.n_q_heads < 1 || c.n_kv_heads < 1 || c.n_q_heads % c.n_kv_heads)
@@ -518,16 +519,33 @@ sd_status sparse_gist_prefill_init(const gp_config* cfg, gp_handle** out) {
     return fail(SD_EINVAL, "softmax_scale must be finite and > 0 (got %g)", c.softmax_scale);
   gp_handle* h = new (std::nothrow) gp_handle();
   if (!h) return fail(SD_EINVAL, "gist prefill init: out of host memory");
-  h->plan.cfg = c;
-  h->plan.G = c.n_q_heads / c.n_kv_heads;
-  h->plan.M = int32_t(c.n_tokens / c.chunk_size);
+  sd::GistPlan& p = h->plan;
+  p.cfg = c;
+  p.G = c.n_q_heads / c.n_kv_heads;
+  p.M = int32_t(c.n_tokens / c.chunk_size);
+  p.R = p.M + c.n_tokens;
+  p.nslab = int32_t((p.R + sd::kGpSlab - 1) / sd::kGpSlab);
+  const int64_t heads = int64_t(c.batch) * c.n_kv_heads;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  p.o_vmaxp = take(size_t(heads * p.nslab) * 4);
+  p.o_vexp = take(size_t(heads) * 4);
+  p.o_vc = take(size_t(heads * p.R) * size_t(c.head_dim) * 2);
+  p.ws_bytes = off;
+  *workspace_bytes = off;
   *out = h;
   return ok();
 }
 
-sd_status sparse_gist_prefill_attend(const gp_handle* h, const gp_tensors* t, float* out, float* out_gist,
+sd_status sparse_gist_prefill_attend(const gp_handle* h, const gp_tensors* t, void* ws, float* out, float* out_gist,
                                      void* stream) {
   if (!h) return fail(SD_EINVAL, "gist prefill attend: NULL handle");
+  if (!ws) return fail(SD_EWORKSPACE, "gist prefill attend: workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(SD_EWORKSPACE, "gist prefill attend: workspace not 256-byte aligned");
   if (!t) return fail(SD_EINVAL, "gist prefill attend: tensors is NULL");
   const void* ptrs[6] = {t->q, t->k, t->v, t->qg, t->kg, t->vg};
   for (const void* ptr : ptrs)
@@ -541,7 +559,7 @@ sd_status sparse_gist_prefill_attend(const gp_handle* h, const gp_tensors* t, fl
     return fail(SD_EINVAL, "gist prefill: strides must be multiples of 8 elements with rows of at least head_dim");
   if (!out || !out_gist || !aligned16(out) || !aligned16(out_gist))
     return fail(SD_EINVAL, "gist prefill attend: out and out_gist must be non-NULL 16-byte aligned pointers");
-  int e = sd::launch_gist_prefill(h->plan, *t, out, out_gist, stream);
+  int e = sd::launch_gist_prefill(h->plan, *t, static_cast<char*>(ws), out, out_gist, stream);
   if (e) return fail(SD_EHIP, "gist prefill attend: HIP error %d (%s)", e, sd::hip_error_string(e));
   return ok();
 }

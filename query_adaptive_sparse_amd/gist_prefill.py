@@ -32,7 +32,8 @@ class GistPrefill:
         cfg.n_tokens, cfg.chunk_size, cfg.kv_dtype = n_tokens, chunk_size, N.SD_BF16
         cfg.softmax_scale = softmax_scale
         self.cfg = cfg
-        self.handle = N.sparse_gist_prefill_init(cfg)
+        self.handle, self.ws_bytes = N.sparse_gist_prefill_init(cfg)
+        self._ws = None
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -43,9 +44,16 @@ class GistPrefill:
                 pass
             self.handle = None
 
+    def workspace(self, device=None) -> torch.Tensor:
+        """The device workspace (allocated once, 256-byte aligned by the caching allocator)."""
+        if self._ws is None:
+            self._ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device or "cuda")
+            assert self._ws.data_ptr() % 256 == 0
+        return self._ws
+
     def attend(self, t: N.gp_tensors, out: torch.Tensor, out_gist: torch.Tensor):
         """out fp32 [B][Hq][N][d], out_gist fp32 [B][Hq][M][d], both contiguous."""
         for o in (out, out_gist):
             assert o.dtype == torch.float32 and o.is_contiguous()
-        N.sparse_gist_prefill_attend(self.handle, t, out.data_ptr(), out_gist.data_ptr(),
-                                     torch.cuda.current_stream().cuda_stream)
+        N.sparse_gist_prefill_attend(self.handle, t, self.workspace(out.device).data_ptr(), out.data_ptr(),
+                                     out_gist.data_ptr(), torch.cuda.current_stream().cuda_stream)

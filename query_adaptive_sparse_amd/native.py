@@ -165,9 +165,10 @@ def lib() -> ctypes.CDLL:
         L.sparse_prefill_view.restype = st
         L.sparse_prefill_destroy.argtypes = [vp]
         L.sparse_prefill_destroy.restype = None
-        L.sparse_gist_prefill_init.argtypes = [ctypes.POINTER(gp_config), ctypes.POINTER(vp)]
+        L.sparse_gist_prefill_init.argtypes = [ctypes.POINTER(gp_config), ctypes.POINTER(vp),
+                                               ctypes.POINTER(ctypes.c_size_t)]
         L.sparse_gist_prefill_init.restype = st
-        L.sparse_gist_prefill_attend.argtypes = [vp, ctypes.POINTER(gp_tensors), vp, vp, vp]
+        L.sparse_gist_prefill_attend.argtypes = [vp, ctypes.POINTER(gp_tensors), vp, vp, vp, vp]
         L.sparse_gist_prefill_attend.restype = st
         L.sparse_gist_prefill_destroy.argtypes = [vp]
         L.sparse_gist_prefill_destroy.restype = None
@@ -261,14 +262,15 @@ def sparse_prefill_destroy(handle):
 
 
 def sparse_gist_prefill_init(cfg: gp_config):
-    """Returns the handle (the path needs no workspace)."""
+    """Returns (handle, workspace bytes)."""
     h = ctypes.c_void_p()
-    _check(lib().sparse_gist_prefill_init(ctypes.byref(cfg), ctypes.byref(h)))
-    return h
+    n = ctypes.c_size_t(0)
+    _check(lib().sparse_gist_prefill_init(ctypes.byref(cfg), ctypes.byref(h), ctypes.byref(n)))
+    return h, n.value
 
 
-def sparse_gist_prefill_attend(handle, tensors: gp_tensors, out: int, out_gist: int, stream: int):
-    _check(lib().sparse_gist_prefill_attend(handle, ctypes.byref(tensors), out, out_gist, stream))
+def sparse_gist_prefill_attend(handle, tensors: gp_tensors, ws: int, out: int, out_gist: int, stream: int):
+    _check(lib().sparse_gist_prefill_attend(handle, ctypes.byref(tensors), ws, out, out_gist, stream))
 
 
 def sparse_gist_prefill_destroy(handle):

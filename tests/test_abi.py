@@ -313,38 +313,23 @@ def test_gist_init_rejects(kw, status, msg):
 
 
 def test_gist_attend_rejects_before_enqueue():
-    h = N.sparse_gist_prefill_init(_gist_cfg())
+    h, nbytes = N.sparse_gist_prefill_init(_gist_cfg())
+    w = configs.get("p2s")
+    # the fp16 value copy (gists, then raw rows, per sequence and KV head) dominates the workspace
+    assert nbytes >= w.batch * w.n_kv_heads * (w.n_tokens + w.n_tokens // w.chunk_size) * w.head_dim * 2
     L = N.lib()
     t = N.gp_tensors()
-    assert L.sparse_gist_prefill_attend(None, ctypes.byref(t), 0x1000, 0x2000, None) == N.SD_EINVAL
-    assert L.sparse_gist_prefill_attend(h, None, 0x1000, 0x2000, None) == N.SD_EINVAL
-    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), 0x1000, 0x2000, None) == N.SD_EINVAL  # null tensors
+    ws = 0x100000
+    assert L.sparse_gist_prefill_attend(None, ctypes.byref(t), ws, 0x1000, 0x2000, None) == N.SD_EINVAL
+    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), None, 0x1000, 0x2000, None) == N.SD_EWORKSPACE
+    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), ws + 16, 0x1000, 0x2000, None) == N.SD_EWORKSPACE
+    assert L.sparse_gist_prefill_attend(h, None, ws, 0x1000, 0x2000, None) == N.SD_EINVAL
+    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), ws, 0x1000, 0x2000, None) == N.SD_EINVAL  # null tensors
     t.q, t.k, t.v, t.qg, t.kg, t.vg = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000
     t.q_st = t.kv_st = t.qg_st = t.kvg_st = 128
     t.kvg_st = 100                                                      # gist rows not 16-byte aligned
-    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), 0x1000, 0x2000, None) == N.SD_EINVAL
+    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), ws, 0x1000, 0x2000, None) == N.SD_EINVAL
     t.kvg_st = 128
-    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), None, 0x2000, None) == N.SD_EINVAL  # null out
-    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), 0x1000, 0x2008, None) == N.SD_EINVAL  # misaligned
+    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), ws, None, 0x2000, None) == N.SD_EINVAL  # null out
+    assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), ws, 0x1000, 0x2008, None) == N.SD_EINVAL  # misaligned
     N.sparse_gist_prefill_destroy(h)
-
-
-def test_step_rejects_before_enqueue():
-    """The whole-step call checks its handle, workspace, tensors and outputs on the host before it
-    enqueues anything."""
-    L = N.lib()
-    t = N.sd_tensors()
-    h, _ = _init(**_params("c3s"))
-    assert L.sparse_decode_step(None, ctypes.byref(t), 256, 0x2000, 0x3000, None) == N.SD_EINVAL
-    assert L.sparse_decode_step(h, ctypes.byref(t), None, 0x2000, 0x3000, None) == N.SD_EWORKSPACE
-    assert L.sparse_decode_step(h, ctypes.byref(t), 0x104, 0x2000, 0x3000, None) == N.SD_EWORKSPACE
-    assert L.sparse_decode_step(h, None, 256, 0x2000, 0x3000, None) == N.SD_EINVAL
-    assert L.sparse_decode_step(h, ctypes.byref(t), 256, 0x2000, 0x3000, None) == N.SD_EINVAL
-    assert b"q must be" in L.sparse_decode_last_error()
-    t.q, t.q_sb, t.q_sh = 0x10000, 32 * 128, 128
-    t.kg, t.vg, t.g_st = 0x20000, 0x30000, 128
-    t.k, t.v, t.kv_st = 0x40000, 0x50000, 128
-    assert L.sparse_decode_step(h, ctypes.byref(t), 256, None, 0x3000, None) == N.SD_EINVAL
-    assert L.sparse_decode_step(h, ctypes.byref(t), 256, 0x2004, 0x3000, None) == N.SD_EINVAL
-    assert b"step: out" in L.sparse_decode_last_error()
-    N.sparse_decode_destroy(h)
