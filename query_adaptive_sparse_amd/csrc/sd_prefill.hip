@@ -6,9 +6,11 @@
 //                    keys per workgroup (the next block's keys load during a block's MFMAs), on
 //                    the fp64 MFMA (16 keys x 16 queries x 4 dimensions per instruction; chained
 //                    over the dimensions in index order, each output is the sequential fma chain
-//                    of the dot product), and each query's max per key block;
+//                    of the dot product); per key block and query, the max m_b over the visible
+//                    keys and z_b, the sum of exp(scale (s - m_b)) over them;
 //   k_pf_rowmax      every window query's max over its visible keys;
-//   k_pf_zpart       per 2048-key slab and query, the sum of exp(scale (s - max)) over the slab;
+//   k_pf_zslab       per 2048-key slab and query, the sum over the slab's blocks, in order, of
+//                    z_b exp(scale (m_b - max)): the slab's sum of exp(scale (s - max));
 //   k_pf_importance  per key, the sum over the window queries (in order) of the query's softmax
 //                    probability of that key, and the slab's max / min of it;
 //   k_pf_global      per key, the sparse heads' importances summed in head order;
@@ -34,6 +36,7 @@
 //                    positions it did not keep.
 #include "sd_device.h"
 #include "sp_internal.h"
+#include "sd_exp.h"
 
 namespace sd {
 namespace {
@@ -54,18 +57,29 @@ struct PfScoreArgs {
   int W, Hq, G, nkb;
   double* S;       // [B][Hq][L][W] scores, key-major
   double* pmq;     // [B][Hq][nkb][W] each query's max over the block's visible keys
+  double* zb;      // [B][Hq][nkb][W] each query's sum of exp(scale (s - that max)) over them
+  double scale;
   uint32_t* status;
 };
 
 constexpr int kD = 128;
 constexpr int kKRow = kD + 8;  // padded bf16 row in LDS (elements)
 
+// 2^(j/64) for exp_nonpos, copied into LDS by the kernels that use it
+__constant__ double kExp2Tab[64] = {SD_EXP2_64_TABLE};
+__device__ __forceinline__ void load_exp_table(double* etab, int tid, int nt) {
+  for (int i = tid; i < 64; i += nt) etab[i] = kExp2Tab[i];
+}
+
 constexpr int kPfScoreBlocks = 4;  // key blocks per proxy-score workgroup (the window queries load once)
 
 __global__ __launch_bounds__(256) void k_pf_scores(PfScoreArgs a) {
   __shared__ uint16_t qs[kPfMaxWindow * kKRow];
   __shared__ uint16_t ks[kPfKeyBlock * kKRow];
-  __shared__ double wmax[4][kPfMaxWindow];
+  __shared__ double wmax[4][kPfMaxWindow], wz[4][kPfMaxWindow];
+  __shared__ double etab[64];
+  load_exp_table(etab, threadIdx.x, 256);  // read after the loop's first barrier
+  const ExpC ec = exp_consts();
   const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, n = lane & 15, c = lane >> 4;
   if (a.status && blockIdx.x == 0 && h == 0 && b == 0 && tid < 16) a.status[tid] = 0;
@@ -137,10 +151,30 @@ __global__ __launch_bounds__(256) void k_pf_scores(PfScoreArgs a) {
       if (c == 0) wmax[wave][qi] = m;
     }
     __syncthreads();  // every wave is done with ks and has its maxima in wmax
-    if (tid < a.W)
-      a.pmq[((int64_t(b) * a.Hq + h) * a.nkb + kb) * a.W + tid] =
-          fmax(fmax(wmax[0][tid], wmax[1][tid]), fmax(wmax[2][tid], wmax[3][tid]));
+    // each query's block max m (the waves' maxima), then its sum over the wave's visible keys of
+    // exp(scale s - scale m): keys c, c + 4, c + 8, c + 12 of the lane, then the lane groups
+    // (the same sum in every lane), then the waves in order
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int qi = 16 * t + n;
+      const double sm = a.scale * fmax(fmax(wmax[0][qi], wmax[1][qi]), fmax(wmax[2][qi], wmax[3][qi]));
+      double z = 0.0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t key = key0 + 16 * wave + c + 4 * v;
+        if (key < a.L && qi < a.W && key <= qpos0 + qi) z += exp_nonpos(a.scale * acc[t][v] - sm, etab, ec);
+      }
+      z += __shfl_xor(z, 16);
+      z += __shfl_xor(z, 32);
+      if (c == 0) wz[wave][qi] = z;
+    }
     if (kb + 1 < kbB) store();
+    __syncthreads();  // every wave's sums are in wz
+    if (tid < a.W) {
+      const int64_t o = ((int64_t(b) * a.Hq + h) * a.nkb + kb) * a.W + tid;
+      a.pmq[o] = fmax(fmax(wmax[0][tid], wmax[1][tid]), fmax(wmax[2][tid], wmax[3][tid]));
+      a.zb[o] = ((wz[0][tid] + wz[1][tid]) + wz[2][tid]) + wz[3][tid];
+    }
   }
 }
 
@@ -184,26 +218,35 @@ struct PfImpArgs {
   double scale;
 };
 
-// Per slab and window query: the sum over the slab's visible keys of exp(scale s - scale max), keys
-// in order within each of the 4 waves (a quarter of the slab each), the waves in order.
-__global__ __launch_bounds__(256) void k_pf_zpart(PfImpArgs a) {
-  const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int qi = tid & 63, wave = tid >> 6;
-  __shared__ double red[4][kPfMaxWindow];
-  const int64_t row = int64_t(b) * a.Hq + h;
-  const int64_t j0 = int64_t(sl) * kPfSlab, j1 = j0 + kPfSlab < a.L ? j0 + kPfSlab : a.L;
-  const int64_t per = (j1 - j0 + 3) / 4;
-  const int64_t ja = j0 + wave * per, jb = ja + per < j1 ? ja + per : j1;
-  double z = 0.0;
-  if (qi < a.W) {
-    const double mq = a.scale * a.M[row * a.W + qi];
-    const int64_t vis = a.L - a.W + qi;  // last visible key
-    const double* sp = a.S + row * a.L * a.W + qi;
-    for (int64_t j = ja; j < jb && j <= vis; ++j) z += exp(a.scale * sp[j * a.W] - mq);
-  }
-  red[wave][qi] = z;
+// Per slab and window query: the sum over the slab's key blocks, in order, of
+// z_b exp(scale m_b - scale max), z_b the block's sum of exp(scale s - scale m_b) over the query's
+// visible keys and m_b their max (a block with none has z_b = 0 and m_b = -inf and adds 0). Each
+// term is the block's sum of exp(scale s - scale max) up to the rounding of the two factors.
+__global__ __launch_bounds__(kPfMaxWindow) void k_pf_zslab(PfImpArgs a, const double* __restrict__ pmq,
+                                                           const double* __restrict__ zb, int nkb) {
+  constexpr int kBlocks = kPfSlab / kPfKeyBlock;  // key blocks per slab
+  static_assert(kPfSlab % kPfKeyBlock == 0, "slabs are whole key blocks");
+  const int sl = blockIdx.x, h = blockIdx.y, b = blockIdx.z, qi = threadIdx.x;
+  __shared__ double etab[64];
+  load_exp_table(etab, qi, kPfMaxWindow);
   __syncthreads();
-  if (tid < a.W) a.zq[(row * a.nslab + sl) * a.W + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  if (qi >= a.W) return;
+  const ExpC ec = exp_consts();
+  const int64_t row = int64_t(b) * a.Hq + h;
+  const double mq = a.scale * a.M[row * a.W + qi];
+  const int kb0 = sl * kBlocks;
+  double zv[kBlocks], mv[kBlocks];
+#pragma unroll
+  for (int u = 0; u < kBlocks; ++u) {
+    const int kb = kb0 + u < nkb ? kb0 + u : nkb - 1;
+    zv[u] = zb[(row * nkb + kb) * a.W + qi];
+    mv[u] = pmq[(row * nkb + kb) * a.W + qi];
+  }
+  double z = 0.0;
+#pragma unroll
+  for (int u = 0; u < kBlocks; ++u)
+    if (kb0 + u < nkb && zv[u] > 0.0) z += zv[u] * exp_nonpos(a.scale * mv[u] - mq, etab, ec);
+  a.zq[(row * a.nslab + sl) * a.W + qi] = z;
 }
 
 // Per key of the slab: importance = sum over the window queries, in order, of
@@ -214,6 +257,9 @@ __global__ __launch_bounds__(256) void k_pf_importance(PfImpArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   __shared__ double zs[kPfMaxWindow], ms[kPfMaxWindow];  // 1 / Z_q, scale x max_q
   __shared__ double rmax[4], rmin[4];
+  __shared__ double etab[64];
+  load_exp_table(etab, tid, 256);
+  const ExpC ec = exp_consts();
   const int64_t row = int64_t(b) * a.Hq + h;
   if (tid < a.W) {
     double z = 0.0;
@@ -240,10 +286,10 @@ __global__ __launch_bounds__(256) void k_pf_importance(PfImpArgs a) {
           sv[u + 1] = d2.y;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v += exp(a.scale * sv[u] - ms[q8 + u]) * zs[q8 + u];
+        for (int u = 0; u < 8; ++u) v += exp_nonpos(a.scale * sv[u] - ms[q8 + u], etab, ec) * zs[q8 + u];
       }
     } else {
-      for (int qi = qa; qi < a.W; ++qi) v += exp(a.scale * sp[qi] - ms[qi]) * zs[qi];
+      for (int qi = qa; qi < a.W; ++qi) v += exp_nonpos(a.scale * sp[qi] - ms[qi], etab, ec) * zs[qi];
     }
     a.imp[row * a.L + j] = v;
     mx = fmax(mx, v);
@@ -755,6 +801,8 @@ int launch_prefill_select(const PrefillPlan& p, const sp_tensors& t, char* ws, v
   s.nkb = p.nkb;
   s.S = at<double>(ws, p.o_S);
   s.pmq = at<double>(ws, p.o_pmq);
+  s.zb = at<double>(ws, p.o_zb);
+  s.scale = c.softmax_scale;
   s.status = status;
   hipLaunchKernelGGL(k_pf_scores, dim3((p.nkb + kPfScoreBlocks - 1) / kPfScoreBlocks, Hq, B), dim3(256), 0, st, s);
   hipLaunchKernelGGL(k_pf_rowmax, dim3(Hq, B), dim3(1024), 0, st, at<double>(ws, p.o_pmq), p.nkb, W, at<double>(ws, p.o_M));
@@ -770,7 +818,9 @@ int launch_prefill_select(const PrefillPlan& p, const sp_tensors& t, char* ws, v
   ia.Hq = Hq;
   ia.nslab = p.nslab;
   ia.scale = c.softmax_scale;
-  hipLaunchKernelGGL(k_pf_zpart, dim3(p.nslab, Hq, B), dim3(256), 0, st, ia);
+  hipLaunchKernelGGL(k_pf_zslab, dim3(p.nslab, Hq, B), dim3(kPfMaxWindow), 0, st, ia,
+                     static_cast<const double*>(at<double>(ws, p.o_pmq)), static_cast<const double*>(at<double>(ws, p.o_zb)),
+                     p.nkb);
   hipLaunchKernelGGL(k_pf_importance, dim3(p.nslab, Hq, B), dim3(256), 0, st, ia);
   hipLaunchKernelGGL(k_pf_global, dim3(p.nslab, B), dim3(256), 0, st, at<double>(ws, p.o_imp), t.head_mode, Hq, p.L,
                      p.nslab,

@@ -20,7 +20,7 @@ struct PrefillPlan {
   int64_t L, words;
   int64_t Lpad;        // L rounded up to kPfKeyTile: rows per head of the gathered K / V
   int32_t nslab, nkb;  // importance slabs, proxy-score key blocks
-  size_t o_status, o_S, o_pmq, o_M, o_zq, o_imp, o_pmax, o_pmin, o_gimp, o_gpmax, o_gpmin;
+  size_t o_status, o_S, o_pmq, o_zb, o_M, o_zq, o_imp, o_pmax, o_pmin, o_gimp, o_gpmax, o_gpmin;
   size_t o_long, o_bbits, o_budget, o_bits, o_list;
   size_t o_kvc;    // gathered K (bf16) then V (fp16, scaled) rows [B][Hq][Lpad][d]; shares the region of S
   size_t o_vmaxp;  // float [B][Hkv][nslab]: max |v| per slab of each KV head's rows
