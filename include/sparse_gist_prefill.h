@@ -15,12 +15,13 @@
  *     every query's visible keys are a prefix of the gists and a run of its own chunk's raw
  *     tokens; the kernel visits only the 64-key tiles that hold them.
  * Logits are softmax_scale * q . k (bf16 inputs, fp32 accumulation), softmax over the visible
- * keys, outputs fp32.
+ * keys, P.V in fp16 (see sparse_gist_prefill_attend), outputs fp32.
  *
  * Conventions are those of sparse_decode.h: tensors are DEVICE pointers owned by the caller,
  * calls only enqueue on `stream` and never synchronise, every argument check runs on the host
  * before anything is enqueued, and sparse_decode_last_error() reports the last failing call of
- * this thread. The path needs no workspace.
+ * this thread. The attention call takes a caller-owned device workspace of the size init reports
+ * (the library never allocates device memory).
  */
 #ifndef SPARSE_GIST_PREFILL_H
 #define SPARSE_GIST_PREFILL_H
