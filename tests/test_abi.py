@@ -333,3 +333,24 @@ def test_gist_attend_rejects_before_enqueue():
     assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), ws, None, 0x2000, None) == N.SD_EINVAL  # null out
     assert L.sparse_gist_prefill_attend(h, ctypes.byref(t), ws, 0x1000, 0x2008, None) == N.SD_EINVAL  # misaligned
     N.sparse_gist_prefill_destroy(h)
+
+
+def test_step_rejects_before_enqueue():
+    """The whole-step call checks its handle, workspace, tensors and outputs on the host before it
+    enqueues anything."""
+    L = N.lib()
+    t = N.sd_tensors()
+    h, _ = _init(**_params("c3s"))
+    assert L.sparse_decode_step(None, ctypes.byref(t), 256, 0x2000, 0x3000, None) == N.SD_EINVAL
+    assert L.sparse_decode_step(h, ctypes.byref(t), None, 0x2000, 0x3000, None) == N.SD_EWORKSPACE
+    assert L.sparse_decode_step(h, ctypes.byref(t), 0x104, 0x2000, 0x3000, None) == N.SD_EWORKSPACE
+    assert L.sparse_decode_step(h, None, 256, 0x2000, 0x3000, None) == N.SD_EINVAL
+    assert L.sparse_decode_step(h, ctypes.byref(t), 256, 0x2000, 0x3000, None) == N.SD_EINVAL
+    assert b"q must be" in L.sparse_decode_last_error()
+    t.q, t.q_sb, t.q_sh = 0x10000, 32 * 128, 128
+    t.kg, t.vg, t.g_st = 0x20000, 0x30000, 128
+    t.k, t.v, t.kv_st = 0x40000, 0x50000, 128
+    assert L.sparse_decode_step(h, ctypes.byref(t), 256, None, 0x3000, None) == N.SD_EINVAL
+    assert L.sparse_decode_step(h, ctypes.byref(t), 256, 0x2004, 0x3000, None) == N.SD_EINVAL
+    assert b"step: out" in L.sparse_decode_last_error()
+    N.sparse_decode_destroy(h)
