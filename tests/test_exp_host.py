@@ -75,3 +75,21 @@ def test_exp_nonpos_within_2ulp(tmp_path):
     i0 = len(x) - len(special)
     assert got[i0] == 1.0 and got[i0 + 1] == 1.0  # exp(0), exp(-0)
     assert np.all(tail == 0.0), tail
+
+
+def test_exp_table_is_the_generators():
+    """The 2^(j/64) table in sd_exp.h is the one gen_exp_table.py computes (each value correctly
+    rounded from a 60-digit decimal), and each entry is within half an ulp of 2^(j/64) in long
+    double arithmetic."""
+    import re
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("gen_exp_table", ROOT / "query_adaptive_sparse_amd" / "gen_exp_table.py")
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    text = (CSRC / "sd_exp.h").read_text()
+    body = text[text.index("#define SD_EXP2_64_TABLE"):text.index("namespace sd")]
+    vals = [float.fromhex(h) for h in re.findall(r"0x[0-9a-f.]+p[+-]\d+", body)]
+    assert vals == gen.table()
+    for j, v in enumerate(vals):
+        exact = np.power(np.longdouble(2), np.longdouble(j) / 64)
+        assert abs(np.longdouble(v) - exact) <= np.longdouble(np.spacing(v)) / 2, j
