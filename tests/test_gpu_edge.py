@@ -127,6 +127,14 @@ def test_attend_block_counts(blocks):
     _run(w, inp, attend_blocks=blocks)
 
 
+def test_attend_many_partials_per_group():
+    """One sequence with two KV groups cut into 4096 workgroups: about 2,000 partials per group,
+    more than the combine's 1024 threads, so it takes several rounds of lse values and partial rows."""
+    w = replace(configs.get("c3s"), name="c3s_two_groups", batch=1, kv_batch=1, n_q_heads=8, n_kv_heads=2)
+    inp = gen.make_inputs(w, device="cuda")
+    _run(w, inp, attend_blocks=4096)
+
+
 @pytest.mark.parametrize("kind", ["proxy_topp", "summary_topp", "topk"])
 def test_long_rows_all_tied(kind):
     """Long rows whose scores all tie: the crossing bin holds the whole row (more entries than the
