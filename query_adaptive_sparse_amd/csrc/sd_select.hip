@@ -943,15 +943,42 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
   const int64_t row = int64_t(b) * a.Hq + h;
   const int64_t t0 = int64_t(slab) * kLongBlock;
   const int64_t t1c = t0 + kLongBlock < a.len ? t0 + kLongBlock : a.len;  // the slab in the row
+  const bool local = (a.local_mask >> (h / a.G)) & 1;
+  uint32_t* bw = a.bits + row * a.words;
+  static_assert(NT == kBins1, "one lane per coarse bin in the crossing scan");
+  const uint16_t* br = a.cbin + row * a.cstride;
+  constexpr int kVec = kLongBlock / (NT * 8);  // 16-byte pieces per lane
+  // every load of the prologue goes out in one round, before the step's row length and the row's
+  // state are known: piece v of lane tid covers entries t0 + 8 * (tid + NT v) .. + 7 (pieces past
+  // the slab's capacity load its last piece again: rows are padded to a multiple of 8 entries;
+  // entries past the row's length are masked below), and lane tid's coarse bin total
+  uint4 pc[kVec];
+  unsigned long long th = 0, tl = 0;
+  uint32_t tcount = 0;
+  if (!local) {
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) {
+      int64_t e = t0 + 8 * (int64_t(tid) + NT * v);
+      const int64_t last = (t1c - 1) & ~int64_t(7);
+      e = e < last ? e : last;
+      pc[v] = ld16(br + e);
+    }
+    const int64_t o = row * kBins1 + tid;
+    if (a.topp) {
+      th = a.h1h[o];
+      tl = a.h1l[o];
+    } else {
+      tcount = a.h1c[o];
+    }
+  }
+  const int all0 = local ? 0 : a.info[row].all;
   const int64_t len = long_len(a, b);
   const int64_t t1 = t1c < len ? t1c : len;                              // its entries
-  uint32_t* bw = a.bits + row * a.words;
-  if (((a.local_mask >> (h / a.G)) & 1) || t1 <= t0) {
+  if (local || t1 <= t0) {
     for (int64_t w = (t0 >> 5) + tid; w < ((t1c + 31) >> 5); w += NT) bw[w] = 0u;
-    if (tid == 0 && t1 <= t0 && !((a.local_mask >> (h / a.G)) & 1)) a.ccnt[row * a.nb1 + slab] = 0;
+    if (tid == 0 && t1 <= t0 && !local) a.ccnt[row * a.nb1 + slab] = 0;
     return;
   }
-  static_assert(NT == kBins1, "one lane per coarse bin in the crossing scan");
   __shared__ int scnt, hit_bin;
   __shared__ double btot[NT / 64], hit_before;
   if (tid == 0) {
@@ -959,28 +986,14 @@ __global__ __launch_bounds__(kLongThreads) void k_long_mark(LongArgs a) {
     hit_bin = 0x7FFFFFFF;
   }
   __syncthreads();
-  const int all0 = a.info[row].all;
-  const uint16_t* br = a.cbin + row * a.cstride;
   uint8_t* bb = reinterpret_cast<uint8_t*>(bw);
   int32_t* out = a.cidx + (row * a.nb1 + slab) * kResolveCap;
   uint64_t* outk = a.ckey + (row * a.nb1 + slab) * kResolveCap;
   __shared__ int32_t cst[kResolveCap];  // the crossing bin's entries, staged
-  constexpr int kVec = kLongBlock / (NT * 8);  // 16-byte pieces per lane
-  // piece v of lane tid covers entries t0 + 8 * (tid + NT v) .. + 7; pieces past the slab load
-  // the slab's last piece again (rows are padded to a multiple of 8 entries) and are masked
-  uint4 pc[kVec];
-#pragma unroll
-  for (int v = 0; v < kVec; ++v) {
-    int64_t e = t0 + 8 * (int64_t(tid) + NT * v);
-    const int64_t last = (t1 - 1) & ~int64_t(7);
-    e = e < last ? e : last;
-    pc[v] = all0 ? make_uint4(0, 0, 0, 0) : ld16(br + e);
-  }
   bool all = all0;
   int bin1 = 0;
   if (!all0) {
-    const int64_t o = row * kBins1 + tid;
-    const double m = a.topp ? fix_value(a.h1h[o], a.h1l[o]) : double(a.h1c[o]);
+    const double m = a.topp ? fix_value(th, tl) : double(tcount);
     double Z;
     const double incl = block_scan<NT>(m, btot, &Z);
     const double target = a.topp ? a.p * Z : double(long_k(a, b));
@@ -1251,6 +1264,11 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
   if ((a.local_mask >> (h / a.G)) & 1) return;
   const int64_t row = int64_t(b) * a.Hq + h;
+  // the slabs' crossing-bin counts are loaded with the row's state and length (slabs past the
+  // step's length hold a count of 0, written by the marking pass)
+  const int per = (a.nb1 + kResolveThreads - 1) / kResolveThreads;  // slabs per thread
+  double local = 0.0;
+  for (int s = tid * per; s < min(a.nb1, tid * per + per); ++s) local += double(a.ccnt[row * a.nb1 + s]);
   const RowInfo ri = a.info[row];
   if (ri.all) return;
   __shared__ uint64_t keys[kResolveCap];
@@ -1271,12 +1289,10 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
   uint32_t* bw = a.bits + row * a.words;
   const int wexp = ri.wexp;
   const int64_t len = long_len(a, b);
-  const int nb = int((len + kLongBlock - 1) / kLongBlock);  // slabs holding entries
+  const int nb = a.nb1;
   // ---- the crossing bin's entry count over the slabs (slab s owns soff[s] .. soff[s+1] of the
   // gathered entries when they fit the buffer)
-  const int per = (nb + NT - 1) / NT;  // slabs per thread
-  double local = 0.0;
-  for (int s = tid * per; s < min(nb, tid * per + per); ++s) local += double(a.ccnt[row * a.nb1 + s]);
+  const int nthr = (nb + per - 1) / per;  // threads holding slabs
   double tot;
   const double incl = block_scan<NT>(local, wtot, &tot);
   if (tot > double(kResolveCap)) {
@@ -1299,8 +1315,8 @@ __global__ __launch_bounds__(kResolveThreads) void k_long_resolve(LongArgs a) {
     for (int k = 0; k < PER; ++k) {
       const int i = tid + NT * k;
       const int j = i < n ? i : n - 1;
-      // owner thread range: last thread u with soff[u] <= j
-      int lo = 0, hi = NT;
+      // owner thread range: last thread u with soff[u] <= j (threads past nthr hold no slab)
+      int lo = 0, hi = nthr;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (soff[mid] <= j) lo = mid; else hi = mid;
