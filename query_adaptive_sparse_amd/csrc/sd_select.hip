@@ -119,8 +119,8 @@ __device__ int block_first_crossing(int n, double base, double target, WF weight
 }
 
 // ---------------------------------------------------------------------------------------------
-// Selection of rows up to kSmallRowMax entries, fused with the GQA union and the compaction.
-// One 256-thread workgroup per (sequence, query head); the row lives in registers, at most
+// Selection of rows up to kSmallRowMax entries (the GQA union and the compaction follow in
+// k_union_small). One 256-thread workgroup per (sequence, query head); the row lives in registers, at most
 // kLaneEntries per lane:
 //   1. fp64 scores, their range and, for top-p, the masses w = exp(scale*s - scale*smax) and Z
 //      (fixed-order DPP reductions: every lane holds the same bits);
